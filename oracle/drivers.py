@@ -1,0 +1,244 @@
+"""Oracle-side runs of whole workloads, built from the eager recurrences.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+* plain decode: eager outputs for every step plus the exact index trace of a
+  commit every ``interval`` tokens (explainer, "Periodically commit a new
+  checkpoint");
+* speculative rounds: each round appends n drafts, the outputs at all n draft
+  positions come from a scratch continuation of the accepted state, then the
+  rejected suffix is dropped and a commit folds any sequence whose buffer has
+  reached ``commit_len`` (explainer, "Cheap speculative decoding rollback";
+  Abstract: rollback is a buffer-pointer operation, verification is
+  output-only);
+* low-precision emulation: a low-precision checkpoint serves the outputs and
+  is refreshed at each commit either from the high-precision state ("dual") or
+  from itself ("shared") (Abstract: "a low-precision checkpoint to serve output
+  computation ... while a higher-precision checkpoint serves recurrent
+  updates"; explainer, "Separate precisions for serving vs updating state").
+
+Because the eager recurrence started from any state S and run over the buffered
+inputs equals the replay from checkpoint S over the same inputs, serving from
+a checkpoint is emulated by a second eager state that is reset to the
+checkpoint's exact value at every commit.
+"""
+import numpy as np
+
+from . import (m2_eager, m2_recur, m2_decays, gdn_eager, bf16_encode,
+               bf16_decode, e4m3_quant_heads, e4m3_dequant_heads)
+from .index_model import IndexModel
+
+
+# ------------------------------------------------------------- plain decode --
+
+def decode_trace(batch, steps, interval, cap, t0_len=0):
+    """Index trace of plain decode: after each step, (pos, len) of every
+    sequence, with a commit right after the step that brings len to interval.
+    Returns (pos[T,b], len[T,b], committed[T] bool)."""
+    im = IndexModel(batch, cap)
+    im.len[:] = t0_len
+    pos = np.zeros((steps, batch), np.int64)
+    ln = np.zeros((steps, batch), np.int32)
+    com = np.zeros(steps, bool)
+    for t in range(steps):
+        im.append(1)
+        if (im.len >= interval).all():
+            im.commit()
+            com[t] = True
+        pos[t], ln[t] = im.snapshot()
+    return pos, ln, com
+
+
+def m2_decode(A, D, x, B, C, dt, h0, interval, cap):
+    """Plain Mamba-2 decode.  Returns dict(y, pos, len, committed, ckpt) where
+    ckpt is the exact state at the last commit (h0 if none)."""
+    h = np.array(h0, dtype=np.float64, copy=True)
+    T = x.shape[0]
+    pos, ln, com = decode_trace(x.shape[1], T, interval, cap)
+    y = np.empty(x.shape, np.float64)
+    ckpt = h.copy()
+    start = 0
+    for t in range(T):
+        if com[t] or t == T - 1:
+            y[start:t + 1] = m2_eager(A, D, x[start:t + 1], B[start:t + 1],
+                                      C[start:t + 1], dt[start:t + 1], h)
+            start = t + 1
+            if com[t]:
+                ckpt = h.copy()
+    return dict(y=y, pos=pos, len=ln, committed=com, ckpt=ckpt, state=h)
+
+
+def gdn_decode(q, k, v, alpha, beta, S0, interval, cap):
+    """Plain GDN decode; same return layout as m2_decode (o instead of y)."""
+    S = np.array(S0, dtype=np.float64, copy=True)
+    T = q.shape[0]
+    pos, ln, com = decode_trace(q.shape[1], T, interval, cap)
+    o = np.empty(v.shape, np.float64)
+    ckpt = S.copy()
+    start = 0
+    for t in range(T):
+        if com[t] or t == T - 1:
+            o[start:t + 1] = gdn_eager(q[start:t + 1], k[start:t + 1],
+                                       v[start:t + 1], alpha[start:t + 1],
+                                       beta[start:t + 1], S)
+            start = t + 1
+            if com[t]:
+                ckpt = S.copy()
+    return dict(o=o, pos=pos, len=ln, committed=com, ckpt=ckpt, state=S)
+
+
+# ------------------------------------------------------- speculative rounds --
+
+def m2_spec_rounds(A, D, h0, drafts, accept, cap, commit_len):
+    """Speculative verify / rollback rounds on Mamba-2.
+
+    drafts: dict x [R,n,b,H,P], B/C [R,n,b,G,N], dt [R,n,b,H]
+    accept: int [R,b], number of leading drafts kept in each round.
+    Returns dict(y [R,n,b,H,P], pos [R,b], len [R,b], committed [R,b],
+    status, state) -- indices after each round's commit.
+    """
+    x, B, C, dt = drafts["x"], drafts["B"], drafts["C"], drafts["dt"]
+    R, n, batch = x.shape[0], x.shape[1], x.shape[2]
+    h = np.array(h0, dtype=np.float64, copy=True)
+    im = IndexModel(batch, cap)
+    y = np.empty(x.shape, np.float64)
+    pos = np.zeros((R, batch), np.int64)
+    ln = np.zeros((R, batch), np.int32)
+    com = np.zeros((R, batch), bool)
+    for r in range(R):
+        ok = im.append(n)
+        if not ok.all():
+            raise ValueError("speculative round would overflow the ring")
+        # outputs at every draft position from a scratch copy of the state
+        scratch = h.copy()
+        y[r] = m2_eager(A, D, x[r], B[r], C[r], dt[r], scratch)
+        # keep the accepted prefix: advance the real state per accept count
+        acc = np.asarray(accept[r])
+        for a in range(1, n + 1):
+            sel = np.nonzero(acc == a)[0]
+            if sel.size == 0:
+                continue
+            hs = np.ascontiguousarray(h[sel])
+            m2_eager(A, D, x[r, :a][:, sel], B[r, :a][:, sel], C[r, :a][:, sel],
+                     dt[r, :a][:, sel], hs)
+            h[sel] = hs
+        im.rollback(n - acc)
+        com[r] = im.commit(min_len=commit_len)
+        pos[r], ln[r] = im.snapshot()
+    return dict(y=y, pos=pos, len=ln, committed=com, status=im.status, state=h)
+
+
+def gdn_spec_rounds(h0, drafts, accept, cap, commit_len):
+    """Speculative rounds on Gated DeltaNet; drafts: q,k [R,n,b,H,dk], v
+    [R,n,b,H,dv], alpha/beta [R,n,b,H].  Same return layout as m2_spec_rounds
+    with the outputs under "o"."""
+    q, k, v, al, be = (drafts[s] for s in ("q", "k", "v", "alpha", "beta"))
+    R, n, batch = q.shape[0], q.shape[1], q.shape[2]
+    S = np.array(h0, dtype=np.float64, copy=True)
+    im = IndexModel(batch, cap)
+    o = np.empty(v.shape, np.float64)
+    pos = np.zeros((R, batch), np.int64)
+    ln = np.zeros((R, batch), np.int32)
+    com = np.zeros((R, batch), bool)
+    for r in range(R):
+        ok = im.append(n)
+        if not ok.all():
+            raise ValueError("speculative round would overflow the ring")
+        scratch = S.copy()
+        o[r] = gdn_eager(q[r], k[r], v[r], al[r], be[r], scratch)
+        acc = np.asarray(accept[r])
+        for a in range(1, n + 1):
+            sel = np.nonzero(acc == a)[0]
+            if sel.size == 0:
+                continue
+            Ss = np.ascontiguousarray(S[sel])
+            gdn_eager(q[r, :a][:, sel], k[r, :a][:, sel], v[r, :a][:, sel],
+                      al[r, :a][:, sel], be[r, :a][:, sel], Ss)
+            S[sel] = Ss
+        im.rollback(n - acc)
+        com[r] = im.commit(min_len=commit_len)
+        pos[r], ln[r] = im.snapshot()
+    return dict(o=o, pos=pos, len=ln, committed=com, status=im.status, state=S)
+
+
+# ------------------------------------------------- low-precision emulation --
+
+def quantize(state_f32, lp):
+    """Quantise fp32 state tiles [..., R, C] to the low-precision copy.
+
+    Returns (codes, scale or None, exact fp64 value of the copy).
+    bf16: round-to-nearest-even per element.  e4m3: per-tile scale
+    amax/448 then E4M3(s/scale), saturating (OCP FP8 E4M3)."""
+    s = np.ascontiguousarray(state_f32, dtype=np.float32)
+    if lp == "bf16":
+        codes = bf16_encode(s)
+        return codes, None, bf16_decode(codes)
+    if lp == "e4m3":
+        lead, (r, c) = s.shape[:-2], s.shape[-2:]
+        scale, codes = e4m3_quant_heads(s.reshape(lead + (r * c,)))
+        val = e4m3_dequant_heads(scale, codes).reshape(s.shape)
+        return codes.reshape(s.shape), scale, val
+    raise ValueError(lp)
+
+
+def gdn_lowprec(q, k, v, alpha, beta, S0, interval, scheme, lp):
+    """GDN plain decode with a low-precision serving checkpoint.
+
+    scheme "dual": an fp32-class state receives every update; at each commit
+    the low-precision copy is re-quantised from it.  scheme "shared": the
+    low-precision copy is the only checkpoint; each commit folds the buffer
+    into its exact value and re-quantises the result.  In both, every step's
+    output is served from the low-precision copy plus the buffered inputs
+    (commit happens after the output of the step that fills the interval).
+    The state that is quantised is first rounded to fp32, the precision in
+    which a kernel holds it.
+
+    Returns dict(o_emul, o_exact, ckpt_exact [b,H,dv,dk] at the last commit,
+    codes, scale (last commit), commits (step indices)).
+    """
+    T = q.shape[0]
+    exact = np.array(S0, dtype=np.float64, copy=True)
+    codes, scale, val = quantize(exact.astype(np.float32), lp)
+    serve = val.copy()
+    o_emul = np.empty(v.shape, np.float64)
+    o_exact = np.empty(v.shape, np.float64)
+    ckpt_exact = exact.copy()
+    commits = []
+    start = 0
+    for t in range(T):
+        if (t + 1 - start) == interval or t == T - 1:
+            sl = slice(start, t + 1)
+            o_exact[sl] = gdn_eager(q[sl], k[sl], v[sl], alpha[sl], beta[sl], exact)
+            o_emul[sl] = gdn_eager(q[sl], k[sl], v[sl], alpha[sl], beta[sl], serve)
+            if (t + 1 - start) == interval:
+                src = exact if scheme == "dual" else serve
+                codes, scale, val = quantize(src.astype(np.float32), lp)
+                serve = val.copy()
+                ckpt_exact = exact.copy()
+                commits.append(t)
+            start = t + 1
+    return dict(o_emul=o_emul, o_exact=o_exact, ckpt_exact=ckpt_exact,
+                codes=codes, scale=scale, commits=commits, state=exact,
+                serve=serve)
+
+
+def gdn_carry_batched(q_t, ks, alphas, betas):
+    """Backward-carried query for many units at once.
+
+    q_t [U,dk]; ks [U,L,dk]; alphas, betas [U,L].  Returns (q_tilde [U,dk],
+    s [U,L]).  Same arithmetic as replay.gdn_carry, vectorised over units."""
+    q = np.array(q_t, dtype=np.float64, copy=True)
+    ks = np.asarray(ks, np.float64)
+    al = np.asarray(alphas, np.float64)
+    be = np.asarray(betas, np.float64)
+    L = ks.shape[1]
+    s = np.zeros(al.shape)
+    for i in range(L - 1, -1, -1):
+        s[:, i] = be[:, i] * np.einsum("ud,ud->u", ks[:, i], q)
+        q = al[:, i, None] * (q - s[:, i, None] * ks[:, i])
+    return q, s
+
+
+__all__ = ["decode_trace", "m2_decode", "gdn_decode", "m2_spec_rounds",
+           "gdn_spec_rounds", "quantize", "gdn_lowprec", "gdn_carry_batched",
+           "m2_recur", "m2_decays"]

@@ -1,0 +1,252 @@
+/*
+ * rssm.h -- C ABI of librssm.so, the ReplaySSM decode-time state engine for
+ * AMD MI355X (gfx950).
+ *
+ * Source of the method: "ReplaySSM: Cache SSM Inputs, Not State" (arXiv
+ * abstract, mlsanity.com index page) and the frontier.agentik-os.com
+ * explainer "ReplaySSM for hybrid SSM-Transformer stacks".  The state of a
+ * sequence is a checkpoint plus a ring buffer of the SSM inputs received
+ * since the checkpoint; outputs come from the checkpoint and a replay over
+ * the buffer, so the state is not written on ordinary steps; a periodic
+ * commit folds the buffer into a new checkpoint; speculative rollback only
+ * moves the buffer tail; verification computes draft outputs from one
+ * checkpoint read; a low-precision checkpoint may serve the output reads
+ * while an fp32 checkpoint alone receives the folds.
+ *
+ * Layer types: Mamba-2 (SSD) and Gated DeltaNet (GDN), the two the pages
+ * implement.  Their recurrences (not printed on the pages, which say so under
+ * "What is not documented"; textbook forms of the layers listed under
+ * "Builds on"):
+ *   Mamba-2, head h, group g = h*G/H:  a = exp(dt*A_h);
+ *       h_t = a h_{t-1} + dt x_t B_t^T  (P x N);   y_t = h_t C_t + D_h x_t
+ *   GDN, head h:  S_t = alpha S_{t-1} (I - beta k k^T) + beta v k^T  (dv x dk);
+ *       o_t = S_t q_t
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates and frees nothing, keeps no global state, and never
+ *    synchronises implicitly (except rssm_status, which says so).
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
+ *    null stream) and is asynchronous.  Calls on one layer must be ordered
+ *    on one stream; distinct layers may be driven concurrently.
+ *  - Row-major layouts, innermost index contiguous.  Tensors read or written
+ *    with 16-byte vector accesses must be 16-byte aligned (EALIGN otherwise).
+ *  - batch == 0 is valid: the call validates and returns RSSM_OK without
+ *    launching anything.
+ *  - Return codes (host-detected, returned before any launch, no side
+ *    effects) are the RSSM_E* values below.  Errors that depend on device
+ *    data (per-sequence buffer lengths) are reported through the layer's
+ *    sticky `status` word instead; the offending sequence is left unchanged
+ *    (no append, no index change) and its outputs are written as quiet NaN.
+ */
+#ifndef RSSM_H
+#define RSSM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RSSM_ABI_VERSION 1
+
+/* ---- host return codes ------------------------------------------------- */
+#define RSSM_OK            0
+#define RSSM_EINVAL       (-1) /* null pointer, bad enum, bad or inconsistent dims */
+#define RSSM_EUNSUPPORTED (-2) /* shape / scheme combination not instantiated     */
+#define RSSM_EALIGN       (-3) /* a 16-byte-accessed pointer is misaligned         */
+#define RSSM_ERANGE       (-4) /* n_pos < 1, n_pos > capacity, min_len < 0         */
+#define RSSM_EHIP         (-5) /* the HIP runtime reported a launch/copy error     */
+
+/* ---- sticky device status bits (layer->status[0]) ---------------------- */
+#define RSSM_STATUS_OVERFLOW  1u /* an append would exceed `capacity` entries       */
+#define RSSM_STATUS_ROLLBACK  2u /* n_reject < 0 or n_reject > len (past checkpoint)*/
+#define RSSM_STATUS_NONFINITE 4u /* non-finite state met while quantising           */
+
+typedef enum { RSSM_MAMBA2 = 1, RSSM_GDN = 2 } rssm_kind;
+
+/* Checkpoint precision scheme (explainer, "Separate precisions for serving vs
+ * updating state"; abstract: the low-precision copy serves outputs, the
+ * higher-precision checkpoint alone serves recurrent updates). */
+typedef enum {
+  RSSM_F32 = 0,    /* one fp32 checkpoint serves outputs and receives folds        */
+  RSSM_DUAL = 1,   /* ckpt_lp serves outputs; ckpt (fp32) alone receives folds;    */
+                   /* each commit re-quantises ckpt_lp from the new fp32 state     */
+  RSSM_SHARED = 2  /* ckpt_lp is the only checkpoint: outputs read it, commits     */
+                   /* fold from its dequantised value and re-quantise (comparator) */
+} rssm_scheme;
+
+typedef enum {
+  RSSM_LP_NONE = 0,
+  RSSM_BF16 = 1,   /* bfloat16, round to nearest even                              */
+  RSSM_E4M3 = 2    /* OCP FP8 E4M3 with one fp32 scale per (sequence, head):       */
+                   /* scale = amax|S|/448 (1 if amax == 0), code = E4M3(S/scale),  */
+                   /* saturating, round to nearest even; value = code * scale      */
+} rssm_lp;
+
+/*
+ * One SSM layer's state, all device memory owned by the caller.
+ *
+ * Dimensions
+ *   batch     sequences;  nheads  heads per sequence
+ *   ngroups   Mamba-2: groups sharing B and C (head h uses group h*ngroups/nheads,
+ *             nheads % ngroups == 0);  GDN: must be 1
+ *   dim_v     Mamba-2: headdim P;  GDN: dv  (rows of the state)
+ *   dim_k     Mamba-2: dstate N;   GDN: dk  (columns of the state)
+ *   capacity  ring slots per sequence (1..16); entry j since the checkpoint
+ *             lives in slot (ckpt_pos + j) % capacity
+ *   Instantiated: Mamba-2 P=64, N=128 (F32 scheme); GDN dk=dv=128 (all schemes).
+ *
+ * Checkpoints  [batch][nheads][dim_v][dim_k]
+ *   ckpt      fp32; required for F32 and DUAL, NULL for SHARED
+ *   ckpt_lp   uint16 bf16 bits or uint8 E4M3 codes; required for DUAL/SHARED
+ *   lp_scale  fp32 [batch][nheads]; required for E4M3
+ * Per-head parameters (Mamba-2 only): A[nheads] (negative decay rate),
+ *   D[nheads] (skip); NULL for GDN.
+ * Ring buffers (fp32)
+ *   Mamba-2: ring[0] = x  [batch][nheads][capacity][P]
+ *            ring[1] = B  [batch][ngroups][capacity][N]
+ *            ring[2] = dt [batch][nheads][capacity]      ring[3] unused (NULL)
+ *   GDN:     ring[0] = k  [batch][nheads][capacity][dk]
+ *            ring[1] = v  [batch][nheads][capacity][dv]
+ *            ring[2] = alpha, ring[3] = beta  [batch][nheads][capacity]
+ *   (C and q are not buffered: only the current token's output uses them.)
+ * Indices
+ *   ckpt_pos  int64 [batch]  absolute token position of the checkpoint
+ *   len       int32 [batch]  entries buffered since the checkpoint
+ *   arrive    uint32 [batch] scratch counters; must be zero before the first
+ *             call and are left zero by every call (the last workgroup of a
+ *             sequence to finish updates its indices)
+ *   status    uint32 [1]     sticky RSSM_STATUS_* bits
+ */
+typedef struct rssm_layer {
+  int32_t kind, scheme, lp_dtype;
+  int32_t batch, nheads, ngroups, dim_v, dim_k, capacity;
+  int32_t reserved0;
+  float* ckpt;
+  void* ckpt_lp;
+  float* lp_scale;
+  const float* A;
+  const float* D;
+  float* ring[4];
+  int64_t* ckpt_pos;
+  int32_t* len;
+  uint32_t* arrive;
+  uint32_t* status;
+} rssm_layer;
+
+/* Per-position inputs for rssm_verify / rssm_eager_step.  Unused members NULL.
+ * Mamba-2: x [n][batch][H][P], B and C [n][batch][G][N], dt [n][batch][H]
+ * GDN:     q, k [n][batch][H][dk], v [n][batch][H][dv], alpha, beta [n][batch][H]
+ * (n = n_pos for verify, 1 for eager_step). */
+typedef struct rssm_inputs {
+  const float *x, *B, *C, *dt;
+  const float *q, *k, *v, *alpha, *beta;
+} rssm_inputs;
+
+/*
+ * rssm_mamba2_step -- one decode token for every sequence of a Mamba-2 layer.
+ * Explainer "Compute outputs without eagerly updating the checkpoint": append
+ * the step's SSM input to the buffer, then compute the output from the
+ * checkpoint and a replay over the buffer; the checkpoint is not written.
+ *   y_t = Gamma_{c+1..t} h_c C_t + sum_i Gamma_{i+1..t} dt_i (B_i . C_t) x_i + D x_t
+ *   with Gamma_{m..n} = exp(A * sum_{j=m..n} dt_j), i over the buffered entries
+ *   including this one.
+ * x [batch][H][P], B and C [batch][G][N], dt [batch][H] (the discretisation
+ * step, already positive: no bias or softplus is applied); y [batch][H][P].
+ * commit_after != 0: after computing y, fold the whole buffer (this entry
+ * included) into the fp32 checkpoint in the same pass over the state and
+ * reset the buffer (explainer, "Periodically commit a new checkpoint").
+ * Per sequence, len + 1 > capacity sets RSSM_STATUS_OVERFLOW (y = NaN, no
+ * append).  Requires scheme RSSM_F32.
+ */
+int rssm_mamba2_step(const rssm_layer* L, const float* x, const float* B,
+                     const float* C, const float* dt, float* y,
+                     int commit_after, void* stream);
+
+/*
+ * rssm_gdn_step -- one decode token for every sequence of a GDN layer.
+ * Same contract as rssm_mamba2_step.  The output is formed by carrying the
+ * query backwards through the buffered entries (newest first):
+ *   s_i = beta_i (k_i . q);  q <- alpha_i (q - s_i k_i);   o_t = S_c q + sum_i s_i v_i
+ * q, k [batch][H][dk] (unit-norm is the caller's business), v [batch][H][dv],
+ * alpha, beta [batch][H]; o [batch][H][dv].
+ * Output reads use ckpt (F32) or ckpt_lp (DUAL, SHARED).  commit_after is
+ * supported for F32 only (RSSM_EUNSUPPORTED otherwise; use rssm_commit).
+ */
+int rssm_gdn_step(const rssm_layer* L, const float* q, const float* k,
+                  const float* v, const float* alpha, const float* beta,
+                  float* o, int commit_after, void* stream);
+
+/*
+ * rssm_commit -- fold buffers into new checkpoints (explainer, "Periodically
+ * commit a new checkpoint": apply the recurrence from the checkpoint across
+ * every buffered input, write the result as the new checkpoint, reset the
+ * buffer).  A sequence is folded when mask == NULL or mask[b] != 0, and
+ * len[b] >= min_len.  Then ckpt_pos += len, len = 0.
+ *   F32:    ckpt <- fold(ckpt)
+ *   DUAL:   ckpt <- fold(ckpt);  ckpt_lp <- Q(ckpt)      (fp32 alone is updated)
+ *   SHARED: ckpt_lp <- Q(fold(deQ(ckpt_lp)))
+ * A selected sequence with len == 0 keeps its fp32 state; under DUAL its
+ * low-precision copy is refreshed from fp32 (use min_len = 0 once to
+ * initialise ckpt_lp).  mask: device uint8 [batch] or NULL.
+ */
+int rssm_commit(const rssm_layer* L, const uint8_t* mask, int min_len,
+                void* stream);
+
+/*
+ * rssm_verify -- verification of n_pos draft tokens by their outputs alone
+ * (abstract; explainer "Cheap speculative decoding rollback": draft outputs
+ * are recomputed from the checkpoint and the buffered inputs, and no
+ * intermediate state is stored or reloaded).  Appends the n_pos draft
+ * inputs at entries len..len+n_pos-1 and writes, for every draft position j,
+ * the output the layer would produce after drafts 0..j, reading the
+ * checkpoint once.  No state is written; len += n_pos.
+ * in: see rssm_inputs (leading [n_pos]); out [n_pos][batch][H][dim_v].
+ * 1 <= n_pos <= min(8, capacity) (RSSM_ERANGE).  Per sequence,
+ * len + n_pos > capacity sets RSSM_STATUS_OVERFLOW (outputs NaN, no append).
+ * Mamba-2 (F32) and GDN (F32, DUAL, SHARED).
+ */
+int rssm_verify(const rssm_layer* L, int n_pos, const rssm_inputs* in,
+                float* out, void* stream);
+
+/*
+ * rssm_rollback -- reject the last n_reject[b] buffered entries of every
+ * sequence by moving the buffer tail: len -= n_reject (explainer, "Cheap
+ * speculative decoding rollback": rejecting k tokens only moves the tail
+ * back by k; the checkpoint is left as it was).
+ * Ring contents and checkpoints are not touched.  n_reject: device int32
+ * [batch].  n_reject < 0 or > len sets RSSM_STATUS_ROLLBACK and leaves that
+ * sequence unchanged.
+ */
+int rssm_rollback(const rssm_layer* L, const int32_t* n_reject, void* stream);
+
+/*
+ * rssm_eager_step -- the eager baseline the pages compare against (explainer,
+ * "What ReplaySSM is solving": read the entire state, update it with the
+ * current input, write it back, every step).  Reads and rewrites `ckpt` in
+ * place and writes the step output; rings, indices and ckpt_lp are ignored.
+ * in: one token (n = 1); out: y [batch][H][P] or o [batch][H][dv].
+ * Requires the fp32 checkpoint (scheme F32 or DUAL).
+ */
+int rssm_eager_step(const rssm_layer* L, const rssm_inputs* in, float* out,
+                    void* stream);
+
+/*
+ * rssm_status -- synchronise `stream`, copy the layer's sticky status word to
+ * *bits (host pointer), then clear it on the device.  Blocking.
+ */
+int rssm_status(const rssm_layer* L, uint32_t* bits, void* stream);
+
+/* Static description of a return code.  Never NULL. */
+const char* rssm_strerror(int code);
+
+/* RSSM_ABI_VERSION of the loaded library. */
+int rssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RSSM_H */

@@ -1,0 +1,74 @@
+"""Build librssm.so (the HIP kernels + C ABI) for gfx950 with hipcc.
+
+Usage: python -m linear_attention_decode_replayssm_amd.build [-v] [--isa]
+
+Each translation unit is compiled to an object in ``_build/`` (in parallel),
+then linked into ``librssm.so`` next to this file.  ``--isa`` additionally
+keeps the device assembly of every kernel under ``_build/isa/``.
+
+Packed fp32 instructions are disabled for all device code
+(``-target-feature -packed-fp32-ops``): the compiler would otherwise form
+them from ordinary float code.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INC = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "librssm.so")
+
+SOURCES = ["api.cpp", "m2_kernels.hip", "gdn_kernels.hip", "index_kernels.hip"]
+ARCH = "gfx950"
+
+
+def _hipcc():
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def _flags():
+    return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-function", "-I", INC, "-I", CSRC]
+
+
+def _compile(src, verbose, isa):
+    out_dir = BUILD
+    extra = []
+    if isa and src.endswith(".hip"):
+        out_dir = os.path.join(BUILD, "isa")
+        os.makedirs(out_dir, exist_ok=True)
+        extra = ["-save-temps=obj"]
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    lang = ["-x", "hip"] if src.endswith(".cpp") else []
+    cmd = [_hipcc()] + _flags() + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    if verbose and r.stderr.strip():
+        print(r.stderr, flush=True)
+    return obj
+
+
+def build(verbose: bool = False, isa: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose, isa), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv, isa="--isa" in sys.argv))

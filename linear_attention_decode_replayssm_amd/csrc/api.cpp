@@ -1,0 +1,267 @@
+// api.cpp -- the C ABI of librssm.so (declared in include/rssm.h): argument
+// validation, kernel dispatch on the caller's stream, error codes.
+//
+// Every entry point validates everything it can on the host before launching
+// anything; a non-zero return means nothing was enqueued.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rssm.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+inline bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_layer(const rssm_layer* L) {
+  if (!L) return RSSM_EINVAL;
+  if (L->kind != RSSM_MAMBA2 && L->kind != RSSM_GDN) return RSSM_EINVAL;
+  if (L->scheme < RSSM_F32 || L->scheme > RSSM_SHARED) return RSSM_EINVAL;
+  if (L->batch < 0 || L->nheads < 1 || L->ngroups < 1 || L->dim_v < 1 || L->dim_k < 1 ||
+      L->capacity < 1)
+    return RSSM_EINVAL;
+  if ((int64_t)L->batch * L->nheads > (int64_t)INT32_MAX) return RSSM_EUNSUPPORTED;
+  if (L->capacity > rssm::kMaxCap) return RSSM_EUNSUPPORTED;
+  if (L->kind == RSSM_MAMBA2) {
+    if (L->nheads % L->ngroups != 0) return RSSM_EINVAL;
+    if (L->dim_v != 64 || L->dim_k != 128) return RSSM_EUNSUPPORTED;
+    if (L->scheme != RSSM_F32) return RSSM_EUNSUPPORTED;
+  } else {
+    if (L->ngroups != 1) return RSSM_EINVAL;
+    if (L->dim_v != 128 || L->dim_k != 128) return RSSM_EUNSUPPORTED;
+    if (L->scheme != RSSM_F32 && L->lp_dtype != RSSM_BF16 && L->lp_dtype != RSSM_E4M3)
+      return RSSM_EINVAL;
+  }
+  // checkpoints
+  if (L->scheme != RSSM_SHARED) {
+    if (!L->ckpt) return RSSM_EINVAL;
+    if (!a16(L->ckpt)) return RSSM_EALIGN;
+  }
+  if (L->scheme != RSSM_F32) {
+    if (!L->ckpt_lp) return RSSM_EINVAL;
+    if (!a16(L->ckpt_lp)) return RSSM_EALIGN;
+    if (L->lp_dtype == RSSM_E4M3 && !L->lp_scale) return RSSM_EINVAL;
+  }
+  if (L->kind == RSSM_MAMBA2 && (!L->A || !L->D)) return RSSM_EINVAL;
+  return RSSM_OK;
+}
+
+// Rings and indices are needed by every call except the eager step.
+int check_state(const rssm_layer* L) {
+  const int nring = L->kind == RSSM_MAMBA2 ? 3 : 4;
+  for (int i = 0; i < nring; ++i)
+    if (!L->ring[i]) return RSSM_EINVAL;
+  if (!a16(L->ring[0]) || !a16(L->ring[1])) return RSSM_EALIGN;
+  if (!L->ckpt_pos || !L->len || !L->arrive || !L->status) return RSSM_EINVAL;
+  return RSSM_OK;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? RSSM_OK : RSSM_EHIP; }
+
+rssm::M2Args m2_args(const rssm_layer* L) {
+  rssm::M2Args a{};
+  a.ckpt = L->ckpt;
+  a.A = L->A;
+  a.D = L->D;
+  a.ring_x = L->ring[0];
+  a.ring_B = L->ring[1];
+  a.ring_dt = L->ring[2];
+  a.pos = L->ckpt_pos;
+  a.len = L->len;
+  a.arrive = L->arrive;
+  a.status = L->status;
+  a.batch = L->batch;
+  a.H = L->nheads;
+  a.G = L->ngroups;
+  a.cap = L->capacity;
+  a.n_pos = 1;
+  return a;
+}
+
+rssm::GdnArgs gdn_args(const rssm_layer* L) {
+  rssm::GdnArgs a{};
+  a.ckpt = L->ckpt;
+  a.ckpt_lp = L->ckpt_lp;
+  a.lp_scale = L->lp_scale;
+  a.ring_k = L->ring[0];
+  a.ring_v = L->ring[1];
+  a.ring_a = L->ring[2];
+  a.ring_b = L->ring[3];
+  a.pos = L->ckpt_pos;
+  a.len = L->len;
+  a.arrive = L->arrive;
+  a.status = L->status;
+  a.batch = L->batch;
+  a.H = L->nheads;
+  a.cap = L->capacity;
+  a.n_pos = 1;
+  a.scheme = L->scheme;
+  a.lp = L->lp_dtype;
+  return a;
+}
+
+inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int rssm_abi_version(void) { return RSSM_ABI_VERSION; }
+
+const char* rssm_strerror(int code) {
+  switch (code) {
+    case RSSM_OK: return "ok";
+    case RSSM_EINVAL: return "invalid argument (null pointer, bad enum or inconsistent dims)";
+    case RSSM_EUNSUPPORTED: return "shape or scheme not supported by this build";
+    case RSSM_EALIGN: return "pointer not 16-byte aligned";
+    case RSSM_ERANGE: return "count out of range";
+    case RSSM_EHIP: return "HIP runtime error";
+    default: return "unknown error code";
+  }
+}
+
+int rssm_mamba2_step(const rssm_layer* L, const float* x, const float* B, const float* C,
+                     const float* dt, float* y, int commit_after, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (L->kind != RSSM_MAMBA2) return RSSM_EINVAL;
+  if ((rc = check_state(L))) return rc;
+  if (!x || !B || !C || !dt || !y) return RSSM_EINVAL;
+  if (!a16(x) || !a16(B) || !a16(C) || !a16(y)) return RSSM_EALIGN;
+  if (L->batch == 0) return RSSM_OK;
+  rssm::M2Args a = m2_args(L);
+  a.x = x;
+  a.B = B;
+  a.C = C;
+  a.dt = dt;
+  a.y = y;
+  return hip_rc(rssm::launch_m2_step(a, commit_after != 0, S(stream)));
+}
+
+int rssm_gdn_step(const rssm_layer* L, const float* q, const float* k, const float* v,
+                  const float* alpha, const float* beta, float* o, int commit_after,
+                  void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (L->kind != RSSM_GDN) return RSSM_EINVAL;
+  if ((rc = check_state(L))) return rc;
+  if (!q || !k || !v || !alpha || !beta || !o) return RSSM_EINVAL;
+  if (!a16(q) || !a16(k) || !a16(v) || !a16(o)) return RSSM_EALIGN;
+  if (commit_after && L->scheme != RSSM_F32) return RSSM_EUNSUPPORTED;
+  if (L->batch == 0) return RSSM_OK;
+  rssm::GdnArgs a = gdn_args(L);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.o = o;
+  return hip_rc(rssm::launch_gdn_step(a, commit_after != 0, S(stream)));
+}
+
+int rssm_commit(const rssm_layer* L, const uint8_t* mask, int min_len, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if ((rc = check_state(L))) return rc;
+  if (min_len < 0) return RSSM_ERANGE;
+  if (L->batch == 0) return RSSM_OK;
+  if (L->kind == RSSM_MAMBA2) {
+    rssm::M2Args a = m2_args(L);
+    a.mask = mask;
+    a.min_len = min_len;
+    return hip_rc(rssm::launch_m2_commit(a, S(stream)));
+  }
+  rssm::GdnArgs a = gdn_args(L);
+  a.mask = mask;
+  a.min_len = min_len;
+  return hip_rc(rssm::launch_gdn_commit(a, S(stream)));
+}
+
+int rssm_verify(const rssm_layer* L, int n_pos, const rssm_inputs* in, float* out,
+                void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if ((rc = check_state(L))) return rc;
+  if (!in || !out) return RSSM_EINVAL;
+  if (n_pos < 1 || n_pos > L->capacity || n_pos > rssm::kMaxPos) return RSSM_ERANGE;
+  if (!a16(out)) return RSSM_EALIGN;
+  if (L->kind == RSSM_MAMBA2) {
+    if (!in->x || !in->B || !in->C || !in->dt) return RSSM_EINVAL;
+    if (!a16(in->x) || !a16(in->B) || !a16(in->C)) return RSSM_EALIGN;
+    if (L->batch == 0) return RSSM_OK;
+    rssm::M2Args a = m2_args(L);
+    a.x = in->x;
+    a.B = in->B;
+    a.C = in->C;
+    a.dt = in->dt;
+    a.y = out;
+    a.n_pos = n_pos;
+    return hip_rc(rssm::launch_m2_verify(a, S(stream)));
+  }
+  if (!in->q || !in->k || !in->v || !in->alpha || !in->beta) return RSSM_EINVAL;
+  if (!a16(in->q) || !a16(in->k) || !a16(in->v)) return RSSM_EALIGN;
+  if (L->batch == 0) return RSSM_OK;
+  rssm::GdnArgs a = gdn_args(L);
+  a.q = in->q;
+  a.k = in->k;
+  a.v = in->v;
+  a.alpha = in->alpha;
+  a.beta = in->beta;
+  a.o = out;
+  a.n_pos = n_pos;
+  return hip_rc(rssm::launch_gdn_verify(a, S(stream)));
+}
+
+int rssm_rollback(const rssm_layer* L, const int32_t* n_reject, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if ((rc = check_state(L))) return rc;
+  if (!n_reject) return RSSM_EINVAL;
+  if (L->batch == 0) return RSSM_OK;
+  return hip_rc(rssm::launch_rollback(L->ckpt_pos, L->len, L->status, n_reject, L->batch,
+                                      S(stream)));
+}
+
+int rssm_eager_step(const rssm_layer* L, const rssm_inputs* in, float* out, void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (!in || !out) return RSSM_EINVAL;
+  if (L->scheme == RSSM_SHARED) return RSSM_EUNSUPPORTED;
+  if (!a16(out)) return RSSM_EALIGN;
+  if (L->kind == RSSM_MAMBA2) {
+    if (!in->x || !in->B || !in->C || !in->dt) return RSSM_EINVAL;
+    if (!a16(in->x) || !a16(in->B) || !a16(in->C)) return RSSM_EALIGN;
+    if (L->batch == 0) return RSSM_OK;
+    rssm::M2Args a = m2_args(L);
+    a.x = in->x;
+    a.B = in->B;
+    a.C = in->C;
+    a.dt = in->dt;
+    a.y = out;
+    return hip_rc(rssm::launch_m2_eager(a, S(stream)));
+  }
+  if (!in->q || !in->k || !in->v || !in->alpha || !in->beta) return RSSM_EINVAL;
+  if (!a16(in->q) || !a16(in->k) || !a16(in->v)) return RSSM_EALIGN;
+  if (L->batch == 0) return RSSM_OK;
+  rssm::GdnArgs a = gdn_args(L);
+  a.q = in->q;
+  a.k = in->k;
+  a.v = in->v;
+  a.alpha = in->alpha;
+  a.beta = in->beta;
+  a.o = out;
+  return hip_rc(rssm::launch_gdn_eager(a, S(stream)));
+}
+
+int rssm_status(const rssm_layer* L, uint32_t* bits, void* stream) {
+  if (!L || !L->status || !bits) return RSSM_EINVAL;
+  uint32_t h = 0;
+  hipError_t e = hipMemcpyAsync(&h, L->status, sizeof(uint32_t), hipMemcpyDeviceToHost, S(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(S(stream));
+  if (e != hipSuccess) return RSSM_EHIP;
+  *bits = h;
+  return hip_rc(rssm::launch_clear_status(L->status, S(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,176 @@
+// common.hpp -- device helpers shared by the gfx950 kernels of librssm.
+//
+// Wave64 cross-lane reductions, 16-byte streaming loads/stores, the
+// workgroup -> tile mapping across the MI355X's 8 XCDs, and the per-sequence
+// "last workgroup updates the indices" protocol.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rssm {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxCap = 16;   // ring slots per sequence
+constexpr int kMaxPos = 8;    // draft positions per verify call
+
+constexpr uint32_t kStatusOverflow = 1u;
+constexpr uint32_t kStatusRollback = 2u;
+constexpr uint32_t kStatusNonfinite = 4u;
+
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+// ---- memory ---------------------------------------------------------------
+// The checkpoint is streamed once per step and not reused by this kernel:
+// nontemporal loads keep it from evicting the ring entries and inputs that
+// the other heads of the same sequence re-read from L2.
+__device__ __forceinline__ f32x4 ld_nt(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ u32x4 ld_nt_u(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st_nt(float* p, f32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+__device__ __forceinline__ void st_nt_u(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ f32x4 ld4(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+__device__ __forceinline__ void st4(float* p, f32x4 v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) {
+  return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+}
+
+// ---- workgroup -> tile ----------------------------------------------------
+// Consecutive workgroup ids are dispatched round-robin over the 8 XCDs, each
+// with its own L2.  Remap so that every XCD receives one contiguous range of
+// tiles: the heads of one sequence (and the heads of one Mamba-2 group, which
+// share B and C) then land on the same XCD and share its L2.
+__device__ __forceinline__ int tile_index() {
+  const int id = blockIdx.x, n = gridDim.x;
+  if ((n & 7) == 0) return (id & 7) * (n >> 3) + (id >> 3);
+  return id;
+}
+
+// ---- transposed cross-lane reduction --------------------------------------
+// Each lane holds C partial sums; the LPR lanes that differ only in lane bits
+// below log2(LPR) share a row.  Going from the highest of those bits down, a
+// lane keeps the half of its values that its bit selects and adds the
+// partner's copy of that half, so V values cost V-1 shuffles instead of
+// V*log2(LPR).  Once one value is left, the remaining bits are plain
+// butterflies.
+template <int C, int M>
+struct XRed {
+  static __device__ __forceinline__ void run(float* v, int lane) {
+    if constexpr (M == 0) {
+      return;
+    } else if constexpr (C > 1) {
+      const bool up = (lane & M) != 0;
+#pragma unroll
+      for (int j = 0; j < C / 2; ++j) {
+        const float send = up ? v[j] : v[j + C / 2];
+        const float keep = up ? v[j + C / 2] : v[j];
+        v[j] = keep + __shfl_xor(send, M);
+      }
+      XRed<C / 2, M / 2>::run(v, lane);
+    } else {
+      v[0] += __shfl_xor(v[0], M);
+      XRed<1, M / 2>::run(v, lane);
+    }
+  }
+};
+
+// Index bookkeeping for XRed<V, LPR/2>: after the reduction a lane holds
+// VOUT complete sums; value j of lane `lane` is the sum of original index
+// index(lane, j).  Lanes that differ only in the low BFLY bits hold equal
+// results; writer() picks one of them.
+template <int V, int LPR>
+struct XMap {
+  static constexpr int kLogL = ilog2(LPR);
+  static constexpr int kLogV = ilog2(V);
+  static constexpr int VOUT = V > LPR ? V / LPR : 1;
+  static constexpr int BFLY = kLogL > kLogV ? kLogL - kLogV : 0;
+  static __device__ __forceinline__ int index(int lane, int j) {
+    int idx = j, c = V;
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) {
+      if (c > 1) {
+        if (lane & m) idx += c / 2;
+        c /= 2;
+      }
+    }
+    return idx;
+  }
+  static __device__ __forceinline__ bool writer(int lane) {
+    return (lane & ((1 << BFLY) - 1)) == 0;
+  }
+};
+
+template <int V, int LPR>
+__device__ __forceinline__ void xreduce(float (&v)[V], int lane) {
+  XRed<V, LPR / 2>::run(v, lane);
+}
+
+// Full butterfly: every lane of each LPR-lane group ends with all V sums.
+template <int V, int LPR>
+__device__ __forceinline__ void allreduce(float (&v)[V]) {
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) v[j] += __shfl_xor(v[j], m);
+  }
+}
+
+// ---- per-sequence index update --------------------------------------------
+// Every workgroup of sequence b reads len[b]/ckpt_pos[b] at its start and has
+// consumed the values (they shaped all of its work) before it reaches this
+// point.  At its end it counts itself in arrive[b]; the workgroup that
+// completes the count knows that all `nwg` workgroups of the sequence have
+// read the indices, resets the counter and applies the update.  Nothing in
+// this launch reads the indices afterwards and the next launch sees them
+// through the kernel boundary, so the counter needs no fence: a relaxed
+// device-scope atomic.  (A device-scope fence here would write back and
+// invalidate the XCD's L2 once per workgroup.)  Must be reached by all
+// threads.
+struct IndexUpdate {
+  int64_t pos_add;
+  int32_t new_len;
+  bool apply;
+};
+
+__device__ __forceinline__ void arrive_and_update(uint32_t* arrive, int64_t* pos,
+                                                  int32_t* len, int b, int nwg,
+                                                  IndexUpdate u) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old =
+        __hip_atomic_fetch_add(&arrive[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == (uint32_t)(nwg - 1)) {
+      __hip_atomic_store(&arrive[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (u.apply) {
+        pos[b] += u.pos_add;
+        len[b] = u.new_len;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bits) {
+  atomicOr(status, bits);
+}
+
+__device__ __forceinline__ int ring_slot(int slot0, int i, int cap) {
+  int s = slot0 + i;
+  return s >= cap ? s - cap : s;
+}
+
+}  // namespace rssm

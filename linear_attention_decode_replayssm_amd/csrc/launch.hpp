@@ -1,0 +1,69 @@
+// launch.hpp -- internal interface between the C ABI (api.cpp) and the
+// kernel translation units.  Not installed; the public ABI is include/rssm.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rssm {
+
+// Mamba-2 replay/eager/commit/verify arguments.  Pointers as in rssm.h.
+struct M2Args {
+  float* ckpt;          // [b][H][P][N]
+  const float* A;       // [H]
+  const float* D;       // [H]
+  float* ring_x;        // [b][H][cap][P]
+  float* ring_B;        // [b][G][cap][N]
+  float* ring_dt;       // [b][H][cap]
+  int64_t* pos;
+  int32_t* len;
+  uint32_t* arrive;
+  uint32_t* status;
+  const float* x;       // [n][b][H][P]
+  const float* B;       // [n][b][G][N]
+  const float* C;       // [n][b][G][N]
+  const float* dt;      // [n][b][H]
+  float* y;             // [n][b][H][P]
+  const uint8_t* mask;  // commit only
+  int batch, H, G, cap, n_pos, min_len;
+};
+
+// Gated DeltaNet arguments.
+struct GdnArgs {
+  float* ckpt;          // fp32 [b][H][dv][dk] (NULL under SHARED)
+  void* ckpt_lp;        // bf16 / e4m3 codes (NULL under F32)
+  float* lp_scale;      // [b][H] (E4M3)
+  float* ring_k;        // [b][H][cap][dk]
+  float* ring_v;        // [b][H][cap][dv]
+  float* ring_a;        // [b][H][cap]
+  float* ring_b;        // [b][H][cap]
+  int64_t* pos;
+  int32_t* len;
+  uint32_t* arrive;
+  uint32_t* status;
+  const float* q;       // [n][b][H][dk]
+  const float* k;       // [n][b][H][dk]
+  const float* v;       // [n][b][H][dv]
+  const float* alpha;   // [n][b][H]
+  const float* beta;    // [n][b][H]
+  float* o;             // [n][b][H][dv]
+  const uint8_t* mask;
+  int batch, H, cap, n_pos, min_len;
+  int scheme, lp;       // rssm_scheme / rssm_lp values
+};
+
+hipError_t launch_m2_step(const M2Args& a, bool fused, hipStream_t s);
+hipError_t launch_m2_commit(const M2Args& a, hipStream_t s);
+hipError_t launch_m2_verify(const M2Args& a, hipStream_t s);
+hipError_t launch_m2_eager(const M2Args& a, hipStream_t s);
+
+hipError_t launch_gdn_step(const GdnArgs& a, bool fused, hipStream_t s);
+hipError_t launch_gdn_commit(const GdnArgs& a, hipStream_t s);
+hipError_t launch_gdn_verify(const GdnArgs& a, hipStream_t s);
+hipError_t launch_gdn_eager(const GdnArgs& a, hipStream_t s);
+
+hipError_t launch_rollback(int64_t* pos, int32_t* len, uint32_t* status,
+                           const int32_t* n_reject, int batch, hipStream_t s);
+hipError_t launch_clear_status(uint32_t* status, hipStream_t s);
+
+}  // namespace rssm

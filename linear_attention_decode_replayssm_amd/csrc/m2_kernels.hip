@@ -1,0 +1,481 @@
+// m2_kernels.hip -- Mamba-2 (SSD) decode kernels for gfx950.
+//
+// State tile of one (sequence, head): h_c[P=64][N=128] fp32, 32 KiB.
+// One 256-thread workgroup (4 wave64) per tile; 20,480 tiles at batch 256 x
+// 80 heads.  Thread t owns float4 column c4 = t % 32 of rows r0 + 8k,
+// r0 = t / 32, k = 0..7: every load instruction of the workgroup reads 4 KiB
+// of consecutive bytes (1 KiB per wavefront).
+//
+// Replay step (ReplaySSM abstract; explainer "Compute outputs without eagerly
+// updating the checkpoint"), with Gamma_{m..n} = exp(A * sum_{j=m..n} dt_j):
+//   y_t = Gamma_{c+1..t} h_c C_t + sum_i Gamma_{i+1..t} dt_i (B_i . C_t) x_i + D x_t
+// The checkpoint loads are issued first; the replay prologue (B_i . C_t dots,
+// dt suffix sums, decay weights, the sum over buffered x_i) runs while they
+// are in flight; then each row is dotted with C_t and reduced across the 32
+// lanes that hold it.  The checkpoint is not written.
+//
+// Commit (explainer, "Periodically commit a new checkpoint"), a rank-L update:
+//   h <- Gamma_{c+1..t} h_c + sum_i Gamma_{i+1..t} dt_i x_i B_i^T
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace rssm {
+namespace {
+
+constexpr int P = 64;
+constexpr int N = 128;
+constexpr int NT = 256;
+constexpr int LPR = N / 4;     // lanes sharing one state row (one float4 each)
+constexpr int RPL = NT / LPR;  // state rows covered by one workgroup-wide load
+constexpr int NLD = P / RPL;   // float4 loads per thread for the whole tile
+constexpr int QD = NT / P;     // thread groups splitting the buffered-entry sum
+static_assert(LPR <= 64 && 64 % LPR == 0, "a state row must sit in one wave");
+static_assert(P % RPL == 0 && NT % P == 0, "tile geometry");
+
+struct Geo {
+  int b, h, g, tid, lane, c4, r0;
+  long unit, gunit;
+};
+
+__device__ __forceinline__ Geo geometry(const M2Args& a) {
+  Geo q;
+  const int tile = tile_index();
+  q.b = tile / a.H;
+  q.h = tile - q.b * a.H;
+  q.g = q.h / (a.H / a.G);
+  q.tid = threadIdx.x;
+  q.lane = q.tid & 63;
+  q.c4 = q.tid % LPR;
+  q.r0 = q.tid / LPR;
+  q.unit = (long)q.b * a.H + q.h;
+  q.gunit = (long)q.b * a.G + q.g;
+  return q;
+}
+
+__device__ __forceinline__ void load_tile(const float* ck, const Geo& q, f32x4 (&hv)[NLD]) {
+#pragma unroll
+  for (int k = 0; k < NLD; ++k) hv[k] = ld_nt(ck + (k * RPL + q.r0) * N + q.c4 * 4);
+}
+
+__device__ __forceinline__ void store_tile(float* ck, const Geo& q, const f32x4 (&hv)[NLD]) {
+#pragma unroll
+  for (int k = 0; k < NLD; ++k) st_nt(ck + (k * RPL + q.r0) * N + q.c4 * 4, hv[k]);
+}
+
+// ---------------------------------------------------------------- step ----
+// Load order matters: vector loads complete in issue order, so every small
+// load the replay prologue needs (B_i and C_t segments, dt_i, x_i) is issued
+// before the 32 KiB checkpoint stream.  Waiting for them then leaves the
+// stream in flight while the prologue runs.  The ring append is done last,
+// after the stream has been consumed.
+template <bool FUSED>
+__global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
+  const Geo q = geometry(a);
+  const int cap = a.cap;
+  float* ck = a.ckpt + q.unit * (P * N);
+
+  const int len = a.len[q.b];
+  const int64_t pos = a.pos[q.b];
+  const bool ok = len < cap;
+  const int L = len + 1;
+  const int slot0 = (int)(pos % cap);
+  const float Ah = a.A[q.h];
+  const float Dh = a.D[q.h];
+
+  const float* xt = a.x + q.unit * P;
+  const float* Bt = a.B + q.gunit * N;
+  const float* Ct = a.C + q.gunit * N;
+  auto xsrc = [&](int i) -> const float* {
+    return i < len ? a.ring_x + (q.unit * cap + ring_slot(slot0, i, cap)) * P : xt;
+  };
+  auto Bsrc = [&](int i) -> const float* {
+    return i < len ? a.ring_B + (q.gunit * cap + ring_slot(slot0, i, cap)) * N : Bt;
+  };
+
+  // prologue operands: entry ei = tid/16 dots segment sg of B_ei with C_t;
+  // thread (p, qd) sums entries qd, qd+QD, ... of x_i[p]
+  constexpr int SEG = N / 16;
+  constexpr int XPT = kMaxCap / QD;  // buffered x values per thread
+  const int ei = q.tid >> 4, sg = q.tid & 15;
+  const int p = q.tid % P, qd = q.tid / P;
+  f32x4 bseg[SEG / 4], cseg[SEG / 4];
+  float dti = 0.f;
+  float xv[XPT];
+  if (ok) {
+#pragma unroll
+    for (int e = 0; e < SEG / 4; ++e) {
+      bseg[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+      cseg[e] = ld4(Ct + sg * SEG + 4 * e);
+    }
+    if (ei < L) {
+#pragma unroll
+      for (int e = 0; e < SEG / 4; ++e) bseg[e] = ld4(Bsrc(ei) + sg * SEG + 4 * e);
+      if (sg == 0)
+        dti = ei < len ? a.ring_dt[q.unit * cap + ring_slot(slot0, ei, cap)] : a.dt[q.unit];
+    }
+#pragma unroll
+    for (int m = 0; m < XPT; ++m) {
+      const int i = qd + m * QD;
+      xv[m] = i < L ? xsrc(i)[p] : 0.f;
+    }
+  }
+  const f32x4 cdot = ld4(Ct + q.c4 * 4);
+
+  f32x4 hv[NLD];
+  load_tile(ck, q, hv);
+
+  __shared__ float s_e[kMaxCap], s_dt[kMaxCap], s_w[kMaxCap], s_fw[kMaxCap];
+  __shared__ float s_gamma;
+  __shared__ float s_yb[QD][P];
+
+  if (ok) {
+    {  // e_i = B_i . C_t
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < SEG / 4; ++e) part += dot4(bseg[e], cseg[e]);
+      part += __shfl_xor(part, 8);
+      part += __shfl_xor(part, 4);
+      part += __shfl_xor(part, 2);
+      part += __shfl_xor(part, 1);
+      if (sg == 0 && ei < L) {
+        s_e[ei] = part;
+        s_dt[ei] = dti;
+      }
+    }
+    __syncthreads();
+    if (q.tid < L) {  // decay weights from dt suffix sums
+      float suf = 0.f;
+      for (int j = q.tid + 1; j < L; ++j) suf += s_dt[j];
+      const float dec = expf(Ah * suf);
+      s_w[q.tid] = dec * s_dt[q.tid] * s_e[q.tid];
+      if (FUSED) s_fw[q.tid] = dec * s_dt[q.tid];
+      if (q.tid == 0) s_gamma = expf(Ah * (suf + s_dt[0]));
+    }
+    __syncthreads();
+    {  // sum_i w_i x_i[p]
+      float yb = 0.f;
+#pragma unroll
+      for (int m = 0; m < XPT; ++m) {
+        const int i = qd + m * QD;
+        if (i < L) yb += s_w[i] * xv[m];
+      }
+      s_yb[qd][p] = yb;
+    }
+  }
+
+  {  // Gamma * (h_c C_t) + buffered part + D x_t
+    float d[NLD];
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) d[k] = dot4(hv[k], cdot);
+    xreduce<NLD, LPR>(d, q.lane);
+    __syncthreads();
+    using M = XMap<NLD, LPR>;
+    if (M::writer(q.lane)) {
+      const int pr = M::index(q.lane, 0) * RPL + q.r0;
+      float yv;
+      if (ok) {
+        float yb = 0.f;
+#pragma unroll
+        for (int j = 0; j < QD; ++j) yb += s_yb[j][pr];
+        yv = s_gamma * d[0] + yb + Dh * xt[pr];
+      } else {
+        yv = __builtin_nanf("");
+      }
+      a.y[q.unit * P + pr] = yv;
+    }
+  }
+
+  if constexpr (FUSED) {
+    if (ok) {  // fold the whole buffer, this entry included, and store
+      __shared__ __attribute__((aligned(16))) float s_x[kMaxCap][P];
+      __shared__ __attribute__((aligned(16))) float s_B[kMaxCap][N];
+      for (int idx = q.tid; idx < L * P; idx += NT) s_x[idx / P][idx % P] = xsrc(idx / P)[idx % P];
+      for (int idx = q.tid; idx < L * N; idx += NT) s_B[idx / N][idx % N] = Bsrc(idx / N)[idx % N];
+      __syncthreads();
+      const float gam = s_gamma;
+#pragma unroll
+      for (int k = 0; k < NLD; ++k) hv[k] *= gam;
+      for (int i = 0; i < L; ++i) {
+        const f32x4 bi = ld4(&s_B[i][q.c4 * 4]);
+        const float w = s_fw[i];
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) hv[k] += (w * s_x[i][k * RPL + q.r0]) * bi;
+      }
+      store_tile(ck, q, hv);
+    }
+  } else {
+    if (ok) {  // append this step's entry to the ring
+      const int s = ring_slot(slot0, len, cap);
+      if (q.tid < P) a.ring_x[(q.unit * cap + s) * P + q.tid] = xt[q.tid];
+      if (q.tid == 0) a.ring_dt[q.unit * cap + s] = a.dt[q.unit];
+      if ((q.h % (a.H / a.G)) == 0 && q.tid < N)
+        a.ring_B[(q.gunit * cap + s) * N + q.tid] = Bt[q.tid];
+    }
+  }
+
+  IndexUpdate u;
+  u.apply = ok;
+  u.pos_add = FUSED ? L : 0;
+  u.new_len = FUSED ? 0 : L;
+  arrive_and_update(a.arrive, a.pos, a.len, q.b, a.H, u);
+  if (!ok && q.tid == 0) raise_status(a.status, kStatusOverflow);
+}
+
+// -------------------------------------------------------------- commit ----
+__global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
+  const Geo q = geometry(a);
+  const int cap = a.cap;
+  const int len = a.len[q.b];
+  const bool sel = (a.mask == nullptr || a.mask[q.b] != 0) && len >= a.min_len && len > 0;
+  if (!sel) return;  // uniform for all workgroups of the sequence
+
+  float* ck = a.ckpt + q.unit * (P * N);
+  f32x4 hv[NLD];
+  load_tile(ck, q, hv);
+
+  const int L = len;
+  const int slot0 = (int)(a.pos[q.b] % cap);
+  const float Ah = a.A[q.h];
+  __shared__ float s_dt[kMaxCap], s_fw[kMaxCap];
+  __shared__ float s_gamma;
+  __shared__ __attribute__((aligned(16))) float s_x[kMaxCap][P];
+  __shared__ __attribute__((aligned(16))) float s_B[kMaxCap][N];
+  for (int idx = q.tid; idx < L * P; idx += NT) {
+    const int i = idx / P, p = idx % P;
+    s_x[i][p] = a.ring_x[(q.unit * cap + ring_slot(slot0, i, cap)) * P + p];
+  }
+  for (int idx = q.tid; idx < L * N; idx += NT) {
+    const int i = idx / N, n = idx % N;
+    s_B[i][n] = a.ring_B[(q.gunit * cap + ring_slot(slot0, i, cap)) * N + n];
+  }
+  if (q.tid < L) s_dt[q.tid] = a.ring_dt[q.unit * cap + ring_slot(slot0, q.tid, cap)];
+  __syncthreads();
+  if (q.tid < L) {
+    float suf = 0.f;
+    for (int j = q.tid + 1; j < L; ++j) suf += s_dt[j];
+    s_fw[q.tid] = expf(Ah * suf) * s_dt[q.tid];
+    if (q.tid == 0) s_gamma = expf(Ah * (suf + s_dt[0]));
+  }
+  __syncthreads();
+  const float gam = s_gamma;
+#pragma unroll
+  for (int k = 0; k < NLD; ++k) hv[k] *= gam;
+  for (int i = 0; i < L; ++i) {
+    const f32x4 bi = ld4(&s_B[i][q.c4 * 4]);
+    const float w = s_fw[i];
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) hv[k] += (w * s_x[i][k * RPL + q.r0]) * bi;
+  }
+  store_tile(ck, q, hv);
+
+  IndexUpdate u;
+  u.apply = true;
+  u.pos_add = L;
+  u.new_len = 0;
+  arrive_and_update(a.arrive, a.pos, a.len, q.b, a.H, u);
+}
+
+// -------------------------------------------------------------- verify ----
+// n_pos drafts appended at entries len..len+n-1; draft j's output uses
+// entries 0..len+j.  One checkpoint read serves all positions: each row of
+// h_c is dotted with every C_j before the cross-lane reduction.
+template <int NPAD>
+__global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
+  const Geo q = geometry(a);
+  const int cap = a.cap, n = a.n_pos;
+  float* ck = a.ckpt + q.unit * (P * N);
+  f32x4 hv[NLD];
+  load_tile(ck, q, hv);
+
+  const int len = a.len[q.b];
+  const int64_t pos = a.pos[q.b];
+  const bool ok = len + n <= cap;
+  const int LT = len + n;
+  const int slot0 = (int)(pos % cap);
+  const float Ah = a.A[q.h];
+  const float Dh = a.D[q.h];
+  const long sx = (long)a.batch * a.H * P;   // per-draft strides
+  const long sg = (long)a.batch * a.G * N;
+  const long sd = (long)a.batch * a.H;
+
+  __shared__ float s_dt[kMaxCap];
+  __shared__ float s_e[NPAD][kMaxCap];
+  __shared__ float s_w[NPAD][kMaxCap];
+  __shared__ float s_gam[NPAD];
+  __shared__ float s_yb[QD][NPAD][P];
+
+  auto xsrc = [&](int i) -> const float* {
+    return i < len ? a.ring_x + (q.unit * cap + ring_slot(slot0, i, cap)) * P
+                   : a.x + (i - len) * sx + q.unit * P;
+  };
+  auto Bsrc = [&](int i) -> const float* {
+    return i < len ? a.ring_B + (q.gunit * cap + ring_slot(slot0, i, cap)) * N
+                   : a.B + (i - len) * sg + q.gunit * N;
+  };
+  auto dtv = [&](int i) -> float {
+    return i < len ? a.ring_dt[q.unit * cap + ring_slot(slot0, i, cap)]
+                   : a.dt[(i - len) * sd + q.unit];
+  };
+
+  if (ok) {
+    for (int j = 0; j < n; ++j) {  // append the drafts
+      const int s = ring_slot(slot0, len + j, cap);
+      if (q.tid < P) a.ring_x[(q.unit * cap + s) * P + q.tid] = a.x[j * sx + q.unit * P + q.tid];
+      if (q.tid == 0) a.ring_dt[q.unit * cap + s] = a.dt[j * sd + q.unit];
+      if ((q.h % (a.H / a.G)) == 0 && q.tid < N)
+        a.ring_B[(q.gunit * cap + s) * N + q.tid] = a.B[j * sg + q.gunit * N + q.tid];
+    }
+    if (q.tid < LT) s_dt[q.tid] = dtv(q.tid);
+    {  // e_{j,i} = B_i . C_j for i <= len + j, 16 lanes per pair
+      constexpr int SEG = N / 16;
+      const int sgm = q.tid & 15;
+      for (int pass = 0; pass < (NPAD * kMaxCap) / 16; ++pass) {
+        const int pi = pass * 16 + (q.tid >> 4);
+        const int j = pi / kMaxCap, i = pi % kMaxCap;
+        const bool act = j < n && i <= len + j;
+        float part = 0.f;
+        if (act) {
+          const float* bi = Bsrc(i) + sgm * SEG;
+          const float* cj = a.C + j * sg + q.gunit * N + sgm * SEG;
+#pragma unroll
+          for (int e = 0; e < SEG; e += 4) part += dot4(ld4(bi + e), ld4(cj + e));
+        }
+        part += __shfl_xor(part, 8);
+        part += __shfl_xor(part, 4);
+        part += __shfl_xor(part, 2);
+        part += __shfl_xor(part, 1);
+        if (sgm == 0 && act) s_e[j][i] = part;
+      }
+    }
+    __syncthreads();
+    if (q.tid < NPAD * kMaxCap) {
+      const int j = q.tid / kMaxCap, i = q.tid % kMaxCap;
+      const int Lj = len + j + 1;
+      if (j < n && i < Lj) {
+        float suf = 0.f;
+        for (int m = i + 1; m < Lj; ++m) suf += s_dt[m];
+        s_w[j][i] = expf(Ah * suf) * s_dt[i] * s_e[j][i];
+        if (i == 0) s_gam[j] = expf(Ah * (suf + s_dt[0]));
+      }
+    }
+    __syncthreads();
+    {
+      const int p = q.tid % P, qd = q.tid / P;
+      float acc[NPAD];
+#pragma unroll
+      for (int j = 0; j < NPAD; ++j) acc[j] = 0.f;
+      for (int i = qd; i < LT; i += QD) {
+        const float xv = xsrc(i)[p];
+#pragma unroll
+        for (int j = 0; j < NPAD; ++j)
+          if (j < n && i <= len + j) acc[j] += s_w[j][i] * xv;
+      }
+#pragma unroll
+      for (int j = 0; j < NPAD; ++j) s_yb[qd][j][p] = acc[j];
+    }
+  }
+
+  constexpr int V = NLD * NPAD;
+  float d[V];
+#pragma unroll
+  for (int j = 0; j < NPAD; ++j) {
+    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+    if (j < n) c = ld4(a.C + j * sg + q.gunit * N + q.c4 * 4);
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) d[k * NPAD + j] = dot4(hv[k], c);
+  }
+  xreduce<V, LPR>(d, q.lane);
+  __syncthreads();
+  using M = XMap<V, LPR>;
+  if (M::writer(q.lane)) {
+#pragma unroll
+    for (int jj = 0; jj < M::VOUT; ++jj) {
+      const int idx = M::index(q.lane, jj);
+      const int k = idx / NPAD, j = idx % NPAD;
+      if (j < n) {
+        const int p = k * RPL + q.r0;
+        float yv;
+        if (ok) {
+          float yb = 0.f;
+#pragma unroll
+          for (int qd = 0; qd < QD; ++qd) yb += s_yb[qd][j][p];
+          yv = s_gam[j] * d[jj] + yb + Dh * a.x[j * sx + q.unit * P + p];
+        } else {
+          yv = __builtin_nanf("");
+        }
+        a.y[j * sx + q.unit * P + p] = yv;
+      }
+    }
+  }
+
+  IndexUpdate u;
+  u.apply = ok;
+  u.pos_add = 0;
+  u.new_len = LT;
+  arrive_and_update(a.arrive, a.pos, a.len, q.b, a.H, u);
+  if (!ok && q.tid == 0) raise_status(a.status, kStatusOverflow);
+}
+
+// --------------------------------------------------------------- eager ----
+// Read the whole state, update it, write it back, every step.
+__global__ __launch_bounds__(NT) void m2_eager_kernel(M2Args a) {
+  const Geo q = geometry(a);
+  float* ck = a.ckpt + q.unit * (P * N);
+  f32x4 hv[NLD];
+  load_tile(ck, q, hv);
+  const float dtv = a.dt[q.unit];
+  const float dec = expf(dtv * a.A[q.h]);
+  const float* xt = a.x + q.unit * P;
+  const f32x4 bb = ld4(a.B + q.gunit * N + q.c4 * 4);
+  const f32x4 cc = ld4(a.C + q.gunit * N + q.c4 * 4);
+  float d[NLD];
+#pragma unroll
+  for (int k = 0; k < NLD; ++k) {
+    const float xv = dtv * xt[k * RPL + q.r0];
+    hv[k] = dec * hv[k] + xv * bb;
+    d[k] = dot4(hv[k], cc);
+  }
+  store_tile(ck, q, hv);
+  xreduce<NLD, LPR>(d, q.lane);
+  using M = XMap<NLD, LPR>;
+  if (M::writer(q.lane)) {
+    const int p = M::index(q.lane, 0) * RPL + q.r0;
+    a.y[q.unit * P + p] = d[0] + a.D[q.h] * xt[p];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_m2_step(const M2Args& a, bool fused, hipStream_t s) {
+  const dim3 grid((unsigned)(a.batch * a.H)), block(NT);
+  if (fused)
+    hipLaunchKernelGGL(m2_step_kernel<true>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(m2_step_kernel<false>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_m2_commit(const M2Args& a, hipStream_t s) {
+  hipLaunchKernelGGL(m2_commit_kernel, dim3((unsigned)(a.batch * a.H)), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_m2_verify(const M2Args& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.batch * a.H)), block(NT);
+  if (a.n_pos <= 1)
+    hipLaunchKernelGGL(m2_verify_kernel<1>, grid, block, 0, s, a);
+  else if (a.n_pos <= 2)
+    hipLaunchKernelGGL(m2_verify_kernel<2>, grid, block, 0, s, a);
+  else if (a.n_pos <= 4)
+    hipLaunchKernelGGL(m2_verify_kernel<4>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(m2_verify_kernel<8>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_m2_eager(const M2Args& a, hipStream_t s) {
+  hipLaunchKernelGGL(m2_eager_kernel, dim3((unsigned)(a.batch * a.H)), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace rssm

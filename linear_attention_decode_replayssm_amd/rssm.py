@@ -1,0 +1,231 @@
+"""ctypes binding of librssm.so (C ABI in include/rssm.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels behind the C ABI.  PyTorch provides device memory and the current
+stream; there is no fallback of any kind -- if the library is missing, every
+entry point raises.
+
+Entry points keep the C names: :func:`rssm_mamba2_step`, :func:`rssm_gdn_step`,
+:func:`rssm_commit`, :func:`rssm_verify`, :func:`rssm_rollback`,
+:func:`rssm_eager_step`, :func:`rssm_status`, :func:`rssm_strerror`,
+:func:`rssm_abi_version`.  :class:`Layer` allocates one layer's state tensors
+and fills the ``rssm_layer`` descriptor.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librssm.so")
+
+RSSM_OK, RSSM_EINVAL, RSSM_EUNSUPPORTED, RSSM_EALIGN, RSSM_ERANGE, RSSM_EHIP = 0, -1, -2, -3, -4, -5
+STATUS_OVERFLOW, STATUS_ROLLBACK, STATUS_NONFINITE = 1, 2, 4
+RSSM_MAMBA2, RSSM_GDN = 1, 2
+RSSM_F32, RSSM_DUAL, RSSM_SHARED = 0, 1, 2
+RSSM_LP_NONE, RSSM_BF16, RSSM_E4M3 = 0, 1, 2
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+
+
+class rssm_layer(ctypes.Structure):
+    _fields_ = [("kind", _i32), ("scheme", _i32), ("lp_dtype", _i32),
+                ("batch", _i32), ("nheads", _i32), ("ngroups", _i32),
+                ("dim_v", _i32), ("dim_k", _i32), ("capacity", _i32),
+                ("reserved0", _i32),
+                ("ckpt", _vp), ("ckpt_lp", _vp), ("lp_scale", _vp),
+                ("A", _vp), ("D", _vp), ("ring", _vp * 4),
+                ("ckpt_pos", _vp), ("len", _vp), ("arrive", _vp), ("status", _vp)]
+
+
+class rssm_inputs(ctypes.Structure):
+    _fields_ = [("x", _vp), ("B", _vp), ("C", _vp), ("dt", _vp),
+                ("q", _vp), ("k", _vp), ("v", _vp), ("alpha", _vp), ("beta", _vp)]
+
+
+class RssmError(RuntimeError):
+    def __init__(self, code, where):
+        super().__init__(f"{where}: {rssm_strerror(code)} (code {code})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Open librssm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m linear_attention_decode_replayssm_amd.build` "
+                "(or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        L.rssm_mamba2_step.argtypes = [P(rssm_layer), _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp]
+        L.rssm_gdn_step.argtypes = [P(rssm_layer), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp]
+        L.rssm_commit.argtypes = [P(rssm_layer), _vp, ctypes.c_int, _vp]
+        L.rssm_verify.argtypes = [P(rssm_layer), ctypes.c_int, P(rssm_inputs), _vp, _vp]
+        L.rssm_rollback.argtypes = [P(rssm_layer), _vp, _vp]
+        L.rssm_eager_step.argtypes = [P(rssm_layer), P(rssm_inputs), _vp, _vp]
+        L.rssm_status.argtypes = [P(rssm_layer), P(ctypes.c_uint32), _vp]
+        L.rssm_strerror.argtypes = [ctypes.c_int]
+        L.rssm_strerror.restype = ctypes.c_char_p
+        L.rssm_abi_version.restype = ctypes.c_int
+        for f in ("rssm_mamba2_step", "rssm_gdn_step", "rssm_commit", "rssm_verify",
+                  "rssm_rollback", "rssm_eager_step", "rssm_status"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    """Device address of a tensor (or None / an int address)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc, where):
+    if rc != RSSM_OK:
+        raise RssmError(rc, where)
+    return rc
+
+
+def _desc(layer):
+    return layer.desc if isinstance(layer, Layer) else layer
+
+
+def rssm_abi_version() -> int:
+    return lib().rssm_abi_version()
+
+
+def rssm_strerror(code: int) -> str:
+    return lib().rssm_strerror(int(code)).decode()
+
+
+def rssm_mamba2_step(layer, x, B, C, dt, y, commit_after=False, stream=None, check=True):
+    rc = lib().rssm_mamba2_step(ctypes.byref(_desc(layer)), _ptr(x), _ptr(B), _ptr(C), _ptr(dt),
+                                _ptr(y), int(bool(commit_after)), _stream(stream))
+    return _check(rc, "rssm_mamba2_step") if check else rc
+
+
+def rssm_gdn_step(layer, q, k, v, alpha, beta, o, commit_after=False, stream=None, check=True):
+    rc = lib().rssm_gdn_step(ctypes.byref(_desc(layer)), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                             _ptr(beta), _ptr(o), int(bool(commit_after)), _stream(stream))
+    return _check(rc, "rssm_gdn_step") if check else rc
+
+
+def rssm_commit(layer, mask=None, min_len=0, stream=None, check=True):
+    rc = lib().rssm_commit(ctypes.byref(_desc(layer)), _ptr(mask), int(min_len), _stream(stream))
+    return _check(rc, "rssm_commit") if check else rc
+
+
+def make_inputs(x=None, B=None, C=None, dt=None, q=None, k=None, v=None, alpha=None, beta=None):
+    return rssm_inputs(_ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(q), _ptr(k), _ptr(v),
+                       _ptr(alpha), _ptr(beta))
+
+
+def rssm_verify(layer, n_pos, inputs, out, stream=None, check=True):
+    if isinstance(inputs, dict):
+        inputs = make_inputs(**inputs)
+    rc = lib().rssm_verify(ctypes.byref(_desc(layer)), int(n_pos), ctypes.byref(inputs), _ptr(out),
+                           _stream(stream))
+    return _check(rc, "rssm_verify") if check else rc
+
+
+def rssm_rollback(layer, n_reject, stream=None, check=True):
+    rc = lib().rssm_rollback(ctypes.byref(_desc(layer)), _ptr(n_reject), _stream(stream))
+    return _check(rc, "rssm_rollback") if check else rc
+
+
+def rssm_eager_step(layer, inputs, out, stream=None, check=True):
+    if isinstance(inputs, dict):
+        inputs = make_inputs(**inputs)
+    rc = lib().rssm_eager_step(ctypes.byref(_desc(layer)), ctypes.byref(inputs), _ptr(out),
+                               _stream(stream))
+    return _check(rc, "rssm_eager_step") if check else rc
+
+
+def rssm_status(layer, stream=None) -> int:
+    bits = ctypes.c_uint32(0)
+    _check(lib().rssm_status(ctypes.byref(_desc(layer)), ctypes.byref(bits), _stream(stream)),
+           "rssm_status")
+    return bits.value
+
+
+class Layer:
+    """One layer's caller-owned device state, plus its ``rssm_layer`` descriptor.
+
+    Tensors (torch, on ``device``): ``ckpt`` fp32 [b,H,dv,dk] (None under
+    SHARED), ``ckpt_lp`` (uint16 bf16 bits / uint8 E4M3 codes, None under F32),
+    ``lp_scale`` fp32 [b,H] (E4M3), ``A``/``D`` fp32 [H] (Mamba-2), ``rings``,
+    ``ckpt_pos`` int64 [b], ``len`` int32 [b], ``arrive`` int32 [b] (zero),
+    ``status`` int32 [1].
+    """
+
+    def __init__(self, kind, batch, nheads, dim_v, dim_k, capacity, ngroups=1,
+                 scheme=RSSM_F32, lp_dtype=RSSM_LP_NONE, device="cuda"):
+        import torch
+        self.kind, self.scheme, self.lp_dtype = kind, scheme, lp_dtype
+        self.batch, self.nheads, self.ngroups = batch, nheads, ngroups
+        self.dim_v, self.dim_k, self.capacity = dim_v, dim_k, capacity
+        f32 = dict(dtype=torch.float32, device=device)
+        shape = (batch, nheads, dim_v, dim_k)
+        self.ckpt = torch.zeros(shape, **f32) if scheme != RSSM_SHARED else None
+        self.ckpt_lp = None
+        self.lp_scale = None
+        if scheme != RSSM_F32:
+            dt = torch.int16 if lp_dtype == RSSM_BF16 else torch.uint8
+            self.ckpt_lp = torch.zeros(shape, dtype=dt, device=device)
+            if lp_dtype == RSSM_E4M3:
+                self.lp_scale = torch.ones((batch, nheads), **f32)
+        self.A = self.D = None
+        if kind == RSSM_MAMBA2:
+            self.A = torch.zeros(nheads, **f32)
+            self.D = torch.zeros(nheads, **f32)
+            self.rings = [torch.zeros((batch, nheads, capacity, dim_v), **f32),
+                          torch.zeros((batch, ngroups, capacity, dim_k), **f32),
+                          torch.zeros((batch, nheads, capacity), **f32)]
+        else:
+            self.rings = [torch.zeros((batch, nheads, capacity, dim_k), **f32),
+                          torch.zeros((batch, nheads, capacity, dim_v), **f32),
+                          torch.zeros((batch, nheads, capacity), **f32),
+                          torch.zeros((batch, nheads, capacity), **f32)]
+        self.ckpt_pos = torch.zeros(batch, dtype=torch.int64, device=device)
+        self.len = torch.zeros(batch, dtype=torch.int32, device=device)
+        self.arrive = torch.zeros(max(batch, 1), dtype=torch.int32, device=device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.refresh()
+
+    def refresh(self):
+        """(Re)build the descriptor from the current tensors."""
+        rings = (_vp * 4)(*([_ptr(r) for r in self.rings] + [None] * (4 - len(self.rings))))
+        self.desc = rssm_layer(self.kind, self.scheme, self.lp_dtype, self.batch, self.nheads,
+                               self.ngroups, self.dim_v, self.dim_k, self.capacity, 0,
+                               _ptr(self.ckpt), _ptr(self.ckpt_lp), _ptr(self.lp_scale),
+                               _ptr(self.A), _ptr(self.D), rings, _ptr(self.ckpt_pos),
+                               _ptr(self.len), _ptr(self.arrive), _ptr(self.status))
+        return self.desc
+
+    @classmethod
+    def mamba2(cls, batch, nheads, ngroups, headdim, dstate, capacity, device="cuda"):
+        return cls(RSSM_MAMBA2, batch, nheads, headdim, dstate, capacity, ngroups=ngroups,
+                   device=device)
+
+    @classmethod
+    def gdn(cls, batch, nheads, dk, dv, capacity, scheme=RSSM_F32, lp_dtype=RSSM_LP_NONE,
+            device="cuda"):
+        return cls(RSSM_GDN, batch, nheads, dv, dk, capacity, scheme=scheme, lp_dtype=lp_dtype,
+                   device=device)

@@ -9,13 +9,13 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
   positions come from a scratch continuation of the accepted state, then the
   rejected suffix is dropped and a commit folds any sequence whose buffer has
   reached ``commit_len`` (explainer, "Cheap speculative decoding rollback";
-  Abstract: rollback is a buffer-pointer operation, verification is
-  output-only);
+  Abstract: rolling back only moves a pointer into the buffer, and drafts
+  are verified from their outputs without storing intermediate states);
 * low-precision emulation: a low-precision checkpoint serves the outputs and
   is refreshed at each commit either from the high-precision state ("dual") or
-  from itself ("shared") (Abstract: "a low-precision checkpoint to serve output
-  computation ... while a higher-precision checkpoint serves recurrent
-  updates"; explainer, "Separate precisions for serving vs updating state").
+  from itself ("shared") (Abstract: the low-precision copy serves the outputs
+  on most steps and only the high-precision checkpoint takes the recurrent
+  updates; explainer, "Separate precisions for serving vs updating state").
 
 Because the eager recurrence started from any state S and run over the buffered
 inputs equals the replay from checkpoint S over the same inputs, serving from

@@ -1,0 +1,98 @@
+"""Helpers shared by the GPU parity tests: device transfer, error metrics and
+drivers that run the HIP path through the C ABI binding."""
+import numpy as np
+
+from linear_attention_decode_replayssm_amd import rssm as R
+
+TOL_F32 = 1e-4   # max over output vectors of ||got - want||_inf / ||want||_inf
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def dev(a):
+    """numpy -> contiguous device tensor (dtype kept)."""
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    return t.detach().to("cpu").numpy()
+
+
+def vec_rel_err(got, want):
+    """max over vectors (last axis) of ||got - want||_inf / ||want||_inf."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    num = np.abs(got - want).max(axis=-1)
+    den = np.abs(want).max(axis=-1)
+    den = np.where(den > 0, den, 1.0)
+    return float((num / den).max())
+
+
+def indices(layer):
+    return host(layer.ckpt_pos).copy(), host(layer.len).copy()
+
+
+# ------------------------------------------------------------- Mamba-2 --
+
+def m2_layer(A, D, h0, G, cap):
+    b, H, P, N = h0.shape
+    L = R.Layer.mamba2(b, H, G, P, N, cap)
+    L.A.copy_(dev(A))
+    L.D.copy_(dev(D))
+    L.ckpt.copy_(dev(h0))
+    return L
+
+
+def m2_decode(L, steps_dev, interval, fused, record=True):
+    """Plain decode on the GPU: a commit after every `interval`-th step.
+    steps_dev: dict of device tensors x [T,b,H,P], B, C [T,b,G,N], dt [T,b,H].
+    Returns (y device [T,b,H,P], pos [T,b], len [T,b])."""
+    t_ = torch()
+    x, B, C, dt = (steps_dev[k] for k in ("x", "B", "C", "dt"))
+    T = x.shape[0]
+    y = t_.empty_like(x)
+    pos, ln = [], []
+    for t in range(T):
+        commit = (t + 1) % interval == 0
+        R.rssm_mamba2_step(L, x[t], B[t], C[t], dt[t], y[t], commit_after=fused and commit)
+        if commit and not fused:
+            R.rssm_commit(L, None, 0)
+        if record:
+            p, l = indices(L)
+            pos.append(p)
+            ln.append(l)
+    t_.cuda.synchronize()
+    return y, (np.array(pos) if record else None), (np.array(ln) if record else None)
+
+
+# ------------------------------------------------------- Gated DeltaNet --
+
+def gdn_layer(S0, cap, scheme=R.RSSM_F32, lp=R.RSSM_LP_NONE):
+    b, H, dv, dk = S0.shape
+    L = R.Layer.gdn(b, H, dk, dv, cap, scheme=scheme, lp_dtype=lp)
+    if L.ckpt is not None:
+        L.ckpt.copy_(dev(S0))
+    return L
+
+
+def gdn_decode(L, steps_dev, interval, fused, record=True):
+    t_ = torch()
+    q, k, v, al, be = (steps_dev[s] for s in ("q", "k", "v", "alpha", "beta"))
+    T = q.shape[0]
+    o = t_.empty_like(v)
+    pos, ln = [], []
+    for t in range(T):
+        commit = (t + 1) % interval == 0
+        R.rssm_gdn_step(L, q[t], k[t], v[t], al[t], be[t], o[t], commit_after=fused and commit)
+        if commit and not fused:
+            R.rssm_commit(L, None, 0)
+        if record:
+            p, l = indices(L)
+            pos.append(p)
+            ln.append(l)
+    t_.cuda.synchronize()
+    return o, (np.array(pos) if record else None), (np.array(ln) if record else None)

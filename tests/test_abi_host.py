@@ -1,0 +1,189 @@
+"""C ABI host tests (CPU only, no kernel launches).
+
+librssm.so must load without a GPU, export every function include/rssm.h
+declares, and reject bad arguments on the host before launching anything.
+Every call here either fails validation or has batch == 0, which returns
+before any launch, so no device is touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_decode_replayssm_amd import rssm as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rssm.h")
+
+FAKE = 0x10000          # 16-byte aligned stand-in address (never dereferenced)
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(rssm_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for f in ("rssm_mamba2_step", "rssm_gdn_step", "rssm_commit", "rssm_verify",
+              "rssm_rollback", "rssm_eager_step", "rssm_status", "rssm_strerror",
+              "rssm_abi_version"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = R.lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    # exported dynamic symbols of the shared object, read from its ELF table
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", R.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(rssm_\w+)$", out, re.M))
+    assert set(_declared()) <= exported
+
+
+def test_version_and_strerror():
+    assert R.rssm_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert R.rssm_strerror(code)
+    assert "unknown" in R.rssm_strerror(12345)
+
+
+def _m2_desc(**kw):
+    d = dict(kind=R.RSSM_MAMBA2, scheme=R.RSSM_F32, lp_dtype=0, batch=0, nheads=8,
+             ngroups=1, dim_v=64, dim_k=128, capacity=16)
+    d.update(kw)
+    L = R.rssm_layer(d["kind"], d["scheme"], d["lp_dtype"], d["batch"], d["nheads"],
+                     d["ngroups"], d["dim_v"], d["dim_k"], d["capacity"], 0)
+    L.ckpt = kw.get("ckpt", FAKE)
+    L.A = FAKE
+    L.D = FAKE
+    for i in range(3):
+        L.ring[i] = FAKE
+    L.ckpt_pos = L.len = L.arrive = L.status = FAKE
+    return L
+
+
+def _gdn_desc(**kw):
+    d = dict(kind=R.RSSM_GDN, scheme=R.RSSM_F32, lp_dtype=0, batch=0, nheads=4,
+             ngroups=1, dim_v=128, dim_k=128, capacity=8)
+    d.update(kw)
+    L = R.rssm_layer(d["kind"], d["scheme"], d["lp_dtype"], d["batch"], d["nheads"],
+                     d["ngroups"], d["dim_v"], d["dim_k"], d["capacity"], 0)
+    L.ckpt = FAKE
+    if d["scheme"] != R.RSSM_F32:
+        L.ckpt_lp = FAKE
+        L.lp_scale = FAKE
+    for i in range(4):
+        L.ring[i] = FAKE
+    L.ckpt_pos = L.len = L.arrive = L.status = FAKE
+    return L
+
+
+def _step(L, **kw):
+    a = dict(x=FAKE, B=FAKE, C=FAKE, dt=FAKE, y=FAKE)
+    a.update(kw)
+    return R.rssm_mamba2_step(L, a["x"], a["B"], a["C"], a["dt"], a["y"], 0, stream=0,
+                              check=False)
+
+
+def test_empty_batch_is_ok_without_launch():
+    assert _step(_m2_desc(batch=0)) == R.RSSM_OK
+    assert R.rssm_commit(_m2_desc(batch=0), None, 0, stream=0, check=False) == R.RSSM_OK
+    assert R.rssm_rollback(_m2_desc(batch=0), FAKE, stream=0, check=False) == R.RSSM_OK
+    L = _gdn_desc(batch=0)
+    assert R.rssm_gdn_step(L, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, stream=0,
+                           check=False) == R.RSSM_OK
+
+
+def test_null_layer():
+    lib = R.lib()
+    assert lib.rssm_mamba2_step(None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0) == R.RSSM_EINVAL
+    assert lib.rssm_commit(None, None, 0, 0) == R.RSSM_EINVAL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kind=7), R.RSSM_EINVAL),
+    (dict(scheme=9), R.RSSM_EINVAL),
+    (dict(nheads=0), R.RSSM_EINVAL),
+    (dict(batch=-1), R.RSSM_EINVAL),
+    (dict(ngroups=3), R.RSSM_EINVAL),               # 8 % 3 != 0
+    (dict(dim_v=32), R.RSSM_EUNSUPPORTED),
+    (dict(dim_k=64), R.RSSM_EUNSUPPORTED),
+    (dict(capacity=17), R.RSSM_EUNSUPPORTED),
+    (dict(capacity=0), R.RSSM_EINVAL),
+    (dict(scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_BF16), R.RSSM_EUNSUPPORTED),
+    (dict(ckpt=FAKE + 4), R.RSSM_EALIGN),
+    (dict(ckpt=0), R.RSSM_EINVAL),
+])
+def test_m2_layer_validation(kw, code):
+    args = dict(batch=4)
+    args.update(kw)
+    assert _step(_m2_desc(**args)) == code
+
+
+def test_m2_pointer_validation():
+    assert _step(_m2_desc(batch=4), x=None) == R.RSSM_EINVAL
+    assert _step(_m2_desc(batch=4), C=FAKE + 8) == R.RSSM_EALIGN
+    L = _m2_desc(batch=4)
+    L.ring[1] = None
+    assert _step(L) == R.RSSM_EINVAL
+    L = _m2_desc(batch=4)
+    L.arrive = None
+    assert _step(L) == R.RSSM_EINVAL
+    L = _m2_desc(batch=4)
+    L.ring[0] = FAKE + 4
+    assert _step(L) == R.RSSM_EALIGN
+    # wrong layer kind for the entry point
+    assert R.rssm_gdn_step(_m2_desc(batch=4), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0,
+                           stream=0, check=False) == R.RSSM_EINVAL
+
+
+def test_commit_verify_rollback_ranges():
+    L = _m2_desc(batch=4, capacity=12)
+    assert R.rssm_commit(L, None, -1, stream=0, check=False) == R.RSSM_ERANGE
+    inp = R.make_inputs(x=FAKE, B=FAKE, C=FAKE, dt=FAKE)
+    assert R.rssm_verify(L, 0, inp, FAKE, stream=0, check=False) == R.RSSM_ERANGE
+    assert R.rssm_verify(L, 9, inp, FAKE, stream=0, check=False) == R.RSSM_ERANGE
+    L4 = _m2_desc(batch=4, capacity=4)
+    assert R.rssm_verify(L4, 5, inp, FAKE, stream=0, check=False) == R.RSSM_ERANGE
+    assert R.rssm_verify(L, 4, R.make_inputs(x=FAKE, B=FAKE, C=FAKE), FAKE, stream=0,
+                         check=False) == R.RSSM_EINVAL
+    assert R.rssm_rollback(L, None, stream=0, check=False) == R.RSSM_EINVAL
+
+
+def test_gdn_validation():
+    L = _gdn_desc(batch=2, ngroups=2)
+    assert R.rssm_gdn_step(L, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, stream=0,
+                           check=False) == R.RSSM_EINVAL
+    L = _gdn_desc(batch=2, dim_k=64)
+    assert R.rssm_gdn_step(L, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, stream=0,
+                           check=False) == R.RSSM_EUNSUPPORTED
+    L = _gdn_desc(batch=2, scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_BF16)
+    assert R.rssm_gdn_step(L, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, stream=0,
+                           check=False) == R.RSSM_EUNSUPPORTED       # fused needs F32
+    L = _gdn_desc(batch=2, scheme=R.RSSM_DUAL, lp_dtype=0)
+    assert R.rssm_commit(L, None, 0, stream=0, check=False) == R.RSSM_EINVAL
+    L = _gdn_desc(batch=2, scheme=R.RSSM_SHARED, lp_dtype=R.RSSM_E4M3)
+    L.lp_scale = None
+    assert R.rssm_commit(L, None, 0, stream=0, check=False) == R.RSSM_EINVAL
+    L = _gdn_desc(batch=2, scheme=R.RSSM_SHARED, lp_dtype=R.RSSM_BF16)
+    L.ckpt = None
+    inp = R.make_inputs(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE)
+    assert R.rssm_eager_step(L, inp, FAKE, stream=0, check=False) == R.RSSM_EUNSUPPORTED
+    L = _gdn_desc(batch=2)
+    L.ring[3] = None
+    assert R.rssm_commit(L, None, 0, stream=0, check=False) == R.RSSM_EINVAL
+
+
+def test_status_rejects_null():
+    assert R.lib().rssm_status(None, None, None) == R.RSSM_EINVAL
+
+
+def test_product_path_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(R, "_lib", None)
+    monkeypatch.setattr(R, "LIB_PATH", "/nonexistent/librssm.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        R.lib()

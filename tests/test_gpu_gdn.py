@@ -1,0 +1,279 @@
+"""Gated DeltaNet parity: HIP path (through the C ABI) vs the fp64 oracle.
+
+fp32 checkpoints: max over output vectors of ||o - o_oracle||_inf /
+||o_oracle||_inf <= 1e-4; indices bit-exact.  Low-precision checkpoints: the
+dual scheme must stay inside the one-quantisation bound at every step
+(|o - o_exact| <= sum_j delta(S_c[r,j]) |q~_j| + 1e-4 ||o_exact||_inf, with
+S_c the exact checkpoint of the last commit, q~ the carried query, delta half
+an lp ulp), and its codes must equal the oracle's emulated codes or differ by
+one ulp, in at most 1e-3 of the elements.  The shared scheme is the
+comparison scheme: its error is reported.  The codecs are bit-exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import drivers
+from linear_attention_decode_replayssm_amd import rssm as R
+from linear_attention_decode_replayssm_amd import synthetic as syn
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+DK = DV = 128
+
+
+def _case(seed, T, b, H, s0=0.1):
+    S0 = syn.gdn_state0(seed, b, H, DV, DK, std=s0)
+    st = syn.gdn_steps(seed, 0, T, b, H, DK, DV)
+    return S0, st
+
+
+def _names():
+    return ("q", "k", "v", "alpha", "beta")
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["standalone_commit", "fused_commit"])
+def test_decode_small(fused):
+    """batch 4, 4 heads, 64 steps, interval 8 = ring 8, S_0 ~ N(0, 0.1)."""
+    T, b, H, interval, cap = 64, 4, 4, 8, 8
+    S0, st = _case(10, T, b, H)
+    L = gu.gdn_layer(S0, cap)
+    o, pos, ln = gu.gdn_decode(L, {k: gu.dev(v) for k, v in st.items()}, interval, fused)
+    ref = drivers.gdn_decode(*(st[n] for n in _names()), S0, interval, cap)
+    assert gu.vec_rel_err(gu.host(o), ref["o"]) <= gu.TOL_F32
+    np.testing.assert_array_equal(pos, ref["pos"])
+    np.testing.assert_array_equal(ln, ref["len"])
+    assert gu.vec_rel_err(gu.host(L.ckpt), ref["ckpt"]) <= 1e-5
+    assert R.rssm_status(L) == 0
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["standalone_commit", "fused_commit"])
+def test_decode_ragged(fused):
+    """batch 3 x 5 heads (15 workgroups), ring 7, interval 7, 30 steps."""
+    T, b, H, interval, cap = 30, 3, 5, 7, 7
+    S0, st = _case(11, T, b, H)
+    L = gu.gdn_layer(S0, cap)
+    o, pos, ln = gu.gdn_decode(L, {k: gu.dev(v) for k, v in st.items()}, interval, fused)
+    ref = drivers.gdn_decode(*(st[n] for n in _names()), S0, interval, cap)
+    assert gu.vec_rel_err(gu.host(o), ref["o"]) <= gu.TOL_F32
+    np.testing.assert_array_equal(pos, ref["pos"])
+    np.testing.assert_array_equal(ln, ref["len"])
+
+
+def test_long_ring():
+    """ring and interval 16 (the largest ring), 40 steps."""
+    T, b, H, interval, cap = 40, 2, 3, 16, 16
+    S0, st = _case(12, T, b, H)
+    L = gu.gdn_layer(S0, cap)
+    o, pos, ln = gu.gdn_decode(L, {k: gu.dev(v) for k, v in st.items()}, interval, False)
+    ref = drivers.gdn_decode(*(st[n] for n in _names()), S0, interval, cap)
+    assert gu.vec_rel_err(gu.host(o), ref["o"]) <= gu.TOL_F32
+    np.testing.assert_array_equal(ln, ref["len"])
+
+
+def test_eager_small():
+    T, b, H = 48, 4, 4
+    S0, st = _case(13, T, b, H)
+    L = gu.gdn_layer(S0, 8)
+    d = {k: gu.dev(v) for k, v in st.items()}
+    o = gu.torch().empty_like(d["v"])
+    for t in range(T):
+        R.rssm_eager_step(L, {n: d[n][t] for n in _names()}, o[t])
+    S = S0.astype(np.float64)
+    want = oracle.gdn_eager(*(st[n] for n in _names()), S)
+    assert gu.vec_rel_err(gu.host(o), want) <= gu.TOL_F32
+    assert gu.vec_rel_err(gu.host(L.ckpt), S) <= 1e-5
+
+
+def test_serving_shape_sampled():
+    """batch 256, 32 heads, interval 8 = ring 8, S_0 = 0, fused commit; 48
+    steps; three whole sequences recomputed by the oracle."""
+    T, b, H, interval, cap = 48, 256, 32, 8, 8
+    S0, st = _case(14, T, b, H, s0=0.0)
+    L = gu.gdn_layer(S0, cap)
+    d = {k: gu.dev(v) for k, v in st.items()}
+    o, _, _ = gu.gdn_decode(L, d, interval, fused=True, record=False)
+    sel = [1, 128, 254]
+    sub = {k: np.ascontiguousarray(v[:, sel]) for k, v in st.items()}
+    ref = drivers.gdn_decode(*(sub[n] for n in _names()), S0[sel], interval, cap)
+    assert gu.vec_rel_err(gu.host(o[:, sel]), ref["o"]) <= gu.TOL_F32
+    assert gu.vec_rel_err(gu.host(L.ckpt[sel]), ref["ckpt"]) <= 1e-5
+    pos, ln = gu.indices(L)
+    assert (pos == T).all() and (ln == 0).all()
+
+
+def test_verify_rollback_small():
+    rounds, n, b, H, cap, commit_len = 30, 4, 6, 4, 12, 8
+    S0, st = _case(15, rounds * n, b, H)
+    drafts = syn.stack_rounds(st, rounds, n)
+    accept = syn.accept_counts(15, rounds, b, n)
+    L = gu.gdn_layer(S0, cap)
+    dd = {k: gu.dev(v) for k, v in drafts.items()}
+    out = gu.torch().empty_like(dd["v"][0])
+    ys, pos, ln = [], [], []
+    for r in range(rounds):
+        R.rssm_verify(L, n, {nm: dd[nm][r] for nm in _names()}, out)
+        R.rssm_rollback(L, gu.dev((n - accept[r]).astype(np.int32)))
+        R.rssm_commit(L, None, commit_len)
+        ys.append(gu.host(out))
+        p, l = gu.indices(L)
+        pos.append(p)
+        ln.append(l)
+    ref = drivers.gdn_spec_rounds(S0, drafts, accept, cap, commit_len)
+    np.testing.assert_array_equal(np.array(pos), ref["pos"])
+    np.testing.assert_array_equal(np.array(ln), ref["len"])
+    assert gu.vec_rel_err(np.array(ys), ref["o"]) <= gu.TOL_F32
+    assert R.rssm_status(L) == 0
+
+
+# ------------------------------------------------------------- codecs --
+
+def _tiles_with_unit_scale(rng, b, H):
+    """fp32 tiles whose max |value| is exactly 448 (E4M3 scale 1), filled with
+    every E4M3 midpoint (ties), subnormals, zeros and random values."""
+    vals = np.array([oracle.e4m3_decode(np.array([c], np.uint8))[0] for c in range(0x7F)])
+    mids = (vals[:-1] + vals[1:]) / 2
+    pool = np.concatenate([vals, mids, -vals, -mids, [0.0, -0.0],
+                           rng.uniform(-448, 448, 4000), rng.standard_normal(4000) * 1e-2])
+    S = rng.choice(pool, size=(b, H, DV, DK)).astype(np.float32)
+    S[..., 0, 0] = 448.0
+    return S
+
+
+@pytest.mark.parametrize("lp", [R.RSSM_BF16, R.RSSM_E4M3], ids=["bf16", "e4m3"])
+def test_encode_bit_exact(lp):
+    """rssm_commit with empty buffers under DUAL re-quantises ckpt_lp from the
+    fp32 checkpoint: codes and scales equal the oracle's encoders."""
+    rng = np.random.default_rng(16)
+    b, H = 2, 4
+    S = _tiles_with_unit_scale(rng, b, H)
+    if lp == R.RSSM_BF16:
+        S[1] = (rng.standard_normal((H, DV, DK)) * 3).astype(np.float32)
+    L = gu.gdn_layer(S, 8, scheme=R.RSSM_DUAL, lp=lp)
+    R.rssm_commit(L, None, 0)
+    got = gu.host(L.ckpt_lp)
+    if lp == R.RSSM_BF16:
+        want = oracle.bf16_encode(S)
+        np.testing.assert_array_equal(got.view(np.uint16), want)
+    else:
+        scale, want = oracle.e4m3_quant_heads(S.reshape(b, H, -1))
+        np.testing.assert_array_equal(gu.host(L.lp_scale), scale)
+        np.testing.assert_array_equal(got.reshape(b, H, -1), want)
+    assert R.rssm_status(L) == 0
+
+
+@pytest.mark.parametrize("lp", [R.RSSM_BF16, R.RSSM_E4M3], ids=["bf16", "e4m3"])
+def test_decode_bit_exact(lp):
+    """A step with beta = 0, alpha = 1 and q = e_c reads column c of the
+    low-precision checkpoint: o[r] = value(code[r, c]) * scale, exactly."""
+    rng = np.random.default_rng(17)
+    b, H = 2, 2
+    if lp == R.RSSM_E4M3:
+        codes = rng.integers(0, 256, size=(b, H, DV, DK)).astype(np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x01            # no NaN codes
+        scale = np.array([[1.0, 0.375], [2.0 ** -7, 3.0]], np.float32)
+        exact = oracle.e4m3_dequant_heads(scale, codes.reshape(b, H, -1)).reshape(codes.shape)
+    else:
+        f = (rng.standard_normal((b, H, DV, DK)) * 5).astype(np.float32)
+        codes = oracle.bf16_encode(f)
+        exact = oracle.bf16_decode(codes)
+        scale = None
+    L = gu.gdn_layer(np.zeros((b, H, DV, DK), np.float32), 8, scheme=R.RSSM_SHARED, lp=lp)
+    t_ = gu.torch()
+    L.ckpt_lp.copy_(t_.from_numpy(codes.view(np.int16) if lp == R.RSSM_BF16 else codes))
+    if scale is not None:
+        L.lp_scale.copy_(gu.dev(scale))
+    for c in (0, 5, 127):
+        q = np.zeros((b, H, DK), np.float32)
+        q[..., c] = 1.0
+        k = np.zeros((b, H, DK), np.float32)
+        k[..., 1] = 1.0
+        v = rng.standard_normal((b, H, DV)).astype(np.float32)
+        o = t_.empty((b, H, DV), dtype=t_.float32, device="cuda")
+        R.rssm_gdn_step(L, gu.dev(q), gu.dev(k), gu.dev(v), gu.dev(np.ones((b, H), np.float32)),
+                        gu.dev(np.zeros((b, H), np.float32)), o)
+        np.testing.assert_array_equal(gu.host(o), exact[..., c].astype(np.float32))
+        R.rssm_rollback(L, gu.dev(np.ones(b, np.int32)))
+
+
+# ---------------------------------------------------- dual / shared --
+
+def _adjacent_fraction(got, want, lp):
+    """(all codes equal or one ulp apart?, fraction unequal)."""
+    if lp == R.RSSM_BF16:
+        g = got.view(np.uint16).astype(np.int64)
+        w = want.astype(np.int64)
+    else:
+        g = got.astype(np.int64)
+        w = want.astype(np.int64)
+    same_sign = (g & (0x8000 if lp == R.RSSM_BF16 else 0x80)) == (w & (0x8000 if lp == R.RSSM_BF16 else 0x80))
+    diff = np.abs(g - w)
+    adj = (diff == 0) | ((diff == 1) & same_sign) | (((g | w) & ~(0x8000 if lp == R.RSSM_BF16 else 0x80)) <= 1)
+    return bool(adj.all()), float((diff != 0).mean())
+
+
+def _run_lowprec(scheme, lp, T, b, H, interval, seed, slow=False):
+    S0, st = _case(seed, T, b, H, s0=0.0)
+    if slow:   # slow decay: alpha = exp(-softplus(N(-5, 1)))
+        g = np.random.default_rng(seed)
+        st["alpha"] = np.exp(-np.logaddexp(0, g.normal(-5.0, 1.0, st["alpha"].shape))).astype(np.float32)
+    L = gu.gdn_layer(S0, interval, scheme=scheme, lp=lp)
+    if scheme == R.RSSM_DUAL:
+        R.rssm_commit(L, None, 0)          # initial low-precision copy from fp32
+    o, pos, ln = gu.gdn_decode(L, {k: gu.dev(v) for k, v in st.items()}, interval, False)
+    ref = drivers.gdn_lowprec(*(st[n] for n in _names()), S0, interval,
+                              "dual" if scheme == R.RSSM_DUAL else "shared",
+                              "bf16" if lp == R.RSSM_BF16 else "e4m3")
+    return L, gu.host(o), ref, st, pos, ln
+
+
+@pytest.mark.parametrize("lp", [R.RSSM_BF16, R.RSSM_E4M3], ids=["bf16", "e4m3"])
+def test_dual_precision_one_quantisation_bound(lp):
+    T, b, H, interval = 48, 4, 8, 8
+    L, o, ref, st, pos, ln = _run_lowprec(R.RSSM_DUAL, lp, T, b, H, interval, 18)
+    # the exact checkpoint of the last commit before each step, and q~
+    S = np.zeros((b, H, DV, DK))
+    worst = 0.0
+    for t in range(T):
+        c0 = (t // interval) * interval
+        if t == c0:
+            Sc = S.copy()
+        U = b * H
+        qt, _ = drivers.gdn_carry_batched(
+            st["q"][t].reshape(U, DK),
+            st["k"][c0:t + 1].transpose(1, 2, 0, 3).reshape(U, -1, DK),
+            st["alpha"][c0:t + 1].transpose(1, 2, 0).reshape(U, -1),
+            st["beta"][c0:t + 1].transpose(1, 2, 0).reshape(U, -1))
+        if lp == R.RSSM_BF16:
+            delta = 2.0 ** -8 * np.abs(Sc)
+        else:
+            amax = np.abs(Sc).reshape(b, H, -1).max(-1)
+            sc = np.where(amax > 0, amax / 448.0, 1.0)[..., None, None]
+            delta = np.maximum(2.0 ** -4 * np.abs(Sc), 2.0 ** -10 * sc)
+        bound = np.einsum("bhrc,bhc->bhr", delta, np.abs(qt.reshape(b, H, DK)))
+        ex = ref["o_exact"][t]
+        slack = 1e-4 * np.abs(ex).max(axis=-1, keepdims=True)
+        err = np.abs(o[t] - ex)
+        assert np.all(err <= bound + slack), t
+        worst = max(worst, float(((err - bound) / np.abs(ex).max()).max()))
+        oracle.gdn_eager(st["q"][t:t + 1], st["k"][t:t + 1], st["v"][t:t + 1],
+                         st["alpha"][t:t + 1], st["beta"][t:t + 1], S)
+    ok, frac = _adjacent_fraction(gu.host(L.ckpt_lp), ref["codes"], lp)
+    assert ok and frac <= 1e-3, frac
+    assert gu.vec_rel_err(gu.host(L.ckpt), ref["state"]) <= 1e-5     # fp32 path untouched
+    assert R.rssm_status(L) == 0
+
+
+@pytest.mark.parametrize("lp", [R.RSSM_BF16, R.RSSM_E4M3], ids=["bf16", "e4m3"])
+def test_shared_precision_reported(lp, capsys):
+    T, b, H, interval = 48, 4, 8, 8
+    L, o, ref, st, pos, ln = _run_lowprec(R.RSSM_SHARED, lp, T, b, H, interval, 19, slow=True)
+    _, od, refd, _, _, _ = _run_lowprec(R.RSSM_DUAL, lp, T, b, H, interval, 19, slow=True)
+    e_sh = np.abs(o - ref["o_exact"]).mean() / np.abs(ref["o_exact"]).mean()
+    e_du = np.abs(od - refd["o_exact"]).mean() / np.abs(refd["o_exact"]).mean()
+    e_emul = gu.vec_rel_err(o, ref["o_emul"])
+    print(f"lp={lp} slow decay: mean rel err shared {e_sh:.3e}  dual {e_du:.3e}; "
+          f"shared vs its emulation (max vec) {e_emul:.3e}")
+    assert np.isfinite(o).all()
+    assert e_sh > e_du          # feeding lp rounding back into the fold costs accuracy
+    assert R.rssm_status(L) == 0

@@ -1,0 +1,378 @@
+#!/usr/bin/env python3
+"""Benchmark of the ReplaySSM decode-time state engine on one MI355X.
+
+Headline workload: Mamba-2 serving-shape decode, one layer, batch 256, 80
+heads, headdim 64, dstate 128, 8 groups, fp32 checkpoint, commit every 8
+tokens (fused into the 8th step), ring of 8.  One benchmark step = one decode
+token for all 256 sequences: append + replay output (+ the fused commit every
+8th step).  Inputs cycle through a pool of 64 distinct seeded steps that is
+resident in HBM before timing starts.
+
+Printed (one JSON line): seq-tokens/s of the replay path (value), the eager
+read-modify-write kernel's seq-tokens/s on the same GPU and the speedup, the
+HBM roofline of the dominant kernel (the replay step without commit), the
+oracle timed on the host cores on a bounded sample, and secondary figures for
+the Gated DeltaNet decode, speculative verify/rollback rounds and the
+dual-precision GDN stack.
+
+Usage: python bench.py [--gpus 1] [--steps 1024] [--warmup 64] [--no-secondary]
+       [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "seq-tokens/s per SSM layer at batch 256 + HBM GB/s vs peak; speedup vs eager"
+COUNTERS = os.path.join(ROOT, "profiles", "m2_step_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_decode_replayssm_amd", "csrc", f)
+                  for f in ("m2_kernels.hip", "common.hpp")]
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ bytes --
+# Algorithmic bytes (what the method must move; 4 bytes per fp32 element).
+def m2_bytes(b, H, G, P, N):
+    S = b * H * P * N * 4
+    inputs = (b * H * P + 2 * b * G * N + b * H) * 4       # x, B, C, dt
+    entry = (b * H * P + b * G * N + b * H) * 4            # one buffered (x, B, dt)
+    out = b * H * P * 4
+    idx = b * (8 + 4) * 2                                   # read + write pos/len
+    return S, inputs, entry, out, idx
+
+
+def m2_step_bytes(b, H, G, P, N, length):
+    """Replay step with `length` previously buffered entries: checkpoint read,
+    current inputs, the buffered entries, the appended entry, the output."""
+    S, inputs, entry, out, idx = m2_bytes(b, H, G, P, N)
+    return S + inputs + length * entry + entry + out + idx
+
+
+def m2_fused_bytes(b, H, G, P, N, length):
+    """Boundary step with fused commit: as a step, minus the append, plus the
+    checkpoint write."""
+    S, inputs, entry, out, idx = m2_bytes(b, H, G, P, N)
+    return S + inputs + length * entry + out + S + idx
+
+
+def m2_eager_bytes(b, H, G, P, N):
+    S, inputs, entry, out, idx = m2_bytes(b, H, G, P, N)
+    return 2 * S + inputs + out
+
+
+def gdn_bytes(b, H, d, s_ck=4):
+    S = b * H * d * d * s_ck
+    inputs = (3 * b * H * d + 2 * b * H) * 4
+    entry = (2 * b * H * d + 2 * b * H) * 4
+    out = b * H * d * 4
+    return S, inputs, entry, out
+
+
+# ------------------------------------------------------------------ timing --
+def run_m2(torch, R, syn, steps, warmup, seed=0, pool_n=64):
+    b, H, G, P, N, interval, cap = 256, 80, 8, 64, 128, 8, 8
+    A, D = syn.m2_params(seed, H)
+    h0 = syn.m2_state0(seed, b, H, P, N)
+    pool = syn.m2_steps(seed, 0, pool_n, b, H, G, P, N)
+    dev = {k: torch.from_numpy(v).to("cuda") for k, v in pool.items()}
+    L = R.Layer.mamba2(b, H, G, P, N, cap)
+    L.A.copy_(torch.from_numpy(A))
+    L.D.copy_(torch.from_numpy(D))
+    L.ckpt.copy_(torch.from_numpy(h0))
+    y = torch.empty((b, H, P), dtype=torch.float32, device="cuda")
+    t = 0
+
+    def step(ev=None):
+        nonlocal t
+        j = t % pool_n
+        commit = (t + 1) % interval == 0
+        if ev is not None:
+            ev[0].record()
+        R.rssm_mamba2_step(L, dev["x"][j], dev["B"][j], dev["C"][j], dev["dt"][j], y,
+                           commit_after=commit)
+        if ev is not None:
+            ev[1].record()
+        t += 1
+        return commit
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: K steps, events around every launch on the launch stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    kinds, lens = [], []
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        lens.append(t % interval)          # entries buffered before this step
+        kinds.append(step(evs[i]))
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    durs = np.array([a.elapsed_time(b_) for a, b_ in evs])
+    kinds = np.array(kinds)
+    lens = np.array(lens)
+    assert R.rssm_status(L) == 0
+    plain = ~kinds
+    plain_bytes = np.array([m2_step_bytes(b, H, G, P, N, l) for l in lens[plain]])
+    fused_bytes = np.array([m2_fused_bytes(b, H, G, P, N, l) for l in lens[kinds]])
+    res = dict(total_ms=total_ms, seq_tok_s=b * steps / (total_ms * 1e-3),
+               step_us=float(durs[plain].mean() * 1e3),
+               step_bytes=float(plain_bytes.mean()),
+               fused_us=float(durs[kinds].mean() * 1e3) if kinds.any() else None,
+               fused_bytes=float(fused_bytes.mean()) if kinds.any() else None,
+               all_bytes=float(plain_bytes.sum() + fused_bytes.sum()),
+               ckpt_bytes_per_step=(b * H * P * N * 4) * (steps + kinds.sum()) / steps)
+    # eager comparator on the same shapes, same pool
+    L.ckpt.copy_(torch.from_numpy(h0))
+    inputs = [R.make_inputs(x=dev["x"][j], B=dev["B"][j], C=dev["C"][j], dt=dev["dt"][j])
+              for j in range(pool_n)]
+    for i in range(warmup):
+        R.rssm_eager_step(L, inputs[i % pool_n], y)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        R.rssm_eager_step(L, inputs[i % pool_n], y)
+    end.record()
+    torch.cuda.synchronize()
+    eager_ms = start.elapsed_time(end)
+    res["eager_seq_tok_s"] = b * steps / (eager_ms * 1e-3)
+    res["eager_us"] = eager_ms * 1e3 / steps
+    res["eager_gbps"] = m2_eager_bytes(b, H, G, P, N) / (res["eager_us"] * 1e-6) / 1e9
+    res["eager_ckpt_bytes_per_step"] = 2 * b * H * P * N * 4
+    res["shape"] = dict(b=b, H=H, G=G, P=P, N=N, interval=interval, cap=cap)
+    del L, dev
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_gdn(torch, R, syn, steps, warmup, seed=0, pool_n=16):
+    b, H, d, interval, cap = 256, 32, 128, 8, 8
+    pool = syn.gdn_steps(seed, 0, pool_n, b, H, d, d)
+    dev = {k: torch.from_numpy(v).to("cuda") for k, v in pool.items()}
+    L = R.Layer.gdn(b, H, d, d, cap)
+    o = torch.empty((b, H, d), dtype=torch.float32, device="cuda")
+    names = ("q", "k", "v", "alpha", "beta")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def replay(n, t0):
+        for t in range(t0, t0 + n):
+            j = t % pool_n
+            R.rssm_gdn_step(L, *(dev[s][j] for s in names), o,
+                            commit_after=(t + 1) % interval == 0)
+
+    replay(warmup, 0)
+    torch.cuda.synchronize()
+    start.record()
+    replay(steps, warmup)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    assert R.rssm_status(L) == 0
+    inputs = [R.make_inputs(**{s: dev[s][j] for s in names}) for j in range(pool_n)]
+    for i in range(warmup):
+        R.rssm_eager_step(L, inputs[i % pool_n], o)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        R.rssm_eager_step(L, inputs[i % pool_n], o)
+    end.record()
+    torch.cuda.synchronize()
+    ems = start.elapsed_time(end)
+    S, inp, entry, out = gdn_bytes(b, H, d)
+    res = dict(seq_tok_s=b * steps / (ms * 1e-3), eager_seq_tok_s=b * steps / (ems * 1e-3),
+               us_per_step=ms * 1e3 / steps, eager_us=ems * 1e3 / steps,
+               eager_gbps=(2 * S + inp + out) / (ems * 1e-3 / steps) / 1e9)
+    res["speedup_vs_eager"] = res["seq_tok_s"] / res["eager_seq_tok_s"]
+    del L, dev
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
+    """Mamba-2 speculative rounds at the serving shape: verify 4 drafts,
+    roll back the rejected ones, commit at 8 buffered entries; ring 12."""
+    b, H, G, P, N, cap, n, commit_len = 256, 80, 8, 64, 128, 12, 4, 8
+    A, D = syn.m2_params(seed, H)
+    pool = syn.m2_steps(seed, 0, pool_n, b, H, G, P, N)
+    dev = {k: torch.from_numpy(v).to("cuda") for k, v in pool.items()}
+    accept = syn.accept_counts(seed, rounds, b, n)
+    nrej = torch.from_numpy((n - accept).astype(np.int32)).to("cuda")
+    L = R.Layer.mamba2(b, H, G, P, N, cap)
+    L.A.copy_(torch.from_numpy(A))
+    L.D.copy_(torch.from_numpy(D))
+    L.ckpt.copy_(torch.from_numpy(syn.m2_state0(seed, b, H, P, N)))
+    out = torch.empty((n, b, H, P), dtype=torch.float32, device="cuda")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for r in range(rounds):
+        j = (r * n) % pool_n
+        R.rssm_verify(L, n, R.make_inputs(x=dev["x"][j:j + n], B=dev["B"][j:j + n],
+                                          C=dev["C"][j:j + n], dt=dev["dt"][j:j + n]), out)
+        R.rssm_rollback(L, nrej[r])
+        R.rssm_commit(L, None, commit_len)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    assert R.rssm_status(L) == 0
+    res = dict(rounds_per_s=rounds / (ms * 1e-3),
+               accepted_seq_tok_s=float(accept.sum()) / (ms * 1e-3),
+               us_per_round=ms * 1e3 / rounds)
+    del L, dev
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_dual_stack(torch, R, syn, steps, seed=0, layers=12, pool_n=8):
+    """12 GDN layers at batch 256 with a low-precision serving checkpoint,
+    standalone commit every 8 steps; seq-tokens/s through the whole stack."""
+    b, H, d, interval, cap = 256, 32, 128, 8, 8
+    pool = syn.gdn_steps(seed, 0, pool_n, b, H, d, d)
+    dev = {k: torch.from_numpy(v).to("cuda") for k, v in pool.items()}
+    names = ("q", "k", "v", "alpha", "beta")
+    o = torch.empty((b, H, d), dtype=torch.float32, device="cuda")
+    res = {}
+    for scheme, sname in ((R.RSSM_DUAL, "dual"), (R.RSSM_SHARED, "shared")):
+        for lp, lname in ((R.RSSM_BF16, "bf16"), (R.RSSM_E4M3, "e4m3")):
+            Ls = [R.Layer.gdn(b, H, d, d, cap, scheme=scheme, lp_dtype=lp) for _ in range(layers)]
+            for L in Ls:
+                R.rssm_commit(L, None, 0)
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record()
+            for t in range(steps):
+                j = t % pool_n
+                for L in Ls:
+                    R.rssm_gdn_step(L, *(dev[s][j] for s in names), o)
+                    if (t + 1) % interval == 0:
+                        R.rssm_commit(L, None, 0)
+            end.record()
+            torch.cuda.synchronize()
+            ms = start.elapsed_time(end)
+            for L in Ls:
+                assert R.rssm_status(L) == 0
+            res[f"{sname}_{lname}"] = b * steps / (ms * 1e-3)
+            del Ls
+            torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(syn, target_s=12.0, seed=0):
+    """The fp64 oracle's eager recurrence on a bounded sample of the headline
+    workload: 16 sequences x 80 heads, inputs cycling through 16 seeded steps,
+    as many steps as fit in about target_s seconds."""
+    import oracle
+    b, H, G, P, N, pool = 16, 80, 8, 64, 128, 16
+    A, D = syn.m2_params(seed, H)
+    h = syn.m2_state0(seed, b, H, P, N).astype(np.float64)
+    st = syn.m2_steps(seed, 0, pool, b, H, G, P, N)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.m2_eager(A, D, st["x"][:2], st["B"][:2], st["C"][:2], st["dt"][:2], h)
+    per = (time.perf_counter() - t0) / 2
+    n = int(max(pool, min(16384, target_s / max(per, 1e-9))))
+    n = max(pool, (n // pool) * pool)
+    t0 = time.perf_counter()
+    for _ in range(n // pool):
+        oracle.m2_eager(A, D, st["x"], st["B"], st["C"], st["dt"], h)
+    el = time.perf_counter() - t0
+    return {"value": round(b * n / el, 1), "unit": "seq-tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 eager Mamba-2 recurrence (the oracle, OpenMP over units), "
+                      f"{b} sequences x {H} heads x {n} steps of the batch-256 serving shape "
+                      f"(P=64, N=128, G=8); {el:.1f} s on {threads} host threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: every (sequence, head) unit of the state engine is "
+              "independent, so this build runs and reports a single MI355X only "
+              "(--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from linear_attention_decode_replayssm_amd import rssm as R
+    from linear_attention_decode_replayssm_amd import synthetic as syn
+    R.lib()                                   # fail loudly if the HIP library is missing
+    torch.cuda.init()
+
+    m2 = run_m2(torch, R, syn, args.steps, args.warmup)
+    step_gbps = m2["step_bytes"] / (m2["step_us"] * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(COUNTERS):
+        c = json.load(open(COUNTERS))
+        if c.get("kernel_source_sha") == kernel_source_sha():
+            traffic = c.get("hbm_bytes_per_launch")
+    out = {
+        "metric": METRIC,
+        "value": round(m2["seq_tok_s"], 1),
+        "unit": "seq-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m2["total_ms"] / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "mamba2-decode-replay: 1 layer, batch 256, 80 heads, headdim 64, "
+                               "dstate 128, 8 groups, fp32 checkpoint, commit every 8 tokens "
+                               "(fused), ring 8",
+                   "global_batch": 256, "seq_len": args.steps, "parallelism": "single-gpu"},
+        "hbm_gbps": round(m2["all_bytes"] / (m2["total_ms"] * 1e-3) / 1e9, 1),
+        "hbm_frac": round(m2["all_bytes"] / (m2["total_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "eager": {"value": round(m2["eager_seq_tok_s"], 1), "unit": "seq-tokens/s",
+                  "us_per_step": round(m2["eager_us"], 2),
+                  "hbm_gbps": round(m2["eager_gbps"], 1)},
+        "speedup_vs_eager": round(m2["seq_tok_s"] / m2["eager_seq_tok_s"], 4),
+        "ckpt_bytes_per_step_vs_eager": round(m2["ckpt_bytes_per_step"] /
+                                              m2["eager_ckpt_bytes_per_step"], 4),
+        "roofline": {"bound": "hbm", "kernel": "m2_step_kernel<false> (replay step, no commit)",
+                     "achieved": round(step_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(step_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "avg_launch_us": round(m2["step_us"], 3),
+                     "bytes_per_launch": int(m2["step_bytes"]),
+                     "fused_commit_launch_us": round(m2["fused_us"], 3) if m2["fused_us"] else None},
+    }
+    if not args.no_secondary:
+        sec_steps = max(64, min(args.steps, 256))
+        g = run_gdn(torch, R, syn, sec_steps, 16)
+        sp = run_spec(torch, R, syn, 128)
+        du = run_dual_stack(torch, R, syn, 32)
+        out["secondary"] = {
+            "gdn_decode_b256_h32_d128": {k: round(v, 2) for k, v in g.items()},
+            "mamba2_spec_rounds_b256_4drafts": {k: round(v, 1) for k, v in sp.items()},
+            "gdn_12layer_stack_seq_tok_s": {k: round(v, 1) for k, v in du.items()},
+        }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(syn)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -131,35 +131,56 @@ __device__ __forceinline__ void allreduce(float (&v)[V]) {
 }
 
 // ---- per-sequence index update --------------------------------------------
-// Every workgroup of sequence b reads len[b]/ckpt_pos[b] at its start and has
-// consumed the values (they shaped all of its work) before it reaches this
-// point.  At its end it counts itself in arrive[b]; the workgroup that
-// completes the count knows that all `nwg` workgroups of the sequence have
-// read the indices, resets the counter and applies the update.  Nothing in
-// this launch reads the indices afterwards and the next launch sees them
-// through the kernel boundary, so the counter needs no fence: a relaxed
-// device-scope atomic.  (A device-scope fence here would write back and
-// invalidate the XCD's L2 once per workgroup.)  Must be reached by all
-// threads.
+// Every workgroup of sequence b reads len[b] / ckpt_pos[b] at its start.  The
+// workgroup that completes the per-sequence count in arrive[b] knows that all
+// `nwg` workgroups of the sequence have read the indices; it resets the
+// counter and applies the update.  Nothing in the launch reads the indices
+// afterwards and the next launch sees them through the kernel boundary, so
+// the counter needs no fence: a relaxed device-scope atomic.  (A device-scope
+// fence would write back and invalidate the XCD's L2 once per workgroup.)
 struct IndexUpdate {
   int64_t pos_add;
   int32_t new_len;
   bool apply;
 };
 
-__device__ __forceinline__ void arrive_and_update(uint32_t* arrive, int64_t* pos,
-                                                  int32_t* len, int b, int nwg,
-                                                  IndexUpdate u) {
+// Each wave reads the indices with its own scalar load.  Once this returns,
+// every wave of the workgroup has received them: each wave's leader stores a
+// value computed from them to LDS before the barrier, which cannot happen
+// before its loads have returned.  (The barrier does not wait for the
+// workgroup's outstanding vector loads.)
+__device__ __forceinline__ void indices_consumed(int32_t len, int64_t pos) {
+  __shared__ int32_t seen[16];
+  if ((threadIdx.x & 63) == 0) seen[threadIdx.x >> 6] = len ^ (int32_t)pos;
   __syncthreads();
+}
+
+// Early variant: count the workgroup right after its index reads, so that the
+// atomic's round trip overlaps the state stream instead of ending the
+// workgroup.  The increment is computed from the values read (it is 1 for
+// every valid index: len >= 0, pos >= 0), so the atomic cannot be performed
+// before those reads have returned; once the count is complete every
+// workgroup of the sequence holds its copy of the indices and the last one
+// may update them at any time.  Returns the pre-increment count (thread 0).
+__device__ __forceinline__ uint32_t arrive_early(uint32_t* arrive, int b, int32_t len,
+                                                 int64_t pos) {
+  uint32_t old = 0u;
   if (threadIdx.x == 0) {
-    const uint32_t old =
-        __hip_atomic_fetch_add(&arrive[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == (uint32_t)(nwg - 1)) {
-      __hip_atomic_store(&arrive[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (u.apply) {
-        pos[b] += u.pos_add;
-        len[b] = u.new_len;
-      }
+    const uint32_t inc = 1u + (uint32_t)(len < 0) + (uint32_t)(pos < 0);
+    old = __hip_atomic_fetch_add(&arrive[b], inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return old;
+}
+
+// Completes arrive_early: the workgroup that completed the count resets it and
+// applies the update.  Thread 0 only; no barrier needed.
+__device__ __forceinline__ void finish_update(uint32_t* arrive, int64_t* pos, int32_t* len,
+                                              int b, int nwg, uint32_t old, IndexUpdate u) {
+  if (threadIdx.x == 0 && old == (uint32_t)(nwg - 1)) {
+    __hip_atomic_store(&arrive[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (u.apply) {
+      pos[b] += u.pos_add;
+      len[b] = u.new_len;
     }
   }
 }

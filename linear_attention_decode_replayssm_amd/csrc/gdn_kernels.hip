@@ -144,17 +144,6 @@ struct Src {
   }
 };
 
-// Append input position j (0-based) to the ring at entry len + j.
-__device__ __forceinline__ void append_entry(const GdnArgs& a, const Src& src, int j, int tid) {
-  const int s = ring_slot(src.slot0, src.len + j, src.cap);
-  const long u = src.unit;
-  if (tid < DK) a.ring_k[(u * src.cap + s) * DK + tid] = a.k[j * src.sk + u * DK + tid];
-  else if (tid < DK + DV)
-    a.ring_v[(u * src.cap + s) * DV + (tid - DK)] = a.v[j * src.sk + u * DV + (tid - DK)];
-  else if (tid == DK + DV) a.ring_a[u * src.cap + s] = a.alpha[j * src.sd + u];
-  else if (tid == DK + DV + 1) a.ring_b[u * src.cap + s] = a.beta[j * src.sd + u];
-}
-
 template <int EPL>
 __device__ __forceinline__ void load_vec(const float* p, float (&v)[EPL]) {
   if constexpr (EPL % 4 == 0) {
@@ -172,63 +161,120 @@ __device__ __forceinline__ void load_vec(const float* p, float (&v)[EPL]) {
   }
 }
 
+// ---- buffered entries staged in LDS ---------------------------------------
+// Every kernel that replays the buffer first fetches all of its entries
+// (k, v, alpha, beta of up to kMaxCap positions, one float4 of k and v per
+// thread) into registers, issues the state stream after them, and then parks
+// the entries in LDS.  The sequential backward carry and the fold then run
+// from LDS instead of waiting on a dependent global load per entry.
+struct EntrySmem {
+  float k[kMaxCap][DK];
+  float v[kMaxCap][DV];
+  float al[kMaxCap], be[kMaxCap];
+};
+static_assert(kMaxCap * DK / 4 <= NT && kMaxCap * DV / 4 <= NT, "one float4 per thread");
+
+struct EntryRegs {
+  f32x4 k, v;
+  float al, be;
+};
+
+__device__ __forceinline__ EntryRegs fetch_entries(const Src& src, int L, int tid) {
+  EntryRegs e;
+  e.k = e.v = f32x4{0.f, 0.f, 0.f, 0.f};
+  e.al = e.be = 0.f;
+  const int i = tid / (DK / 4), c = (tid % (DK / 4)) * 4;
+  if (i < L) {
+    e.k = ld4(src.k(i) + c);
+    e.v = ld4(src.v(i) + c);
+  }
+  if (tid < L) {
+    e.al = src.alpha(tid);
+    e.be = src.beta(tid);
+  }
+  return e;
+}
+
+__device__ __forceinline__ void stash_entries(const EntryRegs& e, int L, int tid, EntrySmem& s) {
+  const int i = tid / (DK / 4), c = (tid % (DK / 4)) * 4;
+  if (i < L) {
+    st4(&s.k[i][c], e.k);
+    st4(&s.v[i][c], e.v);
+  }
+  if (tid < L) {
+    s.al[tid] = e.al;
+    s.be[tid] = e.be;
+  }
+}
+
+// Write entry i (held in registers by fetch_entries) to its ring slot.
+__device__ __forceinline__ void append_from_regs(const GdnArgs& a, const Src& src,
+                                                 const EntryRegs& e, int i, int tid) {
+  const int s = ring_slot(src.slot0, i, src.cap);
+  const long u = src.unit;
+  const int ei = tid / (DK / 4), c = (tid % (DK / 4)) * 4;
+  if (ei == i) {
+    st4(a.ring_k + (u * src.cap + s) * DK + c, e.k);
+    st4(a.ring_v + (u * src.cap + s) * DV + c, e.v);
+  }
+  if (tid == i) {
+    a.ring_a[u * src.cap + s] = e.al;
+    a.ring_b[u * src.cap + s] = e.be;
+  }
+}
+
 // Backward carry of a query through entries hi..0 (newest first), held as EPL
 // consecutive elements per lane on LPR lanes (lanes repeat every LPR).
 template <int EPL, int LPR>
-__device__ __forceinline__ void carry(const Src& src, int hi, int cl, float (&q)[EPL],
-                                      float (&s)[kMaxCap]) {
+__device__ __forceinline__ void carry(const EntrySmem& s, int hi, int cl, float (&q)[EPL],
+                                      float (&sv)[kMaxCap]) {
 #pragma unroll
   for (int i = kMaxCap - 1; i >= 0; --i) {
     if (i <= hi) {
       float kv[EPL];
-      load_vec<EPL>(src.k(i) + cl * EPL, kv);
+      load_vec<EPL>(&s.k[i][cl * EPL], kv);
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) part += kv[e] * q[e];
 #pragma unroll
       for (int m = LPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m);
-      const float si = src.beta(i) * part;
-      const float al = src.alpha(i);
-      s[i] = si;
+      const float si = s.be[i] * part;
+      const float al = s.al[i];
+      sv[i] = si;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) q[e] = al * (q[e] - si * kv[e]);
     } else {
-      s[i] = 0.f;
+      sv[i] = 0.f;
     }
   }
 }
 
 // ---------------------------------------------------------------- fold ----
-// Shared-memory workspace of the fold (fp32 geometry, whole head per WG).
+// With u_i = beta_i (v_i - alpha_i a_i) and a_i = G_{c+1..i-1} (S_c k_i)
+// + sum_{m<i} G_{m+1..i-1} (k_m . k_i) u_m, every row r satisfies the same
+// unit lower-triangular system (I + diag(beta alpha) Lc) u = z,
+// z_j = beta_j v_j - beta_j alpha_j G_{c+1..j-1} (S_c k_j),
+// Lc[i][m] = G_{m+1..i-1} (k_m . k_i).  Its inverse T is the same for all
+// rows, so it is formed once (L x L) and each row's fold weights
+// U'_i = G_{i+1..t} u_i = sum_j T'[i][j] z_j are independent dot products.
 struct FoldSmem {
-  float k[kMaxCap][DK];
-  float v[kMaxCap][DV];
-  float al[kMaxCap], be[kMaxCap];
   float G[kMaxCap + 1][kMaxCap + 1];   // G[a][e] = prod_{j=a}^{e-1} alpha_j
   float gram[kMaxCap][kMaxCap];        // k_m . k_i
+  float P1[kMaxCap][kMaxCap];          // G_{i+1..} T[i][j] beta_j
+  float P2[kMaxCap][kMaxCap];          // G_{i+1..} T[i][j] beta_j alpha_j G_{..j-1}
   float W[DV][kMaxCap + 1];            // S_c k_i
-  float U[DV][kMaxCap + 1];            // G_{i+1..L-1} u_i
+  float U[DV][kMaxCap + 1];            // U'_i of row r
   float red[NT / 64];
 };
 
-// Fold entries 0..L-1 into the fp32 tile hv (fp32 geometry), in place.
-__device__ void fold_tile(f32x4 (&hv)[F32Geo::NLD], const Src& src, int L, const Geo& q,
+// Fold entries 0..L-1 (staged in es) into the fp32 tile hv (fp32 geometry).
+__device__ void fold_tile(f32x4 (&hv)[F32Geo::NLD], const EntrySmem& es, int L, const Geo& q,
                           FoldSmem& sm) {
   constexpr int RPL = F32Geo::RPL, NLD = F32Geo::NLD, LPR = F32Geo::LPR;
-  for (int idx = q.tid; idx < L * DK; idx += NT) {
-    const int i = idx / DK, c = idx % DK;
-    sm.k[i][c] = src.k(i)[c];
-    sm.v[i][c] = src.v(i)[c];
-  }
-  if (q.tid < L) {
-    sm.al[q.tid] = src.alpha(q.tid);
-    sm.be[q.tid] = src.beta(q.tid);
-  }
-  __syncthreads();
   if (q.tid < (L + 1) * (L + 1)) {
     const int a0 = q.tid / (L + 1), e0 = q.tid % (L + 1);
     float p = 1.f;
-    for (int j = a0; j < e0; ++j) p *= sm.al[j];
+    for (int j = a0; j < e0; ++j) p *= es.al[j];
     sm.G[a0][e0] = p;
   }
   {  // Gram matrix, 16 lanes per pair
@@ -239,7 +285,8 @@ __device__ void fold_tile(f32x4 (&hv)[F32Geo::NLD], const Src& src, int L, const
       float part = 0.f;
       if (m < L && i < L) {
 #pragma unroll
-        for (int e = 0; e < DK / 16; ++e) part += sm.k[m][sgm * (DK / 16) + e] * sm.k[i][sgm * (DK / 16) + e];
+        for (int e = 0; e < DK / 16; ++e)
+          part += es.k[m][sgm * (DK / 16) + e] * es.k[i][sgm * (DK / 16) + e];
       }
       part += __shfl_xor(part, 8);
       part += __shfl_xor(part, 4);
@@ -254,7 +301,7 @@ __device__ void fold_tile(f32x4 (&hv)[F32Geo::NLD], const Src& src, int L, const
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       f32x4 kv = {0.f, 0.f, 0.f, 0.f};
-      if (i0 + jj < L) kv = ld4(&sm.k[i0 + jj][q.cl * 4]);
+      if (i0 + jj < L) kv = ld4(&es.k[i0 + jj][q.cl * 4]);
 #pragma unroll
       for (int k = 0; k < NLD; ++k) d[k * 4 + jj] = dot4(hv[k], kv);
     }
@@ -266,46 +313,63 @@ __device__ void fold_tile(f32x4 (&hv)[F32Geo::NLD], const Src& src, int L, const
     if (i0 + jj < L) sm.W[k * RPL + q.r0][i0 + jj] = d[0];
   }
   __syncthreads();
-  if (q.tid < DV) {  // forward substitution for row r
-    const int r = q.tid;
-    float u[kMaxCap];
+  if (q.tid < L) {  // column j of T = (I + diag(beta alpha) Lc)^-1
+    const int j = q.tid;
+    float t[kMaxCap];
 #pragma unroll
     for (int i = 0; i < kMaxCap; ++i) {
-      u[i] = 0.f;
-      if (i < L) {
-        float acc = sm.G[0][i] * sm.W[r][i];
+      float v = 0.f;
+      if (i == j) {
+        v = 1.f;
+      } else if (i > j && i < L) {
+        float acc = 0.f;
 #pragma unroll
         for (int m = 0; m < kMaxCap; ++m)
-          if (m < i) acc += sm.G[m + 1][i] * sm.gram[m][i] * u[m];
-        u[i] = sm.be[i] * (sm.v[i][r] - sm.al[i] * acc);
+          if (m >= j && m < i) acc += sm.G[m + 1][i] * sm.gram[m][i] * t[m];
+        v = -es.be[i] * es.al[i] * acc;
+      }
+      t[i] = v;
+    }
+    const float bj = es.be[j], bag = es.be[j] * es.al[j] * sm.G[0][j];
+#pragma unroll
+    for (int i = 0; i < kMaxCap; ++i) {
+      if (i < L) {
+        const float w = sm.G[i + 1][L] * t[i];
+        sm.P1[i][j] = w * bj;
+        sm.P2[i][j] = w * bag;
       }
     }
-#pragma unroll
-    for (int i = 0; i < kMaxCap; ++i)
-      if (i < L) sm.U[r][i] = sm.G[i + 1][L] * u[i];
+  }
+  __syncthreads();
+  {  // U'[r][i] = sum_{j<=i} P1[i][j] v_j[r] - P2[i][j] W[r][j]
+    const int r = q.tid % DV, ig = q.tid / DV;
+    for (int i = ig; i < L; i += NT / DV) {
+      float acc = 0.f;
+      for (int j = 0; j <= i; ++j) acc += sm.P1[i][j] * es.v[j][r] - sm.P2[i][j] * sm.W[r][j];
+      sm.U[r][i] = acc;
+    }
   }
   __syncthreads();
   const float gall = sm.G[0][L];
 #pragma unroll
   for (int k = 0; k < NLD; ++k) hv[k] *= gall;
   for (int i = 0; i < L; ++i) {
-    const f32x4 kv = ld4(&sm.k[i][q.cl * 4]);
+    const f32x4 kv = ld4(&es.k[i][q.cl * 4]);
 #pragma unroll
     for (int k = 0; k < NLD; ++k) hv[k] += sm.U[k * RPL + q.r0][i] * kv;
   }
 }
 
-// Workgroup max of |hv|.
+// Workgroup max of |hv|; a NaN anywhere makes the result +inf.
 __device__ float tile_amax(const f32x4 (&hv)[F32Geo::NLD], const Geo& q, float* red) {
   float m = 0.f;
+  bool nan = false;
 #pragma unroll
-  for (int k = 0; k < F32Geo::NLD; ++k)
+  for (int k = 0; k < F32Geo::NLD; ++k) {
     m = fmaxf(m, fmaxf(fmaxf(fabsf(hv[k].x), fabsf(hv[k].y)), fmaxf(fabsf(hv[k].z), fabsf(hv[k].w))));
-  // NaN must survive the reduction: fmaxf would drop it
-#pragma unroll
-  for (int k = 0; k < F32Geo::NLD; ++k)
-    if (!(hv[k].x == hv[k].x && hv[k].y == hv[k].y && hv[k].z == hv[k].z && hv[k].w == hv[k].w))
-      m = __builtin_inff();
+    nan |= !(hv[k].x == hv[k].x && hv[k].y == hv[k].y && hv[k].z == hv[k].z && hv[k].w == hv[k].w);
+  }
+  if (nan) m = __builtin_inff();
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s));
   __syncthreads();
@@ -388,17 +452,14 @@ __device__ __forceinline__ void store_f32_tile(const f32x4 (&hv)[F32Geo::NLD], f
 // ---------------------------------------------------------------- step ----
 // EB: bytes per checkpoint element read for the output (4: ckpt fp32; 2: bf16
 // ckpt_lp; 1: E4M3 ckpt_lp).  FUSED (fp32 only): fold and store after output.
+// Order: buffered entries and the query are fetched, then the state stream is
+// issued, then the entries are parked in LDS while the stream is in flight.
 template <int EB, bool FUSED>
 __global__ __launch_bounds__(NT) void gdn_step_kernel(GdnArgs a) {
   using Gm = LpGeo<EB>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPL = Gm::RPL, NLD = Gm::NLD;
   const Geo q = geometry<LPR>(a);
   const int cap = a.cap;
-
-  const char* base = state_base<EB>(a, q.unit);
-  u32x4 raw[NLD];
-#pragma unroll
-  for (int k = 0; k < NLD; ++k) raw[k] = ld_nt_u(base + ((k * RPL + q.r0) * DK + q.cl * EPL) * EB);
 
   const int len = a.len[q.b];
   const int64_t pos = a.pos[q.b];
@@ -407,13 +468,24 @@ __global__ __launch_bounds__(NT) void gdn_step_kernel(GdnArgs a) {
   Src src{&a, q.unit, len, (int)(pos % cap), cap, 0, 0};
   const float scale = (EB == 1) ? a.lp_scale[q.unit] : 1.f;
 
-  if (ok && !FUSED) append_entry(a, src, 0, q.tid);
-
+  EntryRegs er = fetch_entries(src, ok ? L : 0, q.tid);
   float qv[EPL];
   load_vec<EPL>(a.q + q.unit * DK + q.cl * EPL, qv);
+
+  const char* base = state_base<EB>(a, q.unit);
+  u32x4 raw[NLD];
+#pragma unroll
+  for (int k = 0; k < NLD; ++k) raw[k] = ld_nt_u(base + ((k * RPL + q.r0) * DK + q.cl * EPL) * EB);
+  indices_consumed(len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
+
+  __shared__ __attribute__((aligned(16))) EntrySmem es;
+  stash_entries(er, ok ? L : 0, q.tid, es);
+  __syncthreads();
+
   float s[kMaxCap];
   if (ok) {
-    carry<EPL, LPR>(src, L - 1, q.cl, qv, s);
+    carry<EPL, LPR>(es, L - 1, q.cl, qv, s);
   } else {
 #pragma unroll
     for (int i = 0; i < kMaxCap; ++i) s[i] = 0.f;
@@ -438,7 +510,7 @@ __global__ __launch_bounds__(NT) void gdn_step_kernel(GdnArgs a) {
       ov = scale * d[0];
 #pragma unroll
       for (int i = 0; i < kMaxCap; ++i)
-        if (i < L) ov += s[i] * src.v(i)[r];
+        if (i < L) ov += s[i] * es.v[i][r];
     } else {
       ov = __builtin_nanf("");
     }
@@ -448,22 +520,24 @@ __global__ __launch_bounds__(NT) void gdn_step_kernel(GdnArgs a) {
   if constexpr (FUSED) {
     static_assert(EB == 4, "fused commit folds the fp32 checkpoint");
     if (ok) {
-      __shared__ FoldSmem sm;
+      __shared__ __attribute__((aligned(16))) FoldSmem sm;
       f32x4 hv[NLD];
 #pragma unroll
       for (int k = 0; k < NLD; ++k)
         hv[k] = f32x4{__uint_as_float(raw[k].x), __uint_as_float(raw[k].y),
                       __uint_as_float(raw[k].z), __uint_as_float(raw[k].w)};
-      fold_tile(hv, src, L, q, sm);
+      fold_tile(hv, es, L, q, sm);
       store_f32_tile(hv, a.ckpt + q.unit * (DV * DK), q);
     }
+  } else {
+    if (ok) append_from_regs(a, src, er, len, q.tid);
   }
 
   IndexUpdate u;
   u.apply = ok;
   u.pos_add = FUSED ? L : 0;
   u.new_len = FUSED ? 0 : L;
-  arrive_and_update(a.arrive, a.pos, a.len, q.b, a.H, u);
+  finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
   if (!ok && q.tid == 0) raise_status(a.status, kStatusOverflow);
 }
 
@@ -479,15 +553,22 @@ __global__ __launch_bounds__(NT) void gdn_commit_kernel(GdnArgs a) {
   if (len == 0 && SCHEME != kSchemeDual) {  // nothing to fold, nothing to refresh
     return;
   }
-  __shared__ FoldSmem sm;
+  const int64_t pos = a.pos[q.b];
+  Src src{&a, q.unit, len, (int)(pos % a.cap), a.cap, 0, 0};
+  EntryRegs er = fetch_entries(src, len, q.tid);
   f32x4 hv[F32Geo::NLD];
   if constexpr (SCHEME == kSchemeShared)
     load_lp_as_f32<LP>(hv, a, q);
   else
     load_f32_tile(hv, a.ckpt + q.unit * (DV * DK), q);
-  Src src{&a, q.unit, len, (int)(a.pos[q.b] % a.cap), a.cap, 0, 0};
+  indices_consumed(len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
+  __shared__ __attribute__((aligned(16))) EntrySmem es;
+  __shared__ __attribute__((aligned(16))) FoldSmem sm;
+  stash_entries(er, len, q.tid, es);
+  __syncthreads();
   if (len > 0) {
-    fold_tile(hv, src, len, q, sm);
+    fold_tile(hv, es, len, q, sm);
     if constexpr (SCHEME != kSchemeShared) store_f32_tile(hv, a.ckpt + q.unit * (DV * DK), q);
   }
   if constexpr (SCHEME != kSchemeF32) store_lp<LP>(hv, a, q, sm.red);
@@ -496,7 +577,7 @@ __global__ __launch_bounds__(NT) void gdn_commit_kernel(GdnArgs a) {
   u.apply = len > 0;
   u.pos_add = len;
   u.new_len = 0;
-  arrive_and_update(a.arrive, a.pos, a.len, q.b, a.H, u);
+  finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
 }
 
 // -------------------------------------------------------------- verify ----
@@ -511,11 +592,6 @@ __global__ __launch_bounds__(NT) void gdn_verify_kernel(GdnArgs a) {
   const Geo q = geometry<LPR>(a);
   const int cap = a.cap, n = a.n_pos;
 
-  const char* base = state_base<EB>(a, q.unit);
-  u32x4 raw[NLD];
-#pragma unroll
-  for (int k = 0; k < NLD; ++k) raw[k] = ld_nt_u(base + ((k * RPL + q.r0) * DK + q.cl * EPL) * EB);
-
   const int len = a.len[q.b];
   const int64_t pos = a.pos[q.b];
   const bool ok = len + n <= cap;
@@ -524,26 +600,35 @@ __global__ __launch_bounds__(NT) void gdn_verify_kernel(GdnArgs a) {
   Src src{&a, q.unit, len, (int)(pos % cap), cap, sk, sd};
   const float scale = (EB == 1) ? a.lp_scale[q.unit] : 1.f;
 
+  EntryRegs er = fetch_entries(src, ok ? len + n : 0, q.tid);
+  const int w = q.tid >> 6;
+  float qv[2] = {0.f, 0.f};
+  if (ok && w < n) load_vec<2>(a.q + w * sk + q.unit * DK + 2 * q.lane, qv);
+
+  const char* base = state_base<EB>(a, q.unit);
+  u32x4 raw[NLD];
+#pragma unroll
+  for (int k = 0; k < NLD; ++k) raw[k] = ld_nt_u(base + ((k * RPL + q.r0) * DK + q.cl * EPL) * EB);
+  indices_consumed(len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
+
+  __shared__ __attribute__((aligned(16))) EntrySmem es;
   __shared__ __attribute__((aligned(16))) float s_q[NPAD][DK];
   __shared__ float s_s[NPAD][kMaxCap];
+  stash_entries(er, ok ? len + n : 0, q.tid, es);
+  __syncthreads();
 
-  if (ok) {
-    for (int j = 0; j < n; ++j) append_entry(a, src, j, q.tid);
-    const int w = q.tid >> 6;
-    if (w < n) {  // wave w carries draft w (2 elements per lane)
-      float qv[2];
-      load_vec<2>(a.q + w * sk + q.unit * DK + 2 * q.lane, qv);
-      float s[kMaxCap];
-      carry<2, 64>(src, len + w, q.lane, qv, s);
-      s_q[w][2 * q.lane] = qv[0];
-      s_q[w][2 * q.lane + 1] = qv[1];
-      if (q.lane < kMaxCap) {
-        float sv = 0.f;
+  if (ok && w < n) {  // wave w carries draft w (2 elements per lane)
+    float s[kMaxCap];
+    carry<2, 64>(es, len + w, q.lane, qv, s);
+    s_q[w][2 * q.lane] = qv[0];
+    s_q[w][2 * q.lane + 1] = qv[1];
+    if (q.lane < kMaxCap) {
+      float sv = 0.f;
 #pragma unroll
-        for (int i = 0; i < kMaxCap; ++i)
-          if (i == q.lane) sv = s[i];
-        s_s[w][q.lane] = sv;
-      }
+      for (int i = 0; i < kMaxCap; ++i)
+        if (i == q.lane) sv = s[i];
+      s_s[w][q.lane] = sv;
     }
   }
   __syncthreads();
@@ -576,7 +661,7 @@ __global__ __launch_bounds__(NT) void gdn_verify_kernel(GdnArgs a) {
         float ov;
         if (ok) {
           ov = scale * d[jj];
-          for (int i = 0; i <= len + j; ++i) ov += s_s[j][i] * src.v(i)[r];
+          for (int i = 0; i <= len + j; ++i) ov += s_s[j][i] * es.v[i][r];
         } else {
           ov = __builtin_nanf("");
         }
@@ -584,12 +669,14 @@ __global__ __launch_bounds__(NT) void gdn_verify_kernel(GdnArgs a) {
       }
     }
   }
+  if (ok)
+    for (int j = 0; j < n; ++j) append_from_regs(a, src, er, len + j, q.tid);
 
   IndexUpdate u;
   u.apply = ok;
   u.pos_add = 0;
   u.new_len = len + n;
-  arrive_and_update(a.arrive, a.pos, a.len, q.b, a.H, u);
+  finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
   if (!ok && q.tid == 0) raise_status(a.status, kStatusOverflow);
 }
 

@@ -9,9 +9,10 @@
 // Replay step (ReplaySSM abstract; explainer "Compute outputs without eagerly
 // updating the checkpoint"), with Gamma_{m..n} = exp(A * sum_{j=m..n} dt_j):
 //   y_t = Gamma_{c+1..t} h_c C_t + sum_i Gamma_{i+1..t} dt_i (B_i . C_t) x_i + D x_t
-// The checkpoint loads are issued first; the replay prologue (B_i . C_t dots,
-// dt suffix sums, decay weights, the sum over buffered x_i) runs while they
-// are in flight; then each row is dotted with C_t and reduced across the 32
+// The replay prologue's operands (B_i and C_t segments, dt_i, x_i) are loaded
+// first, the checkpoint stream right after; the prologue (B_i . C_t dots, dt
+// suffix sums, decay weights, the sum over buffered x_i) runs while the stream
+// is in flight; then each row is dotted with C_t and reduced across the 32
 // lanes that hold it.  The checkpoint is not written.
 //
 // Commit (explainer, "Periodically commit a new checkpoint"), a rank-L update:
@@ -123,6 +124,8 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
 
   f32x4 hv[NLD];
   load_tile(ck, q, hv);
+  indices_consumed(len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
 
   __shared__ float s_e[kMaxCap], s_dt[kMaxCap], s_w[kMaxCap], s_fw[kMaxCap];
   __shared__ float s_gamma;
@@ -204,12 +207,19 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
       store_tile(ck, q, hv);
     }
   } else {
-    if (ok) {  // append this step's entry to the ring
+    if (ok) {  // append this step's entry from the registers that loaded it
       const int s = ring_slot(slot0, len, cap);
-      if (q.tid < P) a.ring_x[(q.unit * cap + s) * P + q.tid] = xt[q.tid];
-      if (q.tid == 0) a.ring_dt[q.unit * cap + s] = a.dt[q.unit];
-      if ((q.h % (a.H / a.G)) == 0 && q.tid < N)
-        a.ring_B[(q.gunit * cap + s) * N + q.tid] = Bt[q.tid];
+#pragma unroll
+      for (int m = 0; m < XPT; ++m)
+        if (qd + m * QD == len) a.ring_x[(q.unit * cap + s) * P + p] = xv[m];
+      if (ei == len) {
+        if ((q.h % (a.H / a.G)) == 0) {
+#pragma unroll
+          for (int e = 0; e < SEG / 4; ++e)
+            st4(a.ring_B + (q.gunit * cap + s) * N + sg * SEG + 4 * e, bseg[e]);
+        }
+        if (sg == 0) a.ring_dt[q.unit * cap + s] = dti;
+      }
     }
   }
 
@@ -217,7 +227,7 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
   u.apply = ok;
   u.pos_add = FUSED ? L : 0;
   u.new_len = FUSED ? 0 : L;
-  arrive_and_update(a.arrive, a.pos, a.len, q.b, a.H, u);
+  finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
   if (!ok && q.tid == 0) raise_status(a.status, kStatusOverflow);
 }
 
@@ -229,12 +239,15 @@ __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
   const bool sel = (a.mask == nullptr || a.mask[q.b] != 0) && len >= a.min_len && len > 0;
   if (!sel) return;  // uniform for all workgroups of the sequence
 
+  const int64_t pos = a.pos[q.b];
   float* ck = a.ckpt + q.unit * (P * N);
   f32x4 hv[NLD];
   load_tile(ck, q, hv);
+  indices_consumed(len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
 
   const int L = len;
-  const int slot0 = (int)(a.pos[q.b] % cap);
+  const int slot0 = (int)(pos % cap);
   const float Ah = a.A[q.h];
   __shared__ float s_dt[kMaxCap], s_fw[kMaxCap];
   __shared__ float s_gamma;
@@ -272,7 +285,7 @@ __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
   u.apply = true;
   u.pos_add = L;
   u.new_len = 0;
-  arrive_and_update(a.arrive, a.pos, a.len, q.b, a.H, u);
+  finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
 }
 
 // -------------------------------------------------------------- verify ----
@@ -289,6 +302,8 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
 
   const int len = a.len[q.b];
   const int64_t pos = a.pos[q.b];
+  indices_consumed(len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
   const bool ok = len + n <= cap;
   const int LT = len + n;
   const int slot0 = (int)(pos % cap);
@@ -318,13 +333,6 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   };
 
   if (ok) {
-    for (int j = 0; j < n; ++j) {  // append the drafts
-      const int s = ring_slot(slot0, len + j, cap);
-      if (q.tid < P) a.ring_x[(q.unit * cap + s) * P + q.tid] = a.x[j * sx + q.unit * P + q.tid];
-      if (q.tid == 0) a.ring_dt[q.unit * cap + s] = a.dt[j * sd + q.unit];
-      if ((q.h % (a.H / a.G)) == 0 && q.tid < N)
-        a.ring_B[(q.gunit * cap + s) * N + q.tid] = a.B[j * sg + q.gunit * N + q.tid];
-    }
     if (q.tid < LT) s_dt[q.tid] = dtv(q.tid);
     {  // e_{j,i} = B_i . C_j for i <= len + j, 16 lanes per pair
       constexpr int SEG = N / 16;
@@ -408,11 +416,21 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
     }
   }
 
+  if (ok) {
+    for (int j = 0; j < n; ++j) {  // append the drafts
+      const int s = ring_slot(slot0, len + j, cap);
+      if (q.tid < P) a.ring_x[(q.unit * cap + s) * P + q.tid] = a.x[j * sx + q.unit * P + q.tid];
+      if (q.tid == 0) a.ring_dt[q.unit * cap + s] = a.dt[j * sd + q.unit];
+      if ((q.h % (a.H / a.G)) == 0 && q.tid < N)
+        a.ring_B[(q.gunit * cap + s) * N + q.tid] = a.B[j * sg + q.gunit * N + q.tid];
+    }
+  }
+
   IndexUpdate u;
   u.apply = ok;
   u.pos_add = 0;
   u.new_len = LT;
-  arrive_and_update(a.arrive, a.pos, a.len, q.b, a.H, u);
+  finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
   if (!ok && q.tid == 0) raise_status(a.status, kStatusOverflow);
 }
 

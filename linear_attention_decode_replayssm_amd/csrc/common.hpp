@@ -61,11 +61,51 @@ __device__ __forceinline__ int tile_index() {
   return id;
 }
 
+// ---- reduction partners ----------------------------------------------------
+// Value of a partner lane for reductions over lane bit M.  The partner has the
+// opposite bit M and the same higher bits; its lower bits may differ.  That is
+// all a reduction needs that processes lane bits from high to low (each lane
+// ends with the complete sum, and in the transposed reduction below with the
+// same index assignment as an exact xor partner).  So DPP row permutations
+// serve for M <= 8 (quad_perm for 1 and 2, row_half_mirror i <-> 7-i for 4,
+// row_mirror i <-> 15-i for 8), ds_swizzle xor-16 for 16 and ds_bpermute only
+// for 32.
+template <int M>
+__device__ __forceinline__ float rpartner(float v) {
+  const int x = __float_as_int(v);
+  int r;
+  if constexpr (M == 1)
+    r = __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);
+  else if constexpr (M == 2)
+    r = __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);
+  else if constexpr (M == 4)
+    r = __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false);
+  else if constexpr (M == 8)
+    r = __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false);
+  else if constexpr (M == 16)
+    r = __builtin_amdgcn_ds_swizzle(x, 0x401F);
+  else
+    r = __shfl_xor(x, M);
+  return __int_as_float(r);
+}
+
+// Sum over the LPR lanes of a lane group (every lane receives the sum).
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (LPR >= 64) v += rpartner<32>(v);
+  if constexpr (LPR >= 32) v += rpartner<16>(v);
+  if constexpr (LPR >= 16) v += rpartner<8>(v);
+  if constexpr (LPR >= 8) v += rpartner<4>(v);
+  if constexpr (LPR >= 4) v += rpartner<2>(v);
+  if constexpr (LPR >= 2) v += rpartner<1>(v);
+  return v;
+}
+
 // ---- transposed cross-lane reduction --------------------------------------
 // Each lane holds C partial sums; the LPR lanes that differ only in lane bits
 // below log2(LPR) share a row.  Going from the highest of those bits down, a
 // lane keeps the half of its values that its bit selects and adds the
-// partner's copy of that half, so V values cost V-1 shuffles instead of
+// partner's copy of that half, so V values cost V-1 exchanges instead of
 // V*log2(LPR).  Once one value is left, the remaining bits are plain
 // butterflies.
 template <int C, int M>
@@ -79,11 +119,11 @@ struct XRed {
       for (int j = 0; j < C / 2; ++j) {
         const float send = up ? v[j] : v[j + C / 2];
         const float keep = up ? v[j + C / 2] : v[j];
-        v[j] = keep + __shfl_xor(send, M);
+        v[j] = keep + rpartner<M>(send);
       }
       XRed<C / 2, M / 2>::run(v, lane);
     } else {
-      v[0] += __shfl_xor(v[0], M);
+      v[0] += rpartner<M>(v[0]);
       XRed<1, M / 2>::run(v, lane);
     }
   }
@@ -124,10 +164,7 @@ __device__ __forceinline__ void xreduce(float (&v)[V], int lane) {
 template <int V, int LPR>
 __device__ __forceinline__ void allreduce(float (&v)[V]) {
 #pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) {
-#pragma unroll
-    for (int j = 0; j < V; ++j) v[j] += __shfl_xor(v[j], m);
-  }
+  for (int j = 0; j < V; ++j) v[j] = group_sum<LPR>(v[j]);
 }
 
 // ---- per-sequence index update --------------------------------------------

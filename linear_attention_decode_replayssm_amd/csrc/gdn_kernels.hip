@@ -1,10 +1,15 @@
 // gdn_kernels.hip -- Gated DeltaNet decode kernels for gfx950.
 //
 // State of one (sequence, head): S[dv=128][dk=128], 64 KiB in fp32, 32 KiB in
-// bf16, 16 KiB in E4M3 (+ one fp32 scale).  One 512-thread workgroup (8
-// wave64) per head; 8,192 workgroups at batch 256 x 32 heads.  The state is
-// read with 16-byte lane loads: a row of dk elements is spread over
-// LPR = dk / (16 / element bytes) consecutive lanes.
+// bf16, 16 KiB in E4M3 (+ one fp32 scale).  The state is read with 16-byte
+// lane loads: a row of dk elements is spread over LPR = dk / (16 / element
+// bytes) consecutive lanes.  Kernels whose work is row-independent (replay
+// step, fused and fp32 commit, eager) run one 256-thread workgroup per half
+// head (64 rows): 16,384 workgroups at batch 256 x 32 heads, each with a
+// small register and LDS footprint so that several fit on a CU.  Kernels
+// that need a whole head at once (the per-head E4M3 scale of a
+// low-precision commit, the per-draft waves of verify) run one 512-thread
+// workgroup per head.
 //
 // Recurrence: S_t = alpha S_{t-1} (I - beta k k^T) + beta v k^T, o_t = S_t q_t.
 // Unrolled over the buffered entries i = c+1..t (ReplaySSM: checkpoint +
@@ -23,32 +28,38 @@ namespace {
 
 constexpr int DK = 128;
 constexpr int DV = 128;
-constexpr int NT = 512;
 constexpr int kSchemeF32 = 0, kSchemeDual = 1, kSchemeShared = 2;
 constexpr int kLpBf16 = 1, kLpE4m3 = 2;
 
-// Lane geometry of a state read with 16-byte lane loads of EB-byte elements.
-template <int EB>
+// Lane geometry: NTH threads cover ROWS rows of a head's state with 16-byte
+// lane loads of EB-byte elements.
+template <int EB, int NTH, int ROWS>
 struct LpGeo {
   static constexpr int EPL = 16 / EB;   // elements per lane load
   static constexpr int LPR = DK / EPL;  // lanes per state row
-  static constexpr int RPL = NT / LPR;  // rows per workgroup-wide load
-  static constexpr int NLD = DV / RPL;  // loads per thread
+  static constexpr int RPL = NTH / LPR; // rows per workgroup-wide load
+  static constexpr int NLD = ROWS / RPL;// loads per thread
   static_assert(LPR <= 64 && 64 % LPR == 0, "row must sit in one wave");
+  static_assert(ROWS % RPL == 0, "tile geometry");
 };
-using F32Geo = LpGeo<4>;
 
 struct Geo {
-  int b, h, tid, lane, cl, r0;
+  int b, h, tid, lane, cl, r0, row0;
   long unit;
 };
 
-template <int LPR>
+// Workgroup -> (sequence b, head h, row block): row blocks of a head are
+// adjacent, heads of a sequence are adjacent (tile_index keeps runs of tiles
+// on one XCD).
+template <int LPR, int ROWS>
 __device__ __forceinline__ Geo geometry(const GdnArgs& a) {
+  constexpr int PARTS = DV / ROWS;
   Geo q;
   const int tile = tile_index();
-  q.b = tile / a.H;
-  q.h = tile - q.b * a.H;
+  const int hp = tile / PARTS;
+  q.row0 = (tile - hp * PARTS) * ROWS;
+  q.b = hp / a.H;
+  q.h = hp - q.b * a.H;
   q.tid = threadIdx.x;
   q.lane = q.tid & 63;
   q.cl = q.tid % LPR;
@@ -111,12 +122,14 @@ __device__ __forceinline__ void expand(u32x4 w, float (&f)[16 / EB]) {
   }
 }
 
+// First byte of row `row0` of head `unit`'s state (fp32 checkpoint for EB 4,
+// the low-precision copy otherwise).
 template <int EB>
-__device__ __forceinline__ const char* state_base(const GdnArgs& a, long unit) {
+__device__ __forceinline__ const char* state_base(const GdnArgs& a, long unit, int row0) {
   if constexpr (EB == 4)
-    return reinterpret_cast<const char*>(a.ckpt + unit * (DV * DK));
+    return reinterpret_cast<const char*>(a.ckpt + unit * (DV * DK) + row0 * DK);
   else
-    return reinterpret_cast<const char*>(a.ckpt_lp) + unit * (DV * DK * EB);
+    return reinterpret_cast<const char*>(a.ckpt_lp) + (unit * (DV * DK) + row0 * DK) * EB;
 }
 
 // Entry sources: buffered entries i < len come from the ring, later ones from
@@ -167,27 +180,36 @@ __device__ __forceinline__ void load_vec(const float* p, float (&v)[EPL]) {
 // thread) into registers, issues the state stream after them, and then parks
 // the entries in LDS.  The sequential backward carry and the fold then run
 // from LDS instead of waiting on a dependent global load per entry.
+// k rows are padded by 4 floats so that the 16 rows read by one MFMA operand
+// load (16 lanes, one row each) start in different LDS banks.
+constexpr int kKPitch = DK + 4;
 struct EntrySmem {
-  float k[kMaxCap][DK];
-  float v[kMaxCap][DV];
+  float k[kMaxCap][kKPitch];
+  float v[kMaxCap][kKPitch];
   float al[kMaxCap], be[kMaxCap];
 };
-static_assert(kMaxCap * DK / 4 <= NT && kMaxCap * DV / 4 <= NT, "one float4 per thread");
 
+template <int NTH>
 struct EntryRegs {
-  f32x4 k, v;
+  static constexpr int EPT = kMaxCap * (DK / 4) / NTH;   // float4 chunks per thread
+  static_assert(EPT * NTH == kMaxCap * (DK / 4) && DK == DV, "entry chunking");
+  f32x4 k[EPT], v[EPT];
   float al, be;
 };
 
-__device__ __forceinline__ EntryRegs fetch_entries(const Src& src, int L, int tid) {
-  EntryRegs e;
-  e.k = e.v = f32x4{0.f, 0.f, 0.f, 0.f};
-  e.al = e.be = 0.f;
-  const int i = tid / (DK / 4), c = (tid % (DK / 4)) * 4;
-  if (i < L) {
-    e.k = ld4(src.k(i) + c);
-    e.v = ld4(src.v(i) + c);
+template <int NTH>
+__device__ __forceinline__ EntryRegs<NTH> fetch_entries(const Src& src, int L, int tid) {
+  EntryRegs<NTH> e;
+#pragma unroll
+  for (int x = 0; x < EntryRegs<NTH>::EPT; ++x) {
+    const int ch = tid + x * NTH, i = ch / (DK / 4), c = (ch % (DK / 4)) * 4;
+    e.k[x] = e.v[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (i < L) {
+      e.k[x] = ld4(src.k(i) + c);
+      e.v[x] = ld4(src.v(i) + c);
+    }
   }
+  e.al = e.be = 0.f;
   if (tid < L) {
     e.al = src.alpha(tid);
     e.be = src.beta(tid);
@@ -195,27 +217,37 @@ __device__ __forceinline__ EntryRegs fetch_entries(const Src& src, int L, int ti
   return e;
 }
 
-__device__ __forceinline__ void stash_entries(const EntryRegs& e, int L, int tid, EntrySmem& s) {
-  const int i = tid / (DK / 4), c = (tid % (DK / 4)) * 4;
-  if (i < L) {
-    st4(&s.k[i][c], e.k);
-    st4(&s.v[i][c], e.v);
+// Park the fetched entries in LDS.  Rows L..kMaxCap-1 are written as zeros
+// (fetch_entries zero-fills them), which pads the MFMA operands of the fold.
+template <int NTH>
+__device__ __forceinline__ void stash_entries(const EntryRegs<NTH>& e, int L, int tid,
+                                              EntrySmem& s) {
+  (void)L;
+#pragma unroll
+  for (int x = 0; x < EntryRegs<NTH>::EPT; ++x) {
+    const int ch = tid + x * NTH, i = ch / (DK / 4), c = (ch % (DK / 4)) * 4;
+    st4(&s.k[i][c], e.k[x]);
+    st4(&s.v[i][c], e.v[x]);
   }
-  if (tid < L) {
+  if (tid < kMaxCap) {
     s.al[tid] = e.al;
     s.be[tid] = e.be;
   }
 }
 
 // Write entry i (held in registers by fetch_entries) to its ring slot.
+template <int NTH>
 __device__ __forceinline__ void append_from_regs(const GdnArgs& a, const Src& src,
-                                                 const EntryRegs& e, int i, int tid) {
+                                                 const EntryRegs<NTH>& e, int i, int tid) {
   const int s = ring_slot(src.slot0, i, src.cap);
   const long u = src.unit;
-  const int ei = tid / (DK / 4), c = (tid % (DK / 4)) * 4;
-  if (ei == i) {
-    st4(a.ring_k + (u * src.cap + s) * DK + c, e.k);
-    st4(a.ring_v + (u * src.cap + s) * DV + c, e.v);
+#pragma unroll
+  for (int x = 0; x < EntryRegs<NTH>::EPT; ++x) {
+    const int ch = tid + x * NTH, ei = ch / (DK / 4), c = (ch % (DK / 4)) * 4;
+    if (ei == i) {
+      st4(a.ring_k + (u * src.cap + s) * DK + c, e.k[x]);
+      st4(a.ring_v + (u * src.cap + s) * DV + c, e.v[x]);
+    }
   }
   if (tid == i) {
     a.ring_a[u * src.cap + s] = e.al;
@@ -236,8 +268,7 @@ __device__ __forceinline__ void carry(const EntrySmem& s, int hi, int cl, float 
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) part += kv[e] * q[e];
-#pragma unroll
-      for (int m = LPR / 2; m >= 1; m >>= 1) part += __shfl_xor(part, m);
+      part = group_sum<LPR>(part);
       const float si = s.be[i] * part;
       const float al = s.al[i];
       sv[i] = si;
@@ -251,57 +282,101 @@ __device__ __forceinline__ void carry(const EntrySmem& s, int hi, int cl, float 
 
 // ---------------------------------------------------------------- fold ----
 // With u_i = beta_i (v_i - alpha_i a_i) and a_i = G_{c+1..i-1} (S_c k_i)
-// + sum_{m<i} G_{m+1..i-1} (k_m . k_i) u_m, every row r satisfies the same
-// unit lower-triangular system (I + diag(beta alpha) Lc) u = z,
-// z_j = beta_j v_j - beta_j alpha_j G_{c+1..j-1} (S_c k_j),
-// Lc[i][m] = G_{m+1..i-1} (k_m . k_i).  Its inverse T is the same for all
-// rows, so it is formed once (L x L) and each row's fold weights
-// U'_i = G_{i+1..t} u_i = sum_j T'[i][j] z_j are independent dot products.
+// + sum_{m<i} G_{m+1..i-1} (k_m . k_i) u_m, every row satisfies the same unit
+// lower-triangular system (I + diag(beta alpha) Lc) u = z with
+// z_j = beta_j v_j - beta_j alpha_j G_{c+1..j-1} (S_c k_j) and
+// Lc[i][m] = G_{m+1..i-1} (k_m . k_i).  Its inverse T is formed once per
+// workgroup (L x L); each row's fold weights U'_i = G_{i+1..t} u_i are then
+// independent short dot products, and the new state is
+// S_new = G_{c+1..t} S_c + U' K (rank L).  The state stays in the
+// consecutive-load geometry of the stream (fp32 FMA; see DESIGN for why not
+// MFMA at these shapes).
+template <int ROWS>
 struct FoldSmem {
-  float G[kMaxCap + 1][kMaxCap + 1];   // G[a][e] = prod_{j=a}^{e-1} alpha_j
-  float gram[kMaxCap][kMaxCap];        // k_m . k_i
-  float P1[kMaxCap][kMaxCap];          // G_{i+1..} T[i][j] beta_j
-  float P2[kMaxCap][kMaxCap];          // G_{i+1..} T[i][j] beta_j alpha_j G_{..j-1}
-  float W[DV][kMaxCap + 1];            // S_c k_i
-  float U[DV][kMaxCap + 1];            // U'_i of row r
-  float red[NT / 64];
+  float G[kMaxCap + 1][kMaxCap + 1];   // G[a][e] = prod_{j=a}^{e-1} alpha_j, a <= e <= L
+  float gram[kMaxCap][kMaxCap + 1];    // k_m . k_i
+  float Lc[kMaxCap][kMaxCap + 1];      // G_{m+1..i-1} (k_m . k_i), m < i
+  float P1[kMaxCap][kMaxCap + 1];      //  G_{i+1..} T[i][j] beta_j
+  float P2[kMaxCap][kMaxCap + 1];      // -G_{i+1..} T[i][j] beta_j alpha_j G_{..j-1}
+  float W[ROWS][kMaxCap + 1];          // S_c k_i of the workgroup's rows
+  float U[ROWS][kMaxCap + 1];          // U'_i of the workgroup's rows
+  float red[16];
 };
 
-// Fold entries 0..L-1 (staged in es) into the fp32 tile hv (fp32 geometry).
-__device__ void fold_tile(f32x4 (&hv)[F32Geo::NLD], const EntrySmem& es, int L, const Geo& q,
-                          FoldSmem& sm) {
-  constexpr int RPL = F32Geo::RPL, NLD = F32Geo::NLD, LPR = F32Geo::LPR;
-  if (q.tid < (L + 1) * (L + 1)) {
-    const int a0 = q.tid / (L + 1), e0 = q.tid % (L + 1);
-    float p = 1.f;
-    for (int j = a0; j < e0; ++j) p *= es.al[j];
-    sm.G[a0][e0] = p;
-  }
-  {  // Gram matrix, 16 lanes per pair
-    const int sgm = q.tid & 15;
-    for (int pass = 0; pass < (kMaxCap * kMaxCap) / (NT / 16); ++pass) {
-      const int pi = pass * (NT / 16) + (q.tid >> 4);
-      const int m = pi / kMaxCap, i = pi % kMaxCap;
-      float part = 0.f;
-      if (m < L && i < L) {
+// Gram matrix (16 lanes per pair) and the alpha product table.
+template <int NTH, int ROWS>
+__device__ __forceinline__ void coef_gram_g(const EntrySmem& es, int L, int tid,
+                                            FoldSmem<ROWS>& sm) {
+  const int sgm = tid & 15;
+  for (int pi = tid >> 4; pi < L * L; pi += NTH / 16) {   // uniform per 16 lanes
+    const int m = pi / L, i = pi % L;
+    float part = 0.f;
 #pragma unroll
-        for (int e = 0; e < DK / 16; ++e)
-          part += es.k[m][sgm * (DK / 16) + e] * es.k[i][sgm * (DK / 16) + e];
-      }
-      part += __shfl_xor(part, 8);
-      part += __shfl_xor(part, 4);
-      part += __shfl_xor(part, 2);
-      part += __shfl_xor(part, 1);
-      if (sgm == 0 && m < L && i < L) sm.gram[m][i] = part;
+    for (int e = 0; e < DK / 16; ++e)
+      part += es.k[m][sgm * (DK / 16) + e] * es.k[i][sgm * (DK / 16) + e];
+    part = group_sum<16>(part);
+    if (sgm == 0) sm.gram[m][i] = part;
+  }
+  for (int idx = tid; idx < (kMaxCap + 1) * (kMaxCap + 1); idx += NTH) {
+    const int a0 = idx / (kMaxCap + 1), e0 = idx % (kMaxCap + 1);
+    if (a0 <= e0 && e0 <= L) {
+      float p = 1.f;
+      for (int j = a0; j < e0; ++j) p *= es.al[j];
+      sm.G[a0][e0] = p;
     }
   }
-  // W = S_c k_i, four entries at a time
+}
+
+template <int NTH, int ROWS>
+__device__ __forceinline__ void coef_lc(int L, int tid, FoldSmem<ROWS>& sm) {
+  for (int idx = tid; idx < kMaxCap * kMaxCap; idx += NTH) {
+    const int i = idx / kMaxCap, m = idx % kMaxCap;
+    sm.Lc[i][m] = (m < i && i < L) ? sm.G[m + 1][i] * sm.gram[m][i] : 0.f;
+  }
+}
+
+// T = (I + diag(beta alpha) Lc)^-1 column by column (one thread per column,
+// in registers), folded into the fold-weight matrices P1 and P2.
+template <int ROWS>
+__device__ __forceinline__ void coef_t(const EntrySmem& es, int L, int tid, FoldSmem<ROWS>& sm) {
+  if (tid < kMaxCap) {
+    const int j = tid;
+    float t[kMaxCap];
+#pragma unroll
+    for (int i = 0; i < kMaxCap; ++i) {
+      float v = (i == j && j < L) ? 1.f : 0.f;
+      if (i > j && i < L) {
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) acc += sm.Lc[i][m] * t[m];   // t[m] = 0 for m < j
+        v = -es.be[i] * es.al[i] * acc;
+      }
+      t[i] = v;
+    }
+    const float bj = (j < L) ? es.be[j] : 0.f;
+    const float bag = (j < L) ? es.be[j] * es.al[j] * sm.G[0][j] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxCap; ++i) {
+      const float w = (i < L) ? sm.G[i + 1][L] * t[i] : 0.f;
+      sm.P1[i][j] = w * bj;
+      sm.P2[i][j] = -w * bag;
+    }
+  }
+}
+
+// W = S_c K^T for the workgroup's rows, four entries at a time (FMA dots,
+// transposed cross-lane reduction), stored to sm.W.
+template <int NTH, int ROWS, int NLD>
+__device__ __forceinline__ void fold_w(const f32x4 (&hv)[NLD], const EntrySmem& es, int L,
+                                       const Geo& q, FoldSmem<ROWS>& sm) {
+  using Gm = LpGeo<4, NTH, ROWS>;
+  constexpr int RPL = Gm::RPL, LPR = Gm::LPR;
+  static_assert(NLD == Gm::NLD, "tile registers");
   for (int i0 = 0; i0 < L; i0 += 4) {
     float d[NLD * 4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      f32x4 kv = {0.f, 0.f, 0.f, 0.f};
-      if (i0 + jj < L) kv = ld4(&es.k[i0 + jj][q.cl * 4]);
+      const f32x4 kv = ld4(&es.k[i0 + jj][q.cl * 4]);   // rows >= L are zero
 #pragma unroll
       for (int k = 0; k < NLD; ++k) d[k * 4 + jj] = dot4(hv[k], kv);
     }
@@ -309,47 +384,27 @@ __device__ void fold_tile(f32x4 (&hv)[F32Geo::NLD], const EntrySmem& es, int L, 
     using M = XMap<NLD * 4, LPR>;
     static_assert(M::VOUT == 1 && M::BFLY == 0, "one sum per lane");
     const int idx = M::index(q.lane, 0);
-    const int k = idx / 4, jj = idx % 4;
-    if (i0 + jj < L) sm.W[k * RPL + q.r0][i0 + jj] = d[0];
+    sm.W[(idx / 4) * RPL + q.r0][i0 + idx % 4] = d[0];
   }
-  __syncthreads();
-  if (q.tid < L) {  // column j of T = (I + diag(beta alpha) Lc)^-1
-    const int j = q.tid;
-    float t[kMaxCap];
-#pragma unroll
-    for (int i = 0; i < kMaxCap; ++i) {
-      float v = 0.f;
-      if (i == j) {
-        v = 1.f;
-      } else if (i > j && i < L) {
-        float acc = 0.f;
-#pragma unroll
-        for (int m = 0; m < kMaxCap; ++m)
-          if (m >= j && m < i) acc += sm.G[m + 1][i] * sm.gram[m][i] * t[m];
-        v = -es.be[i] * es.al[i] * acc;
-      }
-      t[i] = v;
-    }
-    const float bj = es.be[j], bag = es.be[j] * es.al[j] * sm.G[0][j];
-#pragma unroll
-    for (int i = 0; i < kMaxCap; ++i) {
-      if (i < L) {
-        const float w = sm.G[i + 1][L] * t[i];
-        sm.P1[i][j] = w * bj;
-        sm.P2[i][j] = w * bag;
-      }
-    }
+}
+
+// U'[r][i] = sum_{j<=i} P1[i][j] v_j[row0 + r] + P2[i][j] W[r][j].
+template <int NTH, int ROWS>
+__device__ __forceinline__ void fold_u(const EntrySmem& es, int L, int row0, int tid,
+                                       FoldSmem<ROWS>& sm) {
+  const int r = tid % ROWS, ig = tid / ROWS;
+  for (int i = ig; i < L; i += NTH / ROWS) {
+    float acc = 0.f;
+    for (int j = 0; j <= i; ++j)
+      acc += sm.P1[i][j] * es.v[j][row0 + r] + sm.P2[i][j] * sm.W[r][j];
+    sm.U[r][i] = acc;
   }
-  __syncthreads();
-  {  // U'[r][i] = sum_{j<=i} P1[i][j] v_j[r] - P2[i][j] W[r][j]
-    const int r = q.tid % DV, ig = q.tid / DV;
-    for (int i = ig; i < L; i += NT / DV) {
-      float acc = 0.f;
-      for (int j = 0; j <= i; ++j) acc += sm.P1[i][j] * es.v[j][r] - sm.P2[i][j] * sm.W[r][j];
-      sm.U[r][i] = acc;
-    }
-  }
-  __syncthreads();
+}
+
+template <int NTH, int ROWS, int NLD>
+__device__ __forceinline__ void fold_update(f32x4 (&hv)[NLD], const EntrySmem& es, int L,
+                                            const Geo& q, const FoldSmem<ROWS>& sm) {
+  constexpr int RPL = LpGeo<4, NTH, ROWS>::RPL;
   const float gall = sm.G[0][L];
 #pragma unroll
   for (int k = 0; k < NLD; ++k) hv[k] *= gall;
@@ -360,32 +415,57 @@ __device__ void fold_tile(f32x4 (&hv)[F32Geo::NLD], const EntrySmem& es, int L, 
   }
 }
 
+// Whole fold of L >= 1 entries (all threads; barriers inside).
+template <int NTH, int ROWS, int NLD>
+__device__ void fold_tile(f32x4 (&hv)[NLD], const EntrySmem& es, int L, int row0, const Geo& q,
+                          FoldSmem<ROWS>& sm) {
+  coef_gram_g<NTH, ROWS>(es, L, q.tid, sm);
+  fold_w<NTH, ROWS, NLD>(hv, es, L, q, sm);
+  __syncthreads();
+  coef_lc<NTH, ROWS>(L, q.tid, sm);
+  __syncthreads();
+  coef_t<ROWS>(es, L, q.tid, sm);
+  __syncthreads();
+  fold_u<NTH, ROWS>(es, L, row0, q.tid, sm);
+  __syncthreads();
+  fold_update<NTH, ROWS, NLD>(hv, es, L, q, sm);
+}
+
 // Workgroup max of |hv|; a NaN anywhere makes the result +inf.
-__device__ float tile_amax(const f32x4 (&hv)[F32Geo::NLD], const Geo& q, float* red) {
+template <int NTH, int NLD>
+__device__ float tile_amax(const f32x4 (&hv)[NLD], const Geo& q, float* red) {
   float m = 0.f;
   bool nan = false;
 #pragma unroll
-  for (int k = 0; k < F32Geo::NLD; ++k) {
+  for (int k = 0; k < NLD; ++k) {
     m = fmaxf(m, fmaxf(fmaxf(fabsf(hv[k].x), fabsf(hv[k].y)), fmaxf(fabsf(hv[k].z), fabsf(hv[k].w))));
     nan |= !(hv[k].x == hv[k].x && hv[k].y == hv[k].y && hv[k].z == hv[k].z && hv[k].w == hv[k].w);
   }
   if (nan) m = __builtin_inff();
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s));
+  m = fmaxf(m, rpartner<32>(m));
+  m = fmaxf(m, rpartner<16>(m));
+  m = fmaxf(m, rpartner<8>(m));
+  m = fmaxf(m, rpartner<4>(m));
+  m = fmaxf(m, rpartner<2>(m));
+  m = fmaxf(m, rpartner<1>(m));
   __syncthreads();
   if (q.lane == 0) red[q.tid >> 6] = m;
   __syncthreads();
   float r = red[0];
 #pragma unroll
-  for (int w = 1; w < NT / 64; ++w) r = fmaxf(r, red[w]);
+  for (int w = 1; w < NTH / 64; ++w) r = fmaxf(r, red[w]);
   return r;
 }
 
-// Write the low-precision copy of the fp32 tile (fp32 geometry).
+using WholeGeo = LpGeo<4, 512, DV>;
+constexpr int kWholeNLD = WholeGeo::NLD;
+
+// Write the low-precision copy of a whole head held in the fp32 geometry of a
+// 512-thread workgroup.
 template <int LP>
-__device__ void store_lp(const f32x4 (&hv)[F32Geo::NLD], const GdnArgs& a, const Geo& q,
+__device__ void store_lp(const f32x4 (&hv)[kWholeNLD], const GdnArgs& a, const Geo& q,
                          float* red) {
-  constexpr int RPL = F32Geo::RPL, NLD = F32Geo::NLD;
+  constexpr int RPL = WholeGeo::RPL, NLD = kWholeNLD;
   if constexpr (LP == kLpBf16) {
     uint16_t* base = reinterpret_cast<uint16_t*>(a.ckpt_lp) + q.unit * (DV * DK);
 #pragma unroll
@@ -396,7 +476,7 @@ __device__ void store_lp(const f32x4 (&hv)[F32Geo::NLD], const GdnArgs& a, const
       *reinterpret_cast<u32x2*>(base + (k * RPL + q.r0) * DK + q.cl * 4) = w;
     }
   } else {
-    const float amax = tile_amax(hv, q, red);
+    const float amax = tile_amax<512, NLD>(hv, q, red);
     const bool fin = amax <= 3.402823466e38f;
     const float scale = (amax > 0.f && fin) ? amax / 448.f : 1.f;
     if (!fin && q.tid == 0) raise_status(a.status, kStatusNonfinite);
@@ -411,11 +491,11 @@ __device__ void store_lp(const f32x4 (&hv)[F32Geo::NLD], const GdnArgs& a, const
   }
 }
 
-// Read the low-precision copy into the fp32 geometry (exact value for bf16;
-// code * scale rounded to fp32 for E4M3).
+// Read a whole head's low-precision copy into the fp32 geometry (exact value
+// for bf16; code * scale rounded to fp32 for E4M3).
 template <int LP>
-__device__ void load_lp_as_f32(f32x4 (&hv)[F32Geo::NLD], const GdnArgs& a, const Geo& q) {
-  constexpr int RPL = F32Geo::RPL, NLD = F32Geo::NLD;
+__device__ void load_lp_as_f32(f32x4 (&hv)[kWholeNLD], const GdnArgs& a, const Geo& q) {
+  constexpr int RPL = WholeGeo::RPL, NLD = kWholeNLD;
   if constexpr (LP == kLpBf16) {
     const uint16_t* base = reinterpret_cast<const uint16_t*>(a.ckpt_lp) + q.unit * (DV * DK);
 #pragma unroll
@@ -435,30 +515,34 @@ __device__ void load_lp_as_f32(f32x4 (&hv)[F32Geo::NLD], const GdnArgs& a, const
   }
 }
 
-__device__ __forceinline__ void load_f32_tile(f32x4 (&hv)[F32Geo::NLD], const float* base,
-                                              const Geo& q) {
+// fp32 rows of a workgroup in the consecutive-load geometry (eager kernel).
+template <int RPL, int NLD>
+__device__ __forceinline__ void load_f32_tile(f32x4 (&hv)[NLD], const float* rows, const Geo& q) {
 #pragma unroll
-  for (int k = 0; k < F32Geo::NLD; ++k)
-    hv[k] = ld_nt(base + (k * F32Geo::RPL + q.r0) * DK + q.cl * 4);
+  for (int k = 0; k < NLD; ++k) hv[k] = ld_nt(rows + (k * RPL + q.r0) * DK + q.cl * 4);
 }
 
-__device__ __forceinline__ void store_f32_tile(const f32x4 (&hv)[F32Geo::NLD], float* base,
-                                               const Geo& q) {
+template <int RPL, int NLD>
+__device__ __forceinline__ void store_f32_tile(const f32x4 (&hv)[NLD], float* rows, const Geo& q) {
 #pragma unroll
-  for (int k = 0; k < F32Geo::NLD; ++k)
-    st_nt(base + (k * F32Geo::RPL + q.r0) * DK + q.cl * 4, hv[k]);
+  for (int k = 0; k < NLD; ++k) st_nt(rows + (k * RPL + q.r0) * DK + q.cl * 4, hv[k]);
 }
 
 // ---------------------------------------------------------------- step ----
 // EB: bytes per checkpoint element read for the output (4: ckpt fp32; 2: bf16
-// ckpt_lp; 1: E4M3 ckpt_lp).  FUSED (fp32 only): fold and store after output.
-// Order: buffered entries and the query are fetched, then the state stream is
-// issued, then the entries are parked in LDS while the stream is in flight.
+// ckpt_lp; 1: E4M3 ckpt_lp).  One 256-thread workgroup per half head, state
+// read with consecutive 16-byte lane loads.  Order: buffered entries and the
+// query are fetched, then the state stream is issued, then the entries are
+// parked in LDS while the stream is in flight.
+constexpr int kStepThreads = 256;
+constexpr int kStepRows = 64;
+
 template <int EB, bool FUSED>
-__global__ __launch_bounds__(NT) void gdn_step_kernel(GdnArgs a) {
-  using Gm = LpGeo<EB>;
+__global__ __launch_bounds__(kStepThreads) void gdn_step_kernel(GdnArgs a) {
+  constexpr int NTH = kStepThreads, ROWS = kStepRows, PARTS = DV / ROWS;
+  using Gm = LpGeo<EB, NTH, ROWS>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPL = Gm::RPL, NLD = Gm::NLD;
-  const Geo q = geometry<LPR>(a);
+  const Geo q = geometry<LPR, ROWS>(a);
   const int cap = a.cap;
 
   const int len = a.len[q.b];
@@ -468,11 +552,11 @@ __global__ __launch_bounds__(NT) void gdn_step_kernel(GdnArgs a) {
   Src src{&a, q.unit, len, (int)(pos % cap), cap, 0, 0};
   const float scale = (EB == 1) ? a.lp_scale[q.unit] : 1.f;
 
-  EntryRegs er = fetch_entries(src, ok ? L : 0, q.tid);
+  EntryRegs<NTH> er = fetch_entries<NTH>(src, ok ? L : 0, q.tid);
   float qv[EPL];
   load_vec<EPL>(a.q + q.unit * DK + q.cl * EPL, qv);
 
-  const char* base = state_base<EB>(a, q.unit);
+  const char* base = state_base<EB>(a, q.unit, q.row0);
   u32x4 raw[NLD];
 #pragma unroll
   for (int k = 0; k < NLD; ++k) raw[k] = ld_nt_u(base + ((k * RPL + q.r0) * DK + q.cl * EPL) * EB);
@@ -480,7 +564,7 @@ __global__ __launch_bounds__(NT) void gdn_step_kernel(GdnArgs a) {
   const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
 
   __shared__ __attribute__((aligned(16))) EntrySmem es;
-  stash_entries(er, ok ? L : 0, q.tid, es);
+  stash_entries<NTH>(er, ok ? L : 0, q.tid, es);
   __syncthreads();
 
   float s[kMaxCap];
@@ -504,7 +588,7 @@ __global__ __launch_bounds__(NT) void gdn_step_kernel(GdnArgs a) {
   xreduce<NLD, LPR>(d, q.lane);
   using M = XMap<NLD, LPR>;
   if (M::writer(q.lane)) {
-    const int r = M::index(q.lane, 0) * RPL + q.r0;
+    const int r = q.row0 + M::index(q.lane, 0) * RPL + q.r0;
     float ov;
     if (ok) {
       ov = scale * d[0];
@@ -517,36 +601,41 @@ __global__ __launch_bounds__(NT) void gdn_step_kernel(GdnArgs a) {
     a.o[q.unit * DV + r] = ov;
   }
 
-  if constexpr (FUSED) {
+  if constexpr (FUSED) {   // fold the whole buffer, this entry included, and store
     static_assert(EB == 4, "fused commit folds the fp32 checkpoint");
     if (ok) {
-      __shared__ __attribute__((aligned(16))) FoldSmem sm;
+      __shared__ __attribute__((aligned(16))) FoldSmem<ROWS> sm;
       f32x4 hv[NLD];
 #pragma unroll
       for (int k = 0; k < NLD; ++k)
         hv[k] = f32x4{__uint_as_float(raw[k].x), __uint_as_float(raw[k].y),
                       __uint_as_float(raw[k].z), __uint_as_float(raw[k].w)};
-      fold_tile(hv, es, L, q, sm);
-      store_f32_tile(hv, a.ckpt + q.unit * (DV * DK), q);
+      fold_tile<NTH, ROWS, NLD>(hv, es, L, q.row0, q, sm);
+      store_f32_tile<RPL, NLD>(hv, a.ckpt + q.unit * (DV * DK) + q.row0 * DK, q);
     }
   } else {
-    if (ok) append_from_regs(a, src, er, len, q.tid);
+    if (ok && q.row0 == 0) append_from_regs<NTH>(a, src, er, len, q.tid);
   }
 
   IndexUpdate u;
   u.apply = ok;
   u.pos_add = FUSED ? L : 0;
   u.new_len = FUSED ? 0 : L;
-  finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
+  finish_update(a.arrive, a.pos, a.len, q.b, a.H * PARTS, arrived, u);
   if (!ok && q.tid == 0) raise_status(a.status, kStatusOverflow);
 }
 
 // -------------------------------------------------------------- commit ----
-// SCHEME/LP select: F32 (fold fp32), DUAL (fold fp32, then re-quantise the
-// copy), SHARED (fold the dequantised copy, re-quantise).
-template <int SCHEME, int LP>
-__global__ __launch_bounds__(NT) void gdn_commit_kernel(GdnArgs a) {
-  const Geo q = geometry<F32Geo::LPR>(a);
+// SCHEME/LP select: F32 (fold fp32; half-head workgroups), DUAL (fold fp32,
+// then re-quantise the copy; whole-head workgroups for the per-head scale),
+// SHARED (fold the dequantised copy, re-quantise; whole head).
+template <int SCHEME, int LP, int NTH>
+__global__ __launch_bounds__(NTH) void gdn_commit_kernel(GdnArgs a) {
+  constexpr int ROWS = NTH / 4, PARTS = DV / ROWS;   // 32 lanes per row, 4 fp32 each
+  using Gm = LpGeo<4, NTH, ROWS>;
+  constexpr int RPL = Gm::RPL, NLD = Gm::NLD;
+  static_assert(SCHEME == kSchemeF32 || ROWS == DV, "low-precision copies need whole heads");
+  const Geo q = geometry<Gm::LPR, ROWS>(a);
   const int len = a.len[q.b];
   const bool sel = (a.mask == nullptr || a.mask[q.b] != 0) && len >= a.min_len;
   if (!sel) return;                         // uniform for the whole sequence
@@ -555,21 +644,22 @@ __global__ __launch_bounds__(NT) void gdn_commit_kernel(GdnArgs a) {
   }
   const int64_t pos = a.pos[q.b];
   Src src{&a, q.unit, len, (int)(pos % a.cap), a.cap, 0, 0};
-  EntryRegs er = fetch_entries(src, len, q.tid);
-  f32x4 hv[F32Geo::NLD];
+  EntryRegs<NTH> er = fetch_entries<NTH>(src, len, q.tid);
+  float* rows = a.ckpt + q.unit * (DV * DK) + q.row0 * DK;
+  f32x4 hv[NLD];
   if constexpr (SCHEME == kSchemeShared)
     load_lp_as_f32<LP>(hv, a, q);
   else
-    load_f32_tile(hv, a.ckpt + q.unit * (DV * DK), q);
+    load_f32_tile<RPL, NLD>(hv, rows, q);
   indices_consumed(len, pos);
   const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
   __shared__ __attribute__((aligned(16))) EntrySmem es;
-  __shared__ __attribute__((aligned(16))) FoldSmem sm;
-  stash_entries(er, len, q.tid, es);
+  __shared__ __attribute__((aligned(16))) FoldSmem<ROWS> sm;
+  stash_entries<NTH>(er, len, q.tid, es);
   __syncthreads();
   if (len > 0) {
-    fold_tile(hv, es, len, q, sm);
-    if constexpr (SCHEME != kSchemeShared) store_f32_tile(hv, a.ckpt + q.unit * (DV * DK), q);
+    fold_tile<NTH, ROWS, NLD>(hv, es, len, q.row0, q, sm);
+    if constexpr (SCHEME != kSchemeShared) store_f32_tile<RPL, NLD>(hv, rows, q);
   }
   if constexpr (SCHEME != kSchemeF32) store_lp<LP>(hv, a, q, sm.red);
 
@@ -577,19 +667,20 @@ __global__ __launch_bounds__(NT) void gdn_commit_kernel(GdnArgs a) {
   u.apply = len > 0;
   u.pos_add = len;
   u.new_len = 0;
-  finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
+  finish_update(a.arrive, a.pos, a.len, q.b, a.H * PARTS, arrived, u);
 }
 
 // -------------------------------------------------------------- verify ----
-// n_pos drafts appended at entries len..len+n-1.  Wave j carries draft j's
-// query backwards through entries len+j..0; then one pass over the checkpoint
-// dots every row with all carried queries.
+// n_pos drafts appended at entries len..len+n-1.  One 512-thread workgroup per
+// head: wave j carries draft j's query backwards through entries len+j..0;
+// then one pass over the checkpoint dots every row with all carried queries.
 template <int EB, int NPAD>
-__global__ __launch_bounds__(NT) void gdn_verify_kernel(GdnArgs a) {
-  using Gm = LpGeo<EB>;
+__global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
+  constexpr int NTH = 512, ROWS = DV;
+  using Gm = LpGeo<EB, NTH, ROWS>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPL = Gm::RPL, NLD = Gm::NLD;
-  static_assert(NPAD <= NT / 64, "one wave per draft position");
-  const Geo q = geometry<LPR>(a);
+  static_assert(NPAD <= NTH / 64, "one wave per draft position");
+  const Geo q = geometry<LPR, ROWS>(a);
   const int cap = a.cap, n = a.n_pos;
 
   const int len = a.len[q.b];
@@ -600,12 +691,12 @@ __global__ __launch_bounds__(NT) void gdn_verify_kernel(GdnArgs a) {
   Src src{&a, q.unit, len, (int)(pos % cap), cap, sk, sd};
   const float scale = (EB == 1) ? a.lp_scale[q.unit] : 1.f;
 
-  EntryRegs er = fetch_entries(src, ok ? len + n : 0, q.tid);
+  EntryRegs<NTH> er = fetch_entries<NTH>(src, ok ? len + n : 0, q.tid);
   const int w = q.tid >> 6;
   float qv[2] = {0.f, 0.f};
   if (ok && w < n) load_vec<2>(a.q + w * sk + q.unit * DK + 2 * q.lane, qv);
 
-  const char* base = state_base<EB>(a, q.unit);
+  const char* base = state_base<EB>(a, q.unit, 0);
   u32x4 raw[NLD];
 #pragma unroll
   for (int k = 0; k < NLD; ++k) raw[k] = ld_nt_u(base + ((k * RPL + q.r0) * DK + q.cl * EPL) * EB);
@@ -615,7 +706,7 @@ __global__ __launch_bounds__(NT) void gdn_verify_kernel(GdnArgs a) {
   __shared__ __attribute__((aligned(16))) EntrySmem es;
   __shared__ __attribute__((aligned(16))) float s_q[NPAD][DK];
   __shared__ float s_s[NPAD][kMaxCap];
-  stash_entries(er, ok ? len + n : 0, q.tid, es);
+  stash_entries<NTH>(er, ok ? len + n : 0, q.tid, es);
   __syncthreads();
 
   if (ok && w < n) {  // wave w carries draft w (2 elements per lane)
@@ -670,7 +761,7 @@ __global__ __launch_bounds__(NT) void gdn_verify_kernel(GdnArgs a) {
     }
   }
   if (ok)
-    for (int j = 0; j < n; ++j) append_from_regs(a, src, er, len + j, q.tid);
+    for (int j = 0; j < n; ++j) append_from_regs<NTH>(a, src, er, len + j, q.tid);
 
   IndexUpdate u;
   u.apply = ok;
@@ -682,17 +773,23 @@ __global__ __launch_bounds__(NT) void gdn_verify_kernel(GdnArgs a) {
 
 // --------------------------------------------------------------- eager ----
 // Per row r: (S k)_r, then S_r <- alpha S_r + beta (v_r - alpha (S k)_r) k^T,
-// then o_r = S_r . q with the updated row; the state is written back.
-__global__ __launch_bounds__(NT) void gdn_eager_kernel(GdnArgs a) {
-  constexpr int RPL = F32Geo::RPL, NLD = F32Geo::NLD, LPR = F32Geo::LPR;
-  const Geo q = geometry<LPR>(a);
-  float* st = a.ckpt + q.unit * (DV * DK);
-  f32x4 hv[NLD];
-  load_f32_tile(hv, st, q);
+// then o_r = S_r . q with the updated row; the state is written back.  One
+// 256-thread workgroup per half head.
+__global__ __launch_bounds__(kStepThreads) void gdn_eager_kernel(GdnArgs a) {
+  constexpr int NTH = kStepThreads, ROWS = kStepRows;
+  using Gm = LpGeo<4, NTH, ROWS>;
+  constexpr int RPL = Gm::RPL, NLD = Gm::NLD, LPR = Gm::LPR;
+  const Geo q = geometry<LPR, ROWS>(a);
   const f32x4 kv = ld4(a.k + q.unit * DK + q.cl * 4);
   const f32x4 qv = ld4(a.q + q.unit * DK + q.cl * 4);
   const float al = a.alpha[q.unit], be = a.beta[q.unit];
-  const float* vv = a.v + q.unit * DV;
+  const float* vv = a.v + q.unit * DV + q.row0;
+  float vr[NLD];
+#pragma unroll
+  for (int k = 0; k < NLD; ++k) vr[k] = vv[k * RPL + q.r0];
+  float* rows = a.ckpt + q.unit * (DV * DK) + q.row0 * DK;
+  f32x4 hv[NLD];
+  load_f32_tile<RPL, NLD>(hv, rows, q);
   float sk[NLD];
 #pragma unroll
   for (int k = 0; k < NLD; ++k) sk[k] = dot4(hv[k], kv);
@@ -700,23 +797,28 @@ __global__ __launch_bounds__(NT) void gdn_eager_kernel(GdnArgs a) {
   float d[NLD];
 #pragma unroll
   for (int k = 0; k < NLD; ++k) {
-    const float coef = be * (vv[k * RPL + q.r0] - al * sk[k]);
+    const float coef = be * (vr[k] - al * sk[k]);
     hv[k] = al * hv[k] + coef * kv;
     d[k] = dot4(hv[k], qv);
   }
-  store_f32_tile(hv, st, q);
+  store_f32_tile<RPL, NLD>(hv, rows, q);
   xreduce<NLD, LPR>(d, q.lane);
   using M = XMap<NLD, LPR>;
   if (M::writer(q.lane)) {
-    const int r = M::index(q.lane, 0) * RPL + q.r0;
+    const int r = q.row0 + M::index(q.lane, 0) * RPL + q.r0;
     a.o[q.unit * DV + r] = d[0];
   }
 }
 
 }  // namespace
 
+static dim3 half_grid(const GdnArgs& a) {
+  return dim3((unsigned)(a.batch * a.H * (DV / kStepRows)));
+}
+static dim3 whole_grid(const GdnArgs& a) { return dim3((unsigned)(a.batch * a.H)); }
+
 hipError_t launch_gdn_step(const GdnArgs& a, bool fused, hipStream_t s) {
-  const dim3 grid((unsigned)(a.batch * a.H)), block(NT);
+  const dim3 grid = half_grid(a), block(kStepThreads);
   if (a.scheme == kSchemeF32) {
     if (fused)
       hipLaunchKernelGGL((gdn_step_kernel<4, true>), grid, block, 0, s, a);
@@ -731,22 +833,27 @@ hipError_t launch_gdn_step(const GdnArgs& a, bool fused, hipStream_t s) {
 }
 
 hipError_t launch_gdn_commit(const GdnArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.batch * a.H)), block(NT);
   if (a.scheme == kSchemeF32)
-    hipLaunchKernelGGL((gdn_commit_kernel<kSchemeF32, 0>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gdn_commit_kernel<kSchemeF32, 0, kStepThreads>), half_grid(a),
+                       dim3(kStepThreads), 0, s, a);
   else if (a.scheme == kSchemeDual && a.lp == kLpBf16)
-    hipLaunchKernelGGL((gdn_commit_kernel<kSchemeDual, kLpBf16>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gdn_commit_kernel<kSchemeDual, kLpBf16, 512>), whole_grid(a), dim3(512),
+                       0, s, a);
   else if (a.scheme == kSchemeDual)
-    hipLaunchKernelGGL((gdn_commit_kernel<kSchemeDual, kLpE4m3>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gdn_commit_kernel<kSchemeDual, kLpE4m3, 512>), whole_grid(a), dim3(512),
+                       0, s, a);
   else if (a.lp == kLpBf16)
-    hipLaunchKernelGGL((gdn_commit_kernel<kSchemeShared, kLpBf16>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gdn_commit_kernel<kSchemeShared, kLpBf16, 512>), whole_grid(a),
+                       dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((gdn_commit_kernel<kSchemeShared, kLpE4m3>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gdn_commit_kernel<kSchemeShared, kLpE4m3, 512>), whole_grid(a),
+                       dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
 template <int EB>
-static void launch_gdn_verify_eb(const GdnArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+static void launch_gdn_verify_eb(const GdnArgs& a, hipStream_t s) {
+  const dim3 grid = whole_grid(a), block(512);
   if (a.n_pos <= 1)
     hipLaunchKernelGGL((gdn_verify_kernel<EB, 1>), grid, block, 0, s, a);
   else if (a.n_pos <= 2)
@@ -758,18 +865,17 @@ static void launch_gdn_verify_eb(const GdnArgs& a, dim3 grid, dim3 block, hipStr
 }
 
 hipError_t launch_gdn_verify(const GdnArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.batch * a.H)), block(NT);
   if (a.scheme == kSchemeF32)
-    launch_gdn_verify_eb<4>(a, grid, block, s);
+    launch_gdn_verify_eb<4>(a, s);
   else if (a.lp == kLpBf16)
-    launch_gdn_verify_eb<2>(a, grid, block, s);
+    launch_gdn_verify_eb<2>(a, s);
   else
-    launch_gdn_verify_eb<1>(a, grid, block, s);
+    launch_gdn_verify_eb<1>(a, s);
   return hipGetLastError();
 }
 
 hipError_t launch_gdn_eager(const GdnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(gdn_eager_kernel, dim3((unsigned)(a.batch * a.H)), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(gdn_eager_kernel, half_grid(a), dim3(kStepThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -136,10 +136,7 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < SEG / 4; ++e) part += dot4(bseg[e], cseg[e]);
-      part += __shfl_xor(part, 8);
-      part += __shfl_xor(part, 4);
-      part += __shfl_xor(part, 2);
-      part += __shfl_xor(part, 1);
+      part = group_sum<16>(part);
       if (sg == 0 && ei < L) {
         s_e[ei] = part;
         s_dt[ei] = dti;
@@ -348,10 +345,7 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
 #pragma unroll
           for (int e = 0; e < SEG; e += 4) part += dot4(ld4(bi + e), ld4(cj + e));
         }
-        part += __shfl_xor(part, 8);
-        part += __shfl_xor(part, 4);
-        part += __shfl_xor(part, 2);
-        part += __shfl_xor(part, 1);
+        part = group_sum<16>(part);
         if (sgm == 0 && act) s_e[j][i] = part;
       }
     }

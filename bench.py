@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "seq-tokens/s per SSM layer at batch 256 + HBM GB/s vs peak; speedup vs eager"
 COUNTERS = os.path.join(ROOT, "profiles", "m2_step_counters.json")
+CALIB_COPY_BYTES = 671088640
 KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_decode_replayssm_amd", "csrc", f)
                   for f in ("m2_kernels.hip", "common.hpp")]
 
@@ -315,6 +316,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain device copy of 671,088,640 bytes (counter "
+                         "calibration for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every (sequence, head) unit of the state engine is "
@@ -327,6 +331,15 @@ def main():
     from linear_attention_decode_replayssm_amd import synthetic as syn
     R.lib()                                   # fail loudly if the HIP library is missing
     torch.cuda.init()
+
+    if args.calib_copy:
+        n = CALIB_COPY_BYTES // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
 
     m2 = run_m2(torch, R, syn, args.steps, args.warmup)
     step_gbps = m2["step_bytes"] / (m2["step_us"] * 1e-6) / 1e9

@@ -32,13 +32,15 @@
  *    on one stream; distinct layers may be driven concurrently.
  *  - Row-major layouts, innermost index contiguous.  Tensors read or written
  *    with 16-byte vector accesses must be 16-byte aligned (EALIGN otherwise).
- *  - batch == 0 is valid: the call validates and returns RSSM_OK without
- *    launching anything.
+ *  - batch == 0 is valid: the call validates the descriptor's enums,
+ *    dimensions and counts, and returns RSSM_OK without launching anything.
+ *    Every per-sequence array then holds no elements and may be NULL.
  *  - Return codes (host-detected, returned before any launch, no side
  *    effects) are the RSSM_E* values below.  Errors that depend on device
  *    data (per-sequence buffer lengths) are reported through the layer's
- *    sticky `status` word instead; the offending sequence is left unchanged
- *    (no append, no index change) and its outputs are written as quiet NaN.
+ *    sticky `status` word instead.  For ring overflow and rollback past the
+ *    checkpoint the offending sequence is left unchanged (no append, no
+ *    index change) and its outputs are written as quiet NaN.
  */
 #ifndef RSSM_H
 #define RSSM_H
@@ -62,7 +64,11 @@ extern "C" {
 /* ---- sticky device status bits (layer->status[0]) ---------------------- */
 #define RSSM_STATUS_OVERFLOW  1u /* an append would exceed `capacity` entries       */
 #define RSSM_STATUS_ROLLBACK  2u /* n_reject < 0 or n_reject > len (past checkpoint)*/
-#define RSSM_STATUS_NONFINITE 4u /* non-finite state met while quantising           */
+#define RSSM_STATUS_NONFINITE 4u /* non-finite state met while quantising to E4M3   */
+/* On RSSM_STATUS_NONFINITE the head's E4M3 scale is set to 1 and its codes
+ * saturate (+-inf -> +-448, NaN stays NaN); the fp32 checkpoint and the
+ * indices are updated as for any commit.  bf16 copies carry inf and NaN
+ * natively and raise no bit. */
 
 typedef enum { RSSM_MAMBA2 = 1, RSSM_GDN = 2 } rssm_kind;
 

@@ -14,7 +14,7 @@ namespace {
 
 inline bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_layer(const rssm_layer* L) {
+int check_layer_dims(const rssm_layer* L) {
   if (!L) return RSSM_EINVAL;
   if (L->kind != RSSM_MAMBA2 && L->kind != RSSM_GDN) return RSSM_EINVAL;
   if (L->scheme < RSSM_F32 || L->scheme > RSSM_SHARED) return RSSM_EINVAL;
@@ -33,6 +33,12 @@ int check_layer(const rssm_layer* L) {
     if (L->scheme != RSSM_F32 && L->lp_dtype != RSSM_BF16 && L->lp_dtype != RSSM_E4M3)
       return RSSM_EINVAL;
   }
+  return RSSM_OK;
+}
+
+// Pointer checks of the descriptor.  Skipped at batch == 0, where every
+// per-sequence array holds no elements and may be NULL.
+int check_layer_ptrs(const rssm_layer* L) {
   // checkpoints
   if (L->scheme != RSSM_SHARED) {
     if (!L->ckpt) return RSSM_EINVAL;
@@ -123,13 +129,13 @@ const char* rssm_strerror(int code) {
 
 int rssm_mamba2_step(const rssm_layer* L, const float* x, const float* B, const float* C,
                      const float* dt, float* y, int commit_after, void* stream) {
-  int rc = check_layer(L);
+  int rc = check_layer_dims(L);
   if (rc) return rc;
   if (L->kind != RSSM_MAMBA2) return RSSM_EINVAL;
-  if ((rc = check_state(L))) return rc;
+  if (L->batch == 0) return RSSM_OK;
+  if ((rc = check_layer_ptrs(L)) || (rc = check_state(L))) return rc;
   if (!x || !B || !C || !dt || !y) return RSSM_EINVAL;
   if (!a16(x) || !a16(B) || !a16(C) || !a16(y)) return RSSM_EALIGN;
-  if (L->batch == 0) return RSSM_OK;
   rssm::M2Args a = m2_args(L);
   a.x = x;
   a.B = B;
@@ -142,14 +148,14 @@ int rssm_mamba2_step(const rssm_layer* L, const float* x, const float* B, const 
 int rssm_gdn_step(const rssm_layer* L, const float* q, const float* k, const float* v,
                   const float* alpha, const float* beta, float* o, int commit_after,
                   void* stream) {
-  int rc = check_layer(L);
+  int rc = check_layer_dims(L);
   if (rc) return rc;
   if (L->kind != RSSM_GDN) return RSSM_EINVAL;
-  if ((rc = check_state(L))) return rc;
-  if (!q || !k || !v || !alpha || !beta || !o) return RSSM_EINVAL;
-  if (!a16(q) || !a16(k) || !a16(v) || !a16(o)) return RSSM_EALIGN;
   if (commit_after && L->scheme != RSSM_F32) return RSSM_EUNSUPPORTED;
   if (L->batch == 0) return RSSM_OK;
+  if ((rc = check_layer_ptrs(L)) || (rc = check_state(L))) return rc;
+  if (!q || !k || !v || !alpha || !beta || !o) return RSSM_EINVAL;
+  if (!a16(q) || !a16(k) || !a16(v) || !a16(o)) return RSSM_EALIGN;
   rssm::GdnArgs a = gdn_args(L);
   a.q = q;
   a.k = k;
@@ -161,11 +167,11 @@ int rssm_gdn_step(const rssm_layer* L, const float* q, const float* k, const flo
 }
 
 int rssm_commit(const rssm_layer* L, const uint8_t* mask, int min_len, void* stream) {
-  int rc = check_layer(L);
+  int rc = check_layer_dims(L);
   if (rc) return rc;
-  if ((rc = check_state(L))) return rc;
   if (min_len < 0) return RSSM_ERANGE;
   if (L->batch == 0) return RSSM_OK;
+  if ((rc = check_layer_ptrs(L)) || (rc = check_state(L))) return rc;
   if (L->kind == RSSM_MAMBA2) {
     rssm::M2Args a = m2_args(L);
     a.mask = mask;
@@ -180,16 +186,17 @@ int rssm_commit(const rssm_layer* L, const uint8_t* mask, int min_len, void* str
 
 int rssm_verify(const rssm_layer* L, int n_pos, const rssm_inputs* in, float* out,
                 void* stream) {
-  int rc = check_layer(L);
+  int rc = check_layer_dims(L);
   if (rc) return rc;
-  if ((rc = check_state(L))) return rc;
-  if (!in || !out) return RSSM_EINVAL;
+  if (!in) return RSSM_EINVAL;
   if (n_pos < 1 || n_pos > L->capacity || n_pos > rssm::kMaxPos) return RSSM_ERANGE;
+  if (L->batch == 0) return RSSM_OK;
+  if ((rc = check_layer_ptrs(L)) || (rc = check_state(L))) return rc;
+  if (!out) return RSSM_EINVAL;
   if (!a16(out)) return RSSM_EALIGN;
   if (L->kind == RSSM_MAMBA2) {
     if (!in->x || !in->B || !in->C || !in->dt) return RSSM_EINVAL;
     if (!a16(in->x) || !a16(in->B) || !a16(in->C)) return RSSM_EALIGN;
-    if (L->batch == 0) return RSSM_OK;
     rssm::M2Args a = m2_args(L);
     a.x = in->x;
     a.B = in->B;
@@ -201,7 +208,6 @@ int rssm_verify(const rssm_layer* L, int n_pos, const rssm_inputs* in, float* ou
   }
   if (!in->q || !in->k || !in->v || !in->alpha || !in->beta) return RSSM_EINVAL;
   if (!a16(in->q) || !a16(in->k) || !a16(in->v)) return RSSM_EALIGN;
-  if (L->batch == 0) return RSSM_OK;
   rssm::GdnArgs a = gdn_args(L);
   a.q = in->q;
   a.k = in->k;
@@ -214,25 +220,27 @@ int rssm_verify(const rssm_layer* L, int n_pos, const rssm_inputs* in, float* ou
 }
 
 int rssm_rollback(const rssm_layer* L, const int32_t* n_reject, void* stream) {
-  int rc = check_layer(L);
+  int rc = check_layer_dims(L);
   if (rc) return rc;
-  if ((rc = check_state(L))) return rc;
-  if (!n_reject) return RSSM_EINVAL;
   if (L->batch == 0) return RSSM_OK;
+  if ((rc = check_layer_ptrs(L)) || (rc = check_state(L))) return rc;
+  if (!n_reject) return RSSM_EINVAL;
   return hip_rc(rssm::launch_rollback(L->ckpt_pos, L->len, L->status, n_reject, L->batch,
                                       S(stream)));
 }
 
 int rssm_eager_step(const rssm_layer* L, const rssm_inputs* in, float* out, void* stream) {
-  int rc = check_layer(L);
+  int rc = check_layer_dims(L);
   if (rc) return rc;
-  if (!in || !out) return RSSM_EINVAL;
+  if (!in) return RSSM_EINVAL;
   if (L->scheme == RSSM_SHARED) return RSSM_EUNSUPPORTED;
+  if (L->batch == 0) return RSSM_OK;
+  if ((rc = check_layer_ptrs(L))) return rc;
+  if (!out) return RSSM_EINVAL;
   if (!a16(out)) return RSSM_EALIGN;
   if (L->kind == RSSM_MAMBA2) {
     if (!in->x || !in->B || !in->C || !in->dt) return RSSM_EINVAL;
     if (!a16(in->x) || !a16(in->B) || !a16(in->C)) return RSSM_EALIGN;
-    if (L->batch == 0) return RSSM_OK;
     rssm::M2Args a = m2_args(L);
     a.x = in->x;
     a.B = in->B;
@@ -243,7 +251,6 @@ int rssm_eager_step(const rssm_layer* L, const rssm_inputs* in, float* out, void
   }
   if (!in->q || !in->k || !in->v || !in->alpha || !in->beta) return RSSM_EINVAL;
   if (!a16(in->q) || !a16(in->k) || !a16(in->v)) return RSSM_EALIGN;
-  if (L->batch == 0) return RSSM_OK;
   rssm::GdnArgs a = gdn_args(L);
   a.q = in->q;
   a.k = in->k;

@@ -99,6 +99,22 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
   return (uint32_t)w;
 }
 
+// As e4m3_pack4, for a tile that holds NaN or an infinity: infinities
+// saturate to +-448 like any large value; a NaN gets the E4M3 NaN code with
+// its sign (the clamp above would have turned it into a number).
+__device__ uint32_t e4m3_pack4_nonfinite(float a, float b, float c, float d) {
+  uint32_t w = e4m3_pack4(a, b, c, d);
+  const float v[4] = {a, b, c, d};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (v[i] != v[i]) {
+      const uint32_t nan = ((__float_as_uint(v[i]) >> 24) & 0x80u) | 0x7Fu;
+      w = (w & ~(0xFFu << (8 * i))) | (nan << (8 * i));
+    }
+  }
+  return w;
+}
+
 template <int EB>
 __device__ __forceinline__ void expand(u32x4 w, float (&f)[16 / EB]) {
   if constexpr (EB == 4) {
@@ -481,11 +497,18 @@ __device__ void store_lp(const f32x4 (&hv)[kWholeNLD], const GdnArgs& a, const G
     const float scale = (amax > 0.f && fin) ? amax / 448.f : 1.f;
     if (!fin && q.tid == 0) raise_status(a.status, kStatusNonfinite);
     uint8_t* base = reinterpret_cast<uint8_t*>(a.ckpt_lp) + q.unit * (DV * DK);
+    if (fin) {   // uniform over the workgroup: amax is the whole head's
 #pragma unroll
-    for (int k = 0; k < NLD; ++k) {
-      const uint32_t w = e4m3_pack4(hv[k].x / scale, hv[k].y / scale, hv[k].z / scale,
-                                    hv[k].w / scale);
-      *reinterpret_cast<uint32_t*>(base + (k * RPL + q.r0) * DK + q.cl * 4) = w;
+      for (int k = 0; k < NLD; ++k) {
+        const uint32_t w = e4m3_pack4(hv[k].x / scale, hv[k].y / scale, hv[k].z / scale,
+                                      hv[k].w / scale);
+        *reinterpret_cast<uint32_t*>(base + (k * RPL + q.r0) * DK + q.cl * 4) = w;
+      }
+    } else {     // scale 1: the values are encoded as they are
+      for (int k = 0; k < NLD; ++k) {
+        const uint32_t w = e4m3_pack4_nonfinite(hv[k].x, hv[k].y, hv[k].z, hv[k].w);
+        *reinterpret_cast<uint32_t*>(base + (k * RPL + q.r0) * DK + q.cl * 4) = w;
+      }
     }
     if (q.tid == 0) a.lp_scale[q.unit] = scale;
   }

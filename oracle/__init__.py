@@ -51,6 +51,7 @@ def lib():
         L.orc_e4m3_encode.argtypes = [_l, _fp, _u8p]
         L.orc_e4m3_decode.argtypes = [_l, _u8p, _dp]
         L.orc_e4m3_quant_heads.argtypes = [_l, _l, _fp, _fp, _u8p]
+        L.orc_e4m3_quant_heads.restype = _l
         _lib = L
     return _lib
 
@@ -163,10 +164,12 @@ def e4m3_decode(c):
     return out
 
 
-def e4m3_quant_heads(tiles):
+def e4m3_quant_heads(tiles, return_nonfinite=False):
     """Per-head scaled E4M3: tiles [..., per_head] fp32 -> (scale[...], codes).
 
-    scale = amax/448 (fp32; 1 if amax == 0), code = E4M3(s / scale).
+    scale = amax/448 (fp32; 1 if amax == 0), code = E4M3(s / scale).  A tile
+    holding a NaN or an infinity gets scale 1 and is encoded as it is.  With
+    return_nonfinite, also returns the number of such tiles.
     """
     tiles = np.ascontiguousarray(tiles, dtype=np.float32)
     lead = tiles.shape[:-1]
@@ -174,9 +177,9 @@ def e4m3_quant_heads(tiles):
     nh = int(np.prod(lead)) if lead else 1
     scale = np.empty(lead, dtype=np.float32)
     codes = np.empty(tiles.shape, dtype=np.uint8)
-    lib().orc_e4m3_quant_heads(nh, per, tiles.reshape(-1), scale.reshape(-1),
-                               codes.reshape(-1))
-    return scale, codes
+    bad = lib().orc_e4m3_quant_heads(nh, per, tiles.reshape(-1), scale.reshape(-1),
+                                     codes.reshape(-1))
+    return (scale, codes, int(bad)) if return_nonfinite else (scale, codes)
 
 
 def e4m3_dequant_heads(scale, codes):

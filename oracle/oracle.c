@@ -215,6 +215,7 @@ static uint8_t e4m3_encode_one(float f) {
   memcpy(&bits, &f, 4);
   uint8_t sign = (uint8_t)((bits >> 24) & 0x80u);
   if (isnan(f)) return (uint8_t)(sign | 0x7Fu);
+  if (isinf(f)) return (uint8_t)(sign | 0x7Eu);  /* no infinity: saturates to 448 */
   double a = fabs((double)f);
   if (a == 0.0) return sign;
   int e;
@@ -259,22 +260,30 @@ void orc_e4m3_decode(long n, const uint8_t* in, double* out) {
  *   amax  = max |s| over the tile (fp32)
  *   scale = amax / 448 in fp32 arithmetic, or 1 when amax is 0
  *   code  = E4M3(s / scale) with the fp32 quotient rounded once (IEEE)
+ * A tile holding a NaN or an infinity has no meaningful amax: its scale is 1
+ * and its values are encoded as they are (saturating, NaN kept).
  * The decisions are taken in fp32, the precision in which a kernel holds its
- * state, so that identical fp32 tiles give identical codes.                 */
-void orc_e4m3_quant_heads(long nheads, long per_head, const float* s,
+ * state, so that identical fp32 tiles give identical codes.
+ * Returns the number of tiles that held a non-finite value.                 */
+long orc_e4m3_quant_heads(long nheads, long per_head, const float* s,
                           float* scale, uint8_t* out) {
+  long nonfinite = 0;
   for (long h = 0; h < nheads; ++h) {
     const float* tile = s + h * per_head;
     float amax = 0.0f;
+    int finite = 1;
     for (long i = 0; i < per_head; ++i) {
       float v = fabsf(tile[i]);
+      if (!isfinite(v)) finite = 0;
       if (v > amax) amax = v;
     }
-    volatile float sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+    nonfinite += !finite;
+    volatile float sc = (finite && amax > 0.0f) ? amax / 448.0f : 1.0f;
     scale[h] = sc;
     for (long i = 0; i < per_head; ++i) {
       volatile float qv = tile[i] / sc;
       out[h * per_head + i] = e4m3_encode_one(qv);
     }
   }
+  return nonfinite;
 }

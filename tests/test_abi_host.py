@@ -98,6 +98,34 @@ def test_empty_batch_is_ok_without_launch():
                            check=False) == R.RSSM_OK
 
 
+def test_empty_batch_accepts_null_arrays():
+    """At batch 0 every per-sequence array holds no elements: NULL is
+    accepted everywhere, while enums, dims and counts are still validated."""
+    def bare(kind, scheme=R.RSSM_F32, lp=0):
+        m2 = kind == R.RSSM_MAMBA2
+        return R.rssm_layer(kind, scheme, lp, 0, 8 if m2 else 4, 1, 64 if m2 else 128, 128,
+                            8, 0)
+    m2, gdn = bare(R.RSSM_MAMBA2), bare(R.RSSM_GDN, R.RSSM_DUAL, R.RSSM_E4M3)
+    none = R.make_inputs()
+    for L in (m2, gdn):
+        assert R.rssm_commit(L, None, 0, stream=0, check=False) == R.RSSM_OK
+        assert R.rssm_rollback(L, None, stream=0, check=False) == R.RSSM_OK
+        assert R.rssm_verify(L, 3, none, None, stream=0, check=False) == R.RSSM_OK
+        assert R.rssm_eager_step(L, none, None, stream=0, check=False) == R.RSSM_OK
+        assert R.rssm_verify(L, 9, none, None, stream=0, check=False) == R.RSSM_ERANGE
+        assert R.rssm_commit(L, None, -1, stream=0, check=False) == R.RSSM_ERANGE
+    assert R.rssm_mamba2_step(m2, None, None, None, None, None, 1, stream=0,
+                              check=False) == R.RSSM_OK
+    assert R.rssm_gdn_step(gdn, None, None, None, None, None, None, 0, stream=0,
+                           check=False) == R.RSSM_OK
+    assert R.rssm_gdn_step(gdn, None, None, None, None, None, None, 1, stream=0,
+                           check=False) == R.RSSM_EUNSUPPORTED
+    assert R.rssm_mamba2_step(gdn, None, None, None, None, None, 0, stream=0,
+                              check=False) == R.RSSM_EINVAL
+    shared = bare(R.RSSM_GDN, R.RSSM_SHARED, R.RSSM_BF16)
+    assert R.rssm_eager_step(shared, none, None, stream=0, check=False) == R.RSSM_EUNSUPPORTED
+
+
 def test_null_layer():
     lib = R.lib()
     assert lib.rssm_mamba2_step(None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0) == R.RSSM_EINVAL

@@ -24,20 +24,7 @@ def _case(seed, T, b, H, G, P=64, N=128):
     return A, D, h0, st
 
 
-def _check_outputs(y, want, x, D):
-    """y: 1e-4 max vector relative error.  State part y - D x: the same 1e-4
-    relative to its own size, plus 4 ulp of the vector's largest |y|, because
-    y is delivered in fp32 and its rounding (up to half an ulp of |y|) is all
-    that can be recovered of a state part that is much smaller than D x."""
-    assert gu.vec_rel_err(y, want) <= gu.TOL_F32
-    dx = D[None, None, :, None].astype(np.float64) * x
-    got_s = np.asarray(y, np.float64) - dx
-    want_s = np.asarray(want, np.float64) - dx
-    err = np.abs(got_s - want_s).max(axis=-1)
-    allow = gu.TOL_F32 * np.abs(want_s).max(axis=-1) + 4 * 2.0 ** -24 * np.abs(want).max(axis=-1)
-    worst = np.unravel_index(np.argmax(err - allow), err.shape)
-    assert np.all(err <= allow), (worst, err[worst], allow[worst],
-                                  np.abs(want_s[worst]).max(), np.abs(want[worst]).max())
+_check_outputs = gu.check_m2_outputs
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["standalone_commit", "fused_commit"])

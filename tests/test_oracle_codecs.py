@@ -57,6 +57,8 @@ def test_e4m3_decode_all_codes():
     (2.0 ** -9, 0x01), (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02),
     (1.0, 0x38), (1.0625, 0x38), (1.1875, 0x3A), (-0.0, 0x80), (0.0, 0x00),
     (2.0 ** -6, 0x08), (240.0, 0x77), (256.0, 0x78),
+    # E4M3 has no infinity; the saturating conversion maps it to the largest finite
+    (math.inf, 0x7E), (-math.inf, 0xFE),
 ])
 def test_e4m3_spec_values(value, code):
     assert int(oracle.e4m3_encode(np.array([value], np.float32))[0]) == code
@@ -148,3 +150,24 @@ def test_e4m3_per_head_scale():
         err = np.abs(deq - tiles[h])
         bound = np.maximum(2.0 ** -4 * np.abs(tiles[h]), 2.0 ** -10 * scale[h]) * 1.0001
         assert np.all(err <= bound)
+
+
+def test_e4m3_nonfinite_tile_is_encoded_unscaled():
+    """A tile holding NaN or an infinity has no usable amax: scale 1, every
+    value encoded as it is (saturating), NaN kept; other tiles unaffected."""
+    rng = np.random.default_rng(23)
+    tiles = (rng.standard_normal((4, 64)) * 1000).astype(np.float32)
+    tiles[1, 7] = np.nan
+    tiles[2, 3] = -np.inf
+    scale, codes, bad = oracle.e4m3_quant_heads(tiles, return_nonfinite=True)
+    assert bad == 2
+    assert scale[1] == 1.0 and scale[2] == 1.0
+    for h in (1, 2):
+        for v, c in zip(tiles[h].tolist(), codes[h].tolist()):
+            if math.isnan(v):
+                assert c & 0x7F == 0x7F
+            else:
+                assert c == _e4m3_nearest(max(-448.0, min(448.0, v))), (v, c)
+    s_ok, c_ok = oracle.e4m3_quant_heads(tiles[[0, 3]])
+    np.testing.assert_array_equal(scale[[0, 3]], s_ok)
+    np.testing.assert_array_equal(codes[[0, 3]], c_ok)

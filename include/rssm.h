@@ -51,7 +51,8 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 1
+#define RSSM_ABI_VERSION 2
+#define RSSM_ARRIVE_STRIDE 32   /* uint32 elements between two sequences' counters */
 
 /* ---- host return codes ------------------------------------------------- */
 #define RSSM_OK            0
@@ -121,9 +122,11 @@ typedef enum {
  * Indices
  *   ckpt_pos  int64 [batch]  absolute token position of the checkpoint
  *   len       int32 [batch]  entries buffered since the checkpoint
- *   arrive    uint32 [batch] scratch counters; must be zero before the first
- *             call and are left zero by every call (the last workgroup of a
- *             sequence to finish updates its indices)
+ *   arrive    uint32 [batch][RSSM_ARRIVE_STRIDE] scratch counters (element
+ *             [b][0] is sequence b's; one 128-byte line per sequence, because
+ *             atomics to one line are serialised); must be zero before the
+ *             first call and are left zero by every call (the last workgroup
+ *             of a sequence to finish updates its indices)
  *   status    uint32 [1]     sticky RSSM_STATUS_* bits
  */
 typedef struct rssm_layer {

@@ -645,7 +645,7 @@ __global__ __launch_bounds__(kStepThreads) void gdn_step_kernel(GdnArgs a) {
   u.pos_add = FUSED ? L : 0;
   u.new_len = FUSED ? 0 : L;
   finish_update(a.arrive, a.pos, a.len, q.b, a.H * PARTS, arrived, u);
-  if (!ok && q.tid == 0) raise_status(a.status, kStatusOverflow);
+  if (!ok && last_arrival(arrived, a.H * PARTS)) raise_status(a.status, kStatusOverflow);
 }
 
 // -------------------------------------------------------------- commit ----
@@ -791,7 +791,7 @@ __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
   u.pos_add = 0;
   u.new_len = len + n;
   finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
-  if (!ok && q.tid == 0) raise_status(a.status, kStatusOverflow);
+  if (!ok && last_arrival(arrived, a.H)) raise_status(a.status, kStatusOverflow);
 }
 
 // --------------------------------------------------------------- eager ----

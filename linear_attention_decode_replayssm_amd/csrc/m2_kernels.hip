@@ -225,7 +225,7 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
   u.pos_add = FUSED ? L : 0;
   u.new_len = FUSED ? 0 : L;
   finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
-  if (!ok && q.tid == 0) raise_status(a.status, kStatusOverflow);
+  if (!ok && last_arrival(arrived, a.H)) raise_status(a.status, kStatusOverflow);
 }
 
 // -------------------------------------------------------------- commit ----
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   u.pos_add = 0;
   u.new_len = LT;
   finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
-  if (!ok && q.tid == 0) raise_status(a.status, kStatusOverflow);
+  if (!ok && last_arrival(arrived, a.H)) raise_status(a.status, kStatusOverflow);
 }
 
 // --------------------------------------------------------------- eager ----

@@ -22,6 +22,8 @@ STATUS_OVERFLOW, STATUS_ROLLBACK, STATUS_NONFINITE = 1, 2, 4
 RSSM_MAMBA2, RSSM_GDN = 1, 2
 RSSM_F32, RSSM_DUAL, RSSM_SHARED = 0, 1, 2
 RSSM_LP_NONE, RSSM_BF16, RSSM_E4M3 = 0, 1, 2
+RSSM_ABI_VERSION = 2
+RSSM_ARRIVE_STRIDE = 32   # uint32 elements between two sequences' arrival counters
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -75,6 +77,9 @@ def lib():
         for f in ("rssm_mamba2_step", "rssm_gdn_step", "rssm_commit", "rssm_verify",
                   "rssm_rollback", "rssm_eager_step", "rssm_status"):
             getattr(L, f).restype = ctypes.c_int
+        if L.rssm_abi_version() != RSSM_ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} implements ABI {L.rssm_abi_version()}, this binding "
+                               f"{RSSM_ABI_VERSION}: rebuild the library")
         _lib = L
     return _lib
 
@@ -171,7 +176,7 @@ class Layer:
     Tensors (torch, on ``device``): ``ckpt`` fp32 [b,H,dv,dk] (None under
     SHARED), ``ckpt_lp`` (uint16 bf16 bits / uint8 E4M3 codes, None under F32),
     ``lp_scale`` fp32 [b,H] (E4M3), ``A``/``D`` fp32 [H] (Mamba-2), ``rings``,
-    ``ckpt_pos`` int64 [b], ``len`` int32 [b], ``arrive`` int32 [b] (zero),
+    ``ckpt_pos`` int64 [b], ``len`` int32 [b], ``arrive`` int32 [b * RSSM_ARRIVE_STRIDE] (zero),
     ``status`` int32 [1].
     """
 
@@ -205,7 +210,8 @@ class Layer:
                           torch.zeros((batch, nheads, capacity), **f32)]
         self.ckpt_pos = torch.zeros(batch, dtype=torch.int64, device=device)
         self.len = torch.zeros(batch, dtype=torch.int32, device=device)
-        self.arrive = torch.zeros(max(batch, 1), dtype=torch.int32, device=device)
+        self.arrive = torch.zeros(max(batch, 1) * RSSM_ARRIVE_STRIDE, dtype=torch.int32,
+                                  device=device)
         self.status = torch.zeros(1, dtype=torch.int32, device=device)
         self.refresh()
 

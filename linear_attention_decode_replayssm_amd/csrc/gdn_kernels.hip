@@ -296,6 +296,31 @@ __device__ __forceinline__ void carry(const EntrySmem& s, int hi, int cl, float 
   }
 }
 
+// As carry(), for the replay step: instead of keeping every s_i, accumulate
+// sum_i s_i v_i[r] for the lane's own output row r on the way.
+template <int EPL, int LPR>
+__device__ __forceinline__ float carry_acc(const EntrySmem& s, int hi, int cl, int r,
+                                           float (&q)[EPL]) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = kMaxCap - 1; i >= 0; --i) {
+    if (i <= hi) {
+      float kv[EPL];
+      load_vec<EPL>(&s.k[i][cl * EPL], kv);
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) part += kv[e] * q[e];
+      part = group_sum<LPR>(part);
+      const float si = s.be[i] * part;
+      const float al = s.al[i];
+      acc += si * s.v[i][r];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) q[e] = al * (q[e] - si * kv[e]);
+    }
+  }
+  return acc;
+}
+
 // ---------------------------------------------------------------- fold ----
 // With u_i = beta_i (v_i - alpha_i a_i) and a_i = G_{c+1..i-1} (S_c k_i)
 // + sum_{m<i} G_{m+1..i-1} (k_m . k_i) u_m, every row satisfies the same unit
@@ -559,10 +584,15 @@ __device__ __forceinline__ void store_f32_tile(const f32x4 (&hv)[NLD], float* ro
 // parked in LDS while the stream is in flight.
 constexpr int kStepThreads = 256;
 constexpr int kStepRows = 64;
+// Rows per step workgroup.  A low-precision head is 32 KiB (bf16) or 16 KiB
+// (E4M3): half of it is too little stream to cover the workgroup's fixed
+// chain (index read, entry fetch, backward carry), so those take whole heads.
+template <int EB>
+constexpr int step_rows() { return EB == 4 ? kStepRows : DV; }
 
 template <int EB, bool FUSED>
 __global__ __launch_bounds__(kStepThreads) void gdn_step_kernel(GdnArgs a) {
-  constexpr int NTH = kStepThreads, ROWS = kStepRows, PARTS = DV / ROWS;
+  constexpr int NTH = kStepThreads, ROWS = step_rows<EB>(), PARTS = DV / ROWS;
   using Gm = LpGeo<EB, NTH, ROWS>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPL = Gm::RPL, NLD = Gm::NLD;
   const Geo q = geometry<LPR, ROWS>(a);
@@ -590,13 +620,10 @@ __global__ __launch_bounds__(kStepThreads) void gdn_step_kernel(GdnArgs a) {
   stash_entries<NTH>(er, ok ? L : 0, q.tid, es);
   __syncthreads();
 
-  float s[kMaxCap];
-  if (ok) {
-    carry<EPL, LPR>(es, L - 1, q.cl, qv, s);
-  } else {
-#pragma unroll
-    for (int i = 0; i < kMaxCap; ++i) s[i] = 0.f;
-  }
+  using M = XMap<NLD, LPR>;
+  const int r_out = q.row0 + M::index(q.lane, 0) * RPL + q.r0;   // this lane's output row
+  float obuf = 0.f;
+  if (ok) obuf = carry_acc<EPL, LPR>(es, L - 1, q.cl, r_out, qv);
 
   float d[NLD];
 #pragma unroll
@@ -609,20 +636,7 @@ __global__ __launch_bounds__(kStepThreads) void gdn_step_kernel(GdnArgs a) {
     d[k] = acc;
   }
   xreduce<NLD, LPR>(d, q.lane);
-  using M = XMap<NLD, LPR>;
-  if (M::writer(q.lane)) {
-    const int r = q.row0 + M::index(q.lane, 0) * RPL + q.r0;
-    float ov;
-    if (ok) {
-      ov = scale * d[0];
-#pragma unroll
-      for (int i = 0; i < kMaxCap; ++i)
-        if (i < L) ov += s[i] * es.v[i][r];
-    } else {
-      ov = __builtin_nanf("");
-    }
-    a.o[q.unit * DV + r] = ov;
-  }
+  if (M::writer(q.lane)) a.o[q.unit * DV + r_out] = ok ? scale * d[0] + obuf : __builtin_nanf("");
 
   if constexpr (FUSED) {   // fold the whole buffer, this entry included, and store
     static_assert(EB == 4, "fused commit folds the fp32 checkpoint");
@@ -841,16 +855,16 @@ static dim3 half_grid(const GdnArgs& a) {
 static dim3 whole_grid(const GdnArgs& a) { return dim3((unsigned)(a.batch * a.H)); }
 
 hipError_t launch_gdn_step(const GdnArgs& a, bool fused, hipStream_t s) {
-  const dim3 grid = half_grid(a), block(kStepThreads);
+  const dim3 block(kStepThreads);
   if (a.scheme == kSchemeF32) {
     if (fused)
-      hipLaunchKernelGGL((gdn_step_kernel<4, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((gdn_step_kernel<4, true>), half_grid(a), block, 0, s, a);
     else
-      hipLaunchKernelGGL((gdn_step_kernel<4, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((gdn_step_kernel<4, false>), half_grid(a), block, 0, s, a);
   } else if (a.lp == kLpBf16) {
-    hipLaunchKernelGGL((gdn_step_kernel<2, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gdn_step_kernel<2, false>), whole_grid(a), block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((gdn_step_kernel<1, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gdn_step_kernel<1, false>), whole_grid(a), block, 0, s, a);
   }
   return hipGetLastError();
 }

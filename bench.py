@@ -12,8 +12,8 @@ Printed (one JSON line): seq-tokens/s of the replay path (value), the eager
 read-modify-write kernel's seq-tokens/s on the same GPU and the speedup, the
 HBM roofline of the dominant kernel (the replay step without commit), the
 oracle timed on the host cores on a bounded sample, and secondary figures for
-the Gated DeltaNet decode, speculative verify/rollback rounds and the
-dual-precision GDN stack.
+the Gated DeltaNet decode, speculative verify/rollback rounds, the
+dual-precision GDN stack and a sweep of the Mamba-2 commit interval.
 
 Usage: python bench.py [--gpus 1] [--steps 1024] [--warmup 64] [--no-secondary]
        [--no-cpu]
@@ -214,6 +214,51 @@ def run_gdn(torch, R, syn, steps, warmup, seed=0, pool_n=16):
     return res
 
 
+def run_m2_interval_sweep(torch, R, syn, steps, seed=0, pool_n=16,
+                          intervals=(1, 2, 4, 8, 16)):
+    """Replay cost vs state traffic: the headline Mamba-2 shape with the fused
+    commit every `interval` tokens (ring = interval).  Interval 1 writes the
+    state every step, like the eager kernel."""
+    b, H, G, P, N = 256, 80, 8, 64, 128
+    A, D = syn.m2_params(seed, H)
+    pool = syn.m2_steps(seed, 0, pool_n, b, H, G, P, N)
+    dev = {k: torch.from_numpy(v).to("cuda") for k, v in pool.items()}
+    h0 = torch.from_numpy(syn.m2_state0(seed, b, H, P, N))
+    y = torch.empty((b, H, P), dtype=torch.float32, device="cuda")
+    res = {}
+    for interval in intervals:
+        L = R.Layer.mamba2(b, H, G, P, N, interval)
+        L.A.copy_(torch.from_numpy(A))
+        L.D.copy_(torch.from_numpy(D))
+        L.ckpt.copy_(h0)
+
+        def run(n):
+            for t in range(n):
+                j = t % pool_n
+                R.rssm_mamba2_step(L, dev["x"][j], dev["B"][j], dev["C"][j], dev["dt"][j], y,
+                                   commit_after=(t + 1) % interval == 0)
+
+        run(2 * interval)                      # whole cycles: the timed run starts at len 0
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = (steps // interval) * interval
+        torch.cuda.synchronize()
+        start.record()
+        run(n)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end)
+        assert R.rssm_status(L) == 0
+        byt = sum(m2_fused_bytes(b, H, G, P, N, l) if l == interval - 1 else
+                  m2_step_bytes(b, H, G, P, N, l) for l in (t % interval for t in range(n)))
+        res[str(interval)] = dict(seq_tok_s=round(b * n / (ms * 1e-3), 1),
+                                  bytes_per_step=round(byt / n),
+                                  hbm_gbps=round(byt / (ms * 1e-3) / 1e9, 1))
+        del L
+        torch.cuda.empty_cache()
+    del dev
+    return res
+
+
 def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     """Mamba-2 speculative rounds at the serving shape: verify 4 drafts,
     roll back the rejected ones, commit at 8 buffered entries; ring 12."""
@@ -241,9 +286,21 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end)
     assert R.rssm_status(L) == 0
+    # algorithmic bytes of the whole run from the per-sequence length trace
+    S, inputs, entry, out_b, _ = m2_bytes(1, H, G, P, N)   # per sequence
+    ln = np.zeros(b, np.int64)
+    total = 0
+    for r in range(rounds):
+        total += b * (S + n * (inputs + out_b + entry)) + entry * int(ln.sum())   # verify
+        ln += accept[r]                                          # append n, roll back n - a
+        com = ln >= commit_len
+        total += int(com.sum()) * 2 * S + entry * int(ln[com].sum())             # commit
+        ln[com] = 0
     res = dict(rounds_per_s=rounds / (ms * 1e-3),
                accepted_seq_tok_s=float(accept.sum()) / (ms * 1e-3),
-               us_per_round=ms * 1e3 / rounds)
+               us_per_round=ms * 1e3 / rounds,
+               bytes_per_round=total / rounds,
+               hbm_gbps=total / (ms * 1e-3) / 1e9)
     del L, dev
     torch.cuda.empty_cache()
     return res
@@ -302,11 +359,21 @@ def cpu_baseline(syn, target_s=12.0, seed=0):
     for _ in range(n // pool):
         oracle.m2_eager(A, D, st["x"], st["B"], st["C"], st["dt"], h)
     el = time.perf_counter() - t0
+    # one host thread, for context: 2 sequences x 80 heads x 64 steps
+    oracle.set_threads(1)
+    h1 = h[:2].copy()
+    sub = {k: np.ascontiguousarray(v[:, :2]) for k, v in st.items()}
+    t1 = time.perf_counter()
+    for _ in range(4):
+        oracle.m2_eager(A, D, sub["x"], sub["B"], sub["C"], sub["dt"], h1)
+    el1 = time.perf_counter() - t1
+    oracle.set_threads(threads)
     return {"value": round(b * n / el, 1), "unit": "seq-tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"fp64 eager Mamba-2 recurrence (the oracle, OpenMP over units), "
                       f"{b} sequences x {H} heads x {n} steps of the batch-256 serving shape "
-                      f"(P=64, N=128, G=8); {el:.1f} s on {threads} host threads"}
+                      f"(P=64, N=128, G=8); {el:.1f} s on {threads} host threads",
+            "value_1thread": round(2 * 4 * pool / el1, 1)}
 
 
 def main():
@@ -385,10 +452,12 @@ def main():
         g = run_gdn(torch, R, syn, sec_steps, 16)
         sp = run_spec(torch, R, syn, 128)
         du = run_dual_stack(torch, R, syn, 32)
+        sw = run_m2_interval_sweep(torch, R, syn, 256)
         out["secondary"] = {
             "gdn_decode_b256_h32_d128": {k: round(v, 2) for k, v in g.items()},
             "mamba2_spec_rounds_b256_4drafts": {k: round(v, 1) for k, v in sp.items()},
             "gdn_12layer_stack_seq_tok_s": {k: round(v, 1) for k, v in du.items()},
+            "mamba2_commit_interval_sweep": sw,
         }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(syn)

@@ -103,7 +103,7 @@ typedef enum {
  *   dim_k     Mamba-2: dstate N;   GDN: dk  (columns of the state)
  *   capacity  ring slots per sequence (1..16); entry j since the checkpoint
  *             lives in slot (ckpt_pos + j) % capacity
- *   Instantiated: Mamba-2 P=64, N=128 (F32 scheme); GDN dk=dv=128 (all schemes).
+ *   Instantiated: Mamba-2 P=64, N=128; GDN dk=dv=128; all schemes for both.
  *
  * Checkpoints  [batch][nheads][dim_v][dim_k]
  *   ckpt      fp32; required for F32 and DUAL, NULL for SHARED
@@ -168,7 +168,9 @@ typedef struct rssm_inputs {
  * included) into the fp32 checkpoint in the same pass over the state and
  * reset the buffer (explainer, "Periodically commit a new checkpoint").
  * Per sequence, len + 1 > capacity sets RSSM_STATUS_OVERFLOW (y = NaN, no
- * append).  Requires scheme RSSM_F32.
+ * append).  Output reads use ckpt (F32) or ckpt_lp (DUAL, SHARED; E4M3 values
+ * are code * lp_scale).  commit_after is supported for F32 only
+ * (RSSM_EUNSUPPORTED otherwise; use rssm_commit).
  */
 int rssm_mamba2_step(const rssm_layer* L, const float* x, const float* B,
                      const float* C, const float* dt, float* y,
@@ -215,7 +217,7 @@ int rssm_commit(const rssm_layer* L, const uint8_t* mask, int min_len,
  * in: see rssm_inputs (leading [n_pos]); out [n_pos][batch][H][dim_v].
  * 1 <= n_pos <= min(8, capacity) (RSSM_ERANGE).  Per sequence,
  * len + n_pos > capacity sets RSSM_STATUS_OVERFLOW (outputs NaN, no append).
- * Mamba-2 (F32) and GDN (F32, DUAL, SHARED).
+ * Mamba-2 and GDN, all schemes (DUAL and SHARED read ckpt_lp).
  */
 int rssm_verify(const rssm_layer* L, int n_pos, const rssm_inputs* in,
                 float* out, void* stream);
@@ -234,10 +236,15 @@ int rssm_rollback(const rssm_layer* L, const int32_t* n_reject, void* stream);
 /*
  * rssm_eager_step -- the eager baseline the pages compare against (explainer,
  * "What ReplaySSM is solving": read the entire state, update it with the
- * current input, write it back, every step).  Reads and rewrites `ckpt` in
- * place and writes the step output; rings, indices and ckpt_lp are ignored.
+ * current input, write it back, every step).  Rewrites the checkpoint in
+ * place and writes the step output; rings and indices are ignored.
  * in: one token (n = 1); out: y [batch][H][P] or o [batch][H][dv].
- * Requires the fp32 checkpoint (scheme F32 or DUAL).
+ * F32 and DUAL update the fp32 checkpoint `ckpt`.  SHARED (Mamba-2) is the
+ * comparator that keeps the recurrent state in low precision only (explainer,
+ * "What ReplaySSM is solving": the rounding then feeds every later update):
+ * ckpt_lp is decoded, updated in fp32, the output is taken from the updated
+ * values, and the result is re-encoded into ckpt_lp (and lp_scale).  SHARED
+ * GDN layers return RSSM_EUNSUPPORTED.
  */
 int rssm_eager_step(const rssm_layer* L, const rssm_inputs* in, float* out,
                     void* stream);

@@ -26,13 +26,12 @@ int check_layer_dims(const rssm_layer* L) {
   if (L->kind == RSSM_MAMBA2) {
     if (L->nheads % L->ngroups != 0) return RSSM_EINVAL;
     if (L->dim_v != 64 || L->dim_k != 128) return RSSM_EUNSUPPORTED;
-    if (L->scheme != RSSM_F32) return RSSM_EUNSUPPORTED;
   } else {
     if (L->ngroups != 1) return RSSM_EINVAL;
     if (L->dim_v != 128 || L->dim_k != 128) return RSSM_EUNSUPPORTED;
-    if (L->scheme != RSSM_F32 && L->lp_dtype != RSSM_BF16 && L->lp_dtype != RSSM_E4M3)
-      return RSSM_EINVAL;
   }
+  if (L->scheme != RSSM_F32 && L->lp_dtype != RSSM_BF16 && L->lp_dtype != RSSM_E4M3)
+    return RSSM_EINVAL;
   return RSSM_OK;
 }
 
@@ -68,6 +67,10 @@ int hip_rc(hipError_t e) { return e == hipSuccess ? RSSM_OK : RSSM_EHIP; }
 rssm::M2Args m2_args(const rssm_layer* L) {
   rssm::M2Args a{};
   a.ckpt = L->ckpt;
+  a.ckpt_lp = L->ckpt_lp;
+  a.lp_scale = L->lp_scale;
+  a.scheme = L->scheme;
+  a.lp = L->lp_dtype;
   a.A = L->A;
   a.D = L->D;
   a.ring_x = L->ring[0];
@@ -132,6 +135,7 @@ int rssm_mamba2_step(const rssm_layer* L, const float* x, const float* B, const 
   int rc = check_layer_dims(L);
   if (rc) return rc;
   if (L->kind != RSSM_MAMBA2) return RSSM_EINVAL;
+  if (commit_after && L->scheme != RSSM_F32) return RSSM_EUNSUPPORTED;
   if (L->batch == 0) return RSSM_OK;
   if ((rc = check_layer_ptrs(L)) || (rc = check_state(L))) return rc;
   if (!x || !B || !C || !dt || !y) return RSSM_EINVAL;
@@ -233,7 +237,7 @@ int rssm_eager_step(const rssm_layer* L, const rssm_inputs* in, float* out, void
   int rc = check_layer_dims(L);
   if (rc) return rc;
   if (!in) return RSSM_EINVAL;
-  if (L->scheme == RSSM_SHARED) return RSSM_EUNSUPPORTED;
+  if (L->kind == RSSM_GDN && L->scheme == RSSM_SHARED) return RSSM_EUNSUPPORTED;
   if (L->batch == 0) return RSSM_OK;
   if ((rc = check_layer_ptrs(L))) return rc;
   if (!out) return RSSM_EINVAL;

@@ -22,6 +22,7 @@
 //   S_new = G_{c+1..t} S_c + sum_i G_{i+1..t} u_i k_i^T      (G: products of alpha)
 #include "common.hpp"
 #include "launch.hpp"
+#include "lp_codec.hpp"
 
 namespace rssm {
 namespace {
@@ -29,7 +30,6 @@ namespace {
 constexpr int DK = 128;
 constexpr int DV = 128;
 constexpr int kSchemeF32 = 0, kSchemeDual = 1, kSchemeShared = 2;
-constexpr int kLpBf16 = 1, kLpE4m3 = 2;
 
 // Lane geometry: NTH threads cover ROWS rows of a head's state with 16-byte
 // lane loads of EB-byte elements.
@@ -66,76 +66,6 @@ __device__ __forceinline__ Geo geometry(const GdnArgs& a) {
   q.r0 = q.tid / LPR;
   q.unit = (long)q.b * a.H + q.h;
   return q;
-}
-
-// ---- element codecs --------------------------------------------------------
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// bf16 round-to-nearest-even of an fp32 value (NaN -> quiet NaN, sign kept).
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-// OCP E4M3 code pair -> fp32 via the gfx950 conversion (bytes 0,1 or 2,3).
-__device__ __forceinline__ f32x2 e4m3_pair(uint32_t w, bool hi) {
-  return hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true)
-            : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-}
-
-// Four fp32 values (already divided by the scale) -> four E4M3 codes.
-// Values are clamped to the largest finite magnitude first, so the
-// conversion never overflows: saturating, round to nearest even.
-__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
-  a = fminf(fmaxf(a, -448.f), 448.f);
-  b = fminf(fmaxf(b, -448.f), 448.f);
-  c = fminf(fmaxf(c, -448.f), 448.f);
-  d = fminf(fmaxf(d, -448.f), 448.f);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return (uint32_t)w;
-}
-
-// As e4m3_pack4, for a tile that holds NaN or an infinity: infinities
-// saturate to +-448 like any large value; a NaN gets the E4M3 NaN code with
-// its sign (the clamp above would have turned it into a number).
-__device__ uint32_t e4m3_pack4_nonfinite(float a, float b, float c, float d) {
-  uint32_t w = e4m3_pack4(a, b, c, d);
-  const float v[4] = {a, b, c, d};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (v[i] != v[i]) {
-      const uint32_t nan = ((__float_as_uint(v[i]) >> 24) & 0x80u) | 0x7Fu;
-      w = (w & ~(0xFFu << (8 * i))) | (nan << (8 * i));
-    }
-  }
-  return w;
-}
-
-template <int EB>
-__device__ __forceinline__ void expand(u32x4 w, float (&f)[16 / EB]) {
-  if constexpr (EB == 4) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(w[e]);
-  } else if constexpr (EB == 2) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f[2 * e] = bf16_lo(w[e]);
-      f[2 * e + 1] = bf16_hi(w[e]);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const f32x2 lo = e4m3_pair(w[e], false), hi = e4m3_pair(w[e], true);
-      f[4 * e] = lo.x;
-      f[4 * e + 1] = lo.y;
-      f[4 * e + 2] = hi.x;
-      f[4 * e + 3] = hi.y;
-    }
-  }
 }
 
 // First byte of row `row0` of head `unit`'s state (fp32 checkpoint for EB 4,
@@ -472,95 +402,23 @@ __device__ void fold_tile(f32x4 (&hv)[NLD], const EntrySmem& es, int L, int row0
   fold_update<NTH, ROWS, NLD>(hv, es, L, q, sm);
 }
 
-// Workgroup max of |hv|; a NaN anywhere makes the result +inf.
-template <int NTH, int NLD>
-__device__ float tile_amax(const f32x4 (&hv)[NLD], const Geo& q, float* red) {
-  float m = 0.f;
-  bool nan = false;
-#pragma unroll
-  for (int k = 0; k < NLD; ++k) {
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(hv[k].x), fabsf(hv[k].y)), fmaxf(fabsf(hv[k].z), fabsf(hv[k].w))));
-    nan |= !(hv[k].x == hv[k].x && hv[k].y == hv[k].y && hv[k].z == hv[k].z && hv[k].w == hv[k].w);
-  }
-  if (nan) m = __builtin_inff();
-  m = fmaxf(m, rpartner<32>(m));
-  m = fmaxf(m, rpartner<16>(m));
-  m = fmaxf(m, rpartner<8>(m));
-  m = fmaxf(m, rpartner<4>(m));
-  m = fmaxf(m, rpartner<2>(m));
-  m = fmaxf(m, rpartner<1>(m));
-  __syncthreads();
-  if (q.lane == 0) red[q.tid >> 6] = m;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < NTH / 64; ++w) r = fmaxf(r, red[w]);
-  return r;
-}
-
 using WholeGeo = LpGeo<4, 512, DV>;
 constexpr int kWholeNLD = WholeGeo::NLD;
 
-// Write the low-precision copy of a whole head held in the fp32 geometry of a
-// 512-thread workgroup.
 template <int LP>
-__device__ void store_lp(const f32x4 (&hv)[kWholeNLD], const GdnArgs& a, const Geo& q,
-                         float* red) {
-  constexpr int RPL = WholeGeo::RPL, NLD = kWholeNLD;
-  if constexpr (LP == kLpBf16) {
-    uint16_t* base = reinterpret_cast<uint16_t*>(a.ckpt_lp) + q.unit * (DV * DK);
-#pragma unroll
-    for (int k = 0; k < NLD; ++k) {
-      u32x2 w;
-      w.x = bf16_rne(hv[k].x) | (bf16_rne(hv[k].y) << 16);
-      w.y = bf16_rne(hv[k].z) | (bf16_rne(hv[k].w) << 16);
-      *reinterpret_cast<u32x2*>(base + (k * RPL + q.r0) * DK + q.cl * 4) = w;
-    }
-  } else {
-    const float amax = tile_amax<512, NLD>(hv, q, red);
-    const bool fin = amax <= 3.402823466e38f;
-    const float scale = (amax > 0.f && fin) ? amax / 448.f : 1.f;
-    if (!fin && q.tid == 0) raise_status(a.status, kStatusNonfinite);
-    uint8_t* base = reinterpret_cast<uint8_t*>(a.ckpt_lp) + q.unit * (DV * DK);
-    if (fin) {   // uniform over the workgroup: amax is the whole head's
-#pragma unroll
-      for (int k = 0; k < NLD; ++k) {
-        const uint32_t w = e4m3_pack4(hv[k].x / scale, hv[k].y / scale, hv[k].z / scale,
-                                      hv[k].w / scale);
-        *reinterpret_cast<uint32_t*>(base + (k * RPL + q.r0) * DK + q.cl * 4) = w;
-      }
-    } else {     // scale 1: the values are encoded as they are
-      for (int k = 0; k < NLD; ++k) {
-        const uint32_t w = e4m3_pack4_nonfinite(hv[k].x, hv[k].y, hv[k].z, hv[k].w);
-        *reinterpret_cast<uint32_t*>(base + (k * RPL + q.r0) * DK + q.cl * 4) = w;
-      }
-    }
-    if (q.tid == 0) a.lp_scale[q.unit] = scale;
-  }
+__device__ __forceinline__ void store_lp(const f32x4 (&hv)[kWholeNLD], const GdnArgs& a,
+                                         const Geo& q, float* red) {
+  char* lp = reinterpret_cast<char*>(a.ckpt_lp) + q.unit * (DV * DK) * (LP == kLpBf16 ? 2 : 1);
+  store_lp_tile<LP, 512, kWholeNLD, WholeGeo::RPL, DK>(
+      hv, lp, a.lp_scale ? a.lp_scale + q.unit : nullptr, a.status, q.r0, q.cl, red);
 }
 
-// Read a whole head's low-precision copy into the fp32 geometry (exact value
-// for bf16; code * scale rounded to fp32 for E4M3).
 template <int LP>
-__device__ void load_lp_as_f32(f32x4 (&hv)[kWholeNLD], const GdnArgs& a, const Geo& q) {
-  constexpr int RPL = WholeGeo::RPL, NLD = kWholeNLD;
-  if constexpr (LP == kLpBf16) {
-    const uint16_t* base = reinterpret_cast<const uint16_t*>(a.ckpt_lp) + q.unit * (DV * DK);
-#pragma unroll
-    for (int k = 0; k < NLD; ++k) {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(base + (k * RPL + q.r0) * DK + q.cl * 4);
-      hv[k] = f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
-    }
-  } else {
-    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.ckpt_lp) + q.unit * (DV * DK);
-    const float scale = a.lp_scale[q.unit];
-#pragma unroll
-    for (int k = 0; k < NLD; ++k) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(base + (k * RPL + q.r0) * DK + q.cl * 4);
-      const f32x2 lo = e4m3_pair(w, false), hi = e4m3_pair(w, true);
-      hv[k] = f32x4{lo.x * scale, lo.y * scale, hi.x * scale, hi.y * scale};
-    }
-  }
+__device__ __forceinline__ void load_lp_as_f32(f32x4 (&hv)[kWholeNLD], const GdnArgs& a,
+                                               const Geo& q) {
+  const char* lp = reinterpret_cast<const char*>(a.ckpt_lp) + q.unit * (DV * DK) * (LP == kLpBf16 ? 2 : 1);
+  load_lp_tile<LP, kWholeNLD, WholeGeo::RPL, DK>(hv, lp, a.lp_scale ? a.lp_scale + q.unit : nullptr,
+                                                 q.r0, q.cl);
 }
 
 // fp32 rows of a workgroup in the consecutive-load geometry (eager kernel).

@@ -9,7 +9,9 @@ namespace rssm {
 
 // Mamba-2 replay/eager/commit/verify arguments.  Pointers as in rssm.h.
 struct M2Args {
-  float* ckpt;          // [b][H][P][N]
+  float* ckpt;          // [b][H][P][N] fp32 (NULL under SHARED)
+  void* ckpt_lp;        // [b][H][P][N] bf16 / E4M3 codes (NULL under F32)
+  float* lp_scale;      // [b][H] (E4M3)
   const float* A;       // [H]
   const float* D;       // [H]
   float* ring_x;        // [b][H][cap][P]
@@ -26,6 +28,7 @@ struct M2Args {
   float* y;             // [n][b][H][P]
   const uint8_t* mask;  // commit only
   int batch, H, G, cap, n_pos, min_len;
+  int scheme, lp;       // rssm_scheme / rssm_lp values
 };
 
 // Gated DeltaNet arguments.

@@ -19,6 +19,7 @@
 //   h <- Gamma_{c+1..t} h_c + sum_i Gamma_{i+1..t} dt_i x_i B_i^T
 #include "common.hpp"
 #include "launch.hpp"
+#include "lp_codec.hpp"
 
 namespace rssm {
 namespace {
@@ -32,6 +33,65 @@ constexpr int NLD = P / RPL;   // float4 loads per thread for the whole tile
 constexpr int QD = NT / P;     // thread groups splitting the buffered-entry sum
 static_assert(LPR <= 64 && 64 % LPR == 0, "a state row must sit in one wave");
 static_assert(P % RPL == 0 && NT % P == 0, "tile geometry");
+constexpr int kSchemeF32 = 0, kSchemeDual = 1, kSchemeShared = 2;
+
+// Read geometry of a checkpoint of EB-byte elements (4: fp32, 2: bf16, 1:
+// E4M3): 16-byte lane loads, LPR lanes per row of N elements.
+template <int EB>
+struct RdGeo {
+  static constexpr int EPL = 16 / EB;    // elements per lane load
+  static constexpr int LPR = N / EPL;    // lanes per state row
+  static constexpr int RPL = NT / LPR;   // rows per workgroup-wide load
+  static constexpr int NLD = P / RPL;    // loads per thread
+  static_assert(LPR <= 64 && 64 % LPR == 0 && P % RPL == 0, "read geometry");
+};
+
+// First byte of head `unit`'s checkpoint that the output reads.
+template <int EB>
+__device__ __forceinline__ const char* read_base(const M2Args& a, long unit) {
+  if constexpr (EB == 4)
+    return reinterpret_cast<const char*>(a.ckpt + unit * (P * N));
+  else
+    return reinterpret_cast<const char*>(a.ckpt_lp) + unit * (P * N) * EB;
+}
+
+template <int EB>
+__device__ __forceinline__ void load_raw(const M2Args& a, long unit, int tid,
+                                         u32x4 (&raw)[RdGeo<EB>::NLD]) {
+  using Gm = RdGeo<EB>;
+  const char* base = read_base<EB>(a, unit);
+  const int cl = tid % Gm::LPR, r0 = tid / Gm::LPR;
+#pragma unroll
+  for (int k = 0; k < Gm::NLD; ++k)
+    raw[k] = ld_nt_u(base + ((k * Gm::RPL + r0) * N + cl * Gm::EPL) * EB);
+}
+
+// Row dots of the raw tile with a vector held as EPL elements per lane
+// (column block cl): d[k] for row k * RPL + r0.
+template <int EB>
+__device__ __forceinline__ void row_dots(const u32x4 (&raw)[RdGeo<EB>::NLD],
+                                         const float (&cv)[RdGeo<EB>::EPL],
+                                         float (&d)[RdGeo<EB>::NLD]) {
+  using Gm = RdGeo<EB>;
+#pragma unroll
+  for (int k = 0; k < Gm::NLD; ++k) {
+    float f[Gm::EPL];
+    expand<EB>(raw[k], f);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < Gm::EPL; ++e) acc += f[e] * cv[e];
+    d[k] = acc;
+  }
+}
+
+template <int EPL>
+__device__ __forceinline__ void load_seg(const float* p, float (&v)[EPL]) {
+#pragma unroll
+  for (int e = 0; e < EPL; e += 4) {
+    const f32x4 t = ld4(p + e);
+    v[e] = t.x; v[e + 1] = t.y; v[e + 2] = t.z; v[e + 3] = t.w;
+  }
+}
 
 struct Geo {
   int b, h, g, tid, lane, c4, r0;
@@ -69,8 +129,10 @@ __device__ __forceinline__ void store_tile(float* ck, const Geo& q, const f32x4 
 // before the 32 KiB checkpoint stream.  Waiting for them then leaves the
 // stream in flight while the prologue runs.  The ring append is done last,
 // after the stream has been consumed.
-template <bool FUSED>
+template <int EB, bool FUSED>
 __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
+  using Gm = RdGeo<EB>;
+  static_assert(!FUSED || EB == 4, "the fused commit folds the fp32 checkpoint");
   const Geo q = geometry(a);
   const int cap = a.cap;
   float* ck = a.ckpt + q.unit * (P * N);
@@ -120,10 +182,13 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
       xv[m] = i < L ? xsrc(i)[p] : 0.f;
     }
   }
-  const f32x4 cdot = ld4(Ct + q.c4 * 4);
+  const int cl = q.tid % Gm::LPR, rr0 = q.tid / Gm::LPR;   // read geometry
+  float cv[Gm::EPL];
+  load_seg<Gm::EPL>(Ct + cl * Gm::EPL, cv);
+  const float scale = (EB == 1) ? a.lp_scale[q.unit] : 1.f;
 
-  f32x4 hv[NLD];
-  load_tile(ck, q, hv);
+  u32x4 raw[Gm::NLD];
+  load_raw<EB>(a, q.unit, q.tid, raw);
   indices_consumed(len, pos);
   const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
 
@@ -164,20 +229,19 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
   }
 
   {  // Gamma * (h_c C_t) + buffered part + D x_t
-    float d[NLD];
-#pragma unroll
-    for (int k = 0; k < NLD; ++k) d[k] = dot4(hv[k], cdot);
-    xreduce<NLD, LPR>(d, q.lane);
+    float d[Gm::NLD];
+    row_dots<EB>(raw, cv, d);
+    xreduce<Gm::NLD, Gm::LPR>(d, q.lane);
     __syncthreads();
-    using M = XMap<NLD, LPR>;
+    using M = XMap<Gm::NLD, Gm::LPR>;
     if (M::writer(q.lane)) {
-      const int pr = M::index(q.lane, 0) * RPL + q.r0;
+      const int pr = M::index(q.lane, 0) * Gm::RPL + rr0;
       float yv;
       if (ok) {
         float yb = 0.f;
 #pragma unroll
         for (int j = 0; j < QD; ++j) yb += s_yb[j][pr];
-        yv = s_gamma * d[0] + yb + Dh * xt[pr];
+        yv = s_gamma * (scale * d[0]) + yb + Dh * xt[pr];
       } else {
         yv = __builtin_nanf("");
       }
@@ -187,6 +251,11 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
 
   if constexpr (FUSED) {
     if (ok) {  // fold the whole buffer, this entry included, and store
+      f32x4 hv[NLD];   // the fp32 read geometry is the tile geometry
+#pragma unroll
+      for (int k = 0; k < NLD; ++k)
+        hv[k] = f32x4{__uint_as_float(raw[k].x), __uint_as_float(raw[k].y),
+                      __uint_as_float(raw[k].z), __uint_as_float(raw[k].w)};
       __shared__ __attribute__((aligned(16))) float s_x[kMaxCap][P];
       __shared__ __attribute__((aligned(16))) float s_B[kMaxCap][N];
       for (int idx = q.tid; idx < L * P; idx += NT) s_x[idx / P][idx % P] = xsrc(idx / P)[idx % P];
@@ -229,17 +298,28 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
 }
 
 // -------------------------------------------------------------- commit ----
+// SCHEME/LP: F32 folds the fp32 checkpoint; DUAL folds fp32 and then writes
+// the low-precision image of the result (with len 0 it only refreshes the
+// image); SHARED folds the dequantised low-precision copy and re-encodes it.
+// One workgroup holds a whole head, so the E4M3 scale's amax is local.
+template <int SCHEME, int LP>
 __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
   const Geo q = geometry(a);
   const int cap = a.cap;
   const int len = a.len[q.b];
-  const bool sel = (a.mask == nullptr || a.mask[q.b] != 0) && len >= a.min_len && len > 0;
+  const bool sel = (a.mask == nullptr || a.mask[q.b] != 0) && len >= a.min_len &&
+                   (len > 0 || SCHEME == kSchemeDual);
   if (!sel) return;  // uniform for all workgroups of the sequence
 
   const int64_t pos = a.pos[q.b];
   float* ck = a.ckpt + q.unit * (P * N);
+  char* lp = reinterpret_cast<char*>(a.ckpt_lp) + q.unit * (P * N) * (LP == kLpBf16 ? 2 : 1);
+  float* lps = a.lp_scale ? a.lp_scale + q.unit : nullptr;
   f32x4 hv[NLD];
-  load_tile(ck, q, hv);
+  if constexpr (SCHEME == kSchemeShared)
+    load_lp_tile<LP, NLD, RPL, N>(hv, lp, lps, q.r0, q.c4);
+  else
+    load_tile(ck, q, hv);
   indices_consumed(len, pos);
   const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
 
@@ -248,38 +328,43 @@ __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
   const float Ah = a.A[q.h];
   __shared__ float s_dt[kMaxCap], s_fw[kMaxCap];
   __shared__ float s_gamma;
+  __shared__ float s_red[NT / 64];
   __shared__ __attribute__((aligned(16))) float s_x[kMaxCap][P];
   __shared__ __attribute__((aligned(16))) float s_B[kMaxCap][N];
-  for (int idx = q.tid; idx < L * P; idx += NT) {
-    const int i = idx / P, p = idx % P;
-    s_x[i][p] = a.ring_x[(q.unit * cap + ring_slot(slot0, i, cap)) * P + p];
-  }
-  for (int idx = q.tid; idx < L * N; idx += NT) {
-    const int i = idx / N, n = idx % N;
-    s_B[i][n] = a.ring_B[(q.gunit * cap + ring_slot(slot0, i, cap)) * N + n];
-  }
-  if (q.tid < L) s_dt[q.tid] = a.ring_dt[q.unit * cap + ring_slot(slot0, q.tid, cap)];
-  __syncthreads();
-  if (q.tid < L) {
-    float suf = 0.f;
-    for (int j = q.tid + 1; j < L; ++j) suf += s_dt[j];
-    s_fw[q.tid] = expf(Ah * suf) * s_dt[q.tid];
-    if (q.tid == 0) s_gamma = expf(Ah * (suf + s_dt[0]));
-  }
-  __syncthreads();
-  const float gam = s_gamma;
+  if (L > 0) {
+    for (int idx = q.tid; idx < L * P; idx += NT) {
+      const int i = idx / P, p = idx % P;
+      s_x[i][p] = a.ring_x[(q.unit * cap + ring_slot(slot0, i, cap)) * P + p];
+    }
+    for (int idx = q.tid; idx < L * N; idx += NT) {
+      const int i = idx / N, n = idx % N;
+      s_B[i][n] = a.ring_B[(q.gunit * cap + ring_slot(slot0, i, cap)) * N + n];
+    }
+    if (q.tid < L) s_dt[q.tid] = a.ring_dt[q.unit * cap + ring_slot(slot0, q.tid, cap)];
+    __syncthreads();
+    if (q.tid < L) {
+      float suf = 0.f;
+      for (int j = q.tid + 1; j < L; ++j) suf += s_dt[j];
+      s_fw[q.tid] = expf(Ah * suf) * s_dt[q.tid];
+      if (q.tid == 0) s_gamma = expf(Ah * (suf + s_dt[0]));
+    }
+    __syncthreads();
+    const float gam = s_gamma;
 #pragma unroll
-  for (int k = 0; k < NLD; ++k) hv[k] *= gam;
-  for (int i = 0; i < L; ++i) {
-    const f32x4 bi = ld4(&s_B[i][q.c4 * 4]);
-    const float w = s_fw[i];
+    for (int k = 0; k < NLD; ++k) hv[k] *= gam;
+    for (int i = 0; i < L; ++i) {
+      const f32x4 bi = ld4(&s_B[i][q.c4 * 4]);
+      const float w = s_fw[i];
 #pragma unroll
-    for (int k = 0; k < NLD; ++k) hv[k] += (w * s_x[i][k * RPL + q.r0]) * bi;
+      for (int k = 0; k < NLD; ++k) hv[k] += (w * s_x[i][k * RPL + q.r0]) * bi;
+    }
+    if constexpr (SCHEME != kSchemeShared) store_tile(ck, q, hv);
   }
-  store_tile(ck, q, hv);
+  if constexpr (SCHEME != kSchemeF32)
+    store_lp_tile<LP, NT, NLD, RPL, N>(hv, lp, lps, a.status, q.r0, q.c4, s_red);
 
   IndexUpdate u;
-  u.apply = true;
+  u.apply = L > 0;
   u.pos_add = L;
   u.new_len = 0;
   finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
@@ -289,13 +374,15 @@ __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
 // n_pos drafts appended at entries len..len+n-1; draft j's output uses
 // entries 0..len+j.  One checkpoint read serves all positions: each row of
 // h_c is dotted with every C_j before the cross-lane reduction.
-template <int NPAD>
+template <int EB, int NPAD>
 __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
+  using Gm = RdGeo<EB>;
   const Geo q = geometry(a);
   const int cap = a.cap, n = a.n_pos;
-  float* ck = a.ckpt + q.unit * (P * N);
-  f32x4 hv[NLD];
-  load_tile(ck, q, hv);
+  u32x4 raw[Gm::NLD];
+  load_raw<EB>(a, q.unit, q.tid, raw);
+  const int cl = q.tid % Gm::LPR, rr0 = q.tid / Gm::LPR;
+  const float scale = (EB == 1) ? a.lp_scale[q.unit] : 1.f;
 
   const int len = a.len[q.b];
   const int64_t pos = a.pos[q.b];
@@ -315,6 +402,12 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   __shared__ float s_w[NPAD][kMaxCap];
   __shared__ float s_gam[NPAD];
   __shared__ float s_yb[QD][NPAD][P];
+  __shared__ __attribute__((aligned(16))) float s_C[NPAD][N];   // the drafts' C_j
+  for (int idx = q.tid; idx < NPAD * N; idx += NT) {
+    const int j = idx / N, c = idx % N;
+    s_C[j][c] = j < n ? a.C[j * sg + q.gunit * N + c] : 0.f;
+  }
+  __syncthreads();
 
   auto xsrc = [&](int i) -> const float* {
     return i < len ? a.ring_x + (q.unit * cap + ring_slot(slot0, i, cap)) * P
@@ -377,31 +470,39 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
     }
   }
 
-  constexpr int V = NLD * NPAD;
+  constexpr int V = Gm::NLD * NPAD;
   float d[V];
 #pragma unroll
-  for (int j = 0; j < NPAD; ++j) {
-    f32x4 c = {0.f, 0.f, 0.f, 0.f};
-    if (j < n) c = ld4(a.C + j * sg + q.gunit * N + q.c4 * 4);
+  for (int k = 0; k < Gm::NLD; ++k) {
+    float f[Gm::EPL];
+    expand<EB>(raw[k], f);
 #pragma unroll
-    for (int k = 0; k < NLD; ++k) d[k * NPAD + j] = dot4(hv[k], c);
+    for (int j = 0; j < NPAD; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < Gm::EPL; e += 4) {
+        const f32x4 c = ld4(&s_C[j][cl * Gm::EPL + e]);
+        acc += f[e] * c.x + f[e + 1] * c.y + f[e + 2] * c.z + f[e + 3] * c.w;
+      }
+      d[k * NPAD + j] = acc;
+    }
   }
-  xreduce<V, LPR>(d, q.lane);
+  xreduce<V, Gm::LPR>(d, q.lane);
   __syncthreads();
-  using M = XMap<V, LPR>;
+  using M = XMap<V, Gm::LPR>;
   if (M::writer(q.lane)) {
 #pragma unroll
     for (int jj = 0; jj < M::VOUT; ++jj) {
       const int idx = M::index(q.lane, jj);
       const int k = idx / NPAD, j = idx % NPAD;
       if (j < n) {
-        const int p = k * RPL + q.r0;
+        const int p = k * Gm::RPL + rr0;
         float yv;
         if (ok) {
           float yb = 0.f;
 #pragma unroll
           for (int qd = 0; qd < QD; ++qd) yb += s_yb[qd][j][p];
-          yv = s_gam[j] * d[jj] + yb + Dh * a.x[j * sx + q.unit * P + p];
+          yv = s_gam[j] * (scale * d[jj]) + yb + Dh * a.x[j * sx + q.unit * P + p];
         } else {
           yv = __builtin_nanf("");
         }
@@ -429,12 +530,22 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
 }
 
 // --------------------------------------------------------------- eager ----
-// Read the whole state, update it, write it back, every step.
+// Read the whole state, update it, write it back, every step.  LP = 0: the
+// fp32 checkpoint.  LP = bf16 / E4M3: the comparator that keeps the state in
+// low precision only (the shared scheme's copy): decode, update in fp32,
+// output from the updated values, re-encode, so that the rounding of every
+// step feeds the next one.
+template <int LP>
 __global__ __launch_bounds__(NT) void m2_eager_kernel(M2Args a) {
   const Geo q = geometry(a);
   float* ck = a.ckpt + q.unit * (P * N);
+  char* lp = reinterpret_cast<char*>(a.ckpt_lp) + q.unit * (P * N) * (LP == kLpBf16 ? 2 : 1);
+  float* lps = a.lp_scale ? a.lp_scale + q.unit : nullptr;
   f32x4 hv[NLD];
-  load_tile(ck, q, hv);
+  if constexpr (LP == 0)
+    load_tile(ck, q, hv);
+  else
+    load_lp_tile<LP, NLD, RPL, N>(hv, lp, lps, q.r0, q.c4);
   const float dtv = a.dt[q.unit];
   const float dec = expf(dtv * a.A[q.h]);
   const float* xt = a.x + q.unit * P;
@@ -447,7 +558,12 @@ __global__ __launch_bounds__(NT) void m2_eager_kernel(M2Args a) {
     hv[k] = dec * hv[k] + xv * bb;
     d[k] = dot4(hv[k], cc);
   }
-  store_tile(ck, q, hv);
+  if constexpr (LP == 0) {
+    store_tile(ck, q, hv);
+  } else {
+    __shared__ float s_red[NT / 64];
+    store_lp_tile<LP, NT, NLD, RPL, N>(hv, lp, lps, a.status, q.r0, q.c4, s_red);
+  }
   xreduce<NLD, LPR>(d, q.lane);
   using M = XMap<NLD, LPR>;
   if (M::writer(q.lane)) {
@@ -460,33 +576,65 @@ __global__ __launch_bounds__(NT) void m2_eager_kernel(M2Args a) {
 
 hipError_t launch_m2_step(const M2Args& a, bool fused, hipStream_t s) {
   const dim3 grid((unsigned)(a.batch * a.H)), block(NT);
-  if (fused)
-    hipLaunchKernelGGL(m2_step_kernel<true>, grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL(m2_step_kernel<false>, grid, block, 0, s, a);
+  if (a.scheme == kSchemeF32) {
+    if (fused)
+      hipLaunchKernelGGL((m2_step_kernel<4, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((m2_step_kernel<4, false>), grid, block, 0, s, a);
+  } else if (a.lp == kLpBf16) {
+    hipLaunchKernelGGL((m2_step_kernel<2, false>), grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((m2_step_kernel<1, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_m2_commit(const M2Args& a, hipStream_t s) {
-  hipLaunchKernelGGL(m2_commit_kernel, dim3((unsigned)(a.batch * a.H)), dim3(NT), 0, s, a);
+  const dim3 grid((unsigned)(a.batch * a.H)), block(NT);
+  if (a.scheme == kSchemeF32)
+    hipLaunchKernelGGL((m2_commit_kernel<kSchemeF32, 0>), grid, block, 0, s, a);
+  else if (a.scheme == kSchemeDual && a.lp == kLpBf16)
+    hipLaunchKernelGGL((m2_commit_kernel<kSchemeDual, kLpBf16>), grid, block, 0, s, a);
+  else if (a.scheme == kSchemeDual)
+    hipLaunchKernelGGL((m2_commit_kernel<kSchemeDual, kLpE4m3>), grid, block, 0, s, a);
+  else if (a.lp == kLpBf16)
+    hipLaunchKernelGGL((m2_commit_kernel<kSchemeShared, kLpBf16>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((m2_commit_kernel<kSchemeShared, kLpE4m3>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_m2_verify(const M2Args& a, hipStream_t s) {
+template <int EB>
+static void launch_m2_verify_eb(const M2Args& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.batch * a.H)), block(NT);
   if (a.n_pos <= 1)
-    hipLaunchKernelGGL(m2_verify_kernel<1>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((m2_verify_kernel<EB, 1>), grid, block, 0, s, a);
   else if (a.n_pos <= 2)
-    hipLaunchKernelGGL(m2_verify_kernel<2>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((m2_verify_kernel<EB, 2>), grid, block, 0, s, a);
   else if (a.n_pos <= 4)
-    hipLaunchKernelGGL(m2_verify_kernel<4>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((m2_verify_kernel<EB, 4>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL(m2_verify_kernel<8>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((m2_verify_kernel<EB, 8>), grid, block, 0, s, a);
+}
+
+hipError_t launch_m2_verify(const M2Args& a, hipStream_t s) {
+  if (a.scheme == kSchemeF32)
+    launch_m2_verify_eb<4>(a, s);
+  else if (a.lp == kLpBf16)
+    launch_m2_verify_eb<2>(a, s);
+  else
+    launch_m2_verify_eb<1>(a, s);
   return hipGetLastError();
 }
 
 hipError_t launch_m2_eager(const M2Args& a, hipStream_t s) {
-  hipLaunchKernelGGL(m2_eager_kernel, dim3((unsigned)(a.batch * a.H)), dim3(NT), 0, s, a);
+  const dim3 grid((unsigned)(a.batch * a.H)), block(NT);
+  if (a.scheme != kSchemeShared)
+    hipLaunchKernelGGL((m2_eager_kernel<0>), grid, block, 0, s, a);
+  else if (a.lp == kLpBf16)
+    hipLaunchKernelGGL((m2_eager_kernel<kLpBf16>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((m2_eager_kernel<kLpE4m3>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -226,9 +226,10 @@ class Layer:
         return self.desc
 
     @classmethod
-    def mamba2(cls, batch, nheads, ngroups, headdim, dstate, capacity, device="cuda"):
+    def mamba2(cls, batch, nheads, ngroups, headdim, dstate, capacity, scheme=RSSM_F32,
+               lp_dtype=RSSM_LP_NONE, device="cuda"):
         return cls(RSSM_MAMBA2, batch, nheads, headdim, dstate, capacity, ngroups=ngroups,
-                   device=device)
+                   scheme=scheme, lp_dtype=lp_dtype, device=device)
 
     @classmethod
     def gdn(cls, batch, nheads, dk, dv, capacity, scheme=RSSM_F32, lp_dtype=RSSM_LP_NONE,

@@ -15,7 +15,10 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
   is refreshed at each commit either from the high-precision state ("dual") or
   from itself ("shared") (Abstract: the low-precision copy serves the outputs
   on most steps and only the high-precision checkpoint takes the recurrent
-  updates; explainer, "Separate precisions for serving vs updating state").
+  updates; explainer, "Separate precisions for serving vs updating state");
+* the eager recurrence with its state stored in low precision, re-encoded
+  after every step (explainer, "What ReplaySSM is solving": rounding fed back
+  into every later update).
 
 Because the eager recurrence started from any state S and run over the buffered
 inputs equals the replay from checkpoint S over the same inputs, serving from
@@ -181,8 +184,10 @@ def quantize(state_f32, lp):
     raise ValueError(lp)
 
 
-def gdn_lowprec(q, k, v, alpha, beta, S0, interval, scheme, lp):
-    """GDN plain decode with a low-precision serving checkpoint.
+def _lowprec(run, state0, T, out_shape, interval, scheme, lp):
+    """Plain decode with a low-precision serving checkpoint; `run(sl, state)`
+    runs the eager recurrence over steps `sl` from `state` (fp64, updated in
+    place) and returns their outputs.
 
     scheme "dual": an fp32-class state receives every update; at each commit
     the low-precision copy is re-quantised from it.  scheme "shared": the
@@ -191,25 +196,20 @@ def gdn_lowprec(q, k, v, alpha, beta, S0, interval, scheme, lp):
     output is served from the low-precision copy plus the buffered inputs
     (commit happens after the output of the step that fills the interval).
     The state that is quantised is first rounded to fp32, the precision in
-    which a kernel holds it.
-
-    Returns dict(o_emul, o_exact, ckpt_exact [b,H,dv,dk] at the last commit,
-    codes, scale (last commit), commits (step indices)).
-    """
-    T = q.shape[0]
-    exact = np.array(S0, dtype=np.float64, copy=True)
+    which a kernel holds it."""
+    exact = np.array(state0, dtype=np.float64, copy=True)
     codes, scale, val = quantize(exact.astype(np.float32), lp)
     serve = val.copy()
-    o_emul = np.empty(v.shape, np.float64)
-    o_exact = np.empty(v.shape, np.float64)
+    o_emul = np.empty(out_shape, np.float64)
+    o_exact = np.empty(out_shape, np.float64)
     ckpt_exact = exact.copy()
     commits = []
     start = 0
     for t in range(T):
         if (t + 1 - start) == interval or t == T - 1:
             sl = slice(start, t + 1)
-            o_exact[sl] = gdn_eager(q[sl], k[sl], v[sl], alpha[sl], beta[sl], exact)
-            o_emul[sl] = gdn_eager(q[sl], k[sl], v[sl], alpha[sl], beta[sl], serve)
+            o_exact[sl] = run(sl, exact)
+            o_emul[sl] = run(sl, serve)
             if (t + 1 - start) == interval:
                 src = exact if scheme == "dual" else serve
                 codes, scale, val = quantize(src.astype(np.float32), lp)
@@ -220,6 +220,56 @@ def gdn_lowprec(q, k, v, alpha, beta, S0, interval, scheme, lp):
     return dict(o_emul=o_emul, o_exact=o_exact, ckpt_exact=ckpt_exact,
                 codes=codes, scale=scale, commits=commits, state=exact,
                 serve=serve)
+
+
+def gdn_lowprec(q, k, v, alpha, beta, S0, interval, scheme, lp):
+    """GDN plain decode with a low-precision serving checkpoint (see _lowprec).
+
+    Returns dict(o_emul, o_exact, ckpt_exact [b,H,dv,dk] at the last commit,
+    codes, scale (last commit), commits (step indices))."""
+    def run(sl, S):
+        return gdn_eager(q[sl], k[sl], v[sl], alpha[sl], beta[sl], S)
+    return _lowprec(run, S0, q.shape[0], v.shape, interval, scheme, lp)
+
+
+def m2_lowprec(A, D, x, B, C, dt, h0, interval, scheme, lp):
+    """Mamba-2 plain decode with a low-precision serving checkpoint (see
+    _lowprec); outputs under "o_emul" / "o_exact", shape of x."""
+    def run(sl, h):
+        return m2_eager(A, D, x[sl], B[sl], C[sl], dt[sl], h)
+    return _lowprec(run, h0, x.shape[0], x.shape, interval, scheme, lp)
+
+
+def _eager_lowprec(run, state0, T, out_shape, lp):
+    """Eager recurrence whose state lives in low precision only (explainer,
+    "What ReplaySSM is solving": storing the recurrent state in low precision
+    feeds its rounding back into every later update).  Each step decodes the
+    stored copy, runs one exact step from it, takes the output from the
+    updated state, rounds that state to fp32 (the precision a kernel holds it
+    in) and re-encodes it.  Returns dict(o, o_exact, codes, scale, state)."""
+    exact = np.array(state0, dtype=np.float64, copy=True)
+    codes, scale, val = quantize(exact.astype(np.float32), lp)
+    o = np.empty(out_shape, np.float64)
+    o_exact = np.empty(out_shape, np.float64)
+    for t in range(T):
+        sl = slice(t, t + 1)
+        o_exact[sl] = run(sl, exact)
+        cur = val.copy()
+        o[sl] = run(sl, cur)
+        codes, scale, val = quantize(cur.astype(np.float32), lp)
+    return dict(o=o, o_exact=o_exact, codes=codes, scale=scale, state=exact, serve=val)
+
+
+def m2_eager_lowprec(A, D, x, B, C, dt, h0, lp):
+    def run(sl, h):
+        return m2_eager(A, D, x[sl], B[sl], C[sl], dt[sl], h)
+    return _eager_lowprec(run, h0, x.shape[0], x.shape, lp)
+
+
+def gdn_eager_lowprec(q, k, v, alpha, beta, S0, lp):
+    def run(sl, S):
+        return gdn_eager(q[sl], k[sl], v[sl], alpha[sl], beta[sl], S)
+    return _eager_lowprec(run, S0, q.shape[0], v.shape, lp)
 
 
 def gdn_carry_batched(q_t, ks, alphas, betas):

@@ -48,6 +48,34 @@ def check_m2_outputs(y, want, x, D):
                                   np.abs(want_s[worst]).max(), np.abs(want[worst]).max())
 
 
+def codes_close(got, want, lp_is_bf16, got_scale=None, want_scale=None, near_zero=1e-6):
+    """Compare a GPU low-precision copy with the oracle's emulated one.
+
+    got / want: codes of shape [b, H, R, C] (bf16 bits as uint16/int16, or
+    E4M3 bytes); scales [b, H] for E4M3.  A code pair is accepted when equal,
+    one step apart with the same sign, or when both decoded values lie within
+    near_zero x the head's largest magnitude of zero (there the sign itself is
+    fp32 rounding noise of the state being encoded).  Returns (all accepted,
+    fraction of unequal codes)."""
+    import oracle
+    sign = 0x8000 if lp_is_bf16 else 0x80
+    g = (np.asarray(got).view(np.uint16) if lp_is_bf16 else np.asarray(got)).astype(np.int64)
+    w = np.asarray(want).astype(np.int64)
+    b, H = g.shape[:2]
+    if lp_is_bf16:
+        gv = oracle.bf16_decode(g.astype(np.uint16))
+        wv = oracle.bf16_decode(w.astype(np.uint16))
+    else:
+        gv = oracle.e4m3_dequant_heads(got_scale, g.astype(np.uint8).reshape(b, H, -1)).reshape(g.shape)
+        wv = oracle.e4m3_dequant_heads(want_scale, w.astype(np.uint8).reshape(b, H, -1)).reshape(w.shape)
+    amax = np.abs(wv).reshape(b, H, -1).max(-1)[:, :, None, None]
+    diff = np.abs(g - w)
+    ok = (diff == 0) | ((diff == 1) & ((g & sign) == (w & sign)))
+    ok |= ((g | w) & (sign - 1)) <= 1                     # zero and the smallest magnitude
+    ok |= (np.abs(gv) <= near_zero * amax) & (np.abs(wv) <= near_zero * amax)
+    return bool(ok.all()), float((diff != 0).mean())
+
+
 def indices(layer):
     return host(layer.ckpt_pos).copy(), host(layer.len).copy()
 

@@ -123,7 +123,7 @@ def test_empty_batch_accepts_null_arrays():
     assert R.rssm_mamba2_step(gdn, None, None, None, None, None, 0, stream=0,
                               check=False) == R.RSSM_EINVAL
     shared = bare(R.RSSM_GDN, R.RSSM_SHARED, R.RSSM_BF16)
-    assert R.rssm_eager_step(shared, none, None, stream=0, check=False) == R.RSSM_EUNSUPPORTED
+    assert R.rssm_eager_step(shared, none, None, stream=0, check=False) == R.RSSM_EUNSUPPORTED   # GDN eager-lp
 
 
 def test_null_layer():
@@ -142,7 +142,8 @@ def test_null_layer():
     (dict(dim_k=64), R.RSSM_EUNSUPPORTED),
     (dict(capacity=17), R.RSSM_EUNSUPPORTED),
     (dict(capacity=0), R.RSSM_EINVAL),
-    (dict(scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_BF16), R.RSSM_EUNSUPPORTED),
+    (dict(scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_BF16), R.RSSM_EINVAL),   # ckpt_lp missing
+    (dict(scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_LP_NONE), R.RSSM_EINVAL),
     (dict(ckpt=FAKE + 4), R.RSSM_EALIGN),
     (dict(ckpt=0), R.RSSM_EINVAL),
 ])

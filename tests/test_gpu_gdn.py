@@ -6,7 +6,8 @@ dual scheme must stay inside the one-quantisation bound at every step
 (|o - o_exact| <= sum_j delta(S_c[r,j]) |q~_j| + 1e-4 ||o_exact||_inf, with
 S_c the exact checkpoint of the last commit, q~ the carried query, delta half
 an lp ulp), and its codes must equal the oracle's emulated codes or differ by
-one ulp, in at most 1e-3 of the elements.  The shared scheme is the
+one ulp (or both decode to within 1e-6 of the head's amax of zero), in at
+most 1e-3 of the elements.  The shared scheme is the
 comparison scheme: its error is reported.  The codecs are bit-exact.
 """
 import numpy as np
@@ -198,20 +199,6 @@ def test_decode_bit_exact(lp):
 
 # ---------------------------------------------------- dual / shared --
 
-def _adjacent_fraction(got, want, lp):
-    """(all codes equal or one ulp apart?, fraction unequal)."""
-    if lp == R.RSSM_BF16:
-        g = got.view(np.uint16).astype(np.int64)
-        w = want.astype(np.int64)
-    else:
-        g = got.astype(np.int64)
-        w = want.astype(np.int64)
-    same_sign = (g & (0x8000 if lp == R.RSSM_BF16 else 0x80)) == (w & (0x8000 if lp == R.RSSM_BF16 else 0x80))
-    diff = np.abs(g - w)
-    adj = (diff == 0) | ((diff == 1) & same_sign) | (((g | w) & ~(0x8000 if lp == R.RSSM_BF16 else 0x80)) <= 1)
-    return bool(adj.all()), float((diff != 0).mean())
-
-
 def _run_lowprec(scheme, lp, T, b, H, interval, seed, slow=False):
     S0, st = _case(seed, T, b, H, s0=0.0)
     if slow:   # slow decay: alpha = exp(-softplus(N(-5, 1)))
@@ -258,7 +245,8 @@ def test_dual_precision_one_quantisation_bound(lp):
         worst = max(worst, float(((err - bound) / np.abs(ex).max()).max()))
         oracle.gdn_eager(st["q"][t:t + 1], st["k"][t:t + 1], st["v"][t:t + 1],
                          st["alpha"][t:t + 1], st["beta"][t:t + 1], S)
-    ok, frac = _adjacent_fraction(gu.host(L.ckpt_lp), ref["codes"], lp)
+    ok, frac = gu.codes_close(gu.host(L.ckpt_lp), ref["codes"], lp == R.RSSM_BF16,
+                              None if L.lp_scale is None else gu.host(L.lp_scale), ref["scale"])
     assert ok and frac <= 1e-3, frac
     assert gu.vec_rel_err(gu.host(L.ckpt), ref["state"]) <= 1e-5     # fp32 path untouched
     assert R.rssm_status(L) == 0

@@ -239,12 +239,11 @@ int rssm_rollback(const rssm_layer* L, const int32_t* n_reject, void* stream);
  * current input, write it back, every step).  Rewrites the checkpoint in
  * place and writes the step output; rings and indices are ignored.
  * in: one token (n = 1); out: y [batch][H][P] or o [batch][H][dv].
- * F32 and DUAL update the fp32 checkpoint `ckpt`.  SHARED (Mamba-2) is the
- * comparator that keeps the recurrent state in low precision only (explainer,
- * "What ReplaySSM is solving": the rounding then feeds every later update):
- * ckpt_lp is decoded, updated in fp32, the output is taken from the updated
- * values, and the result is re-encoded into ckpt_lp (and lp_scale).  SHARED
- * GDN layers return RSSM_EUNSUPPORTED.
+ * F32 and DUAL update the fp32 checkpoint `ckpt`.  SHARED is the comparator
+ * that keeps the recurrent state in low precision only (explainer, "What
+ * ReplaySSM is solving": the rounding then feeds every later update): ckpt_lp
+ * is decoded, updated in fp32, the output is taken from the updated values,
+ * and the result is re-encoded into ckpt_lp (and lp_scale).
  */
 int rssm_eager_step(const rssm_layer* L, const rssm_inputs* in, float* out,
                     void* stream);

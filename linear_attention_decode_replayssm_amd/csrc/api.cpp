@@ -237,7 +237,6 @@ int rssm_eager_step(const rssm_layer* L, const rssm_inputs* in, float* out, void
   int rc = check_layer_dims(L);
   if (rc) return rc;
   if (!in) return RSSM_EINVAL;
-  if (L->kind == RSSM_GDN && L->scheme == RSSM_SHARED) return RSSM_EUNSUPPORTED;
   if (L->batch == 0) return RSSM_OK;
   if ((rc = check_layer_ptrs(L))) return rc;
   if (!out) return RSSM_EINVAL;

@@ -668,10 +668,14 @@ __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
 
 // --------------------------------------------------------------- eager ----
 // Per row r: (S k)_r, then S_r <- alpha S_r + beta (v_r - alpha (S k)_r) k^T,
-// then o_r = S_r . q with the updated row; the state is written back.  One
-// 256-thread workgroup per half head.
-__global__ __launch_bounds__(kStepThreads) void gdn_eager_kernel(GdnArgs a) {
-  constexpr int NTH = kStepThreads, ROWS = kStepRows;
+// then o_r = S_r . q with the updated row; the state is written back.
+// LP = 0: the fp32 checkpoint, one 256-thread workgroup per half head.
+// LP = bf16 / E4M3: the comparator that keeps the state in low precision only
+// (decode, update in fp32, output from the updated rows, re-encode), one
+// 512-thread workgroup per head for the per-head scale.
+template <int LP>
+__global__ __launch_bounds__(LP == 0 ? kStepThreads : 512) void gdn_eager_kernel(GdnArgs a) {
+  constexpr int NTH = LP == 0 ? kStepThreads : 512, ROWS = LP == 0 ? kStepRows : DV;
   using Gm = LpGeo<4, NTH, ROWS>;
   constexpr int RPL = Gm::RPL, NLD = Gm::NLD, LPR = Gm::LPR;
   const Geo q = geometry<LPR, ROWS>(a);
@@ -684,7 +688,10 @@ __global__ __launch_bounds__(kStepThreads) void gdn_eager_kernel(GdnArgs a) {
   for (int k = 0; k < NLD; ++k) vr[k] = vv[k * RPL + q.r0];
   float* rows = a.ckpt + q.unit * (DV * DK) + q.row0 * DK;
   f32x4 hv[NLD];
-  load_f32_tile<RPL, NLD>(hv, rows, q);
+  if constexpr (LP == 0)
+    load_f32_tile<RPL, NLD>(hv, rows, q);
+  else
+    load_lp_as_f32<LP>(hv, a, q);
   float sk[NLD];
 #pragma unroll
   for (int k = 0; k < NLD; ++k) sk[k] = dot4(hv[k], kv);
@@ -696,7 +703,12 @@ __global__ __launch_bounds__(kStepThreads) void gdn_eager_kernel(GdnArgs a) {
     hv[k] = al * hv[k] + coef * kv;
     d[k] = dot4(hv[k], qv);
   }
-  store_f32_tile<RPL, NLD>(hv, rows, q);
+  if constexpr (LP == 0) {
+    store_f32_tile<RPL, NLD>(hv, rows, q);
+  } else {
+    __shared__ float s_red[NTH / 64];
+    store_lp<LP>(hv, a, q, s_red);
+  }
   xreduce<NLD, LPR>(d, q.lane);
   using M = XMap<NLD, LPR>;
   if (M::writer(q.lane)) {
@@ -770,7 +782,12 @@ hipError_t launch_gdn_verify(const GdnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gdn_eager(const GdnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(gdn_eager_kernel, half_grid(a), dim3(kStepThreads), 0, s, a);
+  if (a.scheme != kSchemeShared)
+    hipLaunchKernelGGL((gdn_eager_kernel<0>), half_grid(a), dim3(kStepThreads), 0, s, a);
+  else if (a.lp == kLpBf16)
+    hipLaunchKernelGGL((gdn_eager_kernel<kLpBf16>), whole_grid(a), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((gdn_eager_kernel<kLpE4m3>), whole_grid(a), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -19,6 +19,21 @@ HEADER = os.path.join(ROOT, "include", "rssm.h")
 FAKE = 0x10000          # 16-byte aligned stand-in address (never dereferenced)
 
 
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0   # counts devices without initialising them
+    except Exception:
+        return False
+
+
+# The stand-in addresses are only safe where nothing can be launched: should a
+# validation ever let one of these calls through, a visible GPU would receive
+# a kernel with bogus pointers.  On a machine with a GPU these host tests are
+# skipped (the GPU tests cover the same entry points with real buffers).
+pytestmark = pytest.mark.skipif(_gpu_visible(), reason="host-only tests with stand-in pointers")
+
+
 def _declared():
     text = open(HEADER).read()
     return sorted(set(re.findall(r"^(?:int|const char\*)\s+(rssm_\w+)\s*\(", text, re.M)))
@@ -123,7 +138,7 @@ def test_empty_batch_accepts_null_arrays():
     assert R.rssm_mamba2_step(gdn, None, None, None, None, None, 0, stream=0,
                               check=False) == R.RSSM_EINVAL
     shared = bare(R.RSSM_GDN, R.RSSM_SHARED, R.RSSM_BF16)
-    assert R.rssm_eager_step(shared, none, None, stream=0, check=False) == R.RSSM_EUNSUPPORTED   # GDN eager-lp
+    assert R.rssm_eager_step(shared, none, None, stream=0, check=False) == R.RSSM_OK
 
 
 def test_null_layer():
@@ -200,8 +215,9 @@ def test_gdn_validation():
     assert R.rssm_commit(L, None, 0, stream=0, check=False) == R.RSSM_EINVAL
     L = _gdn_desc(batch=2, scheme=R.RSSM_SHARED, lp_dtype=R.RSSM_BF16)
     L.ckpt = None
+    L.ckpt_lp = None                  # the eager comparator of SHARED needs the copy
     inp = R.make_inputs(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE)
-    assert R.rssm_eager_step(L, inp, FAKE, stream=0, check=False) == R.RSSM_EUNSUPPORTED
+    assert R.rssm_eager_step(L, inp, FAKE, stream=0, check=False) == R.RSSM_EINVAL
     L = _gdn_desc(batch=2)
     L.ring[3] = None
     assert R.rssm_commit(L, None, 0, stream=0, check=False) == R.RSSM_EINVAL

@@ -265,3 +265,84 @@ def test_shared_precision_reported(lp, capsys):
     assert np.isfinite(o).all()
     assert e_sh > e_du          # feeding lp rounding back into the fold costs accuracy
     assert R.rssm_status(L) == 0
+
+
+# ------------------------------------------------ eager low-precision state --
+
+def _host_lp(rng, b, H, lp):
+    if lp == R.RSSM_E4M3:
+        codes = rng.integers(0, 256, size=(b, H, DV, DK)).astype(np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x05
+        scale = rng.uniform(1e-4, 4e-4, size=(b, H)).astype(np.float32)
+        exact = oracle.e4m3_dequant_heads(scale, codes.reshape(b, H, -1)).reshape(codes.shape)
+        return codes, scale, exact
+    f = (rng.standard_normal((b, H, DV, DK)) * 0.1).astype(np.float32)
+    codes = oracle.bf16_encode(f)
+    return codes, None, oracle.bf16_decode(codes)
+
+
+def _load_lp(L, codes, scale, lp):
+    t_ = gu.torch()
+    L.ckpt_lp.copy_(t_.from_numpy(codes.view(np.int16) if lp == R.RSSM_BF16 else codes))
+    if scale is not None:
+        L.lp_scale.copy_(gu.dev(scale))
+
+
+@pytest.mark.parametrize("lp", [R.RSSM_BF16, R.RSSM_E4M3], ids=["bf16", "e4m3"])
+def test_eager_low_precision_one_step(lp):
+    """The eager comparator on a SHARED layer: one step from a host-made copy
+    gives the exact step from the decoded state (fp32 tolerance), and the new
+    copy is the codec image of the updated state."""
+    rng = np.random.default_rng(120)
+    b, H = 3, 4
+    codes, scale, exact = _host_lp(rng, b, H, lp)
+    st = syn.gdn_steps(120, 0, 1, b, H, DK, DV)
+    L = gu.gdn_layer(np.zeros((b, H, DV, DK), np.float32), 4, scheme=R.RSSM_SHARED, lp=lp)
+    _load_lp(L, codes, scale, lp)
+    o = gu.torch().empty((b, H, DV), dtype=gu.torch().float32, device="cuda")
+    R.rssm_eager_step(L, {n: gu.dev(st[n][0]) for n in _names()}, o)
+    S = exact.copy()
+    want = oracle.gdn_eager(*(st[n] for n in _names()), S)
+    assert gu.vec_rel_err(gu.host(o)[None], want) <= gu.TOL_F32
+    name = "bf16" if lp == R.RSSM_BF16 else "e4m3"
+    wc, ws, _ = drivers.quantize(S.astype(np.float32), name)
+    ok, frac = gu.codes_close(gu.host(L.ckpt_lp), wc, lp == R.RSSM_BF16,
+                              None if L.lp_scale is None else gu.host(L.lp_scale), ws)
+    assert ok and frac <= 1e-3, frac
+    assert R.rssm_status(L) == 0
+
+
+@pytest.mark.parametrize("lp", [R.RSSM_BF16, R.RSSM_E4M3], ids=["bf16", "e4m3"])
+def test_compounding_reported(lp, capsys):
+    """Slow decay: dual vs shared vs the eager comparator that re-encodes the
+    state every step; errors against the exact recurrence are reported, and
+    the eager comparator's late error must exceed the dual scheme's."""
+    T, b, H, interval = 64, 4, 8, 8
+    S0, st = _case(121, T, b, H, s0=0.0)
+    g = np.random.default_rng(121)
+    st["alpha"] = np.exp(-np.logaddexp(0, g.normal(-5.0, 1.0, st["alpha"].shape))).astype(np.float32)
+    S = S0.astype(np.float64)
+    o_exact = oracle.gdn_eager(*(st[n] for n in _names()), S)
+    outs = {}
+    for name, scheme in (("dual", R.RSSM_DUAL), ("shared", R.RSSM_SHARED)):
+        L = gu.gdn_layer(S0, interval, scheme=scheme, lp=lp)
+        if scheme == R.RSSM_DUAL:
+            R.rssm_commit(L, None, 0)
+        o, _, _ = gu.gdn_decode(L, {k: gu.dev(v) for k, v in st.items()}, interval, False)
+        outs[name] = gu.host(o)
+        assert R.rssm_status(L) == 0
+    L = gu.gdn_layer(S0, interval, scheme=R.RSSM_SHARED, lp=lp)
+    d = {k: gu.dev(v) for k, v in st.items()}
+    oe = gu.torch().empty_like(d["v"])
+    for t in range(T):
+        R.rssm_eager_step(L, {n: d[n][t] for n in _names()}, oe[t])
+    outs["eager_lp"] = gu.host(oe)
+    assert R.rssm_status(L) == 0
+    late = {k: float(np.sqrt(((v[-8:] - o_exact[-8:]) ** 2).mean() / (o_exact[-8:] ** 2).mean()))
+            for k, v in outs.items()}
+    allr = {k: float(np.sqrt(((v - o_exact) ** 2).mean() / (o_exact ** 2).mean()))
+            for k, v in outs.items()}
+    print(f"gdn lp={lp} slow decay, rms rel err (all steps / last 8): "
+          + ", ".join(f"{k} {allr[k]:.2e} / {late[k]:.2e}" for k in outs))
+    assert all(np.isfinite(v).all() for v in outs.values())
+    assert late["eager_lp"] > late["dual"]

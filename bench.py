@@ -13,7 +13,9 @@ read-modify-write kernel's seq-tokens/s on the same GPU and the speedup, the
 HBM roofline of the dominant kernel (the replay step without commit), the
 oracle timed on the host cores on a bounded sample, and secondary figures for
 the Gated DeltaNet decode, speculative verify/rollback rounds, the
-dual-precision GDN stack and a sweep of the Mamba-2 commit interval.
+dual-precision GDN stack (with the eager comparator that keeps the state in
+low precision), a sweep of the Mamba-2 commit interval and the Mamba-2 layer
+with a low-precision checkpoint.
 
 Usage: python bench.py [--gpus 1] [--steps 1024] [--warmup 64] [--no-secondary]
        [--no-cpu]
@@ -315,17 +317,24 @@ def run_dual_stack(torch, R, syn, steps, seed=0, layers=12, pool_n=8):
     names = ("q", "k", "v", "alpha", "beta")
     o = torch.empty((b, H, d), dtype=torch.float32, device="cuda")
     res = {}
-    for scheme, sname in ((R.RSSM_DUAL, "dual"), (R.RSSM_SHARED, "shared")):
+    inputs = [R.make_inputs(**{s: dev[s][j] for s in names}) for j in range(pool_n)]
+    for scheme, sname in ((R.RSSM_DUAL, "dual"), (R.RSSM_SHARED, "shared"), (None, "eager_lp")):
         for lp, lname in ((R.RSSM_BF16, "bf16"), (R.RSSM_E4M3, "e4m3")):
-            Ls = [R.Layer.gdn(b, H, d, d, cap, scheme=scheme, lp_dtype=lp) for _ in range(layers)]
-            for L in Ls:
-                R.rssm_commit(L, None, 0)
+            Ls = [R.Layer.gdn(b, H, d, d, cap, lp_dtype=lp,
+                              scheme=R.RSSM_SHARED if scheme is None else scheme)
+                  for _ in range(layers)]
+            if scheme is not None:
+                for L in Ls:
+                    R.rssm_commit(L, None, 0)
             start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             start.record()
             for t in range(steps):
                 j = t % pool_n
                 for L in Ls:
+                    if scheme is None:        # eager comparator: the state lives in low precision
+                        R.rssm_eager_step(L, inputs[j], o)
+                        continue
                     R.rssm_gdn_step(L, *(dev[s][j] for s in names), o)
                     if (t + 1) % interval == 0:
                         R.rssm_commit(L, None, 0)
@@ -337,6 +346,57 @@ def run_dual_stack(torch, R, syn, steps, seed=0, layers=12, pool_n=8):
             res[f"{sname}_{lname}"] = b * steps / (ms * 1e-3)
             del Ls
             torch.cuda.empty_cache()
+    return res
+
+
+def run_m2_lowprec(torch, R, syn, steps, seed=0, pool_n=16):
+    """Mamba-2 headline shape with a low-precision serving checkpoint (dual:
+    fp32 receives the commits; shared: the copy is the only state) and the
+    eager comparator whose state is stored in low precision; seq-tokens/s of
+    one layer, standalone commit every 8 steps."""
+    b, H, G, P, N, interval = 256, 80, 8, 64, 128, 8
+    A, D = syn.m2_params(seed, H)
+    pool = syn.m2_steps(seed, 0, pool_n, b, H, G, P, N)
+    dev = {k: torch.from_numpy(v).to("cuda") for k, v in pool.items()}
+    h0 = torch.from_numpy(syn.m2_state0(seed, b, H, P, N))
+    y = torch.empty((b, H, P), dtype=torch.float32, device="cuda")
+    res = {}
+    for scheme, sname in ((R.RSSM_DUAL, "dual"), (R.RSSM_SHARED, "shared"), (None, "eager_lp")):
+        for lp, lname in ((R.RSSM_BF16, "bf16"), (R.RSSM_E4M3, "e4m3")):
+            L = R.Layer.mamba2(b, H, G, P, N, interval,
+                               scheme=R.RSSM_SHARED if scheme is None else scheme, lp_dtype=lp)
+            L.A.copy_(torch.from_numpy(A))
+            L.D.copy_(torch.from_numpy(D))
+            if L.ckpt is not None:
+                L.ckpt.copy_(h0)
+                R.rssm_commit(L, None, 0)
+            inputs = [R.make_inputs(x=dev["x"][j], B=dev["B"][j], C=dev["C"][j], dt=dev["dt"][j])
+                      for j in range(pool_n)]
+
+            def run(n):
+                for t in range(n):
+                    j = t % pool_n
+                    if scheme is None:
+                        R.rssm_eager_step(L, inputs[j], y)
+                    else:
+                        R.rssm_mamba2_step(L, dev["x"][j], dev["B"][j], dev["C"][j], dev["dt"][j], y)
+                        if (t + 1) % interval == 0:
+                            R.rssm_commit(L, None, 0)
+
+            run(2 * interval)
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = (steps // interval) * interval
+            torch.cuda.synchronize()
+            start.record()
+            run(n)
+            end.record()
+            torch.cuda.synchronize()
+            ms = start.elapsed_time(end)
+            assert R.rssm_status(L) == 0
+            res[f"{sname}_{lname}"] = round(b * n / (ms * 1e-3), 1)
+            del L
+            torch.cuda.empty_cache()
+    del dev
     return res
 
 
@@ -453,11 +513,13 @@ def main():
         sp = run_spec(torch, R, syn, 128)
         du = run_dual_stack(torch, R, syn, 32)
         sw = run_m2_interval_sweep(torch, R, syn, 256)
+        ml = run_m2_lowprec(torch, R, syn, 128)
         out["secondary"] = {
             "gdn_decode_b256_h32_d128": {k: round(v, 2) for k, v in g.items()},
             "mamba2_spec_rounds_b256_4drafts": {k: round(v, 1) for k, v in sp.items()},
             "gdn_12layer_stack_seq_tok_s": {k: round(v, 1) for k, v in du.items()},
             "mamba2_commit_interval_sweep": sw,
+            "mamba2_lowprec_seq_tok_s": ml,
         }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(syn)

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 2
+#define RSSM_ABI_VERSION 3
 #define RSSM_ARRIVE_STRIDE 32   /* uint32 elements between two sequences' counters */
 
 /* ---- host return codes ------------------------------------------------- */
@@ -221,6 +221,40 @@ int rssm_commit(const rssm_layer* L, const uint8_t* mask, int min_len,
  */
 int rssm_verify(const rssm_layer* L, int n_pos, const rssm_inputs* in,
                 float* out, void* stream);
+
+/*
+ * rssm_verify_tree -- output-only verification of a tree of drafts from one
+ * checkpoint read (explainer, "Why this matters for agentic systems now":
+ * replay from a shared checkpoint along different input buffers, then
+ * discard branches by moving pointers).  Draft j hangs below draft
+ * parent[j] (parent[j] < j), or below the buffer tail when parent[j] == -1;
+ * its output is the layer output after the buffered entries and the drafts
+ * on its path (root first, j last).  parent: HOST int32 [n_nodes], the same
+ * tree for every sequence; in: as rssm_verify with leading [n_nodes];
+ * out [n_nodes][batch][H][dim_v].  Nothing is appended and no index changes:
+ * the caller appends the accepted path with rssm_append_path; rejected
+ * branches are never written.  1 <= n_nodes <= min(8, capacity)
+ * (RSSM_ERANGE); a bad parent gives RSSM_EINVAL.  Per sequence,
+ * len + n_nodes > capacity sets RSSM_STATUS_OVERFLOW (outputs NaN).
+ */
+int rssm_verify_tree(const rssm_layer* L, int n_nodes, const int32_t* parent,
+                     const rssm_inputs* in, float* out, void* stream);
+
+/*
+ * rssm_append_path -- append, for every sequence b, the inputs of drafts
+ * path[b][0 .. path_len[b]) (indices into the verify inputs `in`, leading
+ * [n_nodes]) at the buffer tail, in that order: len += path_len[b].  For
+ * an accepted root-to-node path of rssm_verify_tree this leaves the layer as
+ * plain decoding of the accepted tokens would.  path: device int32
+ * [batch][depth]; path_len: device int32 [batch], 0..depth.
+ * 1 <= depth <= n_nodes <= 8 (RSSM_ERANGE).  Per sequence, a path that
+ * overflows the ring or names a draft outside 0..n_nodes-1 sets
+ * RSSM_STATUS_OVERFLOW and leaves the sequence unchanged.  Uses x, B, dt
+ * (Mamba-2) or k, v, alpha, beta (GDN) of `in`.
+ */
+int rssm_append_path(const rssm_layer* L, int n_nodes, const int32_t* path,
+                     const int32_t* path_len, int depth, const rssm_inputs* in,
+                     void* stream);
 
 /*
  * rssm_rollback -- reject the last n_reject[b] buffered entries of every

@@ -112,6 +112,47 @@ rssm::GdnArgs gdn_args(const rssm_layer* L) {
 
 inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Shared by rssm_verify (a chain: anc[j] = drafts 0..j, appended) and
+// rssm_verify_tree (ancestor masks from the parent array, nothing appended).
+int verify_common(const rssm_layer* L, int n_pos, const uint32_t* anc, int append,
+                  const rssm_inputs* in, float* out, void* stream) {
+  int rc = check_layer_dims(L);
+  if (rc) return rc;
+  if (!in) return RSSM_EINVAL;
+  if (n_pos < 1 || n_pos > L->capacity || n_pos > rssm::kMaxPos) return RSSM_ERANGE;
+  if (L->batch == 0) return RSSM_OK;
+  if ((rc = check_layer_ptrs(L)) || (rc = check_state(L))) return rc;
+  if (!out) return RSSM_EINVAL;
+  if (!a16(out)) return RSSM_EALIGN;
+  if (L->kind == RSSM_MAMBA2) {
+    if (!in->x || !in->B || !in->C || !in->dt) return RSSM_EINVAL;
+    if (!a16(in->x) || !a16(in->B) || !a16(in->C)) return RSSM_EALIGN;
+    rssm::M2Args a = m2_args(L);
+    a.x = in->x;
+    a.B = in->B;
+    a.C = in->C;
+    a.dt = in->dt;
+    a.y = out;
+    a.n_pos = n_pos;
+    for (int j = 0; j < n_pos; ++j) a.anc[j] = anc[j];
+    a.append = append;
+    return hip_rc(rssm::launch_m2_verify(a, S(stream)));
+  }
+  if (!in->q || !in->k || !in->v || !in->alpha || !in->beta) return RSSM_EINVAL;
+  if (!a16(in->q) || !a16(in->k) || !a16(in->v)) return RSSM_EALIGN;
+  rssm::GdnArgs a = gdn_args(L);
+  a.q = in->q;
+  a.k = in->k;
+  a.v = in->v;
+  a.alpha = in->alpha;
+  a.beta = in->beta;
+  a.o = out;
+  a.n_pos = n_pos;
+  for (int j = 0; j < n_pos; ++j) a.anc[j] = anc[j];
+  a.append = append;
+  return hip_rc(rssm::launch_gdn_verify(a, S(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -190,37 +231,55 @@ int rssm_commit(const rssm_layer* L, const uint8_t* mask, int min_len, void* str
 
 int rssm_verify(const rssm_layer* L, int n_pos, const rssm_inputs* in, float* out,
                 void* stream) {
+  uint32_t anc[rssm::kMaxPos] = {};
+  for (int j = 0; j < rssm::kMaxPos; ++j) anc[j] = (2u << j) - 1u;   // drafts 0..j
+  return verify_common(L, n_pos, anc, 1, in, out, stream);
+}
+
+int rssm_verify_tree(const rssm_layer* L, int n_nodes, const int32_t* parent,
+                     const rssm_inputs* in, float* out, void* stream) {
+  if (!parent) return RSSM_EINVAL;
+  if (n_nodes < 1 || n_nodes > rssm::kMaxPos) return RSSM_ERANGE;
+  uint32_t anc[rssm::kMaxPos] = {};
+  for (int j = 0; j < n_nodes; ++j) {
+    if (parent[j] < -1 || parent[j] >= j) return RSSM_EINVAL;   // parents come first
+    anc[j] = (1u << j) | (parent[j] >= 0 ? anc[parent[j]] : 0u);
+  }
+  return verify_common(L, n_nodes, anc, 0, in, out, stream);
+}
+
+int rssm_append_path(const rssm_layer* L, int n_nodes, const int32_t* path,
+                     const int32_t* path_len, int depth, const rssm_inputs* in, void* stream) {
   int rc = check_layer_dims(L);
   if (rc) return rc;
   if (!in) return RSSM_EINVAL;
-  if (n_pos < 1 || n_pos > L->capacity || n_pos > rssm::kMaxPos) return RSSM_ERANGE;
+  if (n_nodes < 1 || n_nodes > rssm::kMaxPos || depth < 1 || depth > n_nodes) return RSSM_ERANGE;
   if (L->batch == 0) return RSSM_OK;
   if ((rc = check_layer_ptrs(L)) || (rc = check_state(L))) return rc;
-  if (!out) return RSSM_EINVAL;
-  if (!a16(out)) return RSSM_EALIGN;
+  if (!path || !path_len) return RSSM_EINVAL;
   if (L->kind == RSSM_MAMBA2) {
-    if (!in->x || !in->B || !in->C || !in->dt) return RSSM_EINVAL;
-    if (!a16(in->x) || !a16(in->B) || !a16(in->C)) return RSSM_EALIGN;
+    if (!in->x || !in->B || !in->dt) return RSSM_EINVAL;
     rssm::M2Args a = m2_args(L);
     a.x = in->x;
     a.B = in->B;
-    a.C = in->C;
     a.dt = in->dt;
-    a.y = out;
-    a.n_pos = n_pos;
-    return hip_rc(rssm::launch_m2_verify(a, S(stream)));
+    a.n_pos = n_nodes;
+    a.path = path;
+    a.path_len = path_len;
+    a.depth = depth;
+    return hip_rc(rssm::launch_m2_append_path(a, S(stream)));
   }
-  if (!in->q || !in->k || !in->v || !in->alpha || !in->beta) return RSSM_EINVAL;
-  if (!a16(in->q) || !a16(in->k) || !a16(in->v)) return RSSM_EALIGN;
+  if (!in->k || !in->v || !in->alpha || !in->beta) return RSSM_EINVAL;
   rssm::GdnArgs a = gdn_args(L);
-  a.q = in->q;
   a.k = in->k;
   a.v = in->v;
   a.alpha = in->alpha;
   a.beta = in->beta;
-  a.o = out;
-  a.n_pos = n_pos;
-  return hip_rc(rssm::launch_gdn_verify(a, S(stream)));
+  a.n_pos = n_nodes;
+  a.path = path;
+  a.path_len = path_len;
+  a.depth = depth;
+  return hip_rc(rssm::launch_gdn_append_path(a, S(stream)));
 }
 
 int rssm_rollback(const rssm_layer* L, const int32_t* n_reject, void* stream) {

@@ -226,6 +226,33 @@ __device__ __forceinline__ void carry(const EntrySmem& s, int hi, int cl, float 
   }
 }
 
+// As carry(), through the entries on one draft's path only: buffered entries
+// 0..len-1 and the drafts whose bit is set in `anc` (entry len + m <-> bit m),
+// up to entry hi.  Entries off the path get s_i = 0.
+template <int EPL, int LPR>
+__device__ __forceinline__ void carry_path(const EntrySmem& s, int len, uint32_t anc, int hi,
+                                           int cl, float (&q)[EPL], float (&sv)[kMaxCap]) {
+#pragma unroll
+  for (int i = kMaxCap - 1; i >= 0; --i) {
+    const bool on = i <= hi && (i < len || ((anc >> (i - len)) & 1u));
+    if (on) {
+      float kv[EPL];
+      load_vec<EPL>(&s.k[i][cl * EPL], kv);
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) part += kv[e] * q[e];
+      part = group_sum<LPR>(part);
+      const float si = s.be[i] * part;
+      const float al = s.al[i];
+      sv[i] = si;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) q[e] = al * (q[e] - si * kv[e]);
+    } else {
+      sv[i] = 0.f;
+    }
+  }
+}
+
 // As carry(), for the replay step: instead of keeping every s_i, accumulate
 // sum_i s_i v_i[r] for the lane's own output row r on the way.
 template <int EPL, int LPR>
@@ -566,7 +593,9 @@ __global__ __launch_bounds__(NTH) void gdn_commit_kernel(GdnArgs a) {
 }
 
 // -------------------------------------------------------------- verify ----
-// n_pos drafts appended at entries len..len+n-1.  One 512-thread workgroup per
+// n_pos drafts at entries len..len+n-1; draft j's output uses the buffered
+// entries and the drafts on its path (a.anc[j]); a chain (a.append) appends
+// the drafts, a tree appends nothing.  One 512-thread workgroup per
 // head: wave j carries draft j's query backwards through entries len+j..0;
 // then one pass over the checkpoint dots every row with all carried queries.
 template <int EB, int NPAD>
@@ -606,7 +635,7 @@ __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
 
   if (ok && w < n) {  // wave w carries draft w (2 elements per lane)
     float s[kMaxCap];
-    carry<2, 64>(es, len + w, q.lane, qv, s);
+    carry_path<2, 64>(es, len, a.anc[w], len + w, q.lane, qv, s);
     s_q[w][2 * q.lane] = qv[0];
     s_q[w][2 * q.lane + 1] = qv[1];
     if (q.lane < kMaxCap) {
@@ -656,10 +685,11 @@ __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
     }
   }
   if (ok)
-    for (int j = 0; j < n; ++j) append_from_regs<NTH>(a, src, er, len + j, q.tid);
+    if (a.append)
+      for (int j = 0; j < n; ++j) append_from_regs<NTH>(a, src, er, len + j, q.tid);
 
   IndexUpdate u;
-  u.apply = ok;
+  u.apply = ok && a.append;
   u.pos_add = 0;
   u.new_len = len + n;
   finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
@@ -714,6 +744,48 @@ __global__ __launch_bounds__(LP == 0 ? kStepThreads : 512) void gdn_eager_kernel
   if (M::writer(q.lane)) {
     const int r = q.row0 + M::index(q.lane, 0) * RPL + q.r0;
     a.o[q.unit * DV + r] = d[0];
+  }
+}
+
+// ----------------------------------------------------------- append path ----
+// As m2_append_path_kernel: one workgroup per sequence appends the drafts
+// path[b][0..path_len[b]) (k, v, alpha, beta of every head) at entries len..
+// and sets len += path_len; an overflowing or out-of-range path leaves the
+// sequence unchanged and raises RSSM_STATUS_OVERFLOW.
+__global__ __launch_bounds__(256) void gdn_append_path_kernel(GdnArgs a) {
+  const int b = blockIdx.x, cap = a.cap, n = a.n_pos;
+  const int len = a.len[b];
+  const int pl = a.path_len[b];
+  bool ok = pl >= 0 && pl <= a.depth && len + pl <= cap;
+  for (int k = 0; ok && k < pl; ++k) {
+    const int j = a.path[(long)b * a.depth + k];
+    ok = j >= 0 && j < n;
+  }
+  if (ok) {
+    const int slot0 = (int)(a.pos[b] % cap);
+    const long sk = (long)a.batch * a.H * DK, sv = (long)a.batch * a.H * DV, sd = (long)a.batch * a.H;
+    for (int k = 0; k < pl; ++k) {
+      const int j = a.path[(long)b * a.depth + k];
+      const int s = ring_slot(slot0, len + k, cap);
+      for (int idx = threadIdx.x; idx < a.H * DK; idx += 256) {
+        const long unit = (long)b * a.H + idx / DK;
+        a.ring_k[(unit * cap + s) * DK + idx % DK] = a.k[j * sk + unit * DK + idx % DK];
+      }
+      for (int idx = threadIdx.x; idx < a.H * DV; idx += 256) {
+        const long unit = (long)b * a.H + idx / DV;
+        a.ring_v[(unit * cap + s) * DV + idx % DV] = a.v[j * sv + unit * DV + idx % DV];
+      }
+      for (int h = threadIdx.x; h < a.H; h += 256) {
+        const long unit = (long)b * a.H + h;
+        a.ring_a[unit * cap + s] = a.alpha[j * sd + unit];
+        a.ring_b[unit * cap + s] = a.beta[j * sd + unit];
+      }
+    }
+  }
+  __syncthreads();   // every thread has read len before it changes
+  if (threadIdx.x == 0) {
+    if (ok) a.len[b] = len + pl;
+    else raise_status(a.status, kStatusOverflow);
   }
 }
 
@@ -778,6 +850,11 @@ hipError_t launch_gdn_verify(const GdnArgs& a, hipStream_t s) {
     launch_gdn_verify_eb<2>(a, s);
   else
     launch_gdn_verify_eb<1>(a, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_gdn_append_path(const GdnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(gdn_append_path_kernel, dim3((unsigned)a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -29,6 +29,13 @@ struct M2Args {
   const uint8_t* mask;  // commit only
   int batch, H, G, cap, n_pos, min_len;
   int scheme, lp;       // rssm_scheme / rssm_lp values
+  // verify: anc[j] has bit m set when draft m lies on the path to draft j
+  // (j included); append != 0 appends the drafts (linear chains only)
+  uint32_t anc[8];
+  int append;
+  const int32_t* path;      // append_path: [b][depth] draft indices
+  const int32_t* path_len;  // append_path: [b]
+  int depth;
 };
 
 // Gated DeltaNet arguments.
@@ -53,6 +60,11 @@ struct GdnArgs {
   const uint8_t* mask;
   int batch, H, cap, n_pos, min_len;
   int scheme, lp;       // rssm_scheme / rssm_lp values
+  uint32_t anc[8];      // as in M2Args
+  int append;
+  const int32_t* path;
+  const int32_t* path_len;
+  int depth;
 };
 
 hipError_t launch_m2_step(const M2Args& a, bool fused, hipStream_t s);
@@ -64,6 +76,9 @@ hipError_t launch_gdn_step(const GdnArgs& a, bool fused, hipStream_t s);
 hipError_t launch_gdn_commit(const GdnArgs& a, hipStream_t s);
 hipError_t launch_gdn_verify(const GdnArgs& a, hipStream_t s);
 hipError_t launch_gdn_eager(const GdnArgs& a, hipStream_t s);
+
+hipError_t launch_m2_append_path(const M2Args& a, hipStream_t s);
+hipError_t launch_gdn_append_path(const GdnArgs& a, hipStream_t s);
 
 hipError_t launch_rollback(int64_t* pos, int32_t* len, uint32_t* status,
                            const int32_t* n_reject, int batch, hipStream_t s);

@@ -371,8 +371,9 @@ __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
 }
 
 // -------------------------------------------------------------- verify ----
-// n_pos drafts appended at entries len..len+n-1; draft j's output uses
-// entries 0..len+j.  One checkpoint read serves all positions: each row of
+// n_pos drafts at entries len..len+n-1; draft j's output uses the buffered
+// entries and the drafts on its path (a.anc[j]: for a chain, drafts 0..j).
+// A chain (a.append) appends the drafts; a tree appends nothing.  One checkpoint read serves all positions: each row of
 // h_c is dotted with every C_j before the cross-lane reduction.
 template <int EB, int NPAD>
 __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
@@ -424,13 +425,16 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
 
   if (ok) {
     if (q.tid < LT) s_dt[q.tid] = dtv(q.tid);
-    {  // e_{j,i} = B_i . C_j for i <= len + j, 16 lanes per pair
+    auto on_path = [&](int j, int i) -> bool {   // entry i feeds draft j's output
+      return i < len || ((a.anc[j] >> (i - len)) & 1u);
+    };
+    {  // e_{j,i} = B_i . C_j for the entries on draft j's path, 16 lanes per pair
       constexpr int SEG = N / 16;
       const int sgm = q.tid & 15;
       for (int pass = 0; pass < (NPAD * kMaxCap) / 16; ++pass) {
         const int pi = pass * 16 + (q.tid >> 4);
         const int j = pi / kMaxCap, i = pi % kMaxCap;
-        const bool act = j < n && i <= len + j;
+        const bool act = j < n && i < LT && on_path(j, i);
         float part = 0.f;
         if (act) {
           const float* bi = Bsrc(i) + sgm * SEG;
@@ -445,12 +449,20 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
     __syncthreads();
     if (q.tid < NPAD * kMaxCap) {
       const int j = q.tid / kMaxCap, i = q.tid % kMaxCap;
-      const int Lj = len + j + 1;
+      const int Lj = len + j + 1;   // draft j is the last entry on its path
       if (j < n && i < Lj) {
-        float suf = 0.f;
-        for (int m = i + 1; m < Lj; ++m) suf += s_dt[m];
-        s_w[j][i] = expf(Ah * suf) * s_dt[i] * s_e[j][i];
-        if (i == 0) s_gam[j] = expf(Ah * (suf + s_dt[0]));
+        if (on_path(j, i)) {
+          float suf = 0.f;
+          for (int m = i + 1; m < Lj; ++m)
+            if (on_path(j, m)) suf += s_dt[m];
+          s_w[j][i] = expf(Ah * suf) * s_dt[i] * s_e[j][i];
+        }
+        if (i == 0) {   // Gamma over the whole path
+          float tot = 0.f;
+          for (int m = 0; m < Lj; ++m)
+            if (on_path(j, m)) tot += s_dt[m];
+          s_gam[j] = expf(Ah * tot);
+        }
       }
     }
     __syncthreads();
@@ -463,7 +475,7 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
         const float xv = xsrc(i)[p];
 #pragma unroll
         for (int j = 0; j < NPAD; ++j)
-          if (j < n && i <= len + j) acc[j] += s_w[j][i] * xv;
+          if (j < n && i <= len + j && on_path(j, i)) acc[j] += s_w[j][i] * xv;
       }
 #pragma unroll
       for (int j = 0; j < NPAD; ++j) s_yb[qd][j][p] = acc[j];
@@ -511,8 +523,8 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
     }
   }
 
-  if (ok) {
-    for (int j = 0; j < n; ++j) {  // append the drafts
+  if (ok && a.append) {
+    for (int j = 0; j < n; ++j) {  // append the drafts (a chain)
       const int s = ring_slot(slot0, len + j, cap);
       if (q.tid < P) a.ring_x[(q.unit * cap + s) * P + q.tid] = a.x[j * sx + q.unit * P + q.tid];
       if (q.tid == 0) a.ring_dt[q.unit * cap + s] = a.dt[j * sd + q.unit];
@@ -522,11 +534,56 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   }
 
   IndexUpdate u;
-  u.apply = ok;
+  u.apply = ok && a.append;
   u.pos_add = 0;
   u.new_len = LT;
   finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
   if (!ok && last_arrival(arrived, a.H)) raise_status(a.status, kStatusOverflow);
+}
+
+// ----------------------------------------------------------- append path ----
+// Append, for every sequence b, the drafts path[b][0..path_len[b]) (indices
+// into the verify inputs) at entries len.., then len += path_len.  One
+// workgroup per sequence walks all heads, so it alone reads and writes the
+// sequence's indices.  A path that would overflow the ring, or names a draft
+// outside 0..n_pos-1, leaves the sequence unchanged and raises
+// RSSM_STATUS_OVERFLOW.
+__global__ __launch_bounds__(NT) void m2_append_path_kernel(M2Args a) {
+  const int b = blockIdx.x, cap = a.cap, n = a.n_pos;
+  const int len = a.len[b];
+  const int pl = a.path_len[b];
+  bool ok = pl >= 0 && pl <= a.depth && len + pl <= cap;
+  for (int k = 0; ok && k < pl; ++k) {
+    const int j = a.path[(long)b * a.depth + k];
+    ok = j >= 0 && j < n;
+  }
+  if (ok) {
+    const int slot0 = (int)(a.pos[b] % cap);
+    const long sx = (long)a.batch * a.H * P, sg = (long)a.batch * a.G * N, sd = (long)a.batch * a.H;
+    const int hpg = a.H / a.G;
+    for (int k = 0; k < pl; ++k) {
+      const int j = a.path[(long)b * a.depth + k];
+      const int s = ring_slot(slot0, len + k, cap);
+      for (int idx = threadIdx.x; idx < a.H * P; idx += NT) {
+        const long unit = (long)b * a.H + idx / P;
+        a.ring_x[(unit * cap + s) * P + idx % P] = a.x[j * sx + unit * P + idx % P];
+      }
+      for (int idx = threadIdx.x; idx < a.G * N; idx += NT) {
+        const long gunit = (long)b * a.G + idx / N;
+        a.ring_B[(gunit * cap + s) * N + idx % N] = a.B[j * sg + gunit * N + idx % N];
+      }
+      for (int h = threadIdx.x; h < a.H; h += NT) {
+        const long unit = (long)b * a.H + h;
+        a.ring_dt[unit * cap + s] = a.dt[j * sd + unit];
+      }
+    }
+    (void)hpg;
+  }
+  __syncthreads();   // every thread has read len before it changes
+  if (threadIdx.x == 0) {
+    if (ok) a.len[b] = len + pl;
+    else raise_status(a.status, kStatusOverflow);
+  }
 }
 
 // --------------------------------------------------------------- eager ----
@@ -624,6 +681,11 @@ hipError_t launch_m2_verify(const M2Args& a, hipStream_t s) {
     launch_m2_verify_eb<2>(a, s);
   else
     launch_m2_verify_eb<1>(a, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_m2_append_path(const M2Args& a, hipStream_t s) {
+  hipLaunchKernelGGL(m2_append_path_kernel, dim3((unsigned)a.batch), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 

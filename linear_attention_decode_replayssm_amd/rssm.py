@@ -22,7 +22,7 @@ STATUS_OVERFLOW, STATUS_ROLLBACK, STATUS_NONFINITE = 1, 2, 4
 RSSM_MAMBA2, RSSM_GDN = 1, 2
 RSSM_F32, RSSM_DUAL, RSSM_SHARED = 0, 1, 2
 RSSM_LP_NONE, RSSM_BF16, RSSM_E4M3 = 0, 1, 2
-RSSM_ABI_VERSION = 2
+RSSM_ABI_VERSION = 3
 RSSM_ARRIVE_STRIDE = 32   # uint32 elements between two sequences' arrival counters
 
 _vp = ctypes.c_void_p
@@ -69,13 +69,18 @@ def lib():
         L.rssm_commit.argtypes = [P(rssm_layer), _vp, ctypes.c_int, _vp]
         L.rssm_verify.argtypes = [P(rssm_layer), ctypes.c_int, P(rssm_inputs), _vp, _vp]
         L.rssm_rollback.argtypes = [P(rssm_layer), _vp, _vp]
+        L.rssm_verify_tree.argtypes = [P(rssm_layer), ctypes.c_int, P(ctypes.c_int32),
+                                       P(rssm_inputs), _vp, _vp]
+        L.rssm_append_path.argtypes = [P(rssm_layer), ctypes.c_int, _vp, _vp, ctypes.c_int,
+                                       P(rssm_inputs), _vp]
         L.rssm_eager_step.argtypes = [P(rssm_layer), P(rssm_inputs), _vp, _vp]
         L.rssm_status.argtypes = [P(rssm_layer), P(ctypes.c_uint32), _vp]
         L.rssm_strerror.argtypes = [ctypes.c_int]
         L.rssm_strerror.restype = ctypes.c_char_p
         L.rssm_abi_version.restype = ctypes.c_int
         for f in ("rssm_mamba2_step", "rssm_gdn_step", "rssm_commit", "rssm_verify",
-                  "rssm_rollback", "rssm_eager_step", "rssm_status"):
+                  "rssm_rollback", "rssm_eager_step", "rssm_status", "rssm_verify_tree",
+                  "rssm_append_path"):
             getattr(L, f).restype = ctypes.c_int
         if L.rssm_abi_version() != RSSM_ABI_VERSION:
             raise RuntimeError(f"{LIB_PATH} implements ABI {L.rssm_abi_version()}, this binding "
@@ -148,6 +153,27 @@ def rssm_verify(layer, n_pos, inputs, out, stream=None, check=True):
     rc = lib().rssm_verify(ctypes.byref(_desc(layer)), int(n_pos), ctypes.byref(inputs), _ptr(out),
                            _stream(stream))
     return _check(rc, "rssm_verify") if check else rc
+
+
+def rssm_verify_tree(layer, parent, inputs, out, stream=None, check=True):
+    """parent: host sequence of int (parent[j] < j, -1 = below the buffer tail)."""
+    if isinstance(inputs, dict):
+        inputs = make_inputs(**inputs)
+    n = len(parent)
+    arr = (ctypes.c_int32 * max(n, 1))(*[int(p) for p in parent])
+    rc = lib().rssm_verify_tree(ctypes.byref(_desc(layer)), n, arr, ctypes.byref(inputs),
+                                _ptr(out), _stream(stream))
+    return _check(rc, "rssm_verify_tree") if check else rc
+
+
+def rssm_append_path(layer, n_nodes, path, path_len, inputs, stream=None, check=True):
+    """path: device int32 [batch][depth]; path_len: device int32 [batch]."""
+    if isinstance(inputs, dict):
+        inputs = make_inputs(**inputs)
+    depth = int(path.shape[1]) if hasattr(path, "shape") else int(path[1])
+    rc = lib().rssm_append_path(ctypes.byref(_desc(layer)), int(n_nodes), _ptr(path),
+                                _ptr(path_len), depth, ctypes.byref(inputs), _stream(stream))
+    return _check(rc, "rssm_append_path") if check else rc
 
 
 def rssm_rollback(layer, n_reject, stream=None, check=True):

@@ -164,6 +164,45 @@ def gdn_spec_rounds(h0, drafts, accept, cap, commit_len):
     return dict(o=o, pos=pos, len=ln, committed=com, status=im.status, state=S)
 
 
+# ------------------------------------------------------------- draft trees --
+
+def tree_paths(parent):
+    """Root-first list of the drafts on each draft's path (itself last)."""
+    paths = []
+    for j, p in enumerate(parent):
+        if not (-1 <= p < j):
+            raise ValueError("parents must come first")
+        paths.append((paths[p] if p >= 0 else []) + [j])
+    return paths
+
+
+def m2_tree_verify(A, D, h, drafts, parent):
+    """Outputs of every draft of a tree (explainer, "Why this matters for
+    agentic systems now": replay from one checkpoint along different input
+    buffers): draft j's output is the eager recurrence continued from state h
+    over the drafts on its path, root first.  drafts: x [n,b,H,P], B/C
+    [n,b,G,N], dt [n,b,H].  h is not modified.  Returns y [n,b,H,P]."""
+    x, B, C, dt = drafts["x"], drafts["B"], drafts["C"], drafts["dt"]
+    y = np.empty(x.shape, np.float64)
+    for j, path in enumerate(tree_paths(parent)):
+        hs = np.array(h, dtype=np.float64, copy=True)
+        out = m2_eager(A, D, x[path], B[path], C[path], dt[path], hs)
+        y[j] = out[-1]
+    return y
+
+
+def gdn_tree_verify(S, drafts, parent):
+    """As m2_tree_verify for Gated DeltaNet; drafts q, k [n,b,H,dk], v
+    [n,b,H,dv], alpha/beta [n,b,H].  Returns o [n,b,H,dv]."""
+    q, k, v, al, be = (drafts[s] for s in ("q", "k", "v", "alpha", "beta"))
+    o = np.empty(v.shape, np.float64)
+    for j, path in enumerate(tree_paths(parent)):
+        Ss = np.array(S, dtype=np.float64, copy=True)
+        out = gdn_eager(q[path], k[path], v[path], al[path], be[path], Ss)
+        o[j] = out[-1]
+    return o
+
+
 # ------------------------------------------------- low-precision emulation --
 
 def quantize(state_f32, lp):

@@ -60,7 +60,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert R.rssm_abi_version() == R.RSSM_ABI_VERSION == 2
+    assert R.rssm_abi_version() == R.RSSM_ABI_VERSION == 3
     for code in (0, -1, -2, -3, -4, -5):
         assert R.rssm_strerror(code)
     assert "unknown" in R.rssm_strerror(12345)
@@ -232,3 +232,20 @@ def test_product_path_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(R, "LIB_PATH", "/nonexistent/librssm.so")
     with pytest.raises(RuntimeError, match="missing"):
         R.lib()
+
+
+def test_tree_entry_points_validate_on_host():
+    L = _m2_desc(batch=4, capacity=12)
+    inp = R.make_inputs(x=FAKE, B=FAKE, C=FAKE, dt=FAKE)
+    assert R.rssm_verify_tree(L, [-1, 1], inp, FAKE, stream=0, check=False) == R.RSSM_EINVAL
+    assert R.rssm_verify_tree(L, [-1, -2], inp, FAKE, stream=0, check=False) == R.RSSM_EINVAL
+    assert R.rssm_verify_tree(L, [-1] * 9, inp, FAKE, stream=0, check=False) == R.RSSM_ERANGE
+    assert R.rssm_verify_tree(_m2_desc(batch=0), [-1, 0], inp, FAKE, stream=0,
+                              check=False) == R.RSSM_OK
+    lib = R.lib()
+    assert lib.rssm_verify_tree(ctypes.byref(L), 2, None, ctypes.byref(inp), FAKE, None) == R.RSSM_EINVAL
+    assert lib.rssm_append_path(ctypes.byref(L), 4, FAKE, FAKE, 5, ctypes.byref(inp), None) == R.RSSM_ERANGE
+    assert lib.rssm_append_path(ctypes.byref(L), 9, FAKE, FAKE, 1, ctypes.byref(inp), None) == R.RSSM_ERANGE
+    assert lib.rssm_append_path(ctypes.byref(L), 4, None, FAKE, 2, ctypes.byref(inp), None) == R.RSSM_EINVAL
+    L0 = _m2_desc(batch=0)
+    assert lib.rssm_append_path(ctypes.byref(L0), 4, None, None, 2, ctypes.byref(inp), None) == R.RSSM_OK

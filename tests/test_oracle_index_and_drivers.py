@@ -209,3 +209,34 @@ def test_quantise_is_idempotent_on_its_own_output():
         c2, sc2, v2 = drivers.quantize(v1.astype(np.float32), lp)
         np.testing.assert_array_equal(c1, c2)
         np.testing.assert_array_equal(v1, v2)
+
+
+def test_tree_paths():
+    from oracle.drivers import tree_paths
+    assert tree_paths([-1, 0, 0, 1, -1]) == [[0], [0, 1], [0, 2], [0, 1, 3], [4]]
+    import pytest as _pt
+    with _pt.raises(ValueError):
+        tree_paths([-1, 2, 0])
+
+
+def test_tree_verify_chain_equals_speculative_outputs():
+    """A chain (parent[j] = j - 1) is linear verification: outputs equal the
+    eager continuation over the drafts; a star (all parents -1) gives every
+    draft the one-step output from the same state."""
+    import numpy as np
+    import oracle
+    from oracle import drivers
+    rng = np.random.default_rng(7)
+    n, b, H, G, P, N = 4, 2, 4, 2, 4, 8
+    A = -np.exp(rng.uniform(0, 2, H)); D = rng.standard_normal(H)
+    h = rng.standard_normal((b, H, P, N))
+    dr = dict(x=rng.standard_normal((n, b, H, P)), B=rng.standard_normal((n, b, G, N)),
+              C=rng.standard_normal((n, b, G, N)), dt=rng.uniform(0.05, 0.3, (n, b, H)))
+    chain = drivers.m2_tree_verify(A, D, h, dr, [-1, 0, 1, 2])
+    want = oracle.m2_eager(A, D, dr["x"], dr["B"], dr["C"], dr["dt"], h.copy())
+    np.testing.assert_array_equal(chain, want)
+    star = drivers.m2_tree_verify(A, D, h, dr, [-1, -1, -1, -1])
+    for j in range(n):
+        one = oracle.m2_eager(A, D, dr["x"][j:j + 1], dr["B"][j:j + 1], dr["C"][j:j + 1],
+                              dr["dt"][j:j + 1], h.copy())
+        np.testing.assert_array_equal(star[j], one[0])

@@ -14,8 +14,8 @@ HBM roofline of the dominant kernel (the replay step without commit), the
 oracle timed on the host cores on a bounded sample, and secondary figures for
 the Gated DeltaNet decode, speculative verify/rollback rounds, the
 dual-precision GDN stack (with the eager comparator that keeps the state in
-low precision), a sweep of the Mamba-2 commit interval and the Mamba-2 layer
-with a low-precision checkpoint.
+low precision), a sweep of the Mamba-2 commit interval, the Mamba-2 layer
+with a low-precision checkpoint, and draft-tree speculation rounds.
 
 Usage: python bench.py [--gpus 1] [--steps 1024] [--warmup 64] [--no-secondary]
        [--no-cpu]
@@ -308,6 +308,55 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     return res
 
 
+def run_tree_rounds(torch, R, syn, rounds, seed=0):
+    """Mamba-2 headline shape, tree speculation: each round verifies a binary
+    tree of 7 drafts (depth 3) from one checkpoint read, appends a random
+    root-to-node path per sequence (0..3 drafts) and commits sequences whose
+    buffer reached 8; ring 16 (up to 7 buffered + 7 drafts in flight)."""
+    b, H, G, P, N, cap, commit_len = 256, 80, 8, 64, 128, 16, 8
+    parent = [-1, 0, 0, 1, 1, 2, 2]
+    paths = [[0], [0, 1], [0, 2], [0, 1, 3], [0, 1, 4], [0, 2, 5], [0, 2, 6]]
+    n, depth = len(parent), 3
+    A, D = syn.m2_params(seed, H)
+    pool = syn.m2_steps(seed, 0, n, b, H, G, P, N)
+    dev = {k: torch.from_numpy(v).to("cuda") for k, v in pool.items()}
+    inp = R.make_inputs(x=dev["x"], B=dev["B"], C=dev["C"], dt=dev["dt"])
+    g = np.random.default_rng(seed)
+    pick = g.integers(-1, n, size=(rounds, b))
+    arr = np.zeros((rounds, b, depth), np.int32)
+    plen = np.zeros((rounds, b), np.int32)
+    for r in range(rounds):
+        for s_ in range(b):
+            if pick[r, s_] >= 0:
+                p = paths[pick[r, s_]]
+                arr[r, s_, :len(p)] = p
+                plen[r, s_] = len(p)
+    arr_d = torch.from_numpy(arr).to("cuda")
+    plen_d = torch.from_numpy(plen).to("cuda")
+    L = R.Layer.mamba2(b, H, G, P, N, cap)
+    L.A.copy_(torch.from_numpy(A))
+    L.D.copy_(torch.from_numpy(D))
+    L.ckpt.copy_(torch.from_numpy(syn.m2_state0(seed, b, H, P, N)))
+    out = torch.empty((n, b, H, P), dtype=torch.float32, device="cuda")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for r in range(rounds):
+        R.rssm_verify_tree(L, parent, inp, out)
+        R.rssm_append_path(L, n, arr_d[r], plen_d[r], inp)
+        R.rssm_commit(L, None, commit_len)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    assert R.rssm_status(L) == 0
+    res = dict(rounds_per_s=rounds / (ms * 1e-3),
+               accepted_seq_tok_s=float(plen.sum()) / (ms * 1e-3),
+               us_per_round=ms * 1e3 / rounds, drafts_per_round=n)
+    del L, dev
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_dual_stack(torch, R, syn, steps, seed=0, layers=12, pool_n=8):
     """12 GDN layers at batch 256 with a low-precision serving checkpoint,
     standalone commit every 8 steps; seq-tokens/s through the whole stack."""
@@ -514,12 +563,14 @@ def main():
         du = run_dual_stack(torch, R, syn, 32)
         sw = run_m2_interval_sweep(torch, R, syn, 256)
         ml = run_m2_lowprec(torch, R, syn, 128)
+        tr = run_tree_rounds(torch, R, syn, 128)
         out["secondary"] = {
             "gdn_decode_b256_h32_d128": {k: round(v, 2) for k, v in g.items()},
             "mamba2_spec_rounds_b256_4drafts": {k: round(v, 1) for k, v in sp.items()},
             "gdn_12layer_stack_seq_tok_s": {k: round(v, 1) for k, v in du.items()},
             "mamba2_commit_interval_sweep": sw,
             "mamba2_lowprec_seq_tok_s": ml,
+            "mamba2_tree_rounds_b256_7drafts": {k: round(v, 1) for k, v in tr.items()},
         }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(syn)

@@ -634,8 +634,14 @@ __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
   __syncthreads();
 
   if (ok && w < n) {  // wave w carries draft w (2 elements per lane)
+    // its path mask, read with uniform indices (kernel-argument loads), never
+    // indexed by the lane-derived w
+    uint32_t anc = 0u;
+#pragma unroll
+    for (int j = 0; j < NPAD; ++j)
+      if (w == j) anc = a.anc[j];
     float s[kMaxCap];
-    carry_path<2, 64>(es, len, a.anc[w], len + w, q.lane, qv, s);
+    carry_path<2, 64>(es, len, anc, len + w, q.lane, qv, s);
     s_q[w][2 * q.lane] = qv[0];
     s_q[w][2 * q.lane + 1] = qv[1];
     if (q.lane < kMaxCap) {

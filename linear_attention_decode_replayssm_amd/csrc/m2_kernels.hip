@@ -373,22 +373,18 @@ __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
 // -------------------------------------------------------------- verify ----
 // n_pos drafts at entries len..len+n-1; draft j's output uses the buffered
 // entries and the drafts on its path (a.anc[j]: for a chain, drafts 0..j).
-// A chain (a.append) appends the drafts; a tree appends nothing.  One checkpoint read serves all positions: each row of
-// h_c is dotted with every C_j before the cross-lane reduction.
+// A chain (a.append) appends the drafts; a tree appends nothing.  One
+// checkpoint read serves all positions: each row of h_c is dotted with every
+// C_j before the cross-lane reduction.  As in the step kernel, every small
+// operand (the drafts' C_j, B_i segments, dt_i, x_i) is loaded before the
+// checkpoint stream, so the prologue runs while the stream is in flight.
 template <int EB, int NPAD>
 __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   using Gm = RdGeo<EB>;
   const Geo q = geometry(a);
   const int cap = a.cap, n = a.n_pos;
-  u32x4 raw[Gm::NLD];
-  load_raw<EB>(a, q.unit, q.tid, raw);
-  const int cl = q.tid % Gm::LPR, rr0 = q.tid / Gm::LPR;
-  const float scale = (EB == 1) ? a.lp_scale[q.unit] : 1.f;
-
   const int len = a.len[q.b];
   const int64_t pos = a.pos[q.b];
-  indices_consumed(len, pos);
-  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
   const bool ok = len + n <= cap;
   const int LT = len + n;
   const int slot0 = (int)(pos % cap);
@@ -398,18 +394,6 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   const long sg = (long)a.batch * a.G * N;
   const long sd = (long)a.batch * a.H;
 
-  __shared__ float s_dt[kMaxCap];
-  __shared__ float s_e[NPAD][kMaxCap];
-  __shared__ float s_w[NPAD][kMaxCap];
-  __shared__ float s_gam[NPAD];
-  __shared__ float s_yb[QD][NPAD][P];
-  __shared__ __attribute__((aligned(16))) float s_C[NPAD][N];   // the drafts' C_j
-  for (int idx = q.tid; idx < NPAD * N; idx += NT) {
-    const int j = idx / N, c = idx % N;
-    s_C[j][c] = j < n ? a.C[j * sg + q.gunit * N + c] : 0.f;
-  }
-  __syncthreads();
-
   auto xsrc = [&](int i) -> const float* {
     return i < len ? a.ring_x + (q.unit * cap + ring_slot(slot0, i, cap)) * P
                    : a.x + (i - len) * sx + q.unit * P;
@@ -418,118 +402,204 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
     return i < len ? a.ring_B + (q.gunit * cap + ring_slot(slot0, i, cap)) * N
                    : a.B + (i - len) * sg + q.gunit * N;
   };
-  auto dtv = [&](int i) -> float {
-    return i < len ? a.ring_dt[q.unit * cap + ring_slot(slot0, i, cap)]
-                   : a.dt[(i - len) * sd + q.unit];
-  };
+
+  // prologue operands: entry ei = tid/16 holds segment sgm of B_ei (and dt_ei);
+  // thread (p, qd) holds x_i[p] of entries qd, qd+QD, ...; the drafts' C_j
+  // go to LDS (CPT values per thread)
+  constexpr int SEG = N / 16;
+  constexpr int XPT = kMaxCap / QD;
+  constexpr int CPT = (NPAD * N + NT - 1) / NT;
+  const int ei = q.tid >> 4, sgm = q.tid & 15;
+  const int p = q.tid % P, qd = q.tid / P;
+  f32x4 bseg[SEG / 4];
+  float dti = 0.f, xv[XPT], cst[CPT];
+#pragma unroll
+  for (int e = 0; e < SEG / 4; ++e) bseg[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < XPT; ++m) xv[m] = 0.f;
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) cst[u] = 0.f;
+  if (ok) {
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int idx = q.tid + u * NT, j = idx / N;
+      if (idx < NPAD * N && j < n) cst[u] = a.C[j * sg + q.gunit * N + idx % N];
+    }
+    if (ei < LT) {
+#pragma unroll
+      for (int e = 0; e < SEG / 4; ++e) bseg[e] = ld4(Bsrc(ei) + sgm * SEG + 4 * e);
+      if (sgm == 0)
+        dti = ei < len ? a.ring_dt[q.unit * cap + ring_slot(slot0, ei, cap)]
+                       : a.dt[(ei - len) * sd + q.unit];
+    }
+#pragma unroll
+    for (int m = 0; m < XPT; ++m) {
+      const int i = qd + m * QD;
+      if (i < LT) xv[m] = xsrc(i)[p];
+    }
+  }
+  u32x4 raw[Gm::NLD];
+  load_raw<EB>(a, q.unit, q.tid, raw);
+  const int cl = q.tid % Gm::LPR, rr0 = q.tid / Gm::LPR;
+  const float scale = (EB == 1) ? a.lp_scale[q.unit] : 1.f;
+
+  __shared__ __attribute__((aligned(16))) float s_C[NPAD][N];
+  __shared__ __attribute__((aligned(16))) float s_Ba[NPAD][N];   // drafts' B, x, dt
+  __shared__ float s_xa[NPAD][P];                                // for the append
+  __shared__ float s_dta[NPAD];
+  __shared__ float s_dt[kMaxCap];
+  __shared__ float s_e[NPAD][kMaxCap];
+  __shared__ float s_w[NPAD][kMaxCap];
+  __shared__ float s_gam[NPAD];
+  __shared__ float s_yb[QD][NPAD][P];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int idx = q.tid + u * NT;
+    if (idx < NPAD * N) s_C[idx / N][idx % N] = cst[u];
+  }
+  if (sgm == 0) s_dt[ei] = dti;
+  if (a.append) {   // uniform: the drafts' own rows, kept for the append below
+    if (ei >= len && ei < LT) {
+#pragma unroll
+      for (int e = 0; e < SEG / 4; ++e) st4(&s_Ba[ei - len][sgm * SEG + 4 * e], bseg[e]);
+      if (sgm == 0) s_dta[ei - len] = dti;
+    }
+#pragma unroll
+    for (int m = 0; m < XPT; ++m) {
+      const int i = qd + m * QD;
+      if (i >= len && i < LT) s_xa[i - len][p] = xv[m];
+    }
+  }
+  indices_consumed(len, pos);   // its barrier also publishes the LDS above
+  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
 
   if (ok) {
-    if (q.tid < LT) s_dt[q.tid] = dtv(q.tid);
-    auto on_path = [&](int j, int i) -> bool {   // entry i feeds draft j's output
-      return i < len || ((a.anc[j] >> (i - len)) & 1u);
-    };
-    {  // e_{j,i} = B_i . C_j for the entries on draft j's path, 16 lanes per pair
-      constexpr int SEG = N / 16;
-      const int sgm = q.tid & 15;
-      for (int pass = 0; pass < (NPAD * kMaxCap) / 16; ++pass) {
-        const int pi = pass * 16 + (q.tid >> 4);
-        const int j = pi / kMaxCap, i = pi % kMaxCap;
-        const bool act = j < n && i < LT && on_path(j, i);
-        float part = 0.f;
-        if (act) {
-          const float* bi = Bsrc(i) + sgm * SEG;
-          const float* cj = a.C + j * sg + q.gunit * N + sgm * SEG;
+    {  // e_{j,ei} = B_ei . C_j for every draft, 16 lanes per entry
 #pragma unroll
-          for (int e = 0; e < SEG; e += 4) part += dot4(ld4(bi + e), ld4(cj + e));
+      for (int j = 0; j < NPAD; ++j) {
+        float part = 0.f;
+        if (j < n) {
+#pragma unroll
+          for (int e = 0; e < SEG / 4; ++e) part += dot4(bseg[e], ld4(&s_C[j][sgm * SEG + 4 * e]));
         }
         part = group_sum<16>(part);
-        if (sgm == 0 && act) s_e[j][i] = part;
+        if (sgm == 0) s_e[j][ei] = part;
       }
     }
     __syncthreads();
-    if (q.tid < NPAD * kMaxCap) {
+    if (q.tid < NPAD * kMaxCap) {   // decay weights; zero off the path
       const int j = q.tid / kMaxCap, i = q.tid % kMaxCap;
       const int Lj = len + j + 1;   // draft j is the last entry on its path
-      if (j < n && i < Lj) {
-        if (on_path(j, i)) {
-          float suf = 0.f;
-          for (int m = i + 1; m < Lj; ++m)
-            if (on_path(j, m)) suf += s_dt[m];
-          s_w[j][i] = expf(Ah * suf) * s_dt[i] * s_e[j][i];
-        }
-        if (i == 0) {   // Gamma over the whole path
-          float tot = 0.f;
-          for (int m = 0; m < Lj; ++m)
-            if (on_path(j, m)) tot += s_dt[m];
-          s_gam[j] = expf(Ah * tot);
-        }
+      // draft j's path as a mask over entries: the buffer, then its ancestors
+      // and itself.  The masks are read with uniform indices (kernel-argument
+      // loads), never indexed by a lane-varying j.
+      uint32_t anc = 0u;
+#pragma unroll
+      for (int jj = 0; jj < NPAD; ++jj)
+        if (j == jj) anc = a.anc[jj];
+      const uint32_t path = ((1u << len) - 1u) | (anc << len);
+      float w = 0.f;
+      if (j < n && i < Lj && ((path >> i) & 1u)) {
+        float suf = 0.f;
+        for (int m = i + 1; m < Lj; ++m)
+          if ((path >> m) & 1u) suf += s_dt[m];
+        w = expf(Ah * suf) * s_dt[i] * s_e[j][i];
+      }
+      s_w[j][i] = w;
+      if (j < n && i == 0) {   // Gamma over the whole path
+        float tot = 0.f;
+        for (int m = 0; m < Lj; ++m)
+          if ((path >> m) & 1u) tot += s_dt[m];
+        s_gam[j] = expf(Ah * tot);
       }
     }
     __syncthreads();
-    {
-      const int p = q.tid % P, qd = q.tid / P;
+    {  // sum_i w_{j,i} x_i[p], and D x_j[p] from the thread holding entry len + j
       float acc[NPAD];
 #pragma unroll
       for (int j = 0; j < NPAD; ++j) acc[j] = 0.f;
-      for (int i = qd; i < LT; i += QD) {
-        const float xv = xsrc(i)[p];
 #pragma unroll
-        for (int j = 0; j < NPAD; ++j)
-          if (j < n && i <= len + j && on_path(j, i)) acc[j] += s_w[j][i] * xv;
+      for (int m = 0; m < XPT; ++m) {
+        const int i = qd + m * QD;
+#pragma unroll
+        for (int j = 0; j < NPAD; ++j) {
+          acc[j] += s_w[j][i] * xv[m];
+          if (i == len + j) acc[j] += Dh * xv[m];
+        }
       }
 #pragma unroll
       for (int j = 0; j < NPAD; ++j) s_yb[qd][j][p] = acc[j];
     }
   }
 
-  constexpr int V = Gm::NLD * NPAD;
-  float d[V];
+  // Row dots with every C_j, reduced across the LPR lanes of a row.  At most
+  // 32 partial sums per lane at a time: drafts go in chunks of JC.
+  constexpr int JC = (Gm::NLD * NPAD <= 32) ? NPAD : 32 / Gm::NLD;
+  constexpr int NCH = NPAD / JC;
+  constexpr int V = Gm::NLD * JC;
+  using M = XMap<V, Gm::LPR>;
+  float f[Gm::NLD][Gm::EPL];   // the tile, expanded once
 #pragma unroll
-  for (int k = 0; k < Gm::NLD; ++k) {
-    float f[Gm::EPL];
-    expand<EB>(raw[k], f);
+  for (int k = 0; k < Gm::NLD; ++k) expand<EB>(raw[k], f[k]);
+  float res[NCH][M::VOUT];
 #pragma unroll
-    for (int j = 0; j < NPAD; ++j) {
-      float acc = 0.f;
+  for (int c = 0; c < NCH; ++c) {
+    // keep the scheduler from hoisting this chunk's LDS reads into the last
+    if (c > 0) __builtin_amdgcn_sched_barrier(0);
+    float d[V];
+#pragma unroll
+    for (int jl = 0; jl < JC; ++jl) {   // C_j's segment once per draft, then every row
+      const int j = c * JC + jl;
+      float cj[Gm::EPL];
 #pragma unroll
       for (int e = 0; e < Gm::EPL; e += 4) {
-        const f32x4 c = ld4(&s_C[j][cl * Gm::EPL + e]);
-        acc += f[e] * c.x + f[e + 1] * c.y + f[e + 2] * c.z + f[e + 3] * c.w;
+        const f32x4 cv = ld4(&s_C[j][cl * Gm::EPL + e]);
+        cj[e] = cv.x; cj[e + 1] = cv.y; cj[e + 2] = cv.z; cj[e + 3] = cv.w;
       }
-      d[k * NPAD + j] = acc;
+#pragma unroll
+      for (int k = 0; k < Gm::NLD; ++k) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < Gm::EPL; ++e) acc += f[k][e] * cj[e];
+        d[k * JC + jl] = acc;
+      }
     }
+    xreduce<V, Gm::LPR>(d, q.lane);
+#pragma unroll
+    for (int jj = 0; jj < M::VOUT; ++jj) res[c][jj] = d[jj];
   }
-  xreduce<V, Gm::LPR>(d, q.lane);
   __syncthreads();
-  using M = XMap<V, Gm::LPR>;
   if (M::writer(q.lane)) {
 #pragma unroll
-    for (int jj = 0; jj < M::VOUT; ++jj) {
-      const int idx = M::index(q.lane, jj);
-      const int k = idx / NPAD, j = idx % NPAD;
-      if (j < n) {
-        const int p = k * Gm::RPL + rr0;
-        float yv;
-        if (ok) {
-          float yb = 0.f;
+    for (int c = 0; c < NCH; ++c) {
 #pragma unroll
-          for (int qd = 0; qd < QD; ++qd) yb += s_yb[qd][j][p];
-          yv = s_gam[j] * (scale * d[jj]) + yb + Dh * a.x[j * sx + q.unit * P + p];
-        } else {
-          yv = __builtin_nanf("");
+      for (int jj = 0; jj < M::VOUT; ++jj) {
+        const int idx = M::index(q.lane, jj);
+        const int k = idx / JC, j = c * JC + idx % JC;
+        if (j < n) {
+          const int pr = k * Gm::RPL + rr0;
+          float yv;
+          if (ok) {
+            float yb = 0.f;
+#pragma unroll
+            for (int g = 0; g < QD; ++g) yb += s_yb[g][j][pr];
+            yv = s_gam[j] * (scale * res[c][jj]) + yb;
+          } else {
+            yv = __builtin_nanf("");
+          }
+          a.y[j * sx + q.unit * P + pr] = yv;
         }
-        a.y[j * sx + q.unit * P + p] = yv;
       }
     }
   }
 
-  if (ok && a.append) {
-    for (int j = 0; j < n; ++j) {  // append the drafts (a chain)
+  if (ok && a.append) {   // append the drafts (a chain) from LDS
+    for (int j = 0; j < n; ++j) {
       const int s = ring_slot(slot0, len + j, cap);
-      if (q.tid < P) a.ring_x[(q.unit * cap + s) * P + q.tid] = a.x[j * sx + q.unit * P + q.tid];
-      if (q.tid == 0) a.ring_dt[q.unit * cap + s] = a.dt[j * sd + q.unit];
+      if (q.tid < P) a.ring_x[(q.unit * cap + s) * P + q.tid] = s_xa[j][q.tid];
+      if (q.tid == 0) a.ring_dt[q.unit * cap + s] = s_dta[j];
       if ((q.h % (a.H / a.G)) == 0 && q.tid < N)
-        a.ring_B[(q.gunit * cap + s) * N + q.tid] = a.B[j * sg + q.gunit * N + q.tid];
+        a.ring_B[(q.gunit * cap + s) * N + q.tid] = s_Ba[j][q.tid];
     }
   }
 

@@ -18,7 +18,10 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
   updates; explainer, "Separate precisions for serving vs updating state");
 * the eager recurrence with its state stored in low precision, re-encoded
   after every step (explainer, "What ReplaySSM is solving": rounding fed back
-  into every later update).
+  into every later update);
+* prefill: the buffered entries and a whole prompt folded into the state, with
+  the eager output of every prompt token (the pages are silent on prefill; it
+  is read as a commit over a long buffer).
 
 Because the eager recurrence started from any state S and run over the buffered
 inputs equals the replay from checkpoint S over the same inputs, serving from
@@ -200,6 +203,59 @@ def gdn_tree_verify(S, drafts, parent):
         Ss = np.array(S, dtype=np.float64, copy=True)
         out = gdn_eager(q[path], k[path], v[path], al[path], be[path], Ss)
         o[j] = out[-1]
+    return o
+
+
+# ------------------------------------------------------------------ prefill --
+
+def _ragged_ring(ring, ring_len, s):
+    """Sequence s's buffered entries, oldest first: [ring_len[s], 1, ...]."""
+    n = int(ring_len[s])
+    return {k: v[:n, s:s + 1] for k, v in ring.items()}
+
+
+def m2_prefill(A, D, h, ring, ring_len, prompt, mask=None):
+    """Prefill of a prompt into the checkpoint (a fold over a long buffer,
+    explainer "Periodically commit a new checkpoint", applied to a whole
+    prompt).  Per selected sequence: the state continues from h over its
+    ring_len[s] buffered entries (ring x [Lr,b,H,P], B [Lr,b,G,N], dt [Lr,b,H];
+    oldest first; their outputs are not formed), then over the prompt (x
+    [T,b,H,P], B/C [T,b,G,N], dt [T,b,H]) with the eager output of every prompt
+    token.  h [b,H,P,N] fp64 is updated in place for selected sequences.
+    Returns y [T,b,H,P] (NaN for unselected sequences)."""
+    x, B, C, dt = prompt["x"], prompt["B"], prompt["C"], prompt["dt"]
+    y = np.full(x.shape, np.nan)
+    for s in range(x.shape[1]):
+        if mask is not None and not mask[s]:
+            continue
+        hs = np.array(h[s:s + 1], dtype=np.float64, copy=True)
+        r = _ragged_ring(ring, ring_len, s)
+        if r["x"].shape[0]:
+            zc = np.zeros(r["B"].shape, np.float32)   # no output: C does not matter
+            m2_eager(A, D, r["x"], r["B"], zc, r["dt"], hs)
+        y[:, s:s + 1] = m2_eager(A, D, x[:, s:s + 1], B[:, s:s + 1], C[:, s:s + 1],
+                                 dt[:, s:s + 1], hs)
+        h[s:s + 1] = hs
+    return y
+
+
+def gdn_prefill(S, ring, ring_len, prompt, mask=None):
+    """As m2_prefill for Gated DeltaNet: ring k [Lr,b,H,dk], v [Lr,b,H,dv],
+    alpha/beta [Lr,b,H]; prompt q, k [T,b,H,dk], v [T,b,H,dv], alpha/beta
+    [T,b,H].  S [b,H,dv,dk] fp64 updated in place.  Returns o [T,b,H,dv]."""
+    q, k, v, al, be = (prompt[n] for n in ("q", "k", "v", "alpha", "beta"))
+    o = np.full(v.shape, np.nan)
+    for s in range(q.shape[1]):
+        if mask is not None and not mask[s]:
+            continue
+        Ss = np.array(S[s:s + 1], dtype=np.float64, copy=True)
+        r = _ragged_ring(ring, ring_len, s)
+        if r["k"].shape[0]:
+            gdn_eager(np.zeros(r["k"].shape, np.float32), r["k"], r["v"], r["alpha"],
+                      r["beta"], Ss)
+        o[:, s:s + 1] = gdn_eager(q[:, s:s + 1], k[:, s:s + 1], v[:, s:s + 1],
+                                  al[:, s:s + 1], be[:, s:s + 1], Ss)
+        S[s:s + 1] = Ss
     return o
 
 

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 3
+#define RSSM_ABI_VERSION 4
 #define RSSM_ARRIVE_STRIDE 32   /* uint32 elements between two sequences' counters */
 
 /* ---- host return codes ------------------------------------------------- */
@@ -145,10 +145,11 @@ typedef struct rssm_layer {
   uint32_t* status;
 } rssm_layer;
 
-/* Per-position inputs for rssm_verify / rssm_eager_step.  Unused members NULL.
+/* Per-position inputs for rssm_verify / rssm_prefill / rssm_eager_step.
+ * Unused members NULL.
  * Mamba-2: x [n][batch][H][P], B and C [n][batch][G][N], dt [n][batch][H]
  * GDN:     q, k [n][batch][H][dk], v [n][batch][H][dv], alpha, beta [n][batch][H]
- * (n = n_pos for verify, 1 for eager_step). */
+ * (n = n_pos for verify, n_tok for prefill, 1 for eager_step). */
 typedef struct rssm_inputs {
   const float *x, *B, *C, *dt;
   const float *q, *k, *v, *alpha, *beta;
@@ -255,6 +256,31 @@ int rssm_verify_tree(const rssm_layer* L, int n_nodes, const int32_t* parent,
 int rssm_append_path(const rssm_layer* L, int n_nodes, const int32_t* path,
                      const int32_t* path_len, int depth, const rssm_inputs* in,
                      void* stream);
+
+/*
+ * rssm_prefill -- fold a prompt into the checkpoint of every selected
+ * sequence.  The pages describe decode only; a prefill is read as a commit
+ * over a long buffer (explainer, "Periodically commit a new checkpoint":
+ * apply the recurrence from the checkpoint across the inputs and store the
+ * result) whose prompt tokens also get their outputs.  A sequence is selected
+ * when mask == NULL or mask[b] != 0 (mask: device uint8 [batch]).  For a
+ * selected sequence the state continues from its checkpoint over its len
+ * buffered entries (oldest first; they get no output) and then over the
+ * n_tok prompt tokens of `in` (leading [n_tok], laid out as for rssm_verify);
+ * out[t] (leading [n_tok], laid out as rssm_verify's; may be NULL) receives
+ * prompt token t's output, the value plain decoding of the same tokens gives.
+ * Afterwards ckpt_pos += len + n_tok and len = 0.
+ *   F32:    ckpt <- fold(ckpt)
+ *   DUAL:   ckpt <- fold(ckpt);  ckpt_lp <- Q(ckpt)   (outputs from fp32)
+ *   SHARED: ckpt_lp <- Q(fold(deQ(ckpt_lp)))         (outputs from the decoded copy)
+ * The state stays on chip in fp32 for the whole prompt: one read and one
+ * write of the checkpoint per call.  Unselected sequences, and their rows of
+ * out, are not touched.  n_tok >= 1 (RSSM_ERANGE).  Mamba-2 uses x, B, dt
+ * and, when out != NULL, C; GDN uses k, v, alpha, beta and, when out != NULL,
+ * q.  An E4M3 tile holding NaN or an infinity sets RSSM_STATUS_NONFINITE.
+ */
+int rssm_prefill(const rssm_layer* L, int n_tok, const rssm_inputs* in, float* out,
+                 const uint8_t* mask, void* stream);
 
 /*
  * rssm_rollback -- reject the last n_reject[b] buffered entries of every

@@ -248,6 +248,29 @@ int rssm_verify_tree(const rssm_layer* L, int n_nodes, const int32_t* parent,
   return verify_common(L, n_nodes, anc, 0, in, out, stream);
 }
 
+int rssm_prefill(const rssm_layer* L, int n_tok, const rssm_inputs* in, float* out,
+                 const uint8_t* mask, void* stream) {
+  int rc = check_layer_dims(L);
+  if (rc) return rc;
+  if (!in) return RSSM_EINVAL;
+  if (n_tok < 1) return RSSM_ERANGE;
+  if (L->kind == RSSM_GDN) return RSSM_EUNSUPPORTED;
+  if (L->batch == 0) return RSSM_OK;
+  if ((rc = check_layer_ptrs(L)) || (rc = check_state(L))) return rc;
+  if (out && !a16(out)) return RSSM_EALIGN;
+  if (!in->x || !in->B || !in->dt || (out && !in->C)) return RSSM_EINVAL;
+  if (!a16(in->x) || !a16(in->B) || (out && !a16(in->C))) return RSSM_EALIGN;
+  rssm::M2Args a = m2_args(L);
+  a.x = in->x;
+  a.B = in->B;
+  a.C = out ? in->C : nullptr;
+  a.dt = in->dt;
+  a.y = out;
+  a.mask = mask;
+  a.n_pos = n_tok;
+  return hip_rc(rssm::launch_m2_prefill(a, S(stream)));
+}
+
 int rssm_append_path(const rssm_layer* L, int n_nodes, const int32_t* path,
                      const int32_t* path_len, int depth, const rssm_inputs* in, void* stream) {
   int rc = check_layer_dims(L);

@@ -26,7 +26,7 @@ struct M2Args {
   const float* C;       // [n][b][G][N]
   const float* dt;      // [n][b][H]
   float* y;             // [n][b][H][P]
-  const uint8_t* mask;  // commit only
+  const uint8_t* mask;  // commit, prefill
   int batch, H, G, cap, n_pos, min_len;
   int scheme, lp;       // rssm_scheme / rssm_lp values
   // verify: anc[j] has bit m set when draft m lies on the path to draft j
@@ -78,6 +78,7 @@ hipError_t launch_gdn_verify(const GdnArgs& a, hipStream_t s);
 hipError_t launch_gdn_eager(const GdnArgs& a, hipStream_t s);
 
 hipError_t launch_m2_append_path(const M2Args& a, hipStream_t s);
+hipError_t launch_m2_prefill(const M2Args& a, hipStream_t s);   // n_pos = prompt tokens
 hipError_t launch_gdn_append_path(const GdnArgs& a, hipStream_t s);
 
 hipError_t launch_rollback(int64_t* pos, int32_t* len, uint32_t* status,

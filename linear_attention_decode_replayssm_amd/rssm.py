@@ -22,7 +22,7 @@ STATUS_OVERFLOW, STATUS_ROLLBACK, STATUS_NONFINITE = 1, 2, 4
 RSSM_MAMBA2, RSSM_GDN = 1, 2
 RSSM_F32, RSSM_DUAL, RSSM_SHARED = 0, 1, 2
 RSSM_LP_NONE, RSSM_BF16, RSSM_E4M3 = 0, 1, 2
-RSSM_ABI_VERSION = 3
+RSSM_ABI_VERSION = 4
 RSSM_ARRIVE_STRIDE = 32   # uint32 elements between two sequences' arrival counters
 
 _vp = ctypes.c_void_p
@@ -73,6 +73,7 @@ def lib():
                                        P(rssm_inputs), _vp, _vp]
         L.rssm_append_path.argtypes = [P(rssm_layer), ctypes.c_int, _vp, _vp, ctypes.c_int,
                                        P(rssm_inputs), _vp]
+        L.rssm_prefill.argtypes = [P(rssm_layer), ctypes.c_int, P(rssm_inputs), _vp, _vp, _vp]
         L.rssm_eager_step.argtypes = [P(rssm_layer), P(rssm_inputs), _vp, _vp]
         L.rssm_status.argtypes = [P(rssm_layer), P(ctypes.c_uint32), _vp]
         L.rssm_strerror.argtypes = [ctypes.c_int]
@@ -80,7 +81,7 @@ def lib():
         L.rssm_abi_version.restype = ctypes.c_int
         for f in ("rssm_mamba2_step", "rssm_gdn_step", "rssm_commit", "rssm_verify",
                   "rssm_rollback", "rssm_eager_step", "rssm_status", "rssm_verify_tree",
-                  "rssm_append_path"):
+                  "rssm_append_path", "rssm_prefill"):
             getattr(L, f).restype = ctypes.c_int
         if L.rssm_abi_version() != RSSM_ABI_VERSION:
             raise RuntimeError(f"{LIB_PATH} implements ABI {L.rssm_abi_version()}, this binding "
@@ -174,6 +175,16 @@ def rssm_append_path(layer, n_nodes, path, path_len, inputs, stream=None, check=
     rc = lib().rssm_append_path(ctypes.byref(_desc(layer)), int(n_nodes), _ptr(path),
                                 _ptr(path_len), depth, ctypes.byref(inputs), _stream(stream))
     return _check(rc, "rssm_append_path") if check else rc
+
+
+def rssm_prefill(layer, n_tok, inputs, out=None, mask=None, stream=None, check=True):
+    """inputs: leading [n_tok]; out: [n_tok][batch][H][dim_v] or None; mask:
+    device uint8 [batch] or None."""
+    if isinstance(inputs, dict):
+        inputs = make_inputs(**inputs)
+    rc = lib().rssm_prefill(ctypes.byref(_desc(layer)), int(n_tok), ctypes.byref(inputs),
+                            _ptr(out), _ptr(mask), _stream(stream))
+    return _check(rc, "rssm_prefill") if check else rc
 
 
 def rssm_rollback(layer, n_reject, stream=None, check=True):

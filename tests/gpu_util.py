@@ -76,6 +76,31 @@ def codes_close(got, want, lp_is_bf16, got_scale=None, want_scale=None, near_zer
     return bool(ok.all()), float((diff != 0).mean())
 
 
+def codes_within(got, want_state, lp_is_bf16, got_scale=None, rel_tol=1e-5):
+    """A GPU low-precision copy is the encoding of some state within the fp32
+    state tolerance of the exact one: per element, the decoded value lies
+    within tol + delta of the exact value, tol = rel_tol x the row's largest
+    |exact| (the bound the fp32 checkpoint is held to) and delta the codec's
+    half step there (bf16: 2^-8 |s|; E4M3: max(2^-4 |s|, 2^-10 scale)).  Used
+    where the state went through many fp32 steps before the encoding, so that
+    small elements may sit several codes from the emulation's."""
+    import oracle
+    w = np.asarray(want_state, np.float64)
+    b, H = w.shape[:2]
+    if lp_is_bf16:
+        gv = oracle.bf16_decode(np.asarray(got).view(np.uint16))
+    else:
+        g = np.asarray(got).astype(np.uint8)
+        gv = oracle.e4m3_dequant_heads(got_scale, g.reshape(b, H, -1)).reshape(g.shape)
+    tol = rel_tol * np.abs(w).max(axis=-1, keepdims=True)
+    mag = np.abs(w) + tol
+    if lp_is_bf16:
+        delta = 2.0 ** -8 * mag
+    else:
+        delta = np.maximum(2.0 ** -4 * mag, 2.0 ** -10 * np.asarray(got_scale, np.float64)[:, :, None, None])
+    return bool(np.all(np.abs(gv - w) <= tol + delta))
+
+
 def indices(layer):
     return host(layer.ckpt_pos).copy(), host(layer.len).copy()
 

@@ -60,7 +60,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert R.rssm_abi_version() == R.RSSM_ABI_VERSION == 3
+    assert R.rssm_abi_version() == R.RSSM_ABI_VERSION == 4
     for code in (0, -1, -2, -3, -4, -5):
         assert R.rssm_strerror(code)
     assert "unknown" in R.rssm_strerror(12345)
@@ -249,3 +249,17 @@ def test_tree_entry_points_validate_on_host():
     assert lib.rssm_append_path(ctypes.byref(L), 4, None, FAKE, 2, ctypes.byref(inp), None) == R.RSSM_EINVAL
     L0 = _m2_desc(batch=0)
     assert lib.rssm_append_path(ctypes.byref(L0), 4, None, None, 2, ctypes.byref(inp), None) == R.RSSM_OK
+
+
+def test_prefill_validates_on_host():
+    L = _m2_desc(batch=4, capacity=8)
+    inp = R.make_inputs(x=FAKE, B=FAKE, C=FAKE, dt=FAKE)
+    assert R.rssm_prefill(L, 0, inp, FAKE, stream=0, check=False) == R.RSSM_ERANGE
+    assert R.rssm_prefill(L, 5, R.make_inputs(x=FAKE, B=FAKE, dt=FAKE), FAKE, stream=0,
+                          check=False) == R.RSSM_EINVAL            # outputs need C
+    assert R.rssm_prefill(L, 5, R.make_inputs(x=FAKE, B=FAKE, C=FAKE), None, stream=0,
+                          check=False) == R.RSSM_EINVAL            # dt missing
+    assert R.rssm_prefill(L, 5, inp, FAKE + 8, stream=0, check=False) == R.RSSM_EALIGN
+    assert R.rssm_prefill(_m2_desc(batch=0), 5, R.make_inputs(), None, stream=0,
+                          check=False) == R.RSSM_OK
+    assert R.lib().rssm_prefill(None, 5, ctypes.byref(inp), FAKE, None, None) == R.RSSM_EINVAL

@@ -1,0 +1,181 @@
+"""Prefill on the GPU (rssm_prefill) against the fp64 oracle.
+
+A prefill continues every selected sequence's state from its checkpoint over
+its buffered entries and then over a prompt, writes the output of every
+prompt token, stores the folded state and sets ckpt_pos += len + n_tok,
+len = 0.  Checked here:
+* outputs within the fp32 output tolerance and the checkpoint within 1e-5
+  (max vector relative error) of oracle.drivers.m2_prefill, over prompts of 1,
+  16 and 37 tokens (one token, one full chunk, several chunks and a ragged
+  tail) with and without buffered entries, and decoding that continues after
+  the prefill;
+* masked-out sequences (checkpoint, indices and output rows untouched), no
+  outputs requested, two prefills in a row equal to one;
+* low-precision copies: DUAL folds fp32 and re-encodes, SHARED folds the
+  decoded copy; the codes are the encoding of a state within the fp32
+  checkpoint tolerance of the exact one (per element: within that tolerance
+  plus the codec's half step), at most 1e-3 of them differ from the
+  emulation's, and the E4M3 scale is the exact one within 1e-5;
+* the serving shape (batch 256 x 80 heads) on sampled sequences.
+"""
+import numpy as np
+import pytest
+
+from oracle import drivers
+from linear_attention_decode_replayssm_amd import rssm as R
+from linear_attention_decode_replayssm_amd import synthetic as syn
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+P, N = 64, 128
+M2_NAMES = ("x", "B", "C", "dt")
+
+
+def _split(st, a, b):
+    return {k: np.ascontiguousarray(v[a:b]) for k, v in st.items()}
+
+
+def _empty_ring(b, H, G):
+    return dict(x=np.zeros((0, b, H, P)), B=np.zeros((0, b, G, N)), dt=np.zeros((0, b, H)))
+
+
+@pytest.mark.parametrize("T", [1, 16, 37])
+@pytest.mark.parametrize("pre", [0, 5])
+def test_m2_prefill_matches_oracle(T, pre):
+    b, H, G, cap, post = 3, 10, 5, 8, 3
+    seed = 170 + T + pre
+    A, D = syn.m2_params(seed, H)
+    h0 = syn.m2_state0(seed, b, H, P, N)
+    st = syn.m2_steps(seed, 0, pre + T + post, b, H, G, P, N)
+    ring_st, prompt, post_st = _split(st, 0, pre), _split(st, pre, pre + T), _split(st, pre + T, pre + T + post)
+    L = gu.m2_layer(A, D, h0, G, cap)
+    if pre:
+        gu.m2_decode(L, {k: gu.dev(v) for k, v in ring_st.items()}, 1 << 20, False)
+    pd = {k: gu.dev(v) for k, v in prompt.items()}
+    out = gu.torch().empty_like(pd["x"])
+    R.rssm_prefill(L, T, pd, out)
+    h = h0.astype(np.float64)
+    ring = ring_st if pre else _empty_ring(b, H, G)
+    want = drivers.m2_prefill(A, D, h, ring, np.full(b, pre), prompt)
+    gu.check_m2_outputs(gu.host(out), want, prompt["x"], D)
+    assert gu.vec_rel_err(gu.host(L.ckpt), h) <= 1e-5
+    pos, ln = gu.indices(L)
+    assert (pos == pre + T).all() and (ln == 0).all()
+    y, _, _ = gu.m2_decode(L, {k: gu.dev(v) for k, v in post_st.items()}, 1 << 20, False)
+    want_post = drivers.m2_eager(A, D, post_st["x"], post_st["B"], post_st["C"], post_st["dt"], h)
+    gu.check_m2_outputs(gu.host(y), want_post, post_st["x"], D)
+    assert R.rssm_status(L) == 0
+
+
+def test_m2_prefill_mask_and_no_outputs():
+    b, H, G, cap, T = 4, 10, 5, 8, 21
+    A, D = syn.m2_params(180, H)
+    h0 = syn.m2_state0(180, b, H, P, N)
+    st = syn.m2_steps(180, 0, 2 + T, b, H, G, P, N)
+    ring_st, prompt = _split(st, 0, 2), _split(st, 2, 2 + T)
+    L = gu.m2_layer(A, D, h0, G, cap)
+    gu.m2_decode(L, {k: gu.dev(v) for k, v in ring_st.items()}, 1 << 20, False)
+    ck_before = gu.host(L.ckpt).copy()
+    mask = np.array([1, 0, 1, 0], np.uint8)
+    pd = {k: gu.dev(v) for k, v in prompt.items()}
+    out = gu.torch().full(pd["x"].shape, 7.0, device="cuda")
+    R.rssm_prefill(L, T, pd, out, mask=gu.dev(mask))
+    h = h0.astype(np.float64)
+    want = drivers.m2_prefill(A, D, h, ring_st, np.full(b, 2), prompt, mask=mask)
+    o = gu.host(out)
+    sel = mask.astype(bool)
+    gu.check_m2_outputs(o[:, sel], want[:, sel], prompt["x"][:, sel], D)
+    assert (o[:, ~sel] == 7.0).all()
+    ck = gu.host(L.ckpt)
+    np.testing.assert_array_equal(ck[~sel], ck_before[~sel])
+    assert gu.vec_rel_err(ck[sel], h[sel]) <= 1e-5
+    pos, ln = gu.indices(L)
+    assert pos.tolist() == [2 + T, 0, 2 + T, 0] and ln.tolist() == [0, 2, 0, 2]
+
+    # state only (no outputs, C not passed) gives the same checkpoint
+    L2 = gu.m2_layer(A, D, h0, G, cap)
+    gu.m2_decode(L2, {k: gu.dev(v) for k, v in ring_st.items()}, 1 << 20, False)
+    R.rssm_prefill(L2, T, dict(x=pd["x"], B=pd["B"], dt=pd["dt"]), None, mask=gu.dev(mask))
+    np.testing.assert_array_equal(gu.host(L2.ckpt), ck)
+    assert R.rssm_status(L) == 0 and R.rssm_status(L2) == 0
+
+
+def test_m2_two_prefills_equal_one():
+    b, H, G, cap, T1, T2 = 2, 10, 5, 8, 13, 24
+    A, D = syn.m2_params(181, H)
+    h0 = syn.m2_state0(181, b, H, P, N)
+    st = syn.m2_steps(181, 0, T1 + T2, b, H, G, P, N)
+    L1 = gu.m2_layer(A, D, h0, G, cap)
+    pd = {k: gu.dev(v) for k, v in st.items()}
+    out = gu.torch().empty_like(pd["x"])
+    R.rssm_prefill(L1, T1 + T2, pd, out)
+    L2 = gu.m2_layer(A, D, h0, G, cap)
+    out2 = gu.torch().empty_like(pd["x"])
+    R.rssm_prefill(L2, T1, {k: v[:T1] for k, v in pd.items()}, out2[:T1])
+    R.rssm_prefill(L2, T2, {k: v[T1:].contiguous() for k, v in pd.items()}, out2[T1:])
+    assert gu.vec_rel_err(gu.host(out2), gu.host(out)) <= gu.TOL_F32
+    assert gu.vec_rel_err(gu.host(L2.ckpt), gu.host(L1.ckpt)) <= 1e-5
+    np.testing.assert_array_equal(gu.indices(L1)[0], gu.indices(L2)[0])
+
+
+@pytest.mark.parametrize("scheme", [R.RSSM_DUAL, R.RSSM_SHARED], ids=["dual", "shared"])
+@pytest.mark.parametrize("lp", [R.RSSM_BF16, R.RSSM_E4M3], ids=["bf16", "e4m3"])
+def test_m2_prefill_low_precision(scheme, lp):
+    b, H, G, cap, T = 3, 10, 5, 8, 29
+    A, D = syn.m2_params(182, H)
+    st = syn.m2_steps(182, 0, T, b, H, G, P, N)
+    lpn = "bf16" if lp == R.RSSM_BF16 else "e4m3"
+    L = R.Layer.mamba2(b, H, G, P, N, cap, scheme=scheme, lp_dtype=lp)
+    L.A.copy_(gu.dev(A))
+    L.D.copy_(gu.dev(D))
+    h0 = syn.m2_state0(182, b, H, P, N)
+    codes0, scale0, val0 = drivers.quantize(h0, lpn)
+    t_ = gu.torch()
+    L.ckpt_lp.copy_(t_.from_numpy(codes0.view(np.int16) if lp == R.RSSM_BF16 else codes0))
+    if scale0 is not None:
+        L.lp_scale.copy_(gu.dev(np.asarray(scale0, np.float32)))
+    if L.ckpt is not None:
+        L.ckpt.copy_(gu.dev(h0))
+    start = h0.astype(np.float64) if scheme == R.RSSM_DUAL else val0.astype(np.float64)
+    pd = {k: gu.dev(v) for k, v in st.items()}
+    out = t_.empty_like(pd["x"])
+    R.rssm_prefill(L, T, pd, out)
+    h = start.copy()
+    want = drivers.m2_prefill(A, D, h, _empty_ring(b, H, G), np.zeros(b, int), st)
+    gu.check_m2_outputs(gu.host(out), want, st["x"], D)
+    if scheme == R.RSSM_DUAL:
+        assert gu.vec_rel_err(gu.host(L.ckpt), h) <= 1e-5
+    got_scale = None if L.lp_scale is None else gu.host(L.lp_scale)
+    assert gu.codes_within(gu.host(L.ckpt_lp), h, lp == R.RSSM_BF16, got_scale)
+    codes, scale, _ = drivers.quantize(h.astype(np.float32), lpn)
+    ok, frac = gu.codes_close(gu.host(L.ckpt_lp), codes, lp == R.RSSM_BF16, got_scale, scale)
+    assert frac <= 1e-3, frac
+    if lp == R.RSSM_E4M3:
+        assert np.abs(got_scale / scale - 1).max() <= 1e-5
+    assert R.rssm_status(L) == 0
+
+
+def test_m2_prefill_serving_shape_sampled():
+    """Batch 256 x 80 heads, G = 8, a 48-token prompt after 3 buffered
+    entries: every output and the checkpoint of 3 sampled sequences."""
+    b, H, G, cap, pre, T = 256, 80, 8, 8, 3, 48
+    A, D = syn.m2_params(183, H)
+    h0 = syn.m2_state0(183, b, H, P, N)
+    st = syn.m2_steps(183, 0, pre + T, b, H, G, P, N)
+    ring_st, prompt = _split(st, 0, pre), _split(st, pre, pre + T)
+    L = gu.m2_layer(A, D, h0, G, cap)
+    gu.m2_decode(L, {k: gu.dev(v) for k, v in ring_st.items()}, 1 << 20, False, record=False)
+    pd = {k: gu.dev(v) for k, v in prompt.items()}
+    out = gu.torch().empty_like(pd["x"])
+    R.rssm_prefill(L, T, pd, out)
+    o = gu.host(out)
+    ck = gu.host(L.ckpt)
+    for s in (0, 131, 255):
+        h = h0[s:s + 1].astype(np.float64)
+        one = lambda d: {k: np.ascontiguousarray(v[:, s:s + 1]) for k, v in d.items()}
+        want = drivers.m2_prefill(A, D, h, one(ring_st), np.array([pre]), one(prompt))
+        gu.check_m2_outputs(o[:, s:s + 1], want, prompt["x"][:, s:s + 1], D)
+        assert gu.vec_rel_err(ck[s:s + 1], h) <= 1e-5
+    pos, ln = gu.indices(L)
+    assert (pos == pre + T).all() and (ln == 0).all()
+    assert R.rssm_status(L) == 0

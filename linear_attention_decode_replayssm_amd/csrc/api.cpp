@@ -254,21 +254,34 @@ int rssm_prefill(const rssm_layer* L, int n_tok, const rssm_inputs* in, float* o
   if (rc) return rc;
   if (!in) return RSSM_EINVAL;
   if (n_tok < 1) return RSSM_ERANGE;
-  if (L->kind == RSSM_GDN) return RSSM_EUNSUPPORTED;
   if (L->batch == 0) return RSSM_OK;
   if ((rc = check_layer_ptrs(L)) || (rc = check_state(L))) return rc;
   if (out && !a16(out)) return RSSM_EALIGN;
-  if (!in->x || !in->B || !in->dt || (out && !in->C)) return RSSM_EINVAL;
-  if (!a16(in->x) || !a16(in->B) || (out && !a16(in->C))) return RSSM_EALIGN;
-  rssm::M2Args a = m2_args(L);
-  a.x = in->x;
-  a.B = in->B;
-  a.C = out ? in->C : nullptr;
-  a.dt = in->dt;
-  a.y = out;
+  if (L->kind == RSSM_MAMBA2) {
+    if (!in->x || !in->B || !in->dt || (out && !in->C)) return RSSM_EINVAL;
+    if (!a16(in->x) || !a16(in->B) || (out && !a16(in->C))) return RSSM_EALIGN;
+    rssm::M2Args a = m2_args(L);
+    a.x = in->x;
+    a.B = in->B;
+    a.C = out ? in->C : nullptr;
+    a.dt = in->dt;
+    a.y = out;
+    a.mask = mask;
+    a.n_pos = n_tok;
+    return hip_rc(rssm::launch_m2_prefill(a, S(stream)));
+  }
+  if (!in->k || !in->v || !in->alpha || !in->beta || (out && !in->q)) return RSSM_EINVAL;
+  if (!a16(in->k) || !a16(in->v) || (out && !a16(in->q))) return RSSM_EALIGN;
+  rssm::GdnArgs a = gdn_args(L);
+  a.q = out ? in->q : nullptr;
+  a.k = in->k;
+  a.v = in->v;
+  a.alpha = in->alpha;
+  a.beta = in->beta;
+  a.o = out;
   a.mask = mask;
   a.n_pos = n_tok;
-  return hip_rc(rssm::launch_m2_prefill(a, S(stream)));
+  return hip_rc(rssm::launch_gdn_prefill(a, S(stream)));
 }
 
 int rssm_append_path(const rssm_layer* L, int n_nodes, const int32_t* path,

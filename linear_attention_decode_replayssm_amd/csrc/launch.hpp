@@ -57,7 +57,7 @@ struct GdnArgs {
   const float* alpha;   // [n][b][H]
   const float* beta;    // [n][b][H]
   float* o;             // [n][b][H][dv]
-  const uint8_t* mask;
+  const uint8_t* mask;  // commit, prefill
   int batch, H, cap, n_pos, min_len;
   int scheme, lp;       // rssm_scheme / rssm_lp values
   uint32_t anc[8];      // as in M2Args
@@ -80,6 +80,7 @@ hipError_t launch_gdn_eager(const GdnArgs& a, hipStream_t s);
 hipError_t launch_m2_append_path(const M2Args& a, hipStream_t s);
 hipError_t launch_m2_prefill(const M2Args& a, hipStream_t s);   // n_pos = prompt tokens
 hipError_t launch_gdn_append_path(const GdnArgs& a, hipStream_t s);
+hipError_t launch_gdn_prefill(const GdnArgs& a, hipStream_t s);  // n_pos = prompt tokens
 
 hipError_t launch_rollback(int64_t* pos, int32_t* len, uint32_t* status,
                            const int32_t* n_reject, int batch, hipStream_t s);

@@ -88,8 +88,10 @@ struct M2Pre {
   }
 };
 
+// Left alone the compiler gives this kernel ~220 registers (two waves per
+// SIMD); capped at three waves it needs no spills and runs ~1.2x faster.
 template <int SCHEME, int LP>
-__global__ __launch_bounds__(NT) void m2_prefill_kernel(M2Args a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void m2_prefill_kernel(M2Args a) {
   const int tile = tile_index();
   const int b = tile / a.H, h = tile - b * a.H;
   if (a.mask && a.mask[b] == 0) return;   // the whole sequence skips: no arrival
@@ -285,6 +287,311 @@ __global__ __launch_bounds__(NT) void m2_prefill_kernel(M2Args a) {
   finish_update(a.arrive, a.pos, a.len, b, a.H, arrived, u);
 }
 
+// ------------------------------------------------------------------ GDN ----
+// Gated DeltaNet (one 512-thread workgroup per (sequence, head); wave w owns
+// state rows (value index) 16w .. 16w+15, the state kept transposed in
+// accumulators like the Mamba-2 one: tile t, register r of lane l holds
+// S[16w + li][16t + 4lq + r]).  Per row, S <- alpha S + u k^T with
+// u = beta (v - alpha S k).  Over a chunk of Q tokens from the chunk-start
+// state S (prefix products Gp_t = alpha_0 .. alpha_t, G_{i+1..t} the product
+// over i < m <= t, suffix g_i = G_{i+1..Q-1}):
+//   W = S K^T,  z_t = beta_t (v_t - Gp_t W_t),  u = T z with
+//   T = (I + Lm)^-1,  Lm[t][i] = beta_t G_{i+1..t} (k_i . k_t) for i < t,
+//   o_t = Gp_t S q_t + sum_{i<=t} G_{i+1..t} (k_i . q_t) u_i,
+//   S  <- Gp_{Q-1} S + sum_i g_i u_i k_i^T,
+// the eager recurrence regrouped (the same closed form the commit kernels
+// fold with).  W, S Q^T, K K^T, Q K^T, T z, the in-chunk output term and the
+// fold are MFMA products; products over the token index take the token-major
+// accumulator of the previous product as their B operand directly (k-slot lq
+// of register r is token 4 lq + r on both operands).
+constexpr int GD = 128;        // dk = dv
+constexpr int GNT = 512;       // 8 waves x 16 state rows
+constexpr int GPITCH = GD + PAD;
+
+struct GdnChunk {
+  f32x4 k, q, v;
+  float al, be;
+};
+
+struct GdnPre {
+  const float *ring_k, *ring_v, *ring_a, *ring_b, *k, *q, *v, *al, *be;
+  long unit, sk, sd;
+  int cap, slot0, nring, T;
+  bool outs;
+  __device__ int count(int c) const { return c < 0 ? nring : min(Q, T - c * Q); }
+  // thread tid: float4 (tid & 31) of token tid >> 5 for k, q, v; alpha and
+  // beta of token tid for tid < Q.  Padding tokens: k = v = q = 0, alpha = 1,
+  // beta = 0, which leave the state unchanged.
+  __device__ void fetch(int c, GdnChunk& f) const {
+    const int tid = threadIdx.x, n = count(c), i = tid >> 5, c4 = tid & 31;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f.k = f.q = f.v = z;
+    if (i < n) {
+      if (c < 0) {
+        const long e = (unit * cap + ring_slot(slot0, i, cap)) * GD + 4 * c4;
+        f.k = ld4(ring_k + e);
+        f.v = ld4(ring_v + e);
+      } else {
+        const long e = (long)(c * Q + i) * sk + unit * GD + 4 * c4;
+        f.k = ld4(k + e);
+        f.v = ld4(v + e);
+        if (outs) f.q = ld4(q + e);
+      }
+    }
+    f.al = 1.f;
+    f.be = 0.f;
+    if (tid < n) {
+      if (c < 0) {
+        const long e = unit * cap + ring_slot(slot0, tid, cap);
+        f.al = ring_a[e];
+        f.be = ring_b[e];
+      } else {
+        const long e = (long)(c * Q + tid) * sd + unit;
+        f.al = al[e];
+        f.be = be[e];
+      }
+    }
+  }
+};
+
+template <int SCHEME, int LP>
+__global__ __launch_bounds__(GNT) void gdn_prefill_kernel(GdnArgs a) {
+  const int tile = tile_index();
+  const int b = tile / a.H, h = tile - b * a.H;
+  if (a.mask && a.mask[b] == 0) return;   // the whole sequence skips: no arrival
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lq = l >> 4;
+  const int row = 16 * w + li;            // this lane's state row (value index)
+  const int T = a.n_pos;
+  const int len = a.len[b];
+  const int64_t pos = a.pos[b];
+  const long unit = (long)b * a.H + h;
+
+  GdnPre pre;
+  pre.ring_k = a.ring_k;
+  pre.ring_v = a.ring_v;
+  pre.ring_a = a.ring_a;
+  pre.ring_b = a.ring_b;
+  pre.k = a.k;
+  pre.q = a.q;
+  pre.v = a.v;
+  pre.al = a.alpha;
+  pre.be = a.beta;
+  pre.unit = unit;
+  pre.sk = (long)a.batch * a.H * GD;
+  pre.sd = (long)a.batch * a.H;
+  pre.cap = a.cap;
+  pre.slot0 = (int)(pos % a.cap);
+  pre.nring = min(max(len, 0), min(a.cap, Q));
+  pre.T = T;
+  pre.outs = a.o != nullptr;
+
+  const int c0 = pre.nring > 0 ? -1 : 0;
+  const int nch = (T + Q - 1) / Q;
+  GdnChunk f;
+  pre.fetch(c0, f);
+
+  f32x4 acc[8];
+  const long e0 = unit * (GD * GD) + (long)row * GD + 4 * lq;
+  if constexpr (SCHEME == kSchemeShared) {
+    if constexpr (LP == kLpBf16) {
+      const uint16_t* lp = reinterpret_cast<const uint16_t*>(a.ckpt_lp) + e0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(lp + 16 * t);
+        acc[t] = f32x4{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+      }
+    } else {
+      const uint8_t* lp = reinterpret_cast<const uint8_t*>(a.ckpt_lp) + e0;
+      const float sc = a.lp_scale[unit];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(lp + 16 * t);
+        const f32x2 lo = e4m3_pair(v, false), hi = e4m3_pair(v, true);
+        acc[t] = f32x4{lo.x * sc, lo.y * sc, hi.x * sc, hi.y * sc};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = ld_nt(a.ckpt + e0 + 16 * t);
+  }
+  indices_consumed(len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, b, len, pos);
+
+  __shared__ __attribute__((aligned(16))) float s_k[Q][GPITCH];
+  __shared__ __attribute__((aligned(16))) float s_q[Q][GPITCH];
+  __shared__ __attribute__((aligned(16))) float s_v[Q][GPITCH];
+  __shared__ float s_al[Q], s_be[Q], s_gp[Q], s_gs[Q];
+  __shared__ float s_P[8][Q][Q + 1];   // partial K K^T (waves 0-3) and Q K^T (4-7)
+  __shared__ float s_L[Q][Q + 1], s_M[Q][Q + 1], s_T[Q][Q + 1];
+  __shared__ float s_red[GNT / 64];
+
+  for (int c = c0; c < nch; ++c) {
+    {
+      const int i = tid >> 5, c4 = tid & 31;
+      st4(&s_k[i][4 * c4], f.k);
+      st4(&s_q[i][4 * c4], f.q);
+      st4(&s_v[i][4 * c4], f.v);
+      if (tid < Q) {
+        s_al[tid] = f.al;
+        s_be[tid] = f.be;
+      }
+    }
+    __syncthreads();
+    if (c + 1 < nch) pre.fetch(c + 1, f);
+    const int n = pre.count(c);
+    const bool out = c >= 0 && pre.outs;
+
+    if (tid < Q) {   // prefix and suffix alpha products
+      float gp = 1.f, gs = 1.f;
+#pragma unroll
+      for (int m = 0; m < Q; ++m) {
+        const float am = s_al[m];
+        if (m <= tid) gp *= am;
+        else gs *= am;
+      }
+      s_gp[tid] = gp;
+      s_gs[tid] = gs;
+    }
+    if (w < 4 || out) {   // K K^T (waves 0-3) / Q K^T (waves 4-7) over a quarter of dk
+      const int quarter = w & 3;
+      f32x4 e = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int nn = 32 * quarter + 4 * s + lq;
+        const float av = w < 4 ? s_k[li][nn] : s_q[li][nn];
+        e = mfma4(av, s_k[li][nn], e);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_P[w][4 * lq + r][li] = e[r];
+    }
+    __syncthreads();
+    {  // Lm and M, one element per thread of the first 256
+      if (tid < Q * Q) {
+        const int t = tid >> 4, i = tid & 15;
+        float g = 1.f;   // G_{i+1..t}
+        for (int m = i + 1; m <= t; ++m) g *= s_al[m];
+        const float kk = s_P[0][t][i] + s_P[1][t][i] + s_P[2][t][i] + s_P[3][t][i];
+        s_L[t][i] = i < t ? s_be[t] * g * kk : 0.f;
+        if (out) {
+          const float qk = s_P[4][t][i] + s_P[5][t][i] + s_P[6][t][i] + s_P[7][t][i];
+          s_M[t][i] = i <= t ? g * qk : 0.f;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < Q) {   // T = (I + Lm)^-1, column tid, by forward substitution
+      const int j = tid;
+      float col[Q];
+#pragma unroll
+      for (int t = 0; t < Q; ++t) {
+        float v = t == j ? 1.f : 0.f;
+        if (t > j) {
+          float acc2 = 0.f;
+#pragma unroll
+          for (int i = 0; i < t; ++i) acc2 += s_L[t][i] * col[i];   // col[i] = 0 for i < j
+          v = -acc2;
+        }
+        col[t] = v;
+      }
+#pragma unroll
+      for (int t = 0; t < Q; ++t) s_T[t][j] = col[t];
+    }
+    // W^T = K S^T and (outputs) S Q^T, contracting over the state's column index
+    f32x4 wt = {0.f, 0.f, 0.f, 0.f}, oc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const f32x4 kv = ld4(&s_k[li][16 * t + 4 * lq]);
+      wt = mfma4(kv.x, acc[t].x, wt);
+      wt = mfma4(kv.y, acc[t].y, wt);
+      wt = mfma4(kv.z, acc[t].z, wt);
+      wt = mfma4(kv.w, acc[t].w, wt);
+    }
+    if (out) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const f32x4 qv = ld4(&s_q[li][16 * t + 4 * lq]);
+        oc = mfma4(qv.x, acc[t].x, oc);
+        oc = mfma4(qv.y, acc[t].y, oc);
+        oc = mfma4(qv.z, acc[t].z, oc);
+        oc = mfma4(qv.w, acc[t].w, oc);
+      }
+    }
+    __syncthreads();   // s_T complete
+    // z (token 4 lq + r, row `row`), then u = T z
+    f32x4 z;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * lq + r;
+      z[r] = s_be[t] * (s_v[t][row] - s_gp[t] * wt[r]);
+    }
+    f32x4 u = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) u = mfma4(s_T[li][4 * lq + r], z[r], u);
+    if (out) {   // o_t = Gp_t S q_t + sum_i M[t][i] u_i
+      f32x4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = s_gp[4 * lq + r] * oc[r];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o = mfma4(s_M[li][4 * lq + r], u[r], o);
+      const long so = (long)a.batch * a.H * GD;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 4 * lq + r;
+        if (t < n) a.o[(long)(c * Q + t) * so + unit * GD + row] = o[r];
+      }
+    }
+    {  // fold: S <- Gp_{Q-1} S + sum_i g_i u_i k_i^T
+      const float gall = s_gp[Q - 1];
+      float gu[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gu[r] = s_gs[4 * lq + r] * u[r];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        acc[t] *= gall;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t] = mfma4(s_k[4 * lq + r][16 * t + li], gu[r], acc[t]);
+      }
+    }
+    __syncthreads();
+  }
+
+  if constexpr (SCHEME != kSchemeShared) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) st_nt(a.ckpt + e0 + 16 * t, acc[t]);
+  }
+  if constexpr (SCHEME != kSchemeF32) {
+    if constexpr (LP == kLpBf16) {
+      uint16_t* lp = reinterpret_cast<uint16_t*>(a.ckpt_lp) + e0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        u32x2 v;
+        v.x = bf16_rne(acc[t].x) | (bf16_rne(acc[t].y) << 16);
+        v.y = bf16_rne(acc[t].z) | (bf16_rne(acc[t].w) << 16);
+        *reinterpret_cast<u32x2*>(lp + 16 * t) = v;
+      }
+    } else {
+      const float amax = tile_amax<GNT, 8>(acc, s_red);
+      const bool fin = amax <= 3.402823466e38f;
+      const float sc = (amax > 0.f && fin) ? amax / 448.f : 1.f;
+      if (!fin && tid == 0) raise_status(a.status, kStatusNonfinite);
+      uint8_t* lp = reinterpret_cast<uint8_t*>(a.ckpt_lp) + e0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t v = fin ? e4m3_pack4(acc[t].x / sc, acc[t].y / sc, acc[t].z / sc, acc[t].w / sc)
+                               : e4m3_pack4_nonfinite(acc[t].x, acc[t].y, acc[t].z, acc[t].w);
+        *reinterpret_cast<uint32_t*>(lp + 16 * t) = v;
+      }
+      if (tid == 0) a.lp_scale[unit] = sc;
+    }
+  }
+
+  IndexUpdate u;
+  u.apply = true;
+  u.pos_add = (int64_t)len + T;
+  u.new_len = 0;
+  finish_update(a.arrive, a.pos, a.len, b, a.H, arrived, u);
+}
+
 }  // namespace
 
 hipError_t launch_m2_prefill(const M2Args& a, hipStream_t s) {
@@ -299,6 +606,21 @@ hipError_t launch_m2_prefill(const M2Args& a, hipStream_t s) {
     hipLaunchKernelGGL((m2_prefill_kernel<kSchemeShared, kLpBf16>), grid, block, 0, s, a);
   else
     hipLaunchKernelGGL((m2_prefill_kernel<kSchemeShared, kLpE4m3>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gdn_prefill(const GdnArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.batch * a.H)), block(GNT);
+  if (a.scheme == kSchemeF32)
+    hipLaunchKernelGGL((gdn_prefill_kernel<kSchemeF32, 0>), grid, block, 0, s, a);
+  else if (a.scheme == kSchemeDual && a.lp == kLpBf16)
+    hipLaunchKernelGGL((gdn_prefill_kernel<kSchemeDual, kLpBf16>), grid, block, 0, s, a);
+  else if (a.scheme == kSchemeDual)
+    hipLaunchKernelGGL((gdn_prefill_kernel<kSchemeDual, kLpE4m3>), grid, block, 0, s, a);
+  else if (a.lp == kLpBf16)
+    hipLaunchKernelGGL((gdn_prefill_kernel<kSchemeShared, kLpBf16>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gdn_prefill_kernel<kSchemeShared, kLpE4m3>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

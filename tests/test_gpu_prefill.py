@@ -16,7 +16,10 @@ len = 0.  Checked here:
   checkpoint tolerance of the exact one (per element: within that tolerance
   plus the codec's half step), at most 1e-3 of them differ from the
   emulation's, and the E4M3 scale is the exact one within 1e-5;
-* the serving shape (batch 256 x 80 heads) on sampled sequences.
+* the serving shape (batch 256 x 80 heads) on sampled sequences;
+* the same for Gated DeltaNet (batch 256 x 32 heads at the serving shape),
+  plus the delta-rule identity (beta = 1, unit keys, q_t = k_t: every prompt
+  output is v_t).
 """
 import numpy as np
 import pytest
@@ -176,6 +179,148 @@ def test_m2_prefill_serving_shape_sampled():
         want = drivers.m2_prefill(A, D, h, one(ring_st), np.array([pre]), one(prompt))
         gu.check_m2_outputs(o[:, s:s + 1], want, prompt["x"][:, s:s + 1], D)
         assert gu.vec_rel_err(ck[s:s + 1], h) <= 1e-5
+    pos, ln = gu.indices(L)
+    assert (pos == pre + T).all() and (ln == 0).all()
+    assert R.rssm_status(L) == 0
+
+
+# ------------------------------------------------------------- Gated DeltaNet --
+
+DK = 128
+GDN_NAMES = ("q", "k", "v", "alpha", "beta")
+
+
+def _gdn_empty_ring(b, H):
+    return dict(k=np.zeros((0, b, H, DK)), v=np.zeros((0, b, H, DK)),
+                alpha=np.zeros((0, b, H)), beta=np.zeros((0, b, H)))
+
+
+def _gdn_ring(st):
+    return {k: st[k] for k in ("k", "v", "alpha", "beta")}
+
+
+@pytest.mark.parametrize("T", [1, 16, 37])
+@pytest.mark.parametrize("pre", [0, 3])
+def test_gdn_prefill_matches_oracle(T, pre):
+    b, H, cap, post = 3, 5, 8, 2
+    seed = 190 + T + pre
+    S0 = syn.gdn_state0(seed, b, H, DK, DK, std=0.1)
+    st = syn.gdn_steps(seed, 0, pre + T + post, b, H, DK, DK)
+    ring_st, prompt, post_st = _split(st, 0, pre), _split(st, pre, pre + T), _split(st, pre + T, pre + T + post)
+    L = gu.gdn_layer(S0, cap)
+    if pre:
+        gu.gdn_decode(L, {k: gu.dev(v) for k, v in ring_st.items()}, 1 << 20, False)
+    pd = {k: gu.dev(v) for k, v in prompt.items()}
+    out = gu.torch().empty_like(pd["v"])
+    R.rssm_prefill(L, T, pd, out)
+    S = S0.astype(np.float64)
+    ring = _gdn_ring(ring_st) if pre else _gdn_empty_ring(b, H)
+    want = drivers.gdn_prefill(S, ring, np.full(b, pre), prompt)
+    assert gu.vec_rel_err(gu.host(out), want) <= gu.TOL_F32
+    assert gu.vec_rel_err(gu.host(L.ckpt), S) <= 1e-5
+    pos, ln = gu.indices(L)
+    assert (pos == pre + T).all() and (ln == 0).all()
+    o, _, _ = gu.gdn_decode(L, {k: gu.dev(v) for k, v in post_st.items()}, 1 << 20, False)
+    want_post = drivers.gdn_eager(*(post_st[n] for n in GDN_NAMES), S)
+    assert gu.vec_rel_err(gu.host(o), want_post) <= gu.TOL_F32
+    assert R.rssm_status(L) == 0
+
+
+def test_gdn_prefill_delta_rule_identity():
+    """beta = 1 with unit keys and q_t = k_t: every prompt output is v_t."""
+    b, H, cap, T = 2, 4, 8, 40
+    S0 = syn.gdn_state0(195, b, H, DK, DK, std=0.1)
+    st = syn.gdn_steps(195, 0, T, b, H, DK, DK)
+    st["beta"][:] = 1.0
+    st["q"] = st["k"].copy()
+    L = gu.gdn_layer(S0, cap)
+    pd = {k: gu.dev(v) for k, v in st.items()}
+    out = gu.torch().empty_like(pd["v"])
+    R.rssm_prefill(L, T, pd, out)
+    assert gu.vec_rel_err(gu.host(out), st["v"]) <= gu.TOL_F32
+
+
+def test_gdn_prefill_mask_and_no_outputs():
+    b, H, cap, T = 4, 5, 8, 19
+    S0 = syn.gdn_state0(196, b, H, DK, DK, std=0.1)
+    st = syn.gdn_steps(196, 0, 2 + T, b, H, DK, DK)
+    ring_st, prompt = _split(st, 0, 2), _split(st, 2, 2 + T)
+    L = gu.gdn_layer(S0, cap)
+    gu.gdn_decode(L, {k: gu.dev(v) for k, v in ring_st.items()}, 1 << 20, False)
+    ck_before = gu.host(L.ckpt).copy()
+    mask = np.array([0, 1, 1, 0], np.uint8)
+    pd = {k: gu.dev(v) for k, v in prompt.items()}
+    out = gu.torch().full(pd["v"].shape, 7.0, device="cuda")
+    R.rssm_prefill(L, T, pd, out, mask=gu.dev(mask))
+    S = S0.astype(np.float64)
+    want = drivers.gdn_prefill(S, _gdn_ring(ring_st), np.full(b, 2), prompt, mask=mask)
+    o = gu.host(out)
+    sel = mask.astype(bool)
+    assert gu.vec_rel_err(o[:, sel], want[:, sel]) <= gu.TOL_F32
+    assert (o[:, ~sel] == 7.0).all()
+    ck = gu.host(L.ckpt)
+    np.testing.assert_array_equal(ck[~sel], ck_before[~sel])
+    assert gu.vec_rel_err(ck[sel], S[sel]) <= 1e-5
+    pos, ln = gu.indices(L)
+    assert pos.tolist() == [0, 2 + T, 2 + T, 0] and ln.tolist() == [2, 0, 0, 2]
+    L2 = gu.gdn_layer(S0, cap)
+    gu.gdn_decode(L2, {k: gu.dev(v) for k, v in ring_st.items()}, 1 << 20, False)
+    R.rssm_prefill(L2, T, {k: pd[k] for k in ("k", "v", "alpha", "beta")}, None,
+                   mask=gu.dev(mask))
+    np.testing.assert_array_equal(gu.host(L2.ckpt), ck)
+
+
+@pytest.mark.parametrize("scheme", [R.RSSM_DUAL, R.RSSM_SHARED], ids=["dual", "shared"])
+@pytest.mark.parametrize("lp", [R.RSSM_BF16, R.RSSM_E4M3], ids=["bf16", "e4m3"])
+def test_gdn_prefill_low_precision(scheme, lp):
+    b, H, cap, T = 3, 5, 8, 27
+    lpn = "bf16" if lp == R.RSSM_BF16 else "e4m3"
+    S0 = syn.gdn_state0(197, b, H, DK, DK, std=0.1)
+    st = syn.gdn_steps(197, 0, T, b, H, DK, DK)
+    L = gu.gdn_layer(S0, cap, scheme, lp)
+    codes0, scale0, val0 = drivers.quantize(S0, lpn)
+    t_ = gu.torch()
+    L.ckpt_lp.copy_(t_.from_numpy(codes0.view(np.int16) if lp == R.RSSM_BF16 else codes0))
+    if scale0 is not None:
+        L.lp_scale.copy_(gu.dev(np.asarray(scale0, np.float32)))
+    S = (S0 if scheme == R.RSSM_DUAL else val0).astype(np.float64)
+    pd = {k: gu.dev(v) for k, v in st.items()}
+    out = t_.empty_like(pd["v"])
+    R.rssm_prefill(L, T, pd, out)
+    want = drivers.gdn_prefill(S, _gdn_empty_ring(b, H), np.zeros(b, int), st)
+    assert gu.vec_rel_err(gu.host(out), want) <= gu.TOL_F32
+    if scheme == R.RSSM_DUAL:
+        assert gu.vec_rel_err(gu.host(L.ckpt), S) <= 1e-5
+    got_scale = None if L.lp_scale is None else gu.host(L.lp_scale)
+    assert gu.codes_within(gu.host(L.ckpt_lp), S, lp == R.RSSM_BF16, got_scale)
+    codes, scale, _ = drivers.quantize(S.astype(np.float32), lpn)
+    _, frac = gu.codes_close(gu.host(L.ckpt_lp), codes, lp == R.RSSM_BF16, got_scale, scale)
+    assert frac <= 1e-3, frac
+    if lp == R.RSSM_E4M3:
+        assert np.abs(got_scale / scale - 1).max() <= 1e-5
+    assert R.rssm_status(L) == 0
+
+
+def test_gdn_prefill_serving_shape_sampled():
+    """Batch 256 x 32 heads, a 48-token prompt after 3 buffered entries: every
+    output and the checkpoint of 3 sampled sequences."""
+    b, H, cap, pre, T = 256, 32, 8, 3, 48
+    S0 = syn.gdn_state0(198, b, H, DK, DK, std=0.1)
+    st = syn.gdn_steps(198, 0, pre + T, b, H, DK, DK)
+    ring_st, prompt = _split(st, 0, pre), _split(st, pre, pre + T)
+    L = gu.gdn_layer(S0, cap)
+    gu.gdn_decode(L, {k: gu.dev(v) for k, v in ring_st.items()}, 1 << 20, False, record=False)
+    pd = {k: gu.dev(v) for k, v in prompt.items()}
+    out = gu.torch().empty_like(pd["v"])
+    R.rssm_prefill(L, T, pd, out)
+    o = gu.host(out)
+    ck = gu.host(L.ckpt)
+    for s in (0, 77, 255):
+        S = S0[s:s + 1].astype(np.float64)
+        one = lambda d: {k: np.ascontiguousarray(v[:, s:s + 1]) for k, v in d.items()}
+        want = drivers.gdn_prefill(S, _gdn_ring(one(ring_st)), np.array([pre]), one(prompt))
+        assert gu.vec_rel_err(o[:, s:s + 1], want) <= gu.TOL_F32
+        assert gu.vec_rel_err(ck[s:s + 1], S) <= 1e-5
     pos, ln = gu.indices(L)
     assert (pos == pre + T).all() and (ln == 0).all()
     assert R.rssm_status(L) == 0

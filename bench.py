@@ -357,6 +357,68 @@ def run_tree_rounds(torch, R, syn, rounds, seed=0):
     return res
 
 
+# MFMA work of one 16-token prefill chunk of one head (fp32 16x16x4 products as
+# executed): Mamba-2 C B^T, outputs h C^T + W X, fold X^T B; GDN K K^T, Q K^T,
+# S K^T, S Q^T, T z, M u, fold.
+PREFILL_CHUNK_FLOP = {
+    "mamba2": 2 * 16 * 16 * 128 + 2 * 16 * 64 * 128 + 2 * 16 * 64 * 16 + 2 * 64 * 128 * 16,
+    "gdn": 2 * (2 * 16 * 16 * 128) + 2 * (2 * 16 * 128 * 128) + 2 * (2 * 16 * 16 * 128)
+           + 2 * 128 * 128 * 16,
+}
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def run_prefill(torch, R, syn, kind, T=512, reps=5, seed=0, pool_n=64):
+    """Prefill of a T-token prompt into every sequence's checkpoint at the
+    headline decode shape of the layer type, every prompt token's output
+    written.  Inputs: a device pool of pool_n synthetic tokens repeated to T
+    (the kernels' cost does not depend on the values).  Per-launch HIP events;
+    median of `reps` launches after one warmup."""
+    b = 256
+    if kind == "mamba2":
+        H, G, P, N = 80, 8, 64, 128
+        A, D = syn.m2_params(seed, H)
+        pool = syn.m2_steps(seed, 0, pool_n, b, H, G, P, N)
+        L = R.Layer.mamba2(b, H, G, P, N, 8)
+        L.A.copy_(torch.from_numpy(A))
+        L.D.copy_(torch.from_numpy(D))
+        L.ckpt.copy_(torch.from_numpy(syn.m2_state0(seed, b, H, P, N)))
+        names, out_name, dv, state_bytes = ("x", "B", "C", "dt"), "x", P, b * H * P * N * 4
+    else:
+        H, dk = 32, 128
+        pool = syn.gdn_steps(seed, 0, pool_n, b, H, dk, dk)
+        L = R.Layer.gdn(b, H, dk, dk, 8)
+        names, out_name, dv, state_bytes = ("q", "k", "v", "alpha", "beta"), "v", dk, b * H * dk * dk * 4
+    reps_t = T // pool_n
+    dev = {k: torch.from_numpy(pool[k]).to("cuda").repeat((reps_t,) + (1,) * (pool[k].ndim - 1))
+           for k in names}
+    out = torch.empty_like(dev[out_name])
+    inp = R.make_inputs(**dev)
+    ev = []
+    for i in range(reps + 1):
+        a_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        R.rssm_prefill(L, T, inp, out)
+        e_.record()
+        ev.append((a_, e_))
+    torch.cuda.synchronize()
+    assert R.rssm_status(L) == 0
+    ms = float(np.median([a_.elapsed_time(e_) for a_, e_ in ev[1:]]))
+    flop = PREFILL_CHUNK_FLOP[kind] * (T // 16) * b * H
+    in_bytes = sum(int(v.numel()) * 4 for v in dev.values())
+    hbm = 2 * state_bytes + in_bytes + int(out.numel()) * 4
+    tflops = flop / (ms * 1e-3) / 1e12
+    res = dict(prompt_tokens=T, us_per_prefill=round(ms * 1e3, 1),
+               seq_tok_s=round(b * T / (ms * 1e-3), 1),
+               tflops=round(tflops, 1), mfma_f32_peak_tflops=MFMA_F32_PEAK_TFLOPS,
+               mfma_frac=round(tflops / MFMA_F32_PEAK_TFLOPS, 4),
+               flop_per_launch=flop, hbm_bytes_per_launch=hbm,
+               hbm_gbps=round(hbm / (ms * 1e-3) / 1e9, 1))
+    del L, dev, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_dual_stack(torch, R, syn, steps, seed=0, layers=12, pool_n=8):
     """12 GDN layers at batch 256 with a low-precision serving checkpoint,
     standalone commit every 8 steps; seq-tokens/s through the whole stack."""
@@ -564,6 +626,10 @@ def main():
         sw = run_m2_interval_sweep(torch, R, syn, 256)
         ml = run_m2_lowprec(torch, R, syn, 128)
         tr = run_tree_rounds(torch, R, syn, 128)
+        pm = run_prefill(torch, R, syn, "mamba2")
+        pg = run_prefill(torch, R, syn, "gdn")
+        pm["speedup_vs_decode_steps"] = round(pm["seq_tok_s"] / out["value"], 2)
+        pg["speedup_vs_decode_steps"] = round(pg["seq_tok_s"] / g["seq_tok_s"], 2)
         out["secondary"] = {
             "gdn_decode_b256_h32_d128": {k: round(v, 2) for k, v in g.items()},
             "mamba2_spec_rounds_b256_4drafts": {k: round(v, 1) for k, v in sp.items()},
@@ -571,6 +637,8 @@ def main():
             "mamba2_commit_interval_sweep": sw,
             "mamba2_lowprec_seq_tok_s": ml,
             "mamba2_tree_rounds_b256_7drafts": {k: round(v, 1) for k, v in tr.items()},
+            "mamba2_prefill_b256_512tok": pm,
+            "gdn_prefill_b256_512tok": pg,
         }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(syn)

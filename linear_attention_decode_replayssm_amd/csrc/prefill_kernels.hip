@@ -354,8 +354,10 @@ struct GdnPre {
   }
 };
 
+// Capped at four waves per SIMD (two workgroups per CU): 128 registers, no
+// spills, ~1.2x faster than the compiler's choice of 130 (one workgroup).
 template <int SCHEME, int LP>
-__global__ __launch_bounds__(GNT) void gdn_prefill_kernel(GdnArgs a) {
+__global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(4))) void gdn_prefill_kernel(GdnArgs a) {
   const int tile = tile_index();
   const int b = tile / a.H, h = tile - b * a.H;
   if (a.mask && a.mask[b] == 0) return;   // the whole sequence skips: no arrival

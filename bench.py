@@ -560,7 +560,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: every (sequence, head) unit of the state engine is "
-              "independent, so this build runs and reports a single MI355X only "
+              "independent and the library drives one device, so this benchmark runs and reports "
+              "a single MI355X only "
               "(--gpus 1).", file=sys.stderr)
         sys.exit(2)
 

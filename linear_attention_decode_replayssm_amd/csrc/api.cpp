@@ -163,7 +163,7 @@ const char* rssm_strerror(int code) {
   switch (code) {
     case RSSM_OK: return "ok";
     case RSSM_EINVAL: return "invalid argument (null pointer, bad enum or inconsistent dims)";
-    case RSSM_EUNSUPPORTED: return "shape or scheme not supported by this build";
+    case RSSM_EUNSUPPORTED: return "shape or scheme not supported by this library";
     case RSSM_EALIGN: return "pointer not 16-byte aligned";
     case RSSM_ERANGE: return "count out of range";
     case RSSM_EHIP: return "HIP runtime error";

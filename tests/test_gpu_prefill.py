@@ -324,3 +324,49 @@ def test_gdn_prefill_serving_shape_sampled():
     pos, ln = gu.indices(L)
     assert (pos == pre + T).all() and (ln == 0).all()
     assert R.rssm_status(L) == 0
+
+
+def test_prefill_after_a_full_ring():
+    """capacity 16 with all 16 slots buffered: the buffered chunk is a full
+    chunk of its own, then the prompt."""
+    b, H, G, cap, T = 2, 10, 5, 16, 20
+    A, D = syn.m2_params(199, H)
+    h0 = syn.m2_state0(199, b, H, P, N)
+    st = syn.m2_steps(199, 0, cap + T, b, H, G, P, N)
+    ring_st, prompt = _split(st, 0, cap), _split(st, cap, cap + T)
+    L = gu.m2_layer(A, D, h0, G, cap)
+    gu.m2_decode(L, {k: gu.dev(v) for k, v in ring_st.items()}, 1 << 20, False)
+    assert (gu.indices(L)[1] == cap).all()
+    pd = {k: gu.dev(v) for k, v in prompt.items()}
+    out = gu.torch().empty_like(pd["x"])
+    R.rssm_prefill(L, T, pd, out)
+    h = h0.astype(np.float64)
+    want = drivers.m2_prefill(A, D, h, ring_st, np.full(b, cap), prompt)
+    gu.check_m2_outputs(gu.host(out), want, prompt["x"], D)
+    assert gu.vec_rel_err(gu.host(L.ckpt), h) <= 1e-5
+    assert (gu.indices(L)[0] == cap + T).all()
+
+
+@pytest.mark.parametrize("kind", ["m2", "gdn"])
+def test_prefill_nonfinite_e4m3_raises_status(kind):
+    """A NaN input makes the folded tile non-finite: the E4M3 copy gets the
+    non-finite encoding and RSSM_STATUS_NONFINITE is raised; indices advance."""
+    b, H, cap, T = 2, 10 if kind == "m2" else 4, 8, 5
+    if kind == "m2":
+        G = 5
+        st = syn.m2_steps(200, 0, T, b, H, G, P, N)
+        st["x"][2, 1, 3, 7] = np.nan
+        L = R.Layer.mamba2(b, H, G, P, N, cap, scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_E4M3)
+        A, D = syn.m2_params(200, H)
+        L.A.copy_(gu.dev(A))
+        L.D.copy_(gu.dev(D))
+        L.ckpt.copy_(gu.dev(syn.m2_state0(200, b, H, P, N)))
+    else:
+        st = syn.gdn_steps(200, 0, T, b, H, DK, DK)
+        st["v"][2, 1, 3, 7] = np.nan
+        L = gu.gdn_layer(syn.gdn_state0(200, b, H, DK, DK, std=0.1), cap, R.RSSM_DUAL, R.RSSM_E4M3)
+    R.rssm_prefill(L, T, {k: gu.dev(v) for k, v in st.items()}, None)
+    assert R.rssm_status(L) == R.STATUS_NONFINITE
+    scale = gu.host(L.lp_scale)
+    assert scale[1, 3] == 1.0 and np.isfinite(scale).all()
+    assert (gu.indices(L)[0] == T).all()

@@ -37,13 +37,15 @@ constexpr int kSchemeF32 = 0, kSchemeDual = 1, kSchemeShared = 2;
 
 // Read geometry of a checkpoint of EB-byte elements (4: fp32, 2: bf16, 1:
 // E4M3): 16-byte lane loads, LPR lanes per row of N elements.
-template <int EB>
+// ROWS: rows read by one workgroup (P, or HPW * P for HPW consecutive heads,
+// which are contiguous in memory).
+template <int EB, int ROWS = P>
 struct RdGeo {
   static constexpr int EPL = 16 / EB;    // elements per lane load
   static constexpr int LPR = N / EPL;    // lanes per state row
   static constexpr int RPL = NT / LPR;   // rows per workgroup-wide load
-  static constexpr int NLD = P / RPL;    // loads per thread
-  static_assert(LPR <= 64 && 64 % LPR == 0 && P % RPL == 0, "read geometry");
+  static constexpr int NLD = ROWS / RPL; // loads per thread
+  static_assert(LPR <= 64 && 64 % LPR == 0 && ROWS % RPL == 0, "read geometry");
 };
 
 // First byte of head `unit`'s checkpoint that the output reads.
@@ -55,10 +57,10 @@ __device__ __forceinline__ const char* read_base(const M2Args& a, long unit) {
     return reinterpret_cast<const char*>(a.ckpt_lp) + unit * (P * N) * EB;
 }
 
-template <int EB>
+template <int EB, int ROWS = P>
 __device__ __forceinline__ void load_raw(const M2Args& a, long unit, int tid,
-                                         u32x4 (&raw)[RdGeo<EB>::NLD]) {
-  using Gm = RdGeo<EB>;
+                                         u32x4 (&raw)[RdGeo<EB, ROWS>::NLD]) {
+  using Gm = RdGeo<EB, ROWS>;
   const char* base = read_base<EB>(a, unit);
   const int cl = tid % Gm::LPR, r0 = tid / Gm::LPR;
 #pragma unroll
@@ -68,11 +70,11 @@ __device__ __forceinline__ void load_raw(const M2Args& a, long unit, int tid,
 
 // Row dots of the raw tile with a vector held as EPL elements per lane
 // (column block cl): d[k] for row k * RPL + r0.
-template <int EB>
-__device__ __forceinline__ void row_dots(const u32x4 (&raw)[RdGeo<EB>::NLD],
-                                         const float (&cv)[RdGeo<EB>::EPL],
-                                         float (&d)[RdGeo<EB>::NLD]) {
-  using Gm = RdGeo<EB>;
+template <int EB, int ROWS = P>
+__device__ __forceinline__ void row_dots(const u32x4 (&raw)[RdGeo<EB, ROWS>::NLD],
+                                         const float (&cv)[RdGeo<EB, ROWS>::EPL],
+                                         float (&d)[RdGeo<EB, ROWS>::NLD]) {
+  using Gm = RdGeo<EB, ROWS>;
 #pragma unroll
   for (int k = 0; k < Gm::NLD; ++k) {
     float f[Gm::EPL];
@@ -98,11 +100,15 @@ struct Geo {
   long unit, gunit;
 };
 
+// Workgroup -> (sequence b, first head h of HPW consecutive heads of one
+// group).
+template <int HPW = 1>
 __device__ __forceinline__ Geo geometry(const M2Args& a) {
   Geo q;
   const int tile = tile_index();
-  q.b = tile / a.H;
-  q.h = tile - q.b * a.H;
+  const int hb = a.H / HPW;
+  q.b = tile / hb;
+  q.h = (tile - q.b * hb) * HPW;
   q.g = q.h / (a.H / a.G);
   q.tid = threadIdx.x;
   q.lane = q.tid & 63;
@@ -126,14 +132,24 @@ __device__ __forceinline__ void store_tile(float* ck, const Geo& q, const f32x4 
 // ---------------------------------------------------------------- step ----
 // Load order matters: vector loads complete in issue order, so every small
 // load the replay prologue needs (B_i and C_t segments, dt_i, x_i) is issued
-// before the 32 KiB checkpoint stream.  Waiting for them then leaves the
-// stream in flight while the prologue runs.  The ring append is done last,
-// after the stream has been consumed.
-template <int EB, bool FUSED>
+// before the checkpoint stream.  Waiting for them then leaves the stream in
+// flight while the prologue runs.  The ring append is done last, after the
+// stream has been consumed.
+//
+// HPW: heads per workgroup, consecutive heads of one group (their checkpoints
+// are contiguous).  The fp32 and bf16 steps take one head (32 and 16 KiB of
+// stream); the E4M3 step takes two, so that a workgroup streams 16 KiB rather
+// than 8 behind the same fixed chain of index read, operand loads and
+// prologue (53 -> 42 us per step at batch 256 x 80 heads; two bf16 heads per
+// workgroup measured no faster than one).  B_i . C_t is shared by the heads
+// of a group and formed once.
+template <int EB, bool FUSED, int HPW = 1>
 __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
-  using Gm = RdGeo<EB>;
-  static_assert(!FUSED || EB == 4, "the fused commit folds the fp32 checkpoint");
-  const Geo q = geometry(a);
+  constexpr int ROWS = HPW * P;
+  using Gm = RdGeo<EB, ROWS>;
+  static_assert(!FUSED || (EB == 4 && HPW == 1), "the fused commit folds one fp32 head");
+  static_assert(HPW <= 16, "dt of head hl is loaded by lane hl of an entry's 16 lanes");
+  const Geo q = geometry<HPW>(a);
   const int cap = a.cap;
   float* ck = a.ckpt + q.unit * (P * N);
 
@@ -142,28 +158,34 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
   const bool ok = len < cap;
   const int L = len + 1;
   const int slot0 = (int)(pos % cap);
-  const float Ah = a.A[q.h];
-  const float Dh = a.D[q.h];
+  float Ah[HPW], Dh[HPW];
+#pragma unroll
+  for (int hl = 0; hl < HPW; ++hl) {
+    Ah[hl] = a.A[q.h + hl];
+    Dh[hl] = a.D[q.h + hl];
+  }
 
-  const float* xt = a.x + q.unit * P;
+  const float* xt = a.x + q.unit * P;   // HPW heads' x_t, contiguous
   const float* Bt = a.B + q.gunit * N;
   const float* Ct = a.C + q.gunit * N;
-  auto xsrc = [&](int i) -> const float* {
-    return i < len ? a.ring_x + (q.unit * cap + ring_slot(slot0, i, cap)) * P : xt;
+  auto xsrc = [&](int hl, int i) -> const float* {
+    return i < len ? a.ring_x + ((q.unit + hl) * cap + ring_slot(slot0, i, cap)) * P
+                   : xt + hl * P;
   };
   auto Bsrc = [&](int i) -> const float* {
     return i < len ? a.ring_B + (q.gunit * cap + ring_slot(slot0, i, cap)) * N : Bt;
   };
 
-  // prologue operands: entry ei = tid/16 dots segment sg of B_ei with C_t;
-  // thread (p, qd) sums entries qd, qd+QD, ... of x_i[p]
+  // prologue operands: entry ei = tid/16 dots segment sg of B_ei with C_t
+  // (lane sg < HPW also loads head sg's dt_ei); thread (p, qd) sums entries
+  // qd, qd+QD, ... of every head's x_i[p]
   constexpr int SEG = N / 16;
-  constexpr int XPT = kMaxCap / QD;  // buffered x values per thread
+  constexpr int XPT = kMaxCap / QD;  // buffered x values per thread and head
   const int ei = q.tid >> 4, sg = q.tid & 15;
   const int p = q.tid % P, qd = q.tid / P;
   f32x4 bseg[SEG / 4], cseg[SEG / 4];
   float dti = 0.f;
-  float xv[XPT];
+  float xv[HPW][XPT];
   if (ok) {
 #pragma unroll
     for (int e = 0; e < SEG / 4; ++e) {
@@ -173,28 +195,34 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
     if (ei < L) {
 #pragma unroll
       for (int e = 0; e < SEG / 4; ++e) bseg[e] = ld4(Bsrc(ei) + sg * SEG + 4 * e);
-      if (sg == 0)
-        dti = ei < len ? a.ring_dt[q.unit * cap + ring_slot(slot0, ei, cap)] : a.dt[q.unit];
+      if (sg < HPW)
+        dti = ei < len ? a.ring_dt[(q.unit + sg) * cap + ring_slot(slot0, ei, cap)]
+                       : a.dt[q.unit + sg];
     }
 #pragma unroll
-    for (int m = 0; m < XPT; ++m) {
-      const int i = qd + m * QD;
-      xv[m] = i < L ? xsrc(i)[p] : 0.f;
+    for (int hl = 0; hl < HPW; ++hl) {
+#pragma unroll
+      for (int m = 0; m < XPT; ++m) {
+        const int i = qd + m * QD;
+        xv[hl][m] = i < L ? xsrc(hl, i)[p] : 0.f;
+      }
     }
   }
   const int cl = q.tid % Gm::LPR, rr0 = q.tid / Gm::LPR;   // read geometry
   float cv[Gm::EPL];
   load_seg<Gm::EPL>(Ct + cl * Gm::EPL, cv);
-  const float scale = (EB == 1) ? a.lp_scale[q.unit] : 1.f;
+  float scale[HPW];
+#pragma unroll
+  for (int hl = 0; hl < HPW; ++hl) scale[hl] = (EB == 1) ? a.lp_scale[q.unit + hl] : 1.f;
 
   u32x4 raw[Gm::NLD];
-  load_raw<EB>(a, q.unit, q.tid, raw);
+  load_raw<EB, ROWS>(a, q.unit, q.tid, raw);
   indices_consumed(len, pos);
   const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
 
-  __shared__ float s_e[kMaxCap], s_dt[kMaxCap], s_w[kMaxCap], s_fw[kMaxCap];
-  __shared__ float s_gamma;
-  __shared__ float s_yb[QD][P];
+  __shared__ float s_e[kMaxCap], s_dt[HPW][kMaxCap], s_w[HPW][kMaxCap], s_fw[kMaxCap];
+  __shared__ float s_gamma[HPW];
+  __shared__ float s_yb[QD][HPW][P];
 
   if (ok) {
     {  // e_i = B_i . C_t
@@ -202,46 +230,56 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
 #pragma unroll
       for (int e = 0; e < SEG / 4; ++e) part += dot4(bseg[e], cseg[e]);
       part = group_sum<16>(part);
-      if (sg == 0 && ei < L) {
-        s_e[ei] = part;
-        s_dt[ei] = dti;
+      if (sg == 0 && ei < L) s_e[ei] = part;
+      if (sg < HPW && ei < L) s_dt[sg][ei] = dti;
+    }
+    __syncthreads();
+    if (q.tid < HPW * kMaxCap) {  // decay weights from dt suffix sums, per head
+      const int hl = q.tid / kMaxCap, i = q.tid % kMaxCap;
+      if (i < L) {
+        float suf = 0.f;
+        for (int j = i + 1; j < L; ++j) suf += s_dt[hl][j];
+        const float dec = expf(Ah[hl] * suf);
+        s_w[hl][i] = dec * s_dt[hl][i] * s_e[i];
+        if (FUSED) s_fw[i] = dec * s_dt[hl][i];
+        if (i == 0) s_gamma[hl] = expf(Ah[hl] * (suf + s_dt[hl][0]));
       }
     }
     __syncthreads();
-    if (q.tid < L) {  // decay weights from dt suffix sums
-      float suf = 0.f;
-      for (int j = q.tid + 1; j < L; ++j) suf += s_dt[j];
-      const float dec = expf(Ah * suf);
-      s_w[q.tid] = dec * s_dt[q.tid] * s_e[q.tid];
-      if (FUSED) s_fw[q.tid] = dec * s_dt[q.tid];
-      if (q.tid == 0) s_gamma = expf(Ah * (suf + s_dt[0]));
-    }
-    __syncthreads();
-    {  // sum_i w_i x_i[p]
+#pragma unroll
+    for (int hl = 0; hl < HPW; ++hl) {  // sum_i w_i x_i[p]
       float yb = 0.f;
 #pragma unroll
       for (int m = 0; m < XPT; ++m) {
         const int i = qd + m * QD;
-        if (i < L) yb += s_w[i] * xv[m];
+        if (i < L) yb += s_w[hl][i] * xv[hl][m];
       }
-      s_yb[qd][p] = yb;
+      s_yb[qd][hl][p] = yb;
     }
   }
 
   {  // Gamma * (h_c C_t) + buffered part + D x_t
     float d[Gm::NLD];
-    row_dots<EB>(raw, cv, d);
+    row_dots<EB, ROWS>(raw, cv, d);
     xreduce<Gm::NLD, Gm::LPR>(d, q.lane);
     __syncthreads();
     using M = XMap<Gm::NLD, Gm::LPR>;
     if (M::writer(q.lane)) {
-      const int pr = M::index(q.lane, 0) * Gm::RPL + rr0;
+      const int pr = M::index(q.lane, 0) * Gm::RPL + rr0;   // row of the HPW heads
+      const int hl = pr / P, pp = pr - hl * P;
       float yv;
       if (ok) {
         float yb = 0.f;
 #pragma unroll
-        for (int j = 0; j < QD; ++j) yb += s_yb[j][pr];
-        yv = s_gamma * (scale * d[0]) + yb + Dh * xt[pr];
+        for (int j = 0; j < QD; ++j) yb += s_yb[j][hl][pp];
+        float sc = scale[0], dh = Dh[0];
+#pragma unroll
+        for (int k = 1; k < HPW; ++k)
+          if (hl == k) {
+            sc = scale[k];
+            dh = Dh[k];
+          }
+        yv = s_gamma[hl] * (sc * d[0]) + yb + dh * xt[pr];
       } else {
         yv = __builtin_nanf("");
       }
@@ -258,10 +296,10 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
                       __uint_as_float(raw[k].z), __uint_as_float(raw[k].w)};
       __shared__ __attribute__((aligned(16))) float s_x[kMaxCap][P];
       __shared__ __attribute__((aligned(16))) float s_B[kMaxCap][N];
-      for (int idx = q.tid; idx < L * P; idx += NT) s_x[idx / P][idx % P] = xsrc(idx / P)[idx % P];
+      for (int idx = q.tid; idx < L * P; idx += NT) s_x[idx / P][idx % P] = xsrc(0, idx / P)[idx % P];
       for (int idx = q.tid; idx < L * N; idx += NT) s_B[idx / N][idx % N] = Bsrc(idx / N)[idx % N];
       __syncthreads();
-      const float gam = s_gamma;
+      const float gam = s_gamma[0];
 #pragma unroll
       for (int k = 0; k < NLD; ++k) hv[k] *= gam;
       for (int i = 0; i < L; ++i) {
@@ -276,15 +314,18 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
     if (ok) {  // append this step's entry from the registers that loaded it
       const int s = ring_slot(slot0, len, cap);
 #pragma unroll
-      for (int m = 0; m < XPT; ++m)
-        if (qd + m * QD == len) a.ring_x[(q.unit * cap + s) * P + p] = xv[m];
+      for (int hl = 0; hl < HPW; ++hl) {
+#pragma unroll
+        for (int m = 0; m < XPT; ++m)
+          if (qd + m * QD == len) a.ring_x[((q.unit + hl) * cap + s) * P + p] = xv[hl][m];
+      }
       if (ei == len) {
         if ((q.h % (a.H / a.G)) == 0) {
 #pragma unroll
           for (int e = 0; e < SEG / 4; ++e)
             st4(a.ring_B + (q.gunit * cap + s) * N + sg * SEG + 4 * e, bseg[e]);
         }
-        if (sg == 0) a.ring_dt[q.unit * cap + s] = dti;
+        if (sg < HPW) a.ring_dt[(q.unit + sg) * cap + s] = dti;
       }
     }
   }
@@ -293,8 +334,8 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
   u.apply = ok;
   u.pos_add = FUSED ? L : 0;
   u.new_len = FUSED ? 0 : L;
-  finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
-  if (!ok && last_arrival(arrived, a.H)) raise_status(a.status, kStatusOverflow);
+  finish_update(a.arrive, a.pos, a.len, q.b, a.H / HPW, arrived, u);
+  if (!ok && last_arrival(arrived, a.H / HPW)) raise_status(a.status, kStatusOverflow);
 }
 
 // -------------------------------------------------------------- commit ----
@@ -703,6 +744,9 @@ __global__ __launch_bounds__(NT) void m2_eager_kernel(M2Args a) {
 
 hipError_t launch_m2_step(const M2Args& a, bool fused, hipStream_t s) {
   const dim3 grid((unsigned)(a.batch * a.H)), block(NT);
+  // E4M3: two heads per workgroup when a group's head count allows it
+  const bool pair = (a.H / a.G) % 2 == 0;
+  const dim3 grid2((unsigned)(a.batch * (a.H / 2)));
   if (a.scheme == kSchemeF32) {
     if (fused)
       hipLaunchKernelGGL((m2_step_kernel<4, true>), grid, block, 0, s, a);
@@ -711,7 +755,10 @@ hipError_t launch_m2_step(const M2Args& a, bool fused, hipStream_t s) {
   } else if (a.lp == kLpBf16) {
     hipLaunchKernelGGL((m2_step_kernel<2, false>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((m2_step_kernel<1, false>), grid, block, 0, s, a);
+    if (pair)
+      hipLaunchKernelGGL((m2_step_kernel<1, false, 2>), grid2, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((m2_step_kernel<1, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -612,7 +612,7 @@ def main():
         "speedup_vs_eager": round(m2["seq_tok_s"] / m2["eager_seq_tok_s"], 4),
         "ckpt_bytes_per_step_vs_eager": round(m2["ckpt_bytes_per_step"] /
                                               m2["eager_ckpt_bytes_per_step"], 4),
-        "roofline": {"bound": "hbm", "kernel": "m2_step_kernel<4, false> (replay step, no commit)",
+        "roofline": {"bound": "hbm", "kernel": "m2_step_kernel<4, false, 1> (replay step, no commit)",
                      "achieved": round(step_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(step_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "avg_launch_us": round(m2["step_us"], 3),

@@ -120,30 +120,39 @@ def test_gdn_tree_verify_and_append(tree):
     assert R.rssm_status(L) == 0
 
 
+@pytest.mark.parametrize("lp", ["e4m3", "bf16"])
 @pytest.mark.parametrize("kind", ["m2", "gdn"])
-def test_tree_from_low_precision_copy(kind):
-    """A DUAL E4M3 layer verifies its tree from the copy: outputs equal the
-    exact tree outputs from the decoded copy (empty buffer)."""
+def test_tree_from_low_precision_copy(kind, lp):
+    """A DUAL layer verifies its tree from the low-precision copy: outputs
+    equal the exact tree outputs from the decoded copy (empty buffer)."""
     parent = TREES["binary"]
     n, b, H, cap = len(parent), 2, 4, 16
     rng = np.random.default_rng(150)
-    codes = rng.integers(0, 0x7F, size=(b, H, P if kind == "m2" else DK, N if kind == "m2" else DK))
-    codes = (codes | (rng.integers(0, 2, size=codes.shape) << 7)).astype(np.uint8)
-    scale = rng.uniform(1e-4, 4e-4, size=(b, H)).astype(np.float32)
-    exact = oracle.e4m3_dequant_heads(scale, codes.reshape(b, H, -1)).reshape(codes.shape)
+    shape = (b, H, P if kind == "m2" else DK, N if kind == "m2" else DK)
+    if lp == "e4m3":
+        codes = rng.integers(0, 0x7F, size=shape)
+        codes = (codes | (rng.integers(0, 2, size=codes.shape) << 7)).astype(np.uint8)
+        scale = rng.uniform(1e-4, 4e-4, size=(b, H)).astype(np.float32)
+        exact = oracle.e4m3_dequant_heads(scale, codes.reshape(b, H, -1)).reshape(codes.shape)
+    else:
+        codes = oracle.bf16_encode((rng.standard_normal(shape) * 0.1).astype(np.float32))
+        scale = None
+        exact = oracle.bf16_decode(codes)
+    lpc = R.RSSM_E4M3 if lp == "e4m3" else R.RSSM_BF16
     t_ = gu.torch()
     if kind == "m2":
         G = 2
         A, D = syn.m2_params(150, H)
         drafts = syn.m2_steps(150, 0, n, b, H, G, P, N)
-        L = R.Layer.mamba2(b, H, G, P, N, cap, scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_E4M3)
+        L = R.Layer.mamba2(b, H, G, P, N, cap, scheme=R.RSSM_DUAL, lp_dtype=lpc)
         L.A.copy_(gu.dev(A))
         L.D.copy_(gu.dev(D))
     else:
         drafts = syn.gdn_steps(150, 0, n, b, H, DK, DK)
-        L = R.Layer.gdn(b, H, DK, DK, cap, scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_E4M3)
-    L.ckpt_lp.copy_(t_.from_numpy(codes))
-    L.lp_scale.copy_(gu.dev(scale))
+        L = R.Layer.gdn(b, H, DK, DK, cap, scheme=R.RSSM_DUAL, lp_dtype=lpc)
+    L.ckpt_lp.copy_(t_.from_numpy(codes.view(np.int16) if lp == "bf16" else codes))
+    if scale is not None:
+        L.lp_scale.copy_(gu.dev(scale))
     dd = {k: gu.dev(v) for k, v in drafts.items()}
     out = t_.empty_like(dd["x"] if kind == "m2" else dd["v"])
     R.rssm_verify_tree(L, parent, dd, out)

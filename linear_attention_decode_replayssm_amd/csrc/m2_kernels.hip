@@ -353,6 +353,28 @@ __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
   if (!sel) return;  // uniform for all workgroups of the sequence
 
   const int64_t pos = a.pos[q.b];
+  const int L = len;
+  const int slot0 = (int)(pos % cap);
+  // the buffered entries first, into registers (thread tid: x of entry
+  // (tid + 256u) / 64, float4 (tid + 256u) % 32 of B_{(tid + 256u) / 32}, dt_tid):
+  // waiting for them then leaves the state stream in flight
+  constexpr int XR = kMaxCap * P / NT, BR = kMaxCap * N / 4 / NT;
+  float xr[XR];
+  f32x4 br[BR];
+  float dtr = 0.f;
+#pragma unroll
+  for (int u = 0; u < XR; ++u) {
+    const int idx = q.tid + u * NT, i = idx / P;
+    xr[u] = i < L ? a.ring_x[(q.unit * cap + ring_slot(slot0, i, cap)) * P + idx % P] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < BR; ++u) {
+    const int idx = q.tid + u * NT, i = idx / (N / 4);
+    br[u] = i < L ? ld4(a.ring_B + (q.gunit * cap + ring_slot(slot0, i, cap)) * N + 4 * (idx % (N / 4)))
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (q.tid < L) dtr = a.ring_dt[q.unit * cap + ring_slot(slot0, q.tid, cap)];
+
   float* ck = a.ckpt + q.unit * (P * N);
   char* lp = reinterpret_cast<char*>(a.ckpt_lp) + q.unit * (P * N) * (LP == kLpBf16 ? 2 : 1);
   float* lps = a.lp_scale ? a.lp_scale + q.unit : nullptr;
@@ -364,8 +386,6 @@ __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
   indices_consumed(len, pos);
   const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
 
-  const int L = len;
-  const int slot0 = (int)(pos % cap);
   const float Ah = a.A[q.h];
   __shared__ float s_dt[kMaxCap], s_fw[kMaxCap];
   __shared__ float s_gamma;
@@ -373,15 +393,17 @@ __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
   __shared__ __attribute__((aligned(16))) float s_x[kMaxCap][P];
   __shared__ __attribute__((aligned(16))) float s_B[kMaxCap][N];
   if (L > 0) {
-    for (int idx = q.tid; idx < L * P; idx += NT) {
-      const int i = idx / P, p = idx % P;
-      s_x[i][p] = a.ring_x[(q.unit * cap + ring_slot(slot0, i, cap)) * P + p];
+#pragma unroll
+    for (int u = 0; u < XR; ++u) {
+      const int idx = q.tid + u * NT;
+      s_x[idx / P][idx % P] = xr[u];
     }
-    for (int idx = q.tid; idx < L * N; idx += NT) {
-      const int i = idx / N, n = idx % N;
-      s_B[i][n] = a.ring_B[(q.gunit * cap + ring_slot(slot0, i, cap)) * N + n];
+#pragma unroll
+    for (int u = 0; u < BR; ++u) {
+      const int idx = q.tid + u * NT;
+      st4(&s_B[idx / (N / 4)][4 * (idx % (N / 4))], br[u]);
     }
-    if (q.tid < L) s_dt[q.tid] = a.ring_dt[q.unit * cap + ring_slot(slot0, q.tid, cap)];
+    if (q.tid < L) s_dt[q.tid] = dtr;
     __syncthreads();
     if (q.tid < L) {
       float suf = 0.f;

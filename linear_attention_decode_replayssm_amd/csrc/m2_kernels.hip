@@ -223,6 +223,9 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
   __shared__ float s_e[kMaxCap], s_dt[HPW][kMaxCap], s_w[HPW][kMaxCap], s_fw[kMaxCap];
   __shared__ float s_gamma[HPW];
   __shared__ float s_yb[QD][HPW][P];
+  // fused commit: the entries' x_i and B_i, parked from the prologue registers
+  __shared__ __attribute__((aligned(16))) float s_x[FUSED ? kMaxCap : 1][P];
+  __shared__ __attribute__((aligned(16))) float s_B[FUSED ? kMaxCap : 1][N];
 
   if (ok) {
     {  // e_i = B_i . C_t
@@ -232,6 +235,17 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
       part = group_sum<16>(part);
       if (sg == 0 && ei < L) s_e[ei] = part;
       if (sg < HPW && ei < L) s_dt[sg][ei] = dti;
+      if constexpr (FUSED) {   // no second fetch of the entries at the fold
+        if (ei < L) {
+#pragma unroll
+          for (int e = 0; e < SEG / 4; ++e) st4(&s_B[ei][sg * SEG + 4 * e], bseg[e]);
+        }
+#pragma unroll
+        for (int m = 0; m < XPT; ++m) {
+          const int i = qd + m * QD;
+          if (i < L) s_x[i][p] = xv[0][m];
+        }
+      }
     }
     __syncthreads();
     if (q.tid < HPW * kMaxCap) {  // decay weights from dt suffix sums, per head
@@ -294,11 +308,6 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
       for (int k = 0; k < NLD; ++k)
         hv[k] = f32x4{__uint_as_float(raw[k].x), __uint_as_float(raw[k].y),
                       __uint_as_float(raw[k].z), __uint_as_float(raw[k].w)};
-      __shared__ __attribute__((aligned(16))) float s_x[kMaxCap][P];
-      __shared__ __attribute__((aligned(16))) float s_B[kMaxCap][N];
-      for (int idx = q.tid; idx < L * P; idx += NT) s_x[idx / P][idx % P] = xsrc(0, idx / P)[idx % P];
-      for (int idx = q.tid; idx < L * N; idx += NT) s_B[idx / N][idx % N] = Bsrc(idx / N)[idx % N];
-      __syncthreads();
       const float gam = s_gamma[0];
 #pragma unroll
       for (int k = 0; k < NLD; ++k) hv[k] *= gam;

@@ -59,7 +59,7 @@ extern "C" {
 #define RSSM_EINVAL       (-1) /* null pointer, bad enum, bad or inconsistent dims */
 #define RSSM_EUNSUPPORTED (-2) /* shape / scheme combination not instantiated     */
 #define RSSM_EALIGN       (-3) /* a 16-byte-accessed pointer is misaligned         */
-#define RSSM_ERANGE       (-4) /* n_pos < 1, n_pos > capacity, min_len < 0         */
+#define RSSM_ERANGE       (-4) /* n_pos < 1 or > capacity, n_tok < 1, min_len < 0  */
 #define RSSM_EHIP         (-5) /* the HIP runtime reported a launch/copy error     */
 
 /* ---- sticky device status bits (layer->status[0]) ---------------------- */
@@ -68,8 +68,8 @@ extern "C" {
 #define RSSM_STATUS_NONFINITE 4u /* non-finite state met while quantising to E4M3   */
 /* On RSSM_STATUS_NONFINITE the head's E4M3 scale is set to 1 and its codes
  * saturate (+-inf -> +-448, NaN stays NaN); the fp32 checkpoint and the
- * indices are updated as for any commit.  bf16 copies carry inf and NaN
- * natively and raise no bit. */
+ * indices are updated as for any commit or prefill.  bf16 copies carry inf
+ * and NaN natively and raise no bit. */
 
 typedef enum { RSSM_MAMBA2 = 1, RSSM_GDN = 2 } rssm_kind;
 

@@ -263,7 +263,9 @@ def run_m2_interval_sweep(torch, R, syn, steps, seed=0, pool_n=16,
 
 def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     """Mamba-2 speculative rounds at the serving shape: verify 4 drafts,
-    roll back the rejected ones, commit at 8 buffered entries; ring 12."""
+    roll back the rejected ones, commit at 8 buffered entries; ring 12.  Then
+    the same rounds with the eager comparator (state read once, written after
+    every draft)."""
     b, H, G, P, N, cap, n, commit_len = 256, 80, 8, 64, 128, 12, 4, 8
     A, D = syn.m2_params(seed, H)
     pool = syn.m2_steps(seed, 0, pool_n, b, H, G, P, N)
@@ -303,7 +305,36 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
                us_per_round=ms * 1e3 / rounds,
                bytes_per_round=total / rounds,
                hbm_gbps=total / (ms * 1e-3) / 1e9)
-    del L, dev
+    del L
+    torch.cuda.empty_cache()
+
+    # the eager comparator on the same rounds: the state read once per round
+    # and written after every draft (n + 1 state slots, accept = slot move)
+    L = R.Layer.mamba2(b, H, G, P, N, cap)
+    L.A.copy_(torch.from_numpy(A))
+    L.D.copy_(torch.from_numpy(D))
+    slots = torch.empty((n + 1, b, H, P, N), dtype=torch.float32, device="cuda")
+    slots[0].copy_(torch.from_numpy(syn.m2_state0(seed, b, H, P, N)))
+    cur = torch.zeros(b, dtype=torch.int32, device="cuda")
+    acc_d = torch.from_numpy(accept.astype(np.int32)).to("cuda")
+    torch.cuda.synchronize()
+    start.record()
+    for r in range(rounds):
+        j = (r * n) % pool_n
+        R.rssm_eager_spec_round(L, n, R.make_inputs(x=dev["x"][j:j + n], B=dev["B"][j:j + n],
+                                                    C=dev["C"][j:j + n], dt=dev["dt"][j:j + n]),
+                                out, slots, cur)
+        R.rssm_eager_spec_accept(L, n, cur, acc_d[r])
+    end.record()
+    torch.cuda.synchronize()
+    ems = start.elapsed_time(end)
+    assert R.rssm_status(L) == 0
+    ebytes = b * ((1 + n) * S + n * (inputs + out_b))
+    res["eager_rounds_per_s"] = rounds / (ems * 1e-3)
+    res["eager_bytes_per_round"] = float(ebytes)
+    res["eager_hbm_gbps"] = ebytes * rounds / (ems * 1e-3) / 1e9
+    res["speedup_vs_eager_spec"] = ems / ms
+    del L, dev, slots
     torch.cuda.empty_cache()
     return res
 

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 4
+#define RSSM_ABI_VERSION 5
 #define RSSM_ARRIVE_STRIDE 32   /* uint32 elements between two sequences' counters */
 
 /* ---- host return codes ------------------------------------------------- */
@@ -316,6 +316,33 @@ int rssm_status(const rssm_layer* L, uint32_t* bits, void* stream);
 
 /* Static description of a return code.  Never NULL. */
 const char* rssm_strerror(int code);
+
+/*
+ * rssm_eager_spec_round / rssm_eager_spec_accept -- the eager comparator for
+ * speculative decoding.  Without a checkpoint and an input buffer, verifying
+ * drafts while keeping the option to roll back means materialising the state
+ * after every draft (Abstract: ReplaySSM verifies drafts from their outputs
+ * without materialising intermediate states).  The comparator keeps each
+ * sequence's state in a ring of n_pos + 1 caller-owned state slots
+ * (`slots`: device fp32 [n_pos + 1][batch][H][dim_v][dim_k]); cur[b] (device
+ * int32 [batch], 0..n_pos) names the slot holding sequence b's state.
+ *   round:  read slot cur[b] once, apply drafts j = 0..n_pos-1 with the eager
+ *           recurrence, write out[j] (laid out as rssm_verify's) and the state
+ *           after draft j to slot (cur[b] + 1 + j) % (n_pos + 1);
+ *   accept: cur[b] = (cur[b] + n_accept[b]) % (n_pos + 1), n_accept device
+ *           int32 [batch] in 0..n_pos; the state after the last accepted draft
+ *           becomes current.
+ * One state read and n_pos state writes per round, against ReplaySSM's one
+ * read.  n_pos must be the same in both calls and in every round on the same
+ * slots.  F32 layers only (RSSM_EUNSUPPORTED otherwise); 1 <= n_pos <= 8
+ * (RSSM_ERANGE).  The layer's rings, indices and checkpoint are not used.  A
+ * cur[b] or n_accept[b] out of range sets RSSM_STATUS_ROLLBACK and leaves the
+ * sequence unchanged (its outputs NaN).  Inputs as for rssm_verify.
+ */
+int rssm_eager_spec_round(const rssm_layer* L, int n_pos, const rssm_inputs* in, float* out,
+                          float* slots, const int32_t* cur, void* stream);
+int rssm_eager_spec_accept(const rssm_layer* L, int n_pos, int32_t* cur, const int32_t* n_accept,
+                           void* stream);
 
 /* RSSM_ABI_VERSION of the loaded library. */
 int rssm_abi_version(void);

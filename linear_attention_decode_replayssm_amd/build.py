@@ -22,7 +22,8 @@ INC = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librssm.so")
 
-SOURCES = ["api.cpp", "m2_kernels.hip", "gdn_kernels.hip", "index_kernels.hip", "prefill_kernels.hip"]
+SOURCES = ["api.cpp", "m2_kernels.hip", "gdn_kernels.hip", "index_kernels.hip", "prefill_kernels.hip",
+           "eager_spec_kernels.hip"]
 ARCH = "gfx950"
 
 

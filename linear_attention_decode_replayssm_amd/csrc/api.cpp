@@ -359,6 +359,53 @@ int rssm_eager_step(const rssm_layer* L, const rssm_inputs* in, float* out, void
   return hip_rc(rssm::launch_gdn_eager(a, S(stream)));
 }
 
+int rssm_eager_spec_round(const rssm_layer* L, int n_pos, const rssm_inputs* in, float* out,
+                          float* slots, const int32_t* cur, void* stream) {
+  int rc = check_layer_dims(L);
+  if (rc) return rc;
+  if (!in) return RSSM_EINVAL;
+  if (L->scheme != RSSM_F32) return RSSM_EUNSUPPORTED;
+  if (n_pos < 1 || n_pos > rssm::kMaxPos) return RSSM_ERANGE;
+  if (L->batch == 0) return RSSM_OK;
+  if ((rc = check_layer_ptrs(L))) return rc;
+  if (!out || !slots || !cur || !L->status) return RSSM_EINVAL;
+  if (!a16(out) || !a16(slots)) return RSSM_EALIGN;
+  if (L->kind == RSSM_MAMBA2) {
+    if (!in->x || !in->B || !in->C || !in->dt) return RSSM_EINVAL;
+    if (!a16(in->x) || !a16(in->B) || !a16(in->C)) return RSSM_EALIGN;
+    rssm::M2Args a = m2_args(L);
+    a.x = in->x;
+    a.B = in->B;
+    a.C = in->C;
+    a.dt = in->dt;
+    a.y = out;
+    a.n_pos = n_pos;
+    return hip_rc(rssm::launch_m2_eager_spec(a, slots, cur, S(stream)));
+  }
+  if (!in->q || !in->k || !in->v || !in->alpha || !in->beta) return RSSM_EINVAL;
+  if (!a16(in->q) || !a16(in->k) || !a16(in->v)) return RSSM_EALIGN;
+  rssm::GdnArgs a = gdn_args(L);
+  a.q = in->q;
+  a.k = in->k;
+  a.v = in->v;
+  a.alpha = in->alpha;
+  a.beta = in->beta;
+  a.o = out;
+  a.n_pos = n_pos;
+  return hip_rc(rssm::launch_gdn_eager_spec(a, slots, cur, S(stream)));
+}
+
+int rssm_eager_spec_accept(const rssm_layer* L, int n_pos, int32_t* cur, const int32_t* n_accept,
+                           void* stream) {
+  int rc = check_layer_dims(L);
+  if (rc) return rc;
+  if (n_pos < 1 || n_pos > rssm::kMaxPos) return RSSM_ERANGE;
+  if (L->batch == 0) return RSSM_OK;
+  if (!cur || !n_accept || !L->status) return RSSM_EINVAL;
+  return hip_rc(rssm::launch_eager_spec_accept(cur, L->status, n_accept, n_pos, L->batch,
+                                                S(stream)));
+}
+
 int rssm_status(const rssm_layer* L, uint32_t* bits, void* stream) {
   if (!L || !L->status || !bits) return RSSM_EINVAL;
   uint32_t h = 0;

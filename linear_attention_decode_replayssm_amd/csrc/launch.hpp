@@ -82,6 +82,13 @@ hipError_t launch_m2_prefill(const M2Args& a, hipStream_t s);   // n_pos = promp
 hipError_t launch_gdn_append_path(const GdnArgs& a, hipStream_t s);
 hipError_t launch_gdn_prefill(const GdnArgs& a, hipStream_t s);  // n_pos = prompt tokens
 
+// eager speculative comparator: n_pos drafts, state slots [n_pos + 1][...]
+hipError_t launch_m2_eager_spec(const M2Args& a, float* slots, const int32_t* cur, hipStream_t s);
+hipError_t launch_gdn_eager_spec(const GdnArgs& a, float* slots, const int32_t* cur,
+                                 hipStream_t s);
+hipError_t launch_eager_spec_accept(int32_t* cur, uint32_t* status, const int32_t* n_accept,
+                                    int n, int batch, hipStream_t s);
+
 hipError_t launch_rollback(int64_t* pos, int32_t* len, uint32_t* status,
                            const int32_t* n_reject, int batch, hipStream_t s);
 hipError_t launch_clear_status(uint32_t* status, hipStream_t s);

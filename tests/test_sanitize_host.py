@@ -56,8 +56,9 @@ def _gpu_visible():
 def test_abi_host_code_under_sanitizers(tmp_path):
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     hipcc = os.path.join(rocm, "bin", "hipcc")
-    objs = [os.path.join(ROOT, "_build", n + ".o")
-            for n in ("m2_kernels", "gdn_kernels", "index_kernels", "prefill_kernels")]
+    from linear_attention_decode_replayssm_amd import build as hip_build
+    objs = [os.path.join(ROOT, "_build", os.path.splitext(n)[0] + ".o")
+            for n in hip_build.SOURCES if n.endswith(".hip")]
     if not os.path.exists(hipcc) or not all(os.path.exists(o) for o in objs) or \
             not os.path.exists(os.path.join(rocm, "lib", "llvm", "bin", "clang++")):
         pytest.skip("hipcc or the regular build's kernel objects are missing")

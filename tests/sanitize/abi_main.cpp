@@ -61,6 +61,18 @@ int main() {
   in.C = nullptr;
   expect(rssm_prefill(&m2, 3, &in, P(), nullptr, nullptr), RSSM_EINVAL, "prefill C");
   expect(rssm_rollback(&m2, nullptr, nullptr), RSSM_EINVAL, "rollback null");
+  in.C = P();
+  expect(rssm_eager_spec_round(&m2, 0, &in, P(), P(), nullptr, nullptr), RSSM_ERANGE, "spec 0");
+  expect(rssm_eager_spec_round(&m2, 4, &in, P(), nullptr, nullptr, nullptr), RSSM_EINVAL,
+         "spec slots");
+  bad = m2;
+  bad.scheme = RSSM_DUAL;
+  bad.lp_dtype = RSSM_BF16;
+  expect(rssm_eager_spec_round(&bad, 4, &in, P(), P(), nullptr, nullptr), RSSM_EUNSUPPORTED,
+         "spec scheme");
+  expect(rssm_eager_spec_accept(&m2, 9, nullptr, nullptr, nullptr), RSSM_ERANGE, "accept 9");
+  expect(rssm_eager_spec_accept(&m2, 4, nullptr, nullptr, nullptr), RSSM_EINVAL, "accept null");
+  in.C = nullptr;
   expect(rssm_status(nullptr, nullptr, nullptr), RSSM_EINVAL, "status null");
   rssm_layer empty = m2;
   empty.batch = 0;

@@ -263,3 +263,20 @@ def test_prefill_validates_on_host():
     assert R.rssm_prefill(_m2_desc(batch=0), 5, R.make_inputs(), None, stream=0,
                           check=False) == R.RSSM_OK
     assert R.lib().rssm_prefill(None, 5, ctypes.byref(inp), FAKE, None, None) == R.RSSM_EINVAL
+
+
+def test_eager_spec_validates_on_host():
+    L = _m2_desc(batch=4, capacity=8)
+    inp = R.make_inputs(x=FAKE, B=FAKE, C=FAKE, dt=FAKE)
+    assert R.rssm_eager_spec_round(L, 0, inp, FAKE, FAKE, FAKE, stream=0, check=False) == R.RSSM_ERANGE
+    assert R.rssm_eager_spec_round(L, 9, inp, FAKE, FAKE, FAKE, stream=0, check=False) == R.RSSM_ERANGE
+    assert R.rssm_eager_spec_round(L, 4, inp, FAKE, None, FAKE, stream=0, check=False) == R.RSSM_EINVAL
+    assert R.rssm_eager_spec_round(L, 4, inp, FAKE, FAKE + 8, FAKE, stream=0,
+                                   check=False) == R.RSSM_EALIGN
+    D = _m2_desc(batch=4, scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_BF16, ckpt_lp=FAKE)
+    assert R.rssm_eager_spec_round(D, 4, inp, FAKE, FAKE, FAKE, stream=0,
+                                   check=False) == R.RSSM_EUNSUPPORTED
+    assert R.rssm_eager_spec_accept(L, 0, FAKE, FAKE, stream=0, check=False) == R.RSSM_ERANGE
+    assert R.rssm_eager_spec_accept(L, 4, None, FAKE, stream=0, check=False) == R.RSSM_EINVAL
+    assert R.rssm_eager_spec_accept(_m2_desc(batch=0), 4, None, None, stream=0,
+                                    check=False) == R.RSSM_OK

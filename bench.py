@@ -339,6 +339,56 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     return res
 
 
+def run_gdn_spec(torch, R, syn, rounds, seed=0, pool_n=16):
+    """GDN speculative rounds at the GDN serving shape (batch 256 x 32 heads,
+    d 128): verify 4 drafts, roll back the rejected ones, commit at 8; ring
+    12.  Then the same rounds with the eager comparator."""
+    b, H, d, cap, n, commit_len = 256, 32, 128, 12, 4, 8
+    names = ("q", "k", "v", "alpha", "beta")
+    pool = syn.gdn_steps(seed, 0, pool_n, b, H, d, d)
+    dev = {k: torch.from_numpy(pool[k]).to("cuda") for k in names}
+    accept = syn.accept_counts(seed, rounds, b, n)
+    nrej = torch.from_numpy((n - accept).astype(np.int32)).to("cuda")
+    acc_d = torch.from_numpy(accept.astype(np.int32)).to("cuda")
+    out = torch.empty((n, b, H, d), dtype=torch.float32, device="cuda")
+    inp = [R.make_inputs(**{k: dev[k][(r * n) % pool_n:(r * n) % pool_n + n] for k in names})
+           for r in range(pool_n // n)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    L = R.Layer.gdn(b, H, d, d, cap)
+    torch.cuda.synchronize()
+    start.record()
+    for r in range(rounds):
+        R.rssm_verify(L, n, inp[r % len(inp)], out)
+        R.rssm_rollback(L, nrej[r])
+        R.rssm_commit(L, None, commit_len)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    assert R.rssm_status(L) == 0
+    del L
+    torch.cuda.empty_cache()
+    L = R.Layer.gdn(b, H, d, d, cap)
+    slots = torch.zeros((n + 1, b, H, d, d), dtype=torch.float32, device="cuda")
+    cur = torch.zeros(b, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    start.record()
+    for r in range(rounds):
+        R.rssm_eager_spec_round(L, n, inp[r % len(inp)], out, slots, cur)
+        R.rssm_eager_spec_accept(L, n, cur, acc_d[r])
+    end.record()
+    torch.cuda.synchronize()
+    ems = start.elapsed_time(end)
+    assert R.rssm_status(L) == 0
+    res = dict(rounds_per_s=rounds / (ms * 1e-3),
+               accepted_seq_tok_s=float(accept.sum()) / (ms * 1e-3),
+               us_per_round=ms * 1e3 / rounds,
+               eager_rounds_per_s=rounds / (ems * 1e-3),
+               speedup_vs_eager_spec=ems / ms)
+    del L, dev, slots
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_tree_rounds(torch, R, syn, rounds, seed=0):
     """Mamba-2 headline shape, tree speculation: each round verifies a binary
     tree of 7 drafts (depth 3) from one checkpoint read, appends a random
@@ -654,6 +704,7 @@ def main():
         sec_steps = max(64, min(args.steps, 256))
         g = run_gdn(torch, R, syn, sec_steps, 16)
         sp = run_spec(torch, R, syn, 128)
+        gsp = run_gdn_spec(torch, R, syn, 128)
         du = run_dual_stack(torch, R, syn, 32)
         sw = run_m2_interval_sweep(torch, R, syn, 256)
         ml = run_m2_lowprec(torch, R, syn, 128)
@@ -665,6 +716,7 @@ def main():
         out["secondary"] = {
             "gdn_decode_b256_h32_d128": {k: round(v, 2) for k, v in g.items()},
             "mamba2_spec_rounds_b256_4drafts": {k: round(v, 1) for k, v in sp.items()},
+            "gdn_spec_rounds_b256_4drafts": {k: round(v, 1) for k, v in gsp.items()},
             "gdn_12layer_stack_seq_tok_s": {k: round(v, 1) for k, v in du.items()},
             "mamba2_commit_interval_sweep": sw,
             "mamba2_lowprec_seq_tok_s": ml,

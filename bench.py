@@ -339,6 +339,33 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     return res
 
 
+def stream_ceilings(torch, R, nbytes=671088640, reps=10):
+    """Context for the roofline fraction: what the library's streaming probe
+    (rssm_probe_stream: the replay step's workgroup shape and 16-byte
+    nontemporal loads, nothing else) moves over a buffer the size of the
+    headline checkpoint, far above the 256 MB Infinity Cache: read-only, and a
+    copy (bytes read + written per second)."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.empty(nbytes // 8192, dtype=torch.float32, device="cuda")
+    res = {}
+    for name, d, moved in (("read_gbps", None, nbytes), ("copy_gbps", dst, 2 * nbytes)):
+        R.rssm_probe_stream(src, d, sink, nbytes)
+        ev = []
+        for i in range(reps):
+            a_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record()
+            R.rssm_probe_stream(src, d, sink, nbytes)
+            e_.record()
+            ev.append((a_, e_))
+        torch.cuda.synchronize()
+        ms = float(np.median([a_.elapsed_time(e_) for a_, e_ in ev]))
+        res[name] = round(moved / (ms * 1e-3) / 1e9, 1)
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return res
+
+
 def run_gdn_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     """GDN speculative rounds at the GDN serving shape (batch 256 x 32 heads,
     d 128): verify 4 drafts, roll back the rejected ones, commit at 8; ring
@@ -700,6 +727,7 @@ def main():
                      "bytes_per_launch": int(m2["step_bytes"]),
                      "fused_commit_launch_us": round(m2["fused_us"], 3) if m2["fused_us"] else None},
     }
+    out["stream_ceilings"] = stream_ceilings(torch, R)
     if not args.no_secondary:
         sec_steps = max(64, min(args.steps, 256))
         g = run_gdn(torch, R, syn, sec_steps, 16)

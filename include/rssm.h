@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 5
+#define RSSM_ABI_VERSION 6
 #define RSSM_ARRIVE_STRIDE 32   /* uint32 elements between two sequences' counters */
 
 /* ---- host return codes ------------------------------------------------- */
@@ -343,6 +343,19 @@ int rssm_eager_spec_round(const rssm_layer* L, int n_pos, const rssm_inputs* in,
                           float* slots, const int32_t* cur, void* stream);
 int rssm_eager_spec_accept(const rssm_layer* L, int n_pos, int32_t* cur, const int32_t* n_accept,
                            void* stream);
+
+/*
+ * rssm_probe_stream -- a measurement utility, not part of the method: streams
+ * `bytes` (a multiple of 32 KiB, 16-byte aligned) from `src` with the replay
+ * step's workgroup shape and load pattern (256 threads, 32 KiB per
+ * workgroup, 16-byte nontemporal loads).  dst != NULL: copies to dst (same
+ * size and alignment).  dst == NULL: reads only and writes one float per
+ * wave to `sink` (device, bytes / 8 KiB floats).  Gives the streaming ceilings
+ * against which the state kernels' HBM fractions can be read.
+ * RSSM_EINVAL for NULL src (or sink when dst is NULL), RSSM_EALIGN, RSSM_ERANGE
+ * for a size that is not a positive multiple of 32 KiB.
+ */
+int rssm_probe_stream(const void* src, void* dst, float* sink, int64_t bytes, void* stream);
 
 /* RSSM_ABI_VERSION of the loaded library. */
 int rssm_abi_version(void);

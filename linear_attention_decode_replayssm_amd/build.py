@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librssm.so")
 
 SOURCES = ["api.cpp", "m2_kernels.hip", "gdn_kernels.hip", "index_kernels.hip", "prefill_kernels.hip",
-           "eager_spec_kernels.hip"]
+           "eager_spec_kernels.hip", "probe_kernels.hip"]
 ARCH = "gfx950"
 
 

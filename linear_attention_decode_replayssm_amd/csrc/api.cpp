@@ -406,6 +406,13 @@ int rssm_eager_spec_accept(const rssm_layer* L, int n_pos, int32_t* cur, const i
                                                 S(stream)));
 }
 
+int rssm_probe_stream(const void* src, void* dst, float* sink, int64_t bytes, void* stream) {
+  if (!src || (!dst && !sink)) return RSSM_EINVAL;
+  if (!a16(src) || (dst && !a16(dst))) return RSSM_EALIGN;
+  if (bytes <= 0 || bytes % 32768 != 0 || bytes / 32768 > (int64_t)INT32_MAX) return RSSM_ERANGE;
+  return hip_rc(rssm::launch_probe(src, dst, sink, (long)(bytes / 32768), S(stream)));
+}
+
 int rssm_status(const rssm_layer* L, uint32_t* bits, void* stream) {
   if (!L || !L->status || !bits) return RSSM_EINVAL;
   uint32_t h = 0;

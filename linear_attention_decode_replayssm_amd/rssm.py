@@ -22,7 +22,7 @@ STATUS_OVERFLOW, STATUS_ROLLBACK, STATUS_NONFINITE = 1, 2, 4
 RSSM_MAMBA2, RSSM_GDN = 1, 2
 RSSM_F32, RSSM_DUAL, RSSM_SHARED = 0, 1, 2
 RSSM_LP_NONE, RSSM_BF16, RSSM_E4M3 = 0, 1, 2
-RSSM_ABI_VERSION = 5
+RSSM_ABI_VERSION = 6
 RSSM_ARRIVE_STRIDE = 32   # uint32 elements between two sequences' arrival counters
 
 _vp = ctypes.c_void_p
@@ -78,6 +78,7 @@ def lib():
         L.rssm_eager_spec_round.argtypes = [P(rssm_layer), ctypes.c_int, P(rssm_inputs), _vp, _vp,
                                             _vp, _vp]
         L.rssm_eager_spec_accept.argtypes = [P(rssm_layer), ctypes.c_int, _vp, _vp, _vp]
+        L.rssm_probe_stream.argtypes = [_vp, _vp, _vp, ctypes.c_int64, _vp]
         L.rssm_status.argtypes = [P(rssm_layer), P(ctypes.c_uint32), _vp]
         L.rssm_strerror.argtypes = [ctypes.c_int]
         L.rssm_strerror.restype = ctypes.c_char_p
@@ -85,7 +86,7 @@ def lib():
         for f in ("rssm_mamba2_step", "rssm_gdn_step", "rssm_commit", "rssm_verify",
                   "rssm_rollback", "rssm_eager_step", "rssm_status", "rssm_verify_tree",
                   "rssm_append_path", "rssm_prefill", "rssm_eager_spec_round",
-                  "rssm_eager_spec_accept"):
+                  "rssm_eager_spec_accept", "rssm_probe_stream"):
             getattr(L, f).restype = ctypes.c_int
         if L.rssm_abi_version() != RSSM_ABI_VERSION:
             raise RuntimeError(f"{LIB_PATH} implements ABI {L.rssm_abi_version()}, this binding "
@@ -217,6 +218,13 @@ def rssm_eager_spec_accept(layer, n_pos, cur, n_accept, stream=None, check=True)
     rc = lib().rssm_eager_spec_accept(ctypes.byref(_desc(layer)), int(n_pos), _ptr(cur),
                                       _ptr(n_accept), _stream(stream))
     return _check(rc, "rssm_eager_spec_accept") if check else rc
+
+
+def rssm_probe_stream(src, dst, sink, nbytes, stream=None, check=True):
+    """Streaming probe (measurement utility): copy src -> dst, or read src and
+    write one float per wave to sink when dst is None."""
+    rc = lib().rssm_probe_stream(_ptr(src), _ptr(dst), _ptr(sink), int(nbytes), _stream(stream))
+    return _check(rc, "rssm_probe_stream") if check else rc
 
 
 def rssm_status(layer, stream=None) -> int:

@@ -60,7 +60,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert R.rssm_abi_version() == R.RSSM_ABI_VERSION == 5
+    assert R.rssm_abi_version() == R.RSSM_ABI_VERSION == 6
     for code in (0, -1, -2, -3, -4, -5):
         assert R.rssm_strerror(code)
     assert "unknown" in R.rssm_strerror(12345)
@@ -280,3 +280,12 @@ def test_eager_spec_validates_on_host():
     assert R.rssm_eager_spec_accept(L, 4, None, FAKE, stream=0, check=False) == R.RSSM_EINVAL
     assert R.rssm_eager_spec_accept(_m2_desc(batch=0), 4, None, None, stream=0,
                                     check=False) == R.RSSM_OK
+
+
+def test_probe_validates_on_host():
+    lib = R.lib()
+    assert R.rssm_probe_stream(None, None, FAKE, 32768, stream=0, check=False) == R.RSSM_EINVAL
+    assert R.rssm_probe_stream(FAKE, None, None, 32768, stream=0, check=False) == R.RSSM_EINVAL
+    assert R.rssm_probe_stream(FAKE + 4, None, FAKE, 32768, stream=0, check=False) == R.RSSM_EALIGN
+    assert R.rssm_probe_stream(FAKE, None, FAKE, 1000, stream=0, check=False) == R.RSSM_ERANGE
+    assert R.rssm_probe_stream(FAKE, None, FAKE, 0, stream=0, check=False) == R.RSSM_ERANGE

@@ -8,7 +8,11 @@ keeps the device assembly of every kernel under ``_build/isa/``.
 
 Packed fp32 instructions are disabled for all device code
 (``-target-feature -packed-fp32-ops``): the compiler would otherwise form
-them from ordinary float code.
+them from ordinary float code.  The atomic optimizer is off
+(``-amdgpu-atomic-optimizer-strategy=None``): every atomic here is issued by
+one lane, and the optimizer's lane scan reads the returned value right away,
+which makes the issuing wave wait for all of its earlier loads -- the whole
+state stream -- before it reaches the workgroup's first barrier.
 """
 import os
 import subprocess
@@ -35,6 +39,7 @@ def _hipcc():
 def _flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
             "-Wall", "-Wno-unused-function", "-I", INC, "-I", CSRC]
 
 

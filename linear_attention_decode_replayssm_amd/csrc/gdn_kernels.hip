@@ -413,16 +413,24 @@ __device__ __forceinline__ void fold_update(f32x4 (&hv)[NLD], const EntrySmem& e
   }
 }
 
-// Whole fold of L >= 1 entries (all threads; barriers inside).
+// The fold in two halves (all threads; barriers inside; L >= 1).  The first
+// needs only the entries (Gram matrix, alpha products, the triangular
+// inverse and the fold weights), so the kernels run it while the state
+// stream is still in flight; the second needs the state tile.
+template <int NTH, int ROWS>
+__device__ __forceinline__ void fold_coef(const EntrySmem& es, int L, int tid, FoldSmem<ROWS>& sm) {
+  coef_gram_g<NTH, ROWS>(es, L, tid, sm);
+  __syncthreads();
+  coef_lc<NTH, ROWS>(L, tid, sm);
+  __syncthreads();
+  coef_t<ROWS>(es, L, tid, sm);
+  __syncthreads();
+}
+
 template <int NTH, int ROWS, int NLD>
-__device__ void fold_tile(f32x4 (&hv)[NLD], const EntrySmem& es, int L, int row0, const Geo& q,
-                          FoldSmem<ROWS>& sm) {
-  coef_gram_g<NTH, ROWS>(es, L, q.tid, sm);
+__device__ __forceinline__ void fold_apply(f32x4 (&hv)[NLD], const EntrySmem& es, int L, int row0, const Geo& q,
+                           FoldSmem<ROWS>& sm) {
   fold_w<NTH, ROWS, NLD>(hv, es, L, q, sm);
-  __syncthreads();
-  coef_lc<NTH, ROWS>(L, q.tid, sm);
-  __syncthreads();
-  coef_t<ROWS>(es, L, q.tid, sm);
   __syncthreads();
   fold_u<NTH, ROWS>(es, L, row0, q.tid, sm);
   __syncthreads();
@@ -504,6 +512,11 @@ __global__ __launch_bounds__(kStepThreads) void gdn_step_kernel(GdnArgs a) {
   __shared__ __attribute__((aligned(16))) EntrySmem es;
   stash_entries<NTH>(er, ok ? L : 0, q.tid, es);
   __syncthreads();
+  // fused commit: the fold's coefficients while the stream is in flight
+  __shared__ __attribute__((aligned(16))) FoldSmem<FUSED ? ROWS : 1> sm;
+  if constexpr (FUSED) {
+    if (ok) fold_coef<NTH, ROWS>(es, L, q.tid, sm);
+  }
 
   using M = XMap<NLD, LPR>;
   const int r_out = q.row0 + M::index(q.lane, 0) * RPL + q.r0;   // this lane's output row
@@ -526,13 +539,12 @@ __global__ __launch_bounds__(kStepThreads) void gdn_step_kernel(GdnArgs a) {
   if constexpr (FUSED) {   // fold the whole buffer, this entry included, and store
     static_assert(EB == 4, "fused commit folds the fp32 checkpoint");
     if (ok) {
-      __shared__ __attribute__((aligned(16))) FoldSmem<ROWS> sm;
       f32x4 hv[NLD];
 #pragma unroll
       for (int k = 0; k < NLD; ++k)
         hv[k] = f32x4{__uint_as_float(raw[k].x), __uint_as_float(raw[k].y),
                       __uint_as_float(raw[k].z), __uint_as_float(raw[k].w)};
-      fold_tile<NTH, ROWS, NLD>(hv, es, L, q.row0, q, sm);
+      fold_apply<NTH, ROWS, NLD>(hv, es, L, q.row0, q, sm);
       store_f32_tile<RPL, NLD>(hv, a.ckpt + q.unit * (DV * DK) + q.row0 * DK, q);
     }
   } else {
@@ -580,7 +592,8 @@ __global__ __launch_bounds__(NTH) void gdn_commit_kernel(GdnArgs a) {
   stash_entries<NTH>(er, len, q.tid, es);
   __syncthreads();
   if (len > 0) {
-    fold_tile<NTH, ROWS, NLD>(hv, es, len, q.row0, q, sm);
+    fold_coef<NTH, ROWS>(es, len, q.tid, sm);   // while the state stream is in flight
+    fold_apply<NTH, ROWS, NLD>(hv, es, len, q.row0, q, sm);
     if constexpr (SCHEME != kSchemeShared) store_f32_tile<RPL, NLD>(hv, rows, q);
   }
   if constexpr (SCHEME != kSchemeF32) store_lp<LP>(hv, a, q, sm.red);

@@ -37,7 +37,13 @@ METRIC = "seq-tokens/s per SSM layer at batch 256 + HBM GB/s vs peak; speedup vs
 COUNTERS = os.path.join(ROOT, "profiles", "m2_step_counters.json")
 CALIB_COPY_BYTES = 671088640
 KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_decode_replayssm_amd", "csrc", f)
-                  for f in ("m2_kernels.hip", "common.hpp")]
+                  for f in ("m2_kernels.hip", "common.hpp", "lp_codec.hpp", "launch.hpp")] + [
+                      os.path.join(ROOT, "linear_attention_decode_replayssm_amd", "build.py")]
+
+
+def _round1(d):
+    """Round every number of a (nested) dict to one decimal."""
+    return {k: _round1(v) if isinstance(v, dict) else round(v, 1) for k, v in d.items()}
 
 
 def kernel_source_sha():
@@ -308,6 +314,42 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     del L
     torch.cuda.empty_cache()
 
+    # the same rounds with the commit folded into the next verify
+    # (rssm_verify_commit): a due buffer waits for the next round's state read,
+    # so the ring holds up to 11 entries plus the 4 drafts (16 slots)
+    L = R.Layer.mamba2(b, H, G, P, N, 16)
+    L.A.copy_(torch.from_numpy(A))
+    L.D.copy_(torch.from_numpy(D))
+    L.ckpt.copy_(torch.from_numpy(syn.m2_state0(seed, b, H, P, N)))
+    torch.cuda.synchronize()
+    start.record()
+    for r in range(rounds):
+        j = (r * n) % pool_n
+        R.rssm_verify_commit(L, n, R.make_inputs(x=dev["x"][j:j + n], B=dev["B"][j:j + n],
+                                                 C=dev["C"][j:j + n], dt=dev["dt"][j:j + n]),
+                             out, commit_len)
+        R.rssm_rollback(L, nrej[r])
+    end.record()
+    torch.cuda.synchronize()
+    fms = start.elapsed_time(end)
+    assert R.rssm_status(L) == 0
+    ln = np.zeros(b, np.int64)
+    ftotal = 0
+    for r in range(rounds):
+        com = ln >= commit_len
+        ftotal += b * (S + n * (inputs + out_b + entry)) + entry * int(ln.sum())   # verify
+        ftotal += int(com.sum()) * S                                              # fold write
+        ln[com] = 0
+        ln += accept[r]
+    res["fused_commit"] = dict(rounds_per_s=rounds / (fms * 1e-3),
+                               accepted_seq_tok_s=float(accept.sum()) / (fms * 1e-3),
+                               us_per_round=fms * 1e3 / rounds,
+                               bytes_per_round=ftotal / rounds,
+                               hbm_gbps=ftotal / (fms * 1e-3) / 1e9,
+                               speedup_vs_standalone_commit=ms / fms)
+    del L
+    torch.cuda.empty_cache()
+
     # the eager comparator on the same rounds: the state read once per round
     # and written after every draft (n + 1 state slots, accept = slot move)
     L = R.Layer.mamba2(b, H, G, P, N, cap)
@@ -341,21 +383,26 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
 
 def stream_ceilings(torch, R, nbytes=671088640, reps=10):
     """Context for the roofline fraction: what the library's streaming probe
-    (rssm_probe_stream: the replay step's workgroup shape and 16-byte
-    nontemporal loads, nothing else) moves over a buffer the size of the
-    headline checkpoint, far above the 256 MB Infinity Cache: read-only, and a
-    copy (bytes read + written per second)."""
+    moves over a buffer the size of the headline checkpoint, far above the
+    256 MB Infinity Cache: read-only, and a copy (bytes read + written per
+    second).  Two workgroup shapes (rssm_probe_stream_tiles): the replay
+    step's own (32 KiB per 256-thread workgroup, eight 16-byte nontemporal
+    loads per thread, nothing else), and 4 KiB per workgroup with one load per
+    thread (`*_4k`), the fastest pure-stream shape measured on this GPU."""
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    sink = torch.empty(nbytes // 8192, dtype=torch.float32, device="cuda")
+    sink = torch.empty(nbytes // 1024, dtype=torch.float32, device="cuda")
     res = {}
-    for name, d, moved in (("read_gbps", None, nbytes), ("copy_gbps", dst, 2 * nbytes)):
-        R.rssm_probe_stream(src, d, sink, nbytes)
+    for name, d, moved, tile in (("read_gbps", None, nbytes, 32768),
+                                 ("copy_gbps", dst, 2 * nbytes, 32768),
+                                 ("read_gbps_4k", None, nbytes, 4096),
+                                 ("copy_gbps_4k", dst, 2 * nbytes, 4096)):
+        R.rssm_probe_stream_tiles(src, d, sink, nbytes, tile, write_all=False)
         ev = []
         for i in range(reps):
             a_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a_.record()
-            R.rssm_probe_stream(src, d, sink, nbytes)
+            R.rssm_probe_stream_tiles(src, d, sink, nbytes, tile, write_all=False)
             e_.record()
             ev.append((a_, e_))
         torch.cuda.synchronize()
@@ -369,7 +416,8 @@ def stream_ceilings(torch, R, nbytes=671088640, reps=10):
 def run_gdn_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     """GDN speculative rounds at the GDN serving shape (batch 256 x 32 heads,
     d 128): verify 4 drafts, roll back the rejected ones, commit at 8; ring
-    12.  Then the same rounds with the eager comparator."""
+    12.  Then the same rounds with the commit folded into the next verify
+    (rssm_verify_commit, ring 16), and with the eager comparator."""
     b, H, d, cap, n, commit_len = 256, 32, 128, 12, 4, 8
     names = ("q", "k", "v", "alpha", "beta")
     pool = syn.gdn_steps(seed, 0, pool_n, b, H, d, d)
@@ -394,6 +442,19 @@ def run_gdn_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     assert R.rssm_status(L) == 0
     del L
     torch.cuda.empty_cache()
+    # the commit folded into the next verify (ring 16, as for Mamba-2)
+    L = R.Layer.gdn(b, H, d, d, 16)
+    torch.cuda.synchronize()
+    start.record()
+    for r in range(rounds):
+        R.rssm_verify_commit(L, n, inp[r % len(inp)], out, commit_len)
+        R.rssm_rollback(L, nrej[r])
+    end.record()
+    torch.cuda.synchronize()
+    fms = start.elapsed_time(end)
+    assert R.rssm_status(L) == 0
+    del L
+    torch.cuda.empty_cache()
     L = R.Layer.gdn(b, H, d, d, cap)
     slots = torch.zeros((n + 1, b, H, d, d), dtype=torch.float32, device="cuda")
     cur = torch.zeros(b, dtype=torch.int32, device="cuda")
@@ -409,6 +470,10 @@ def run_gdn_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     res = dict(rounds_per_s=rounds / (ms * 1e-3),
                accepted_seq_tok_s=float(accept.sum()) / (ms * 1e-3),
                us_per_round=ms * 1e3 / rounds,
+               fused_commit=dict(rounds_per_s=rounds / (fms * 1e-3),
+                                 accepted_seq_tok_s=float(accept.sum()) / (fms * 1e-3),
+                                 us_per_round=fms * 1e3 / rounds,
+                                 speedup_vs_standalone_commit=ms / fms),
                eager_rounds_per_s=rounds / (ems * 1e-3),
                speedup_vs_eager_spec=ems / ms)
     del L, dev, slots
@@ -743,8 +808,8 @@ def main():
         pg["speedup_vs_decode_steps"] = round(pg["seq_tok_s"] / g["seq_tok_s"], 2)
         out["secondary"] = {
             "gdn_decode_b256_h32_d128": {k: round(v, 2) for k, v in g.items()},
-            "mamba2_spec_rounds_b256_4drafts": {k: round(v, 1) for k, v in sp.items()},
-            "gdn_spec_rounds_b256_4drafts": {k: round(v, 1) for k, v in gsp.items()},
+            "mamba2_spec_rounds_b256_4drafts": _round1(sp),
+            "gdn_spec_rounds_b256_4drafts": _round1(gsp),
             "gdn_12layer_stack_seq_tok_s": {k: round(v, 1) for k, v in du.items()},
             "mamba2_commit_interval_sweep": sw,
             "mamba2_lowprec_seq_tok_s": ml,

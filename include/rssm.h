@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 6
+#define RSSM_ABI_VERSION 7
 #define RSSM_ARRIVE_STRIDE 32   /* uint32 elements between two sequences' counters */
 
 /* ---- host return codes ------------------------------------------------- */
@@ -224,6 +224,25 @@ int rssm_verify(const rssm_layer* L, int n_pos, const rssm_inputs* in,
                 float* out, void* stream);
 
 /*
+ * rssm_verify_commit -- rssm_verify preceded, for every sequence whose buffer
+ * holds len >= min_len entries, by the commit of those entries (explainer,
+ * "Periodically commit a new checkpoint"), both from one read of the
+ * checkpoint: the kernel folds the buffered entries into the checkpoint
+ * while it streams it for the draft outputs, so a speculative loop that
+ * commits a full buffer at its next verify reads the state once per round
+ * instead of twice in the rounds that commit.  For such a sequence
+ * ckpt_pos += len and len = n_pos afterwards (the drafts keep their ring
+ * slots); for the others len += n_pos as in rssm_verify.  Outputs, indices
+ * and checkpoints equal rssm_commit(L, NULL, min_len) followed by
+ * rssm_verify, up to fp32 rounding of the outputs.  Both layer types, F32
+ * checkpoints only (RSSM_EUNSUPPORTED otherwise); min_len >= 1 (RSSM_ERANGE);
+ * other arguments and errors as for rssm_verify (an overflowing sequence is
+ * neither committed nor appended).
+ */
+int rssm_verify_commit(const rssm_layer* L, int n_pos, const rssm_inputs* in, float* out,
+                       int min_len, void* stream);
+
+/*
  * rssm_verify_tree -- output-only verification of a tree of drafts from one
  * checkpoint read (explainer, "Why this matters for agentic systems now":
  * replay from a shared checkpoint along different input buffers, then
@@ -356,6 +375,22 @@ int rssm_eager_spec_accept(const rssm_layer* L, int n_pos, int32_t* cur, const i
  * for a size that is not a positive multiple of 32 KiB.
  */
 int rssm_probe_stream(const void* src, void* dst, float* sink, int64_t bytes, void* stream);
+
+/*
+ * rssm_probe_stream_tiles -- as rssm_probe_stream with a choice of workgroup
+ * tile: tile_bytes = 32768 is rssm_probe_stream; tile_bytes = 4096 gives every
+ * thread of a 256-thread workgroup a single 16-byte load (a pure stream whose
+ * waves live for one memory round trip; the fastest read shape measured on
+ * the MI355X, shown next to the step's own shape).  `bytes` must be a
+ * positive multiple of tile_bytes.  With dst == NULL the sink holds one float
+ * per wave (bytes / (tile_bytes / 4) floats): check != 0 writes every wave's
+ * XOR fold of its words there, as rssm_probe_stream does; check == 0 (for
+ * timing) writes only the folds that equal 0x9E3779B9, so that the read
+ * stream carries no stores.  RSSM_EUNSUPPORTED for another tile size; other
+ * errors as for rssm_probe_stream.
+ */
+int rssm_probe_stream_tiles(const void* src, void* dst, float* sink, int64_t bytes,
+                           int32_t tile_bytes, int32_t check, void* stream);
 
 /* RSSM_ABI_VERSION of the loaded library. */
 int rssm_abi_version(void);

@@ -114,12 +114,14 @@ inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 // Shared by rssm_verify (a chain: anc[j] = drafts 0..j, appended) and
 // rssm_verify_tree (ancestor masks from the parent array, nothing appended).
+// commit_min_len > 0: rssm_verify_commit (F32 checkpoints only).
 int verify_common(const rssm_layer* L, int n_pos, const uint32_t* anc, int append,
-                  const rssm_inputs* in, float* out, void* stream) {
+                  const rssm_inputs* in, float* out, void* stream, int commit_min_len = 0) {
   int rc = check_layer_dims(L);
   if (rc) return rc;
   if (!in) return RSSM_EINVAL;
   if (n_pos < 1 || n_pos > L->capacity || n_pos > rssm::kMaxPos) return RSSM_ERANGE;
+  if (commit_min_len > 0 && L->scheme != RSSM_F32) return RSSM_EUNSUPPORTED;
   if (L->batch == 0) return RSSM_OK;
   if ((rc = check_layer_ptrs(L)) || (rc = check_state(L))) return rc;
   if (!out) return RSSM_EINVAL;
@@ -136,6 +138,7 @@ int verify_common(const rssm_layer* L, int n_pos, const uint32_t* anc, int appen
     a.n_pos = n_pos;
     for (int j = 0; j < n_pos; ++j) a.anc[j] = anc[j];
     a.append = append;
+    a.min_len = commit_min_len;
     return hip_rc(rssm::launch_m2_verify(a, S(stream)));
   }
   if (!in->q || !in->k || !in->v || !in->alpha || !in->beta) return RSSM_EINVAL;
@@ -150,6 +153,7 @@ int verify_common(const rssm_layer* L, int n_pos, const uint32_t* anc, int appen
   a.n_pos = n_pos;
   for (int j = 0; j < n_pos; ++j) a.anc[j] = anc[j];
   a.append = append;
+  a.min_len = commit_min_len;
   return hip_rc(rssm::launch_gdn_verify(a, S(stream)));
 }
 
@@ -234,6 +238,14 @@ int rssm_verify(const rssm_layer* L, int n_pos, const rssm_inputs* in, float* ou
   uint32_t anc[rssm::kMaxPos] = {};
   for (int j = 0; j < rssm::kMaxPos; ++j) anc[j] = (2u << j) - 1u;   // drafts 0..j
   return verify_common(L, n_pos, anc, 1, in, out, stream);
+}
+
+int rssm_verify_commit(const rssm_layer* L, int n_pos, const rssm_inputs* in, float* out,
+                       int min_len, void* stream) {
+  if (min_len < 1) return RSSM_ERANGE;
+  uint32_t anc[rssm::kMaxPos] = {};
+  for (int j = 0; j < rssm::kMaxPos; ++j) anc[j] = (2u << j) - 1u;
+  return verify_common(L, n_pos, anc, 1, in, out, stream, min_len);
 }
 
 int rssm_verify_tree(const rssm_layer* L, int n_nodes, const int32_t* parent,
@@ -406,11 +418,26 @@ int rssm_eager_spec_accept(const rssm_layer* L, int n_pos, int32_t* cur, const i
                                                 S(stream)));
 }
 
-int rssm_probe_stream(const void* src, void* dst, float* sink, int64_t bytes, void* stream) {
+namespace {
+int probe(const void* src, void* dst, float* sink, int64_t bytes, int32_t tile_bytes, int check,
+          void* stream) {
   if (!src || (!dst && !sink)) return RSSM_EINVAL;
+  if (tile_bytes != 32768 && tile_bytes != 4096) return RSSM_EUNSUPPORTED;
   if (!a16(src) || (dst && !a16(dst))) return RSSM_EALIGN;
-  if (bytes <= 0 || bytes % 32768 != 0 || bytes / 32768 > (int64_t)INT32_MAX) return RSSM_ERANGE;
-  return hip_rc(rssm::launch_probe(src, dst, sink, (long)(bytes / 32768), S(stream)));
+  if (bytes <= 0 || bytes % tile_bytes != 0 || bytes / tile_bytes > (int64_t)INT32_MAX)
+    return RSSM_ERANGE;
+  return hip_rc(rssm::launch_probe(src, dst, sink, (long)(bytes / tile_bytes), tile_bytes,
+                                   check, S(stream)));
+}
+}  // namespace
+
+int rssm_probe_stream_tiles(const void* src, void* dst, float* sink, int64_t bytes,
+                           int32_t tile_bytes, int32_t check, void* stream) {
+  return probe(src, dst, sink, bytes, tile_bytes, check, stream);
+}
+
+int rssm_probe_stream(const void* src, void* dst, float* sink, int64_t bytes, void* stream) {
+  return probe(src, dst, sink, bytes, 32768, 1, stream);
 }
 
 int rssm_status(const rssm_layer* L, uint32_t* bits, void* stream) {

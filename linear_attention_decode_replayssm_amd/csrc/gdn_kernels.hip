@@ -614,8 +614,16 @@ __global__ __launch_bounds__(NTH) void gdn_commit_kernel(GdnArgs a) {
 // Eight fp32 drafts take ~90 registers, which leaves two workgroups per CU;
 // capped at six waves per SIMD (three workgroups, a few registers spilled)
 // the 7-draft tree verify runs ~5% faster.
-template <int EB, int NPAD>
+//
+// COMMIT (fp32 checkpoint only): a sequence whose buffer holds at least
+// a.min_len entries also folds those entries into its checkpoint from the
+// same state read (the fold's coefficients while the stream is in flight, the
+// rank-len update after the outputs); its checkpoint moves to the end of the
+// buffer and the drafts become entries 0..n-1 (the same ring slots).  The
+// outputs are those of commit-then-verify.
+template <int EB, int NPAD, bool COMMIT = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NPAD == 8 && EB == 4 ? 6 : 1))) void gdn_verify_kernel(GdnArgs a) {
+  static_assert(!COMMIT || EB == 4, "the fused commit folds the fp32 checkpoint");
   constexpr int NTH = 512, ROWS = DV;
   using Gm = LpGeo<EB, NTH, ROWS>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPL = Gm::RPL, NLD = Gm::NLD;
@@ -626,6 +634,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NPAD == 8 &
   const int len = a.len[q.b];
   const int64_t pos = a.pos[q.b];
   const bool ok = len + n <= cap;
+  const bool fold = COMMIT && ok && len > 0 && len >= a.min_len;   // uniform per sequence
   const long sk = (long)a.batch * a.H * DK;
   const long sd = (long)a.batch * a.H;
   Src src{&a, q.unit, len, (int)(pos % cap), cap, sk, sd};
@@ -648,6 +657,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NPAD == 8 &
   __shared__ float s_s[NPAD][kMaxCap];
   stash_entries<NTH>(er, ok ? len + n : 0, q.tid, es);
   __syncthreads();
+  __shared__ __attribute__((aligned(16))) FoldSmem<COMMIT ? ROWS : 1> sm;
+  if constexpr (COMMIT) {
+    if (fold) fold_coef<NTH, ROWS>(es, len, q.tid, sm);   // while the stream is in flight
+  }
 
   if (ok && w < n) {  // wave w carries draft w (2 elements per lane)
     // its path mask, read with uniform indices (kernel-argument loads), never
@@ -706,14 +719,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NPAD == 8 &
       }
     }
   }
+  if constexpr (COMMIT) {
+    if (fold) {   // the buffered entries folded into the fp32 checkpoint
+      f32x4 hv[NLD];
+#pragma unroll
+      for (int k = 0; k < NLD; ++k)
+        hv[k] = f32x4{__uint_as_float(raw[k].x), __uint_as_float(raw[k].y),
+                      __uint_as_float(raw[k].z), __uint_as_float(raw[k].w)};
+      fold_apply<NTH, ROWS, NLD>(hv, es, len, 0, q, sm);
+      store_f32_tile<RPL, NLD>(hv, a.ckpt + q.unit * (DV * DK), q);
+    }
+  }
   if (ok)
     if (a.append)
       for (int j = 0; j < n; ++j) append_from_regs<NTH>(a, src, er, len + j, q.tid);
 
   IndexUpdate u;
-  u.apply = ok && a.append;
-  u.pos_add = 0;
-  u.new_len = len + n;
+  u.apply = ok && (a.append || fold);
+  u.pos_add = fold ? len : 0;
+  u.new_len = (fold ? 0 : len) + (a.append ? n : 0);
   finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
   if (!ok && last_arrival(arrived, a.H)) raise_status(a.status, kStatusOverflow);
 }
@@ -852,21 +876,23 @@ hipError_t launch_gdn_commit(const GdnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EB>
+template <int EB, bool COMMIT = false>
 static void launch_gdn_verify_eb(const GdnArgs& a, hipStream_t s) {
   const dim3 grid = whole_grid(a), block(512);
   if (a.n_pos <= 1)
-    hipLaunchKernelGGL((gdn_verify_kernel<EB, 1>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gdn_verify_kernel<EB, 1, COMMIT>), grid, block, 0, s, a);
   else if (a.n_pos <= 2)
-    hipLaunchKernelGGL((gdn_verify_kernel<EB, 2>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gdn_verify_kernel<EB, 2, COMMIT>), grid, block, 0, s, a);
   else if (a.n_pos <= 4)
-    hipLaunchKernelGGL((gdn_verify_kernel<EB, 4>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gdn_verify_kernel<EB, 4, COMMIT>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((gdn_verify_kernel<EB, 8>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gdn_verify_kernel<EB, 8, COMMIT>), grid, block, 0, s, a);
 }
 
 hipError_t launch_gdn_verify(const GdnArgs& a, hipStream_t s) {
-  if (a.scheme == kSchemeF32)
+  if (a.min_len > 0)   // fused commit (fp32 checkpoint; checked by the caller)
+    launch_gdn_verify_eb<4, true>(a, s);
+  else if (a.scheme == kSchemeF32)
     launch_gdn_verify_eb<4>(a, s);
   else if (a.lp == kLpBf16)
     launch_gdn_verify_eb<2>(a, s);

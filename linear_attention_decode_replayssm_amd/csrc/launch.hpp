@@ -89,9 +89,10 @@ hipError_t launch_gdn_eager_spec(const GdnArgs& a, float* slots, const int32_t* 
 hipError_t launch_eager_spec_accept(int32_t* cur, uint32_t* status, const int32_t* n_accept,
                                     int n, int batch, hipStream_t s);
 
-// streaming probe: tiles x 32 KiB read (dst == NULL: one float per wave to
-// sink) or copied to dst
-hipError_t launch_probe(const void* src, void* dst, float* sink, long tiles, hipStream_t s);
+// streaming probe: tiles x tile_bytes (32768 or 4096) read (dst == NULL: one
+// float per wave to sink, every wave when check != 0) or copied to dst
+hipError_t launch_probe(const void* src, void* dst, float* sink, long tiles, int tile_bytes,
+                        int check, hipStream_t s);
 
 hipError_t launch_rollback(int64_t* pos, int32_t* len, uint32_t* status,
                            const int32_t* n_reject, int batch, hipStream_t s);

@@ -450,14 +450,23 @@ __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
 // C_j before the cross-lane reduction.  As in the step kernel, every small
 // operand (the drafts' C_j, B_i segments, dt_i, x_i) is loaded before the
 // checkpoint stream, so the prologue runs while the stream is in flight.
-template <int EB, int NPAD>
+//
+// COMMIT (fp32 checkpoint only): a sequence whose buffer holds at least
+// a.min_len entries also folds those entries into its checkpoint from the
+// same read of the state -- the commit that would otherwise precede this
+// verify as a separate pass over the state -- and its checkpoint moves to the
+// end of the buffer; the drafts then sit at entries 0..n-1 of the new buffer
+// (the same ring slots).  The outputs are those of commit-then-verify.
+template <int EB, int NPAD, bool COMMIT = false>
 __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
+  static_assert(!COMMIT || EB == 4, "the fused commit folds the fp32 checkpoint");
   using Gm = RdGeo<EB>;
   const Geo q = geometry(a);
   const int cap = a.cap, n = a.n_pos;
   const int len = a.len[q.b];
   const int64_t pos = a.pos[q.b];
   const bool ok = len + n <= cap;
+  const bool fold = COMMIT && ok && len > 0 && len >= a.min_len;   // uniform per sequence
   const int LT = len + n;
   const int slot0 = (int)(pos % cap);
   const float Ah = a.A[q.h];
@@ -524,12 +533,30 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   __shared__ float s_w[NPAD][kMaxCap];
   __shared__ float s_gam[NPAD];
   __shared__ float s_yb[QD][NPAD][P];
+  // fused commit: the buffered entries' x_i and B_i, parked from the prologue
+  __shared__ __attribute__((aligned(16))) float s_xf[COMMIT ? kMaxCap : 1][P];
+  __shared__ __attribute__((aligned(16))) float s_Bf[COMMIT ? kMaxCap : 1][N];
+  __shared__ float s_fw[COMMIT ? kMaxCap : 1];
+  __shared__ float s_gbuf;
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
     const int idx = q.tid + u * NT;
     if (idx < NPAD * N) s_C[idx / N][idx % N] = cst[u];
   }
   if (sgm == 0) s_dt[ei] = dti;
+  if constexpr (COMMIT) {
+    if (fold) {   // uniform
+      if (ei < len) {
+#pragma unroll
+        for (int e = 0; e < SEG / 4; ++e) st4(&s_Bf[ei][sgm * SEG + 4 * e], bseg[e]);
+      }
+#pragma unroll
+      for (int m = 0; m < XPT; ++m) {
+        const int i = qd + m * QD;
+        if (i < len) s_xf[i][p] = xv[m];
+      }
+    }
+  }
   if (a.append) {   // uniform: the drafts' own rows, kept for the append below
     if (ei >= len && ei < LT) {
 #pragma unroll
@@ -583,6 +610,15 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
         for (int m = 0; m < Lj; ++m)
           if ((path >> m) & 1u) tot += s_dt[m];
         s_gam[j] = expf(Ah * tot);
+      }
+    }
+    if constexpr (COMMIT) {   // the commit's weights over the buffered entries
+      const int i = q.tid - NPAD * kMaxCap;
+      if (fold && i >= 0 && i < len) {
+        float suf = 0.f;
+        for (int m = i + 1; m < len; ++m) suf += s_dt[m];
+        s_fw[i] = expf(Ah * suf) * s_dt[i];
+        if (i == 0) s_gbuf = expf(Ah * (suf + s_dt[0]));
       }
     }
     __syncthreads();
@@ -665,6 +701,22 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
     }
   }
 
+  if constexpr (COMMIT) {
+    if (fold) {   // h <- Gamma_buf h_c + sum_{i<len} fw_i x_i B_i^T, from the expanded tile
+      f32x4 hv[NLD];   // the fp32 read geometry is the tile geometry
+      const float gb = s_gbuf;
+#pragma unroll
+      for (int k = 0; k < NLD; ++k) hv[k] = gb * f32x4{f[k][0], f[k][1], f[k][2], f[k][3]};
+      for (int i = 0; i < len; ++i) {
+        const f32x4 bi = ld4(&s_Bf[i][q.c4 * 4]);
+        const float w = s_fw[i];
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) hv[k] += (w * s_xf[i][k * RPL + q.r0]) * bi;
+      }
+      store_tile(a.ckpt + q.unit * (P * N), q, hv);
+    }
+  }
+
   if (ok && a.append) {   // append the drafts (a chain) from LDS
     for (int j = 0; j < n; ++j) {
       const int s = ring_slot(slot0, len + j, cap);
@@ -676,9 +728,9 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   }
 
   IndexUpdate u;
-  u.apply = ok && a.append;
-  u.pos_add = 0;
-  u.new_len = LT;
+  u.apply = ok && (a.append || fold);
+  u.pos_add = fold ? len : 0;
+  u.new_len = (fold ? 0 : len) + (a.append ? n : 0);
   finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
   if (!ok && last_arrival(arrived, a.H)) raise_status(a.status, kStatusOverflow);
 }
@@ -809,21 +861,23 @@ hipError_t launch_m2_commit(const M2Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int EB>
+template <int EB, bool COMMIT = false>
 static void launch_m2_verify_eb(const M2Args& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.batch * a.H)), block(NT);
   if (a.n_pos <= 1)
-    hipLaunchKernelGGL((m2_verify_kernel<EB, 1>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((m2_verify_kernel<EB, 1, COMMIT>), grid, block, 0, s, a);
   else if (a.n_pos <= 2)
-    hipLaunchKernelGGL((m2_verify_kernel<EB, 2>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((m2_verify_kernel<EB, 2, COMMIT>), grid, block, 0, s, a);
   else if (a.n_pos <= 4)
-    hipLaunchKernelGGL((m2_verify_kernel<EB, 4>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((m2_verify_kernel<EB, 4, COMMIT>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((m2_verify_kernel<EB, 8>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((m2_verify_kernel<EB, 8, COMMIT>), grid, block, 0, s, a);
 }
 
 hipError_t launch_m2_verify(const M2Args& a, hipStream_t s) {
-  if (a.scheme == kSchemeF32)
+  if (a.min_len > 0)   // fused commit (fp32 checkpoint; checked by the caller)
+    launch_m2_verify_eb<4, true>(a, s);
+  else if (a.scheme == kSchemeF32)
     launch_m2_verify_eb<4>(a, s);
   else if (a.lp == kLpBf16)
     launch_m2_verify_eb<2>(a, s);

@@ -22,7 +22,7 @@ STATUS_OVERFLOW, STATUS_ROLLBACK, STATUS_NONFINITE = 1, 2, 4
 RSSM_MAMBA2, RSSM_GDN = 1, 2
 RSSM_F32, RSSM_DUAL, RSSM_SHARED = 0, 1, 2
 RSSM_LP_NONE, RSSM_BF16, RSSM_E4M3 = 0, 1, 2
-RSSM_ABI_VERSION = 6
+RSSM_ABI_VERSION = 7
 RSSM_ARRIVE_STRIDE = 32   # uint32 elements between two sequences' arrival counters
 
 _vp = ctypes.c_void_p
@@ -68,6 +68,8 @@ def lib():
         L.rssm_gdn_step.argtypes = [P(rssm_layer), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp]
         L.rssm_commit.argtypes = [P(rssm_layer), _vp, ctypes.c_int, _vp]
         L.rssm_verify.argtypes = [P(rssm_layer), ctypes.c_int, P(rssm_inputs), _vp, _vp]
+        L.rssm_verify_commit.argtypes = [P(rssm_layer), ctypes.c_int, P(rssm_inputs), _vp,
+                                         ctypes.c_int, _vp]
         L.rssm_rollback.argtypes = [P(rssm_layer), _vp, _vp]
         L.rssm_verify_tree.argtypes = [P(rssm_layer), ctypes.c_int, P(ctypes.c_int32),
                                        P(rssm_inputs), _vp, _vp]
@@ -79,6 +81,8 @@ def lib():
                                             _vp, _vp]
         L.rssm_eager_spec_accept.argtypes = [P(rssm_layer), ctypes.c_int, _vp, _vp, _vp]
         L.rssm_probe_stream.argtypes = [_vp, _vp, _vp, ctypes.c_int64, _vp]
+        L.rssm_probe_stream_tiles.argtypes = [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int32,
+                                              ctypes.c_int32, _vp]
         L.rssm_status.argtypes = [P(rssm_layer), P(ctypes.c_uint32), _vp]
         L.rssm_strerror.argtypes = [ctypes.c_int]
         L.rssm_strerror.restype = ctypes.c_char_p
@@ -86,7 +90,8 @@ def lib():
         for f in ("rssm_mamba2_step", "rssm_gdn_step", "rssm_commit", "rssm_verify",
                   "rssm_rollback", "rssm_eager_step", "rssm_status", "rssm_verify_tree",
                   "rssm_append_path", "rssm_prefill", "rssm_eager_spec_round",
-                  "rssm_eager_spec_accept", "rssm_probe_stream"):
+                  "rssm_eager_spec_accept", "rssm_probe_stream", "rssm_probe_stream_tiles",
+                  "rssm_verify_commit"):
             getattr(L, f).restype = ctypes.c_int
         if L.rssm_abi_version() != RSSM_ABI_VERSION:
             raise RuntimeError(f"{LIB_PATH} implements ABI {L.rssm_abi_version()}, this binding "
@@ -161,6 +166,16 @@ def rssm_verify(layer, n_pos, inputs, out, stream=None, check=True):
     return _check(rc, "rssm_verify") if check else rc
 
 
+def rssm_verify_commit(layer, n_pos, inputs, out, min_len, stream=None, check=True):
+    """rssm_verify, first folding the buffer of every sequence with len >= min_len
+    into its checkpoint from the same state read (fp32 checkpoints)."""
+    if isinstance(inputs, dict):
+        inputs = make_inputs(**inputs)
+    rc = lib().rssm_verify_commit(ctypes.byref(_desc(layer)), int(n_pos), ctypes.byref(inputs),
+                                  _ptr(out), int(min_len), _stream(stream))
+    return _check(rc, "rssm_verify_commit") if check else rc
+
+
 def rssm_verify_tree(layer, parent, inputs, out, stream=None, check=True):
     """parent: host sequence of int (parent[j] < j, -1 = below the buffer tail)."""
     if isinstance(inputs, dict):
@@ -225,6 +240,16 @@ def rssm_probe_stream(src, dst, sink, nbytes, stream=None, check=True):
     write one float per wave to sink when dst is None."""
     rc = lib().rssm_probe_stream(_ptr(src), _ptr(dst), _ptr(sink), int(nbytes), _stream(stream))
     return _check(rc, "rssm_probe_stream") if check else rc
+
+
+def rssm_probe_stream_tiles(src, dst, sink, nbytes, tile_bytes, write_all=True, stream=None,
+                            check=True):
+    """As rssm_probe_stream with a workgroup tile of tile_bytes (32768 or 4096).
+    The read-only pass writes each wave's XOR fold to sink (nbytes /
+    (tile_bytes / 4) floats) when write_all, else (timing) almost never."""
+    rc = lib().rssm_probe_stream_tiles(_ptr(src), _ptr(dst), _ptr(sink), int(nbytes),
+                                       int(tile_bytes), int(bool(write_all)), _stream(stream))
+    return _check(rc, "rssm_probe_stream_tiles") if check else rc
 
 
 def rssm_status(layer, stream=None) -> int:

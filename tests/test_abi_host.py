@@ -60,7 +60,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert R.rssm_abi_version() == R.RSSM_ABI_VERSION == 6
+    assert R.rssm_abi_version() == R.RSSM_ABI_VERSION == 7
     for code in (0, -1, -2, -3, -4, -5):
         assert R.rssm_strerror(code)
     assert "unknown" in R.rssm_strerror(12345)
@@ -282,6 +282,20 @@ def test_eager_spec_validates_on_host():
                                     check=False) == R.RSSM_OK
 
 
+def test_verify_commit_validates_on_host():
+    L = _m2_desc()
+    inp = R.make_inputs(x=FAKE, B=FAKE, C=FAKE, dt=FAKE)
+    V = R.rssm_verify_commit
+    assert V(L, 4, inp, FAKE, 0, stream=0, check=False) == R.RSSM_ERANGE
+    assert V(L, 0, inp, FAKE, 8, stream=0, check=False) == R.RSSM_ERANGE
+    assert V(_gdn_desc(scheme=R.RSSM_SHARED, lp_dtype=R.RSSM_E4M3), 4,
+             R.make_inputs(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE),
+             FAKE, 8, stream=0, check=False) == R.RSSM_EUNSUPPORTED
+    assert V(_m2_desc(scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_BF16), 4, inp, FAKE, 8, stream=0,
+             check=False) == R.RSSM_EUNSUPPORTED
+    assert V(_m2_desc(batch=1), 4, inp, FAKE + 4, 8, stream=0, check=False) == R.RSSM_EALIGN
+
+
 def test_probe_validates_on_host():
     lib = R.lib()
     assert R.rssm_probe_stream(None, None, FAKE, 32768, stream=0, check=False) == R.RSSM_EINVAL
@@ -289,3 +303,10 @@ def test_probe_validates_on_host():
     assert R.rssm_probe_stream(FAKE + 4, None, FAKE, 32768, stream=0, check=False) == R.RSSM_EALIGN
     assert R.rssm_probe_stream(FAKE, None, FAKE, 1000, stream=0, check=False) == R.RSSM_ERANGE
     assert R.rssm_probe_stream(FAKE, None, FAKE, 0, stream=0, check=False) == R.RSSM_ERANGE
+    T = R.rssm_probe_stream_tiles
+    assert T(None, None, FAKE, 4096, 4096, stream=0, check=False) == R.RSSM_EINVAL
+    assert T(FAKE, None, FAKE, 32768, 8192, stream=0, check=False) == R.RSSM_EUNSUPPORTED
+    assert T(FAKE + 4, None, FAKE, 4096, 4096, stream=0, check=False) == R.RSSM_EALIGN
+    assert T(FAKE, FAKE + 8, None, 4096, 4096, stream=0, check=False) == R.RSSM_EALIGN
+    assert T(FAKE, None, FAKE, 6144, 4096, stream=0, check=False) == R.RSSM_ERANGE
+    assert T(FAKE, None, FAKE, 4096, 32768, stream=0, check=False) == R.RSSM_ERANGE

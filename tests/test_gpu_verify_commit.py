@@ -268,3 +268,38 @@ def test_gdn_fold_matches_standalone_commit():
     for r1, r2 in zip(L1.rings, L2.rings):
         np.testing.assert_array_equal(gu.host(r1), gu.host(r2))
     assert R.rssm_status(L1) == 0 and R.rssm_status(L2) == 0
+
+
+def test_gdn_serving_shape_spec_rounds():
+    """batch 256 x 32 heads (d 128), 4 drafts, commit of buffers of 8+ at the
+    next verify, ring 16; 96 rounds.  Index trace of every sequence bit-exact
+    against the integer model; draft outputs of two sequences against the
+    oracle."""
+    rounds, n, b, H, cap, commit_len = 96, 4, 256, 32, 16, 8
+    S0 = syn.gdn_state0(38, b, H, 128, 128)
+    accept = syn.accept_counts(38, rounds, b, n)
+    pool = syn.gdn_steps(38, 0, 64, b, H, 128, 128)
+    pool_dev = {k: gu.dev(v) for k, v in pool.items()}
+    idx = (np.arange(rounds * n) % 64).reshape(rounds, n)
+    t_ = gu.torch()
+    L = gu.gdn_layer(S0, cap)
+    sel = [7, 201]
+    out = t_.empty((n, b, H, 128), dtype=t_.float32, device="cuda")
+    im = IndexModel(b, cap)
+    os_ = []
+    for r in range(rounds):
+        j0 = int(idx[r, 0])
+        R.rssm_verify_commit(L, n, {k: pool_dev[k][j0:j0 + n] for k in _GDN}, out, commit_len)
+        im.commit(min_len=commit_len)
+        assert im.append(n).all()
+        pos, ln = gu.indices(L)
+        np.testing.assert_array_equal(pos, im.pos)
+        np.testing.assert_array_equal(ln, im.len)
+        os_.append(gu.host(out[:, sel]))
+        R.rssm_rollback(L, gu.dev((n - accept[r]).astype(np.int32)))
+        im.rollback(n - accept[r])
+    sub = {k: np.ascontiguousarray(v[:, sel][idx.reshape(-1)]) for k, v in pool.items()}
+    sub = syn.stack_rounds(sub, rounds, n)
+    ref = drivers.gdn_spec_rounds(S0[sel], sub, accept[:, sel], cap, commit_len)
+    assert gu.vec_rel_err(np.array(os_), ref["o"]) <= gu.TOL_F32
+    assert R.rssm_status(L) == 0

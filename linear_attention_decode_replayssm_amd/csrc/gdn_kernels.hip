@@ -622,7 +622,7 @@ __global__ __launch_bounds__(NTH) void gdn_commit_kernel(GdnArgs a) {
 // buffer and the drafts become entries 0..n-1 (the same ring slots).  The
 // outputs are those of commit-then-verify.
 template <int EB, int NPAD, bool COMMIT = false>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((NPAD == 8 && EB == 4) || COMMIT ? 6 : 1))) void gdn_verify_kernel(GdnArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NPAD == 8 && EB == 4 && !COMMIT ? 6 : 1))) void gdn_verify_kernel(GdnArgs a) {
   static_assert(!COMMIT || EB == 4, "the fused commit folds the fp32 checkpoint");
   constexpr int NTH = 512, ROWS = DV;
   using Gm = LpGeo<EB, NTH, ROWS>;

@@ -270,7 +270,8 @@ int rssm_verify_tree(const rssm_layer* L, int n_nodes, const int32_t* parent,
  * 1 <= depth <= n_nodes <= 8 (RSSM_ERANGE).  Per sequence, a path that
  * overflows the ring or names a draft outside 0..n_nodes-1 sets
  * RSSM_STATUS_OVERFLOW and leaves the sequence unchanged.  Uses x, B, dt
- * (Mamba-2) or k, v, alpha, beta (GDN) of `in`.
+ * (Mamba-2) or k, v, alpha, beta (GDN) of `in`; x and B (k and v) are read
+ * with 16-byte accesses and must be 16-byte aligned (RSSM_EALIGN).
  */
 int rssm_append_path(const rssm_layer* L, int n_nodes, const int32_t* path,
                      const int32_t* path_len, int depth, const rssm_inputs* in,

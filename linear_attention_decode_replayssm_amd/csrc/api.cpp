@@ -307,6 +307,7 @@ int rssm_append_path(const rssm_layer* L, int n_nodes, const int32_t* path,
   if (!path || !path_len) return RSSM_EINVAL;
   if (L->kind == RSSM_MAMBA2) {
     if (!in->x || !in->B || !in->dt) return RSSM_EINVAL;
+    if (!a16(in->x) || !a16(in->B)) return RSSM_EALIGN;
     rssm::M2Args a = m2_args(L);
     a.x = in->x;
     a.B = in->B;
@@ -318,6 +319,7 @@ int rssm_append_path(const rssm_layer* L, int n_nodes, const int32_t* path,
     return hip_rc(rssm::launch_m2_append_path(a, S(stream)));
   }
   if (!in->k || !in->v || !in->alpha || !in->beta) return RSSM_EINVAL;
+  if (!a16(in->k) || !a16(in->v)) return RSSM_EALIGN;
   rssm::GdnArgs a = gdn_args(L);
   a.k = in->k;
   a.v = in->v;

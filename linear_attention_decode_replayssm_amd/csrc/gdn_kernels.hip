@@ -794,45 +794,54 @@ __global__ __launch_bounds__(LP == 0 ? kStepThreads : 512) void gdn_eager_kernel
 }
 
 // ----------------------------------------------------------- append path ----
-// As m2_append_path_kernel: one workgroup per sequence appends the drafts
-// path[b][0..path_len[b]) (k, v, alpha, beta of every head) at entries len..
-// and sets len += path_len; an overflowing or out-of-range path leaves the
+// As m2_append_path_kernel, one workgroup per (sequence, head): the head's k,
+// v, alpha and beta of the drafts path[b][0..path_len[b]) are appended at
+// entries len.. with 16-byte accesses, and the last workgroup of the sequence
+// sets len += path_len; an overflowing or out-of-range path leaves the
 // sequence unchanged and raises RSSM_STATUS_OVERFLOW.
 __global__ __launch_bounds__(256) void gdn_append_path_kernel(GdnArgs a) {
-  const int b = blockIdx.x, cap = a.cap, n = a.n_pos;
+  const int tile = tile_index();
+  const int b = tile / a.H, h = tile - b * a.H;
+  const int cap = a.cap, n = a.n_pos;
   const int len = a.len[b];
+  const int64_t pos = a.pos[b];
   const int pl = a.path_len[b];
   bool ok = pl >= 0 && pl <= a.depth && len + pl <= cap;
   for (int k = 0; ok && k < pl; ++k) {
     const int j = a.path[(long)b * a.depth + k];
     ok = j >= 0 && j < n;
   }
+  indices_consumed(len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, b, len, pos);
   if (ok) {
-    const int slot0 = (int)(a.pos[b] % cap);
+    const int slot0 = (int)(pos % cap);
+    const long unit = (long)b * a.H + h;
     const long sk = (long)a.batch * a.H * DK, sv = (long)a.batch * a.H * DV, sd = (long)a.batch * a.H;
-    for (int k = 0; k < pl; ++k) {
+    constexpr int KV = DK / 4, VV = DV / 4;   // float4 chunks of k and v
+    for (int e = threadIdx.x; e < pl * (KV + VV); e += 256) {
+      const int k = e / (KV + VV), c = e - k * (KV + VV);
       const int j = a.path[(long)b * a.depth + k];
-      const int s = ring_slot(slot0, len + k, cap);
-      for (int idx = threadIdx.x; idx < a.H * DK; idx += 256) {
-        const long unit = (long)b * a.H + idx / DK;
-        a.ring_k[(unit * cap + s) * DK + idx % DK] = a.k[j * sk + unit * DK + idx % DK];
-      }
-      for (int idx = threadIdx.x; idx < a.H * DV; idx += 256) {
-        const long unit = (long)b * a.H + idx / DV;
-        a.ring_v[(unit * cap + s) * DV + idx % DV] = a.v[j * sv + unit * DV + idx % DV];
-      }
-      for (int h = threadIdx.x; h < a.H; h += 256) {
-        const long unit = (long)b * a.H + h;
-        a.ring_a[unit * cap + s] = a.alpha[j * sd + unit];
-        a.ring_b[unit * cap + s] = a.beta[j * sd + unit];
-      }
+      const int sl = ring_slot(slot0, len + k, cap);
+      if (c < KV)
+        st4(a.ring_k + (unit * cap + sl) * DK + 4 * c, ld4(a.k + j * sk + unit * DK + 4 * c));
+      else
+        st4(a.ring_v + (unit * cap + sl) * DV + 4 * (c - KV),
+            ld4(a.v + j * sv + unit * DV + 4 * (c - KV)));
+    }
+    if (threadIdx.x < pl) {
+      const int k = threadIdx.x;
+      const int j = a.path[(long)b * a.depth + k];
+      const int sl = ring_slot(slot0, len + k, cap);
+      a.ring_a[unit * cap + sl] = a.alpha[j * sd + unit];
+      a.ring_b[unit * cap + sl] = a.beta[j * sd + unit];
     }
   }
-  __syncthreads();   // every thread has read len before it changes
-  if (threadIdx.x == 0) {
-    if (ok) a.len[b] = len + pl;
-    else raise_status(a.status, kStatusOverflow);
-  }
+  IndexUpdate u;
+  u.apply = ok;
+  u.pos_add = 0;
+  u.new_len = len + pl;
+  finish_update(a.arrive, a.pos, a.len, b, a.H, arrived, u);
+  if (!ok && last_arrival(arrived, a.H)) raise_status(a.status, kStatusOverflow);
 }
 
 }  // namespace
@@ -902,7 +911,7 @@ hipError_t launch_gdn_verify(const GdnArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gdn_append_path(const GdnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(gdn_append_path_kernel, dim3((unsigned)a.batch), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(gdn_append_path_kernel, whole_grid(a), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -738,46 +738,59 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
 // ----------------------------------------------------------- append path ----
 // Append, for every sequence b, the drafts path[b][0..path_len[b]) (indices
 // into the verify inputs) at entries len.., then len += path_len.  One
-// workgroup per sequence walks all heads, so it alone reads and writes the
-// sequence's indices.  A path that would overflow the ring, or names a draft
-// outside 0..n_pos-1, leaves the sequence unchanged and raises
-// RSSM_STATUS_OVERFLOW.
+// workgroup per (sequence, group) copies the group's B and its heads' x and dt
+// with 16-byte accesses; the workgroups of a sequence count themselves in its
+// arrival counter and the last one moves len.  A path that would overflow the
+// ring, or names a draft outside 0..n_pos-1, leaves the sequence unchanged and
+// raises RSSM_STATUS_OVERFLOW (every workgroup of the sequence sees the same
+// path and takes the same decision).
 __global__ __launch_bounds__(NT) void m2_append_path_kernel(M2Args a) {
-  const int b = blockIdx.x, cap = a.cap, n = a.n_pos;
+  const int tile = tile_index();
+  const int b = tile / a.G, g = tile - b * a.G;
+  const int cap = a.cap, n = a.n_pos;
   const int len = a.len[b];
+  const int64_t pos = a.pos[b];
   const int pl = a.path_len[b];
   bool ok = pl >= 0 && pl <= a.depth && len + pl <= cap;
   for (int k = 0; ok && k < pl; ++k) {
     const int j = a.path[(long)b * a.depth + k];
     ok = j >= 0 && j < n;
   }
+  indices_consumed(len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, b, len, pos);
   if (ok) {
-    const int slot0 = (int)(a.pos[b] % cap);
-    const long sx = (long)a.batch * a.H * P, sg = (long)a.batch * a.G * N, sd = (long)a.batch * a.H;
+    const int slot0 = (int)(pos % cap);
     const int hpg = a.H / a.G;
-    for (int k = 0; k < pl; ++k) {
+    const long sx = (long)a.batch * a.H * P, sg = (long)a.batch * a.G * N, sd = (long)a.batch * a.H;
+    const long gunit = (long)b * a.G + g;
+    const long unit0 = (long)b * a.H + (long)g * hpg;   // first head of the group
+    const int XV = hpg * (P / 4), BV = N / 4;           // float4 chunks per entry
+    for (int e = threadIdx.x; e < pl * (XV + BV); e += NT) {
+      const int k = e / (XV + BV), c = e - k * (XV + BV);
       const int j = a.path[(long)b * a.depth + k];
-      const int s = ring_slot(slot0, len + k, cap);
-      for (int idx = threadIdx.x; idx < a.H * P; idx += NT) {
-        const long unit = (long)b * a.H + idx / P;
-        a.ring_x[(unit * cap + s) * P + idx % P] = a.x[j * sx + unit * P + idx % P];
-      }
-      for (int idx = threadIdx.x; idx < a.G * N; idx += NT) {
-        const long gunit = (long)b * a.G + idx / N;
-        a.ring_B[(gunit * cap + s) * N + idx % N] = a.B[j * sg + gunit * N + idx % N];
-      }
-      for (int h = threadIdx.x; h < a.H; h += NT) {
-        const long unit = (long)b * a.H + h;
-        a.ring_dt[unit * cap + s] = a.dt[j * sd + unit];
+      const int sl = ring_slot(slot0, len + k, cap);
+      if (c < XV) {
+        const long unit = unit0 + c / (P / 4);
+        const int o = 4 * (c % (P / 4));
+        st4(a.ring_x + (unit * cap + sl) * P + o, ld4(a.x + j * sx + unit * P + o));
+      } else {
+        const int o = 4 * (c - XV);
+        st4(a.ring_B + (gunit * cap + sl) * N + o, ld4(a.B + j * sg + gunit * N + o));
       }
     }
-    (void)hpg;
+    for (int e = threadIdx.x; e < pl * hpg; e += NT) {
+      const int k = e / hpg, hh = e - k * hpg;
+      const int j = a.path[(long)b * a.depth + k];
+      const long unit = unit0 + hh;
+      a.ring_dt[unit * cap + ring_slot(slot0, len + k, cap)] = a.dt[j * sd + unit];
+    }
   }
-  __syncthreads();   // every thread has read len before it changes
-  if (threadIdx.x == 0) {
-    if (ok) a.len[b] = len + pl;
-    else raise_status(a.status, kStatusOverflow);
-  }
+  IndexUpdate u;
+  u.apply = ok;
+  u.pos_add = 0;
+  u.new_len = len + pl;
+  finish_update(a.arrive, a.pos, a.len, b, a.G, arrived, u);
+  if (!ok && last_arrival(arrived, a.G)) raise_status(a.status, kStatusOverflow);
 }
 
 // --------------------------------------------------------------- eager ----
@@ -887,7 +900,7 @@ hipError_t launch_m2_verify(const M2Args& a, hipStream_t s) {
 }
 
 hipError_t launch_m2_append_path(const M2Args& a, hipStream_t s) {
-  hipLaunchKernelGGL(m2_append_path_kernel, dim3((unsigned)a.batch), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(m2_append_path_kernel, dim3((unsigned)(a.batch * a.G)), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 

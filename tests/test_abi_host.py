@@ -249,6 +249,11 @@ def test_tree_entry_points_validate_on_host():
     assert lib.rssm_append_path(ctypes.byref(L), 4, None, FAKE, 2, ctypes.byref(inp), None) == R.RSSM_EINVAL
     L0 = _m2_desc(batch=0)
     assert lib.rssm_append_path(ctypes.byref(L0), 4, None, None, 2, ctypes.byref(inp), None) == R.RSSM_OK
+    bad = R.make_inputs(x=FAKE + 4, B=FAKE, C=FAKE, dt=FAKE)
+    assert lib.rssm_append_path(ctypes.byref(L), 4, FAKE, FAKE, 2, ctypes.byref(bad), None) == R.RSSM_EALIGN
+    G = _gdn_desc(batch=4, capacity=12)
+    badg = R.make_inputs(q=FAKE, k=FAKE, v=FAKE + 8, alpha=FAKE, beta=FAKE)
+    assert lib.rssm_append_path(ctypes.byref(G), 4, FAKE, FAKE, 2, ctypes.byref(badg), None) == R.RSSM_EALIGN
 
 
 def test_prefill_validates_on_host():

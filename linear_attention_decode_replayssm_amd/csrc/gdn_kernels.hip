@@ -482,10 +482,15 @@ constexpr int kStepRows = 64;
 // chain (index read, entry fetch, backward carry), so those take whole heads.
 template <int EB>
 constexpr int step_rows() { return EB == 4 ? kStepRows : DV; }
+// Threads per step workgroup: an E4M3 head (16 KiB) is read by 128 threads,
+// so that every thread keeps eight 16-byte loads in flight as in the fp32 and
+// bf16 steps.
+template <int EB>
+constexpr int step_threads() { return EB == 1 ? kStepThreads / 2 : kStepThreads; }
 
 template <int EB, bool FUSED>
-__global__ __launch_bounds__(kStepThreads) void gdn_step_kernel(GdnArgs a) {
-  constexpr int NTH = kStepThreads, ROWS = step_rows<EB>(), PARTS = DV / ROWS;
+__global__ __launch_bounds__(step_threads<EB>()) void gdn_step_kernel(GdnArgs a) {
+  constexpr int NTH = step_threads<EB>(), ROWS = step_rows<EB>(), PARTS = DV / ROWS;
   using Gm = LpGeo<EB, NTH, ROWS>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPL = Gm::RPL, NLD = Gm::NLD;
   const Geo q = geometry<LPR, ROWS>(a);
@@ -861,7 +866,8 @@ hipError_t launch_gdn_step(const GdnArgs& a, bool fused, hipStream_t s) {
   } else if (a.lp == kLpBf16) {
     hipLaunchKernelGGL((gdn_step_kernel<2, false>), whole_grid(a), block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((gdn_step_kernel<1, false>), whole_grid(a), block, 0, s, a);
+    hipLaunchKernelGGL((gdn_step_kernel<1, false>), whole_grid(a), dim3(step_threads<1>()), 0,
+                       s, a);
   }
   return hipGetLastError();
 }

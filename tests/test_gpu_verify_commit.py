@@ -303,3 +303,62 @@ def test_gdn_serving_shape_spec_rounds():
     ref = drivers.gdn_spec_rounds(S0[sel], sub, accept[:, sel], cap, commit_len)
     assert gu.vec_rel_err(np.array(os_), ref["o"]) <= gu.TOL_F32
     assert R.rssm_status(L) == 0
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 8])
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_every_draft_width_matches_commit_then_verify(kind, n):
+    """Every instantiated draft width (1, 2, 4 and 8 slots) of the fused
+    kernels against rssm_commit + rssm_verify on ragged buffers (lens 8, 6, 5,
+    3, 0 with min_len 5): indices and rings equal, checkpoints bitwise
+    (Mamba-2) or within fp32 rounding (GDN), outputs within the tolerance."""
+    b, H, cap, min_len, T = 5, 8, 16, 5, 8
+    nrej = gu.dev(np.array([0, 2, 3, 5, 8], np.int32))
+    t_ = gu.torch()
+    if kind == "mamba2":
+        G = 2
+        A, D = syn.m2_params(39, H)
+        h0 = syn.m2_state0(39, b, H, 64, 128)
+        st = {k: gu.dev(v) for k, v in syn.m2_steps(39, 0, T, b, H, G, 64, 128).items()}
+        dr = {k: gu.dev(v) for k, v in syn.m2_steps(39, T, n, b, H, G, 64, 128).items()}
+
+        def prepare():
+            L = gu.m2_layer(A, D, h0, G, cap)
+            y = t_.empty_like(st["x"][0])
+            for t in range(T):
+                R.rssm_mamba2_step(L, st["x"][t], st["B"][t], st["C"][t], st["dt"][t], y)
+            R.rssm_rollback(L, nrej)
+            return L
+        inp = dict(x=dr["x"], B=dr["B"], C=dr["C"], dt=dr["dt"])
+        out_like = dr["x"]
+    else:
+        S0 = syn.gdn_state0(39, b, H, 128, 128, std=0.1)
+        st = {k: gu.dev(v) for k, v in syn.gdn_steps(39, 0, T, b, H, 128, 128).items()}
+        dr = {k: gu.dev(v) for k, v in syn.gdn_steps(39, T, n, b, H, 128, 128).items()}
+
+        def prepare():
+            L = gu.gdn_layer(S0, cap)
+            o = t_.empty_like(st["v"][0])
+            for t in range(T):
+                R.rssm_gdn_step(L, *(st[k][t] for k in _GDN), o)
+            R.rssm_rollback(L, nrej)
+            return L
+        inp = {k: dr[k] for k in _GDN}
+        out_like = dr["v"]
+    L1, L2 = prepare(), prepare()
+    o1, o2 = t_.empty_like(out_like), t_.empty_like(out_like)
+    R.rssm_commit(L1, None, min_len)
+    R.rssm_verify(L1, n, inp, o1)
+    R.rssm_verify_commit(L2, n, inp, o2, min_len)
+    for a_, b_ in zip(gu.indices(L1), gu.indices(L2)):
+        np.testing.assert_array_equal(a_, b_)
+    pos, ln = gu.indices(L2)
+    assert pos.tolist() == [8, 6, 5, 0, 0] and ln.tolist() == [n, n, n, 3 + n, n]
+    if kind == "mamba2":
+        np.testing.assert_array_equal(gu.host(L1.ckpt), gu.host(L2.ckpt))
+    else:
+        assert _tile_rel(gu.host(L2.ckpt), gu.host(L1.ckpt)) <= 1e-5
+    assert gu.vec_rel_err(gu.host(o2), gu.host(o1)) <= gu.TOL_F32
+    for r1, r2 in zip(L1.rings, L2.rings):
+        np.testing.assert_array_equal(gu.host(r1), gu.host(r2))
+    assert R.rssm_status(L1) == 0 and R.rssm_status(L2) == 0

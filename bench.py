@@ -213,8 +213,16 @@ def run_gdn(torch, R, syn, steps, warmup, seed=0, pool_n=16):
     torch.cuda.synchronize()
     ems = start.elapsed_time(end)
     S, inp, entry, out = gdn_bytes(b, H, d)
+    tot = 0   # algorithmic bytes of the timed replay steps (len = t mod interval)
+    for t in range(warmup, warmup + steps):
+        ln = t % interval
+        if (t + 1) % interval == 0:   # fused commit: state read and written
+            tot += 2 * S + inp + ln * entry + out
+        else:                         # replay: state read, entry appended
+            tot += S + inp + ln * entry + entry + out
     res = dict(seq_tok_s=b * steps / (ms * 1e-3), eager_seq_tok_s=b * steps / (ems * 1e-3),
                us_per_step=ms * 1e3 / steps, eager_us=ems * 1e3 / steps,
+               hbm_gbps=tot / (ms * 1e-3) / 1e9, hbm_frac=tot / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                eager_gbps=(2 * S + inp + out) / (ems * 1e-3 / steps) / 1e9)
     res["speedup_vs_eager"] = res["seq_tok_s"] / res["eager_seq_tok_s"]
     del L, dev

@@ -170,8 +170,11 @@ typedef struct rssm_inputs {
  * reset the buffer (explainer, "Periodically commit a new checkpoint").
  * Per sequence, len + 1 > capacity sets RSSM_STATUS_OVERFLOW (y = NaN, no
  * append).  Output reads use ckpt (F32) or ckpt_lp (DUAL, SHARED; E4M3 values
- * are code * lp_scale).  commit_after is supported for F32 only
- * (RSSM_EUNSUPPORTED otherwise; use rssm_commit).
+ * are code * lp_scale).  commit_after is supported for F32 and DUAL
+ * (RSSM_EUNSUPPORTED for SHARED; use rssm_commit).  Under DUAL the committing
+ * step reads the fp32 checkpoint, which it folds anyway, and takes its output
+ * from it; afterwards ckpt_lp holds the image of the new fp32 checkpoint, as
+ * after rssm_commit.
  */
 int rssm_mamba2_step(const rssm_layer* L, const float* x, const float* B,
                      const float* C, const float* dt, float* y,
@@ -184,8 +187,8 @@ int rssm_mamba2_step(const rssm_layer* L, const float* x, const float* B,
  *   s_i = beta_i (k_i . q);  q <- alpha_i (q - s_i k_i);   o_t = S_c q + sum_i s_i v_i
  * q, k [batch][H][dk] (unit-norm is the caller's business), v [batch][H][dv],
  * alpha, beta [batch][H]; o [batch][H][dv].
- * Output reads use ckpt (F32) or ckpt_lp (DUAL, SHARED).  commit_after is
- * supported for F32 only (RSSM_EUNSUPPORTED otherwise; use rssm_commit).
+ * Output reads use ckpt (F32) or ckpt_lp (DUAL, SHARED).  commit_after as
+ * for rssm_mamba2_step (F32 and DUAL).
  */
 int rssm_gdn_step(const rssm_layer* L, const float* q, const float* k,
                   const float* v, const float* alpha, const float* beta,

@@ -180,7 +180,7 @@ int rssm_mamba2_step(const rssm_layer* L, const float* x, const float* B, const 
   int rc = check_layer_dims(L);
   if (rc) return rc;
   if (L->kind != RSSM_MAMBA2) return RSSM_EINVAL;
-  if (commit_after && L->scheme != RSSM_F32) return RSSM_EUNSUPPORTED;
+  if (commit_after && L->scheme == RSSM_SHARED) return RSSM_EUNSUPPORTED;
   if (L->batch == 0) return RSSM_OK;
   if ((rc = check_layer_ptrs(L)) || (rc = check_state(L))) return rc;
   if (!x || !B || !C || !dt || !y) return RSSM_EINVAL;
@@ -200,7 +200,7 @@ int rssm_gdn_step(const rssm_layer* L, const float* q, const float* k, const flo
   int rc = check_layer_dims(L);
   if (rc) return rc;
   if (L->kind != RSSM_GDN) return RSSM_EINVAL;
-  if (commit_after && L->scheme != RSSM_F32) return RSSM_EUNSUPPORTED;
+  if (commit_after && L->scheme == RSSM_SHARED) return RSSM_EUNSUPPORTED;
   if (L->batch == 0) return RSSM_OK;
   if ((rc = check_layer_ptrs(L)) || (rc = check_state(L))) return rc;
   if (!q || !k || !v || !alpha || !beta || !o) return RSSM_EINVAL;

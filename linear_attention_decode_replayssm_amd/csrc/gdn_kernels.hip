@@ -488,9 +488,15 @@ constexpr int step_rows() { return EB == 4 ? kStepRows : DV; }
 template <int EB>
 constexpr int step_threads() { return EB == 1 ? kStepThreads / 2 : kStepThreads; }
 
-template <int EB, bool FUSED>
-__global__ __launch_bounds__(step_threads<EB>()) void gdn_step_kernel(GdnArgs a) {
-  constexpr int NTH = step_threads<EB>(), ROWS = step_rows<EB>(), PARTS = DV / ROWS;
+// LP (fused commit of a DUAL layer): the boundary step folds and stores the
+// fp32 checkpoint as for F32, takes its output from the fp32 checkpoint, and
+// writes the low-precision image of the folded state; the per-head E4M3 scale
+// needs the whole head, so these take one 512-thread workgroup per head.
+template <int EB, bool FUSED, int LP = 0>
+__global__ __launch_bounds__((LP != 0 ? 512 : step_threads<EB>())) void gdn_step_kernel(GdnArgs a) {
+  static_assert(LP == 0 || (FUSED && EB == 4), "a low-precision image is written only by the fused commit");
+  constexpr int NTH = LP != 0 ? 512 : step_threads<EB>();
+  constexpr int ROWS = LP != 0 ? DV : step_rows<EB>(), PARTS = DV / ROWS;
   using Gm = LpGeo<EB, NTH, ROWS>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPL = Gm::RPL, NLD = Gm::NLD;
   const Geo q = geometry<LPR, ROWS>(a);
@@ -551,6 +557,7 @@ __global__ __launch_bounds__(step_threads<EB>()) void gdn_step_kernel(GdnArgs a)
                       __uint_as_float(raw[k].z), __uint_as_float(raw[k].w)};
       fold_apply<NTH, ROWS, NLD>(hv, es, L, q.row0, q, sm);
       store_f32_tile<RPL, NLD>(hv, a.ckpt + q.unit * (DV * DK) + q.row0 * DK, q);
+      if constexpr (LP != 0) store_lp<LP>(hv, a, q, sm.red);   // DUAL: re-quantise the copy
     }
   } else {
     if (ok && q.row0 == 0) append_from_regs<NTH>(a, src, er, len, q.tid);
@@ -863,6 +870,11 @@ hipError_t launch_gdn_step(const GdnArgs& a, bool fused, hipStream_t s) {
       hipLaunchKernelGGL((gdn_step_kernel<4, true>), half_grid(a), block, 0, s, a);
     else
       hipLaunchKernelGGL((gdn_step_kernel<4, false>), half_grid(a), block, 0, s, a);
+  } else if (fused) {   // DUAL (checked by the caller): fold fp32, re-quantise the copy
+    if (a.lp == kLpBf16)
+      hipLaunchKernelGGL((gdn_step_kernel<4, true, kLpBf16>), whole_grid(a), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((gdn_step_kernel<4, true, kLpE4m3>), whole_grid(a), dim3(512), 0, s, a);
   } else if (a.lp == kLpBf16) {
     hipLaunchKernelGGL((gdn_step_kernel<2, false>), whole_grid(a), block, 0, s, a);
   } else {

@@ -143,11 +143,16 @@ __device__ __forceinline__ void store_tile(float* ck, const Geo& q, const f32x4 
 // prologue (53 -> 42 us per step at batch 256 x 80 heads; two bf16 heads per
 // workgroup measured no faster than one).  B_i . C_t is shared by the heads
 // of a group and formed once.
-template <int EB, bool FUSED, int HPW = 1>
+//
+// LP (fused commit of a DUAL layer): the boundary step reads, folds and stores
+// the fp32 checkpoint as for F32, takes its output from the fp32 checkpoint it
+// reads, and then writes the low-precision image of the folded state.
+template <int EB, bool FUSED, int HPW = 1, int LP = 0>
 __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
   constexpr int ROWS = HPW * P;
   using Gm = RdGeo<EB, ROWS>;
   static_assert(!FUSED || (EB == 4 && HPW == 1), "the fused commit folds one fp32 head");
+  static_assert(LP == 0 || FUSED, "a low-precision image is written only by the fused commit");
   static_assert(HPW <= 16, "dt of head hl is loaded by lane hl of an entry's 16 lanes");
   const Geo q = geometry<HPW>(a);
   const int cap = a.cap;
@@ -318,6 +323,12 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
         for (int k = 0; k < NLD; ++k) hv[k] += (w * s_x[i][k * RPL + q.r0]) * bi;
       }
       store_tile(ck, q, hv);
+      if constexpr (LP != 0) {   // DUAL: the serving copy re-quantised from fp32
+        __shared__ float s_red[NT / 64];
+        char* lp = reinterpret_cast<char*>(a.ckpt_lp) + q.unit * (P * N) * (LP == kLpBf16 ? 2 : 1);
+        store_lp_tile<LP, NT, NLD, RPL, N>(hv, lp, a.lp_scale ? a.lp_scale + q.unit : nullptr,
+                                           a.status, q.r0, q.c4, s_red);
+      }
     }
   } else {
     if (ok) {  // append this step's entry from the registers that loaded it
@@ -848,6 +859,11 @@ hipError_t launch_m2_step(const M2Args& a, bool fused, hipStream_t s) {
       hipLaunchKernelGGL((m2_step_kernel<4, true>), grid, block, 0, s, a);
     else
       hipLaunchKernelGGL((m2_step_kernel<4, false>), grid, block, 0, s, a);
+  } else if (fused) {   // DUAL (checked by the caller): fold fp32, re-quantise the copy
+    if (a.lp == kLpBf16)
+      hipLaunchKernelGGL((m2_step_kernel<4, true, 1, kLpBf16>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((m2_step_kernel<4, true, 1, kLpE4m3>), grid, block, 0, s, a);
   } else if (a.lp == kLpBf16) {
     hipLaunchKernelGGL((m2_step_kernel<2, false>), grid, block, 0, s, a);
   } else {

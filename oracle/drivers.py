@@ -279,7 +279,7 @@ def quantize(state_f32, lp):
     raise ValueError(lp)
 
 
-def _lowprec(run, state0, T, out_shape, interval, scheme, lp):
+def _lowprec(run, state0, T, out_shape, interval, scheme, lp, fused=False):
     """Plain decode with a low-precision serving checkpoint; `run(sl, state)`
     runs the eager recurrence over steps `sl` from `state` (fp64, updated in
     place) and returns their outputs.
@@ -291,7 +291,13 @@ def _lowprec(run, state0, T, out_shape, interval, scheme, lp):
     output is served from the low-precision copy plus the buffered inputs
     (commit happens after the output of the step that fills the interval).
     The state that is quantised is first rounded to fp32, the precision in
-    which a kernel holds it."""
+    which a kernel holds it.
+
+    fused (dual only): the step that fills the interval reads the fp32-class
+    state for its fold and serves its own output from it, so that output is
+    the exact one; the other steps and the copy are unchanged."""
+    if fused and scheme != "dual":
+        raise ValueError("a fused commit serves from the fp32 state: dual only")
     exact = np.array(state0, dtype=np.float64, copy=True)
     codes, scale, val = quantize(exact.astype(np.float32), lp)
     serve = val.copy()
@@ -306,6 +312,8 @@ def _lowprec(run, state0, T, out_shape, interval, scheme, lp):
             o_exact[sl] = run(sl, exact)
             o_emul[sl] = run(sl, serve)
             if (t + 1 - start) == interval:
+                if fused:
+                    o_emul[t] = o_exact[t]
                 src = exact if scheme == "dual" else serve
                 codes, scale, val = quantize(src.astype(np.float32), lp)
                 serve = val.copy()
@@ -317,22 +325,22 @@ def _lowprec(run, state0, T, out_shape, interval, scheme, lp):
                 serve=serve)
 
 
-def gdn_lowprec(q, k, v, alpha, beta, S0, interval, scheme, lp):
+def gdn_lowprec(q, k, v, alpha, beta, S0, interval, scheme, lp, fused=False):
     """GDN plain decode with a low-precision serving checkpoint (see _lowprec).
 
     Returns dict(o_emul, o_exact, ckpt_exact [b,H,dv,dk] at the last commit,
     codes, scale (last commit), commits (step indices))."""
     def run(sl, S):
         return gdn_eager(q[sl], k[sl], v[sl], alpha[sl], beta[sl], S)
-    return _lowprec(run, S0, q.shape[0], v.shape, interval, scheme, lp)
+    return _lowprec(run, S0, q.shape[0], v.shape, interval, scheme, lp, fused)
 
 
-def m2_lowprec(A, D, x, B, C, dt, h0, interval, scheme, lp):
+def m2_lowprec(A, D, x, B, C, dt, h0, interval, scheme, lp, fused=False):
     """Mamba-2 plain decode with a low-precision serving checkpoint (see
     _lowprec); outputs under "o_emul" / "o_exact", shape of x."""
     def run(sl, h):
         return m2_eager(A, D, x[sl], B[sl], C[sl], dt[sl], h)
-    return _lowprec(run, h0, x.shape[0], x.shape, interval, scheme, lp)
+    return _lowprec(run, h0, x.shape[0], x.shape, interval, scheme, lp, fused)
 
 
 def _eager_lowprec(run, state0, T, out_shape, lp):

@@ -134,11 +134,13 @@ def test_empty_batch_accepts_null_arrays():
     assert R.rssm_gdn_step(gdn, None, None, None, None, None, None, 0, stream=0,
                            check=False) == R.RSSM_OK
     assert R.rssm_gdn_step(gdn, None, None, None, None, None, None, 1, stream=0,
-                           check=False) == R.RSSM_EUNSUPPORTED
+                           check=False) == R.RSSM_OK           # DUAL: fused commit allowed
     assert R.rssm_mamba2_step(gdn, None, None, None, None, None, 0, stream=0,
                               check=False) == R.RSSM_EINVAL
     shared = bare(R.RSSM_GDN, R.RSSM_SHARED, R.RSSM_BF16)
     assert R.rssm_eager_step(shared, none, None, stream=0, check=False) == R.RSSM_OK
+    assert R.rssm_gdn_step(shared, None, None, None, None, None, None, 1, stream=0,
+                           check=False) == R.RSSM_EUNSUPPORTED   # SHARED: no fused commit
 
 
 def test_null_layer():
@@ -205,9 +207,9 @@ def test_gdn_validation():
     L = _gdn_desc(batch=2, dim_k=64)
     assert R.rssm_gdn_step(L, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, stream=0,
                            check=False) == R.RSSM_EUNSUPPORTED
-    L = _gdn_desc(batch=2, scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_BF16)
+    L = _gdn_desc(batch=2, scheme=R.RSSM_SHARED, lp_dtype=R.RSSM_BF16)
     assert R.rssm_gdn_step(L, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, stream=0,
-                           check=False) == R.RSSM_EUNSUPPORTED       # fused needs F32
+                           check=False) == R.RSSM_EUNSUPPORTED       # fused: F32 or DUAL
     L = _gdn_desc(batch=2, scheme=R.RSSM_DUAL, lp_dtype=0)
     assert R.rssm_commit(L, None, 0, stream=0, check=False) == R.RSSM_EINVAL
     L = _gdn_desc(batch=2, scheme=R.RSSM_SHARED, lp_dtype=R.RSSM_E4M3)

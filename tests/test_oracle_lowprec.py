@@ -159,3 +159,29 @@ def test_eager_lowprec_first_step_error(lp):
     oracle.m2_eager(A, D, x, B, C, dt, h1)
     codes, scale, _ = drivers.quantize(h1.astype(np.float32), lp)
     np.testing.assert_array_equal(e["codes"], codes)
+
+
+@pytest.mark.parametrize("lp", ["bf16", "e4m3"])
+def test_fused_dual_commit_serves_the_boundary_step_exactly(lp):
+    """With the commit fused into the step that fills the interval, that step
+    reads the fp32-class state and its output is the exact one; every other
+    step and the serving copy are those of the standalone commit.  Closed
+    form on the boundary step: a lossless state keeps everything exact, and
+    the unfused emulation already agrees with the fused one off the
+    boundary; the fused error at the boundary is exactly zero."""
+    rng = np.random.default_rng(104)
+    T, b, H, G, interval = 18, 2, 4, 2, 6
+    A = -np.exp(rng.uniform(np.log(0.5), np.log(4.0), H))
+    D = rng.standard_normal(H)
+    h0 = rng.standard_normal((b, H, P, N)) * 0.3
+    x, B, C, dt = _inputs(rng, T, b, H, G)
+    plain = drivers.m2_lowprec(A, D, x, B, C, dt, h0, interval, "dual", lp)
+    fused = drivers.m2_lowprec(A, D, x, B, C, dt, h0, interval, "dual", lp, fused=True)
+    boundary = np.zeros(T, bool)
+    boundary[interval - 1::interval] = True
+    np.testing.assert_array_equal(fused["o_emul"][~boundary], plain["o_emul"][~boundary])
+    np.testing.assert_array_equal(fused["o_emul"][boundary], fused["o_exact"][boundary])
+    assert np.abs(plain["o_emul"][boundary] - plain["o_exact"][boundary]).max() > 0
+    np.testing.assert_array_equal(fused["codes"], plain["codes"])
+    with pytest.raises(ValueError):
+        drivers.m2_lowprec(A, D, x, B, C, dt, h0, interval, "shared", lp, fused=True)

@@ -602,7 +602,10 @@ def run_prefill(torch, R, syn, kind, T=512, reps=5, seed=0, pool_n=64):
 
 def run_dual_stack(torch, R, syn, steps, seed=0, layers=12, pool_n=8):
     """12 GDN layers at batch 256 with a low-precision serving checkpoint,
-    standalone commit every 8 steps; seq-tokens/s through the whole stack."""
+    commit every 8 steps; seq-tokens/s through the whole stack.  DUAL layers
+    fold in the step that fills the interval (commit_after; that step reads
+    fp32), also measured with the standalone commit (`*_standalone`); SHARED
+    layers commit standalone (the fused commit needs the fp32 checkpoint)."""
     b, H, d, interval, cap = 256, 32, 128, 8, 8
     pool = syn.gdn_steps(seed, 0, pool_n, b, H, d, d)
     dev = {k: torch.from_numpy(v).to("cuda") for k, v in pool.items()}
@@ -610,7 +613,9 @@ def run_dual_stack(torch, R, syn, steps, seed=0, layers=12, pool_n=8):
     o = torch.empty((b, H, d), dtype=torch.float32, device="cuda")
     res = {}
     inputs = [R.make_inputs(**{s: dev[s][j] for s in names}) for j in range(pool_n)]
-    for scheme, sname in ((R.RSSM_DUAL, "dual"), (R.RSSM_SHARED, "shared"), (None, "eager_lp")):
+    for scheme, sname, fused in ((R.RSSM_DUAL, "dual", True),
+                                 (R.RSSM_DUAL, "dual_standalone", False),
+                                 (R.RSSM_SHARED, "shared", False), (None, "eager_lp", False)):
         for lp, lname in ((R.RSSM_BF16, "bf16"), (R.RSSM_E4M3, "e4m3")):
             Ls = [R.Layer.gdn(b, H, d, d, cap, lp_dtype=lp,
                               scheme=R.RSSM_SHARED if scheme is None else scheme)
@@ -627,15 +632,18 @@ def run_dual_stack(torch, R, syn, steps, seed=0, layers=12, pool_n=8):
                     if scheme is None:        # eager comparator: the state lives in low precision
                         R.rssm_eager_step(L, inputs[j], o)
                         continue
-                    R.rssm_gdn_step(L, *(dev[s][j] for s in names), o)
-                    if (t + 1) % interval == 0:
+                    boundary = (t + 1) % interval == 0
+                    R.rssm_gdn_step(L, *(dev[s][j] for s in names), o,
+                                    commit_after=fused and boundary)
+                    if boundary and not fused:
                         R.rssm_commit(L, None, 0)
             end.record()
             torch.cuda.synchronize()
             ms = start.elapsed_time(end)
             for L in Ls:
                 assert R.rssm_status(L) == 0
-            res[f"{sname}_{lname}"] = b * steps / (ms * 1e-3)
+            key = f"dual_{lname}_standalone" if sname == "dual_standalone" else f"{sname}_{lname}"
+            res[key] = b * steps / (ms * 1e-3)
             del Ls
             torch.cuda.empty_cache()
     return res
@@ -645,7 +653,8 @@ def run_m2_lowprec(torch, R, syn, steps, seed=0, pool_n=16):
     """Mamba-2 headline shape with a low-precision serving checkpoint (dual:
     fp32 receives the commits; shared: the copy is the only state) and the
     eager comparator whose state is stored in low precision; seq-tokens/s of
-    one layer, standalone commit every 8 steps."""
+    one layer, commit every 8 steps (fused into the step for DUAL, also
+    measured standalone; standalone for SHARED)."""
     b, H, G, P, N, interval = 256, 80, 8, 64, 128, 8
     A, D = syn.m2_params(seed, H)
     pool = syn.m2_steps(seed, 0, pool_n, b, H, G, P, N)
@@ -653,7 +662,9 @@ def run_m2_lowprec(torch, R, syn, steps, seed=0, pool_n=16):
     h0 = torch.from_numpy(syn.m2_state0(seed, b, H, P, N))
     y = torch.empty((b, H, P), dtype=torch.float32, device="cuda")
     res = {}
-    for scheme, sname in ((R.RSSM_DUAL, "dual"), (R.RSSM_SHARED, "shared"), (None, "eager_lp")):
+    for scheme, sname, fused in ((R.RSSM_DUAL, "dual", True),
+                                 (R.RSSM_DUAL, "dual_standalone", False),
+                                 (R.RSSM_SHARED, "shared", False), (None, "eager_lp", False)):
         for lp, lname in ((R.RSSM_BF16, "bf16"), (R.RSSM_E4M3, "e4m3")):
             L = R.Layer.mamba2(b, H, G, P, N, interval,
                                scheme=R.RSSM_SHARED if scheme is None else scheme, lp_dtype=lp)
@@ -671,8 +682,10 @@ def run_m2_lowprec(torch, R, syn, steps, seed=0, pool_n=16):
                     if scheme is None:
                         R.rssm_eager_step(L, inputs[j], y)
                     else:
-                        R.rssm_mamba2_step(L, dev["x"][j], dev["B"][j], dev["C"][j], dev["dt"][j], y)
-                        if (t + 1) % interval == 0:
+                        boundary = (t + 1) % interval == 0
+                        R.rssm_mamba2_step(L, dev["x"][j], dev["B"][j], dev["C"][j], dev["dt"][j], y,
+                                           commit_after=fused and boundary)
+                        if boundary and not fused:
                             R.rssm_commit(L, None, 0)
 
             run(2 * interval)
@@ -685,7 +698,8 @@ def run_m2_lowprec(torch, R, syn, steps, seed=0, pool_n=16):
             torch.cuda.synchronize()
             ms = start.elapsed_time(end)
             assert R.rssm_status(L) == 0
-            res[f"{sname}_{lname}"] = round(b * n / (ms * 1e-3), 1)
+            key = f"dual_{lname}_standalone" if sname == "dual_standalone" else f"{sname}_{lname}"
+            res[key] = round(b * n / (ms * 1e-3), 1)
             del L
             torch.cuda.empty_cache()
     del dev

@@ -812,7 +812,7 @@ def main():
         "pages_context": {
             "standard_decoding_vs_tuned_vllm_batch256": "1.20-1.47x (four hybrid models)",
             "vs_vllm_speculative_decoding": "~1.8x (two 120B-class models)"},
-        "roofline": {"bound": "hbm", "kernel": "m2_step_kernel<4, false, 1> (replay step, no commit)",
+        "roofline": {"bound": "hbm", "kernel": "m2_step_kernel<4, false, 1, 0> (replay step, no commit)",
                      "achieved": round(step_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(step_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "avg_launch_us": round(m2["step_us"], 3),

@@ -264,6 +264,23 @@ int rssm_verify_tree(const rssm_layer* L, int n_nodes, const int32_t* parent,
                      const rssm_inputs* in, float* out, void* stream);
 
 /*
+ * rssm_verify_tree_commit -- rssm_verify_tree preceded, for every sequence
+ * whose buffer holds len >= min_len entries, by the commit of those entries,
+ * both from one read of the checkpoint (as rssm_verify_commit does for a
+ * chain).  For such a sequence ckpt_pos += len and len = 0 afterwards; the
+ * caller then appends the accepted path with rssm_append_path at the new
+ * buffer's entries 0..  With a chain parent array (-1, 0, 1, ...) it serves a
+ * speculative loop that writes only the accepted drafts to the ring: no
+ * rejected draft is appended and no rollback is needed.  Outputs, indices and
+ * checkpoints equal rssm_commit(L, NULL, min_len) followed by
+ * rssm_verify_tree, up to fp32 rounding of the outputs.  F32 checkpoints only
+ * (RSSM_EUNSUPPORTED otherwise); min_len >= 1 (RSSM_ERANGE); other arguments
+ * and errors as for rssm_verify_tree (an overflowing sequence is not folded).
+ */
+int rssm_verify_tree_commit(const rssm_layer* L, int n_nodes, const int32_t* parent,
+                            const rssm_inputs* in, float* out, int min_len, void* stream);
+
+/*
  * rssm_append_path -- append, for every sequence b, the inputs of drafts
  * path[b][0 .. path_len[b]) (indices into the verify inputs `in`, leading
  * [n_nodes]) at the buffer tail, in that order: len += path_len[b].  For

@@ -248,8 +248,9 @@ int rssm_verify_commit(const rssm_layer* L, int n_pos, const rssm_inputs* in, fl
   return verify_common(L, n_pos, anc, 1, in, out, stream, min_len);
 }
 
-int rssm_verify_tree(const rssm_layer* L, int n_nodes, const int32_t* parent,
-                     const rssm_inputs* in, float* out, void* stream) {
+namespace {
+int verify_tree_common(const rssm_layer* L, int n_nodes, const int32_t* parent,
+                       const rssm_inputs* in, float* out, void* stream, int min_len) {
   if (!parent) return RSSM_EINVAL;
   if (n_nodes < 1 || n_nodes > rssm::kMaxPos) return RSSM_ERANGE;
   uint32_t anc[rssm::kMaxPos] = {};
@@ -257,7 +258,19 @@ int rssm_verify_tree(const rssm_layer* L, int n_nodes, const int32_t* parent,
     if (parent[j] < -1 || parent[j] >= j) return RSSM_EINVAL;   // parents come first
     anc[j] = (1u << j) | (parent[j] >= 0 ? anc[parent[j]] : 0u);
   }
-  return verify_common(L, n_nodes, anc, 0, in, out, stream);
+  return verify_common(L, n_nodes, anc, 0, in, out, stream, min_len);
+}
+}  // namespace
+
+int rssm_verify_tree(const rssm_layer* L, int n_nodes, const int32_t* parent,
+                     const rssm_inputs* in, float* out, void* stream) {
+  return verify_tree_common(L, n_nodes, parent, in, out, stream, 0);
+}
+
+int rssm_verify_tree_commit(const rssm_layer* L, int n_nodes, const int32_t* parent,
+                            const rssm_inputs* in, float* out, int min_len, void* stream) {
+  if (min_len < 1) return RSSM_ERANGE;
+  return verify_tree_common(L, n_nodes, parent, in, out, stream, min_len);
 }
 
 int rssm_prefill(const rssm_layer* L, int n_tok, const rssm_inputs* in, float* out,

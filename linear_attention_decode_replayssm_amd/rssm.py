@@ -73,6 +73,8 @@ def lib():
         L.rssm_rollback.argtypes = [P(rssm_layer), _vp, _vp]
         L.rssm_verify_tree.argtypes = [P(rssm_layer), ctypes.c_int, P(ctypes.c_int32),
                                        P(rssm_inputs), _vp, _vp]
+        L.rssm_verify_tree_commit.argtypes = [P(rssm_layer), ctypes.c_int, P(ctypes.c_int32),
+                                              P(rssm_inputs), _vp, ctypes.c_int, _vp]
         L.rssm_append_path.argtypes = [P(rssm_layer), ctypes.c_int, _vp, _vp, ctypes.c_int,
                                        P(rssm_inputs), _vp]
         L.rssm_prefill.argtypes = [P(rssm_layer), ctypes.c_int, P(rssm_inputs), _vp, _vp, _vp]
@@ -91,7 +93,7 @@ def lib():
                   "rssm_rollback", "rssm_eager_step", "rssm_status", "rssm_verify_tree",
                   "rssm_append_path", "rssm_prefill", "rssm_eager_spec_round",
                   "rssm_eager_spec_accept", "rssm_probe_stream", "rssm_probe_stream_tiles",
-                  "rssm_verify_commit"):
+                  "rssm_verify_commit", "rssm_verify_tree_commit"):
             getattr(L, f).restype = ctypes.c_int
         if L.rssm_abi_version() != RSSM_ABI_VERSION:
             raise RuntimeError(f"{LIB_PATH} implements ABI {L.rssm_abi_version()}, this binding "
@@ -185,6 +187,19 @@ def rssm_verify_tree(layer, parent, inputs, out, stream=None, check=True):
     rc = lib().rssm_verify_tree(ctypes.byref(_desc(layer)), n, arr, ctypes.byref(inputs),
                                 _ptr(out), _stream(stream))
     return _check(rc, "rssm_verify_tree") if check else rc
+
+
+def rssm_verify_tree_commit(layer, parent, inputs, out, min_len, stream=None, check=True):
+    """rssm_verify_tree, first folding the buffer of every sequence with
+    len >= min_len into its checkpoint from the same state read (fp32
+    checkpoints); nothing is appended."""
+    if isinstance(inputs, dict):
+        inputs = make_inputs(**inputs)
+    n = len(parent)
+    arr = (ctypes.c_int32 * max(n, 1))(*[int(p) for p in parent])
+    rc = lib().rssm_verify_tree_commit(ctypes.byref(_desc(layer)), n, arr, ctypes.byref(inputs),
+                                       _ptr(out), int(min_len), _stream(stream))
+    return _check(rc, "rssm_verify_tree_commit") if check else rc
 
 
 def rssm_append_path(layer, n_nodes, path, path_len, inputs, stream=None, check=True):

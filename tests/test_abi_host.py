@@ -303,6 +303,17 @@ def test_verify_commit_validates_on_host():
     assert V(_m2_desc(batch=1), 4, inp, FAKE + 4, 8, stream=0, check=False) == R.RSSM_EALIGN
 
 
+def test_verify_tree_commit_validates_on_host():
+    L = _m2_desc()
+    inp = R.make_inputs(x=FAKE, B=FAKE, C=FAKE, dt=FAKE)
+    V = R.rssm_verify_tree_commit
+    assert V(L, [-1, 0], inp, FAKE, 0, stream=0, check=False) == R.RSSM_ERANGE
+    assert V(L, [-1, 1], inp, FAKE, 8, stream=0, check=False) == R.RSSM_EINVAL
+    assert V(_m2_desc(scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_BF16), [-1, 0], inp, FAKE, 8, stream=0,
+             check=False) == R.RSSM_EUNSUPPORTED
+    assert V(L, [-1, 0], inp, FAKE, 8, stream=0, check=False) == R.RSSM_OK       # batch 0
+
+
 def test_probe_validates_on_host():
     lib = R.lib()
     assert R.rssm_probe_stream(None, None, FAKE, 32768, stream=0, check=False) == R.RSSM_EINVAL

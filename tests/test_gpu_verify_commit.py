@@ -362,3 +362,99 @@ def test_every_draft_width_matches_commit_then_verify(kind, n):
     for r1, r2 in zip(L1.rings, L2.rings):
         np.testing.assert_array_equal(gu.host(r1), gu.host(r2))
     assert R.rssm_status(L1) == 0 and R.rssm_status(L2) == 0
+
+
+# ------------------------------------------------------------ draft trees --
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_tree_commit_matches_commit_then_tree(kind):
+    """rssm_verify_tree_commit against rssm_commit + rssm_verify_tree on
+    ragged buffers (lens 9, 6, 5, 3, 0; min_len 5) with a binary tree of 7
+    drafts: indices equal (nothing appended; folded sequences end with len
+    0), checkpoints bitwise (Mamba-2) or within fp32 rounding (GDN), outputs
+    within the tolerance."""
+    b, H, cap, min_len, T = 5, 8, 16, 5, 9
+    parent = [-1, 0, 0, 1, 1, 2, 2]
+    n = len(parent)
+    nrej = gu.dev(np.array([0, 3, 4, 6, 9], np.int32))
+    t_ = gu.torch()
+    if kind == "mamba2":
+        G = 2
+        A, D = syn.m2_params(42, H)
+        h0 = syn.m2_state0(42, b, H, 64, 128)
+        st = {k: gu.dev(v) for k, v in syn.m2_steps(42, 0, T, b, H, G, 64, 128).items()}
+        dr = {k: gu.dev(v) for k, v in syn.m2_steps(42, T, n, b, H, G, 64, 128).items()}
+
+        def prepare():
+            L = gu.m2_layer(A, D, h0, G, cap)
+            y = t_.empty_like(st["x"][0])
+            for t in range(T):
+                R.rssm_mamba2_step(L, st["x"][t], st["B"][t], st["C"][t], st["dt"][t], y)
+            R.rssm_rollback(L, nrej)
+            return L
+        inp = dict(x=dr["x"], B=dr["B"], C=dr["C"], dt=dr["dt"])
+        out_like = dr["x"]
+    else:
+        S0 = syn.gdn_state0(42, b, H, 128, 128, std=0.1)
+        st = {k: gu.dev(v) for k, v in syn.gdn_steps(42, 0, T, b, H, 128, 128).items()}
+        dr = {k: gu.dev(v) for k, v in syn.gdn_steps(42, T, n, b, H, 128, 128).items()}
+
+        def prepare():
+            L = gu.gdn_layer(S0, cap)
+            o = t_.empty_like(st["v"][0])
+            for t in range(T):
+                R.rssm_gdn_step(L, *(st[k][t] for k in _GDN), o)
+            R.rssm_rollback(L, nrej)
+            return L
+        inp = {k: dr[k] for k in _GDN}
+        out_like = dr["v"]
+    L1, L2 = prepare(), prepare()
+    o1, o2 = t_.empty_like(out_like), t_.empty_like(out_like)
+    R.rssm_commit(L1, None, min_len)
+    R.rssm_verify_tree(L1, parent, inp, o1)
+    R.rssm_verify_tree_commit(L2, parent, inp, o2, min_len)
+    for a_, b_ in zip(gu.indices(L1), gu.indices(L2)):
+        np.testing.assert_array_equal(a_, b_)
+    pos, ln = gu.indices(L2)
+    assert pos.tolist() == [9, 6, 5, 0, 0] and ln.tolist() == [0, 0, 0, 3, 0]
+    if kind == "mamba2":
+        np.testing.assert_array_equal(gu.host(L1.ckpt), gu.host(L2.ckpt))
+    else:
+        assert _tile_rel(gu.host(L2.ckpt), gu.host(L1.ckpt)) <= 1e-5
+    assert gu.vec_rel_err(gu.host(o2), gu.host(o1)) <= gu.TOL_F32
+    assert R.rssm_status(L1) == 0 and R.rssm_status(L2) == 0
+
+
+def test_chain_as_tree_appends_only_accepted_drafts():
+    """A speculative loop that writes only accepted drafts to the ring: each
+    round verifies 4 drafts as a chain-shaped tree, folding a buffer of 8+
+    from the same state read (rssm_verify_tree_commit), then appends the
+    accepted prefix (rssm_append_path); no rollback.  Index trace bit-exact
+    against the integer model, draft outputs against the oracle."""
+    rounds, n, b, H, G, cap, commit_len = 40, 4, 8, 8, 2, 16, 8
+    A, D = syn.m2_params(43, H)
+    h0 = syn.m2_state0(43, b, H, 64, 128)
+    drafts = _drafts(43, rounds, n, b, H, G)
+    accept = syn.accept_counts(43, rounds, b, n)
+    d = {k: gu.dev(v) for k, v in drafts.items()}
+    L = gu.m2_layer(A, D, h0, G, cap)
+    out = gu.torch().empty_like(d["x"][0])
+    path = gu.dev(np.tile(np.arange(n, dtype=np.int32), (b, 1)))
+    im = IndexModel(b, cap)
+    ys = []
+    for r in range(rounds):
+        inp = dict(x=d["x"][r], B=d["B"][r], C=d["C"][r], dt=d["dt"][r])
+        R.rssm_verify_tree_commit(L, list(range(-1, n - 1)), inp, out, commit_len)
+        R.rssm_append_path(L, n, path, gu.dev(accept[r].astype(np.int32)), inp)
+        im.commit(min_len=commit_len)
+        im.append(n)
+        im.rollback(n - accept[r])
+        pos, ln = gu.indices(L)
+        np.testing.assert_array_equal(pos, im.pos)
+        np.testing.assert_array_equal(ln, im.len)
+        ys.append(gu.host(out))
+    ref = drivers.m2_spec_rounds(A, D, h0, drafts, accept, cap, commit_len)
+    gu.check_m2_outputs(np.array(ys), ref["y"], drafts["x"], D)
+    R.rssm_commit(L, None, 1)
+    assert _tile_rel(gu.host(L.ckpt), ref["state"]) <= 1e-4
+    assert R.rssm_status(L) == 0

@@ -30,6 +30,11 @@
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
  *    null stream) and is asynchronous.  Calls on one layer must be ordered
  *    on one stream; distinct layers may be driven concurrently.
+ *  - Apart from rssm_status, a call enqueues kernel launches and nothing else
+ *    (no memset, copy or allocation), and the arrival counters are back at
+ *    zero when each launch ends.  A sequence of calls may therefore be
+ *    captured into a HIP graph on `stream` and replayed; the replay reads the
+ *    captured pointers, so new inputs are written into the same buffers.
  *  - Row-major layouts, innermost index contiguous.  Tensors read or written
  *    with 16-byte vector accesses must be 16-byte aligned (EALIGN otherwise).
  *  - batch == 0 is valid: the call validates the descriptor's enums,

@@ -43,9 +43,11 @@
  *  - Return codes (host-detected, returned before any launch, no side
  *    effects) are the RSSM_E* values below.  Errors that depend on device
  *    data (per-sequence buffer lengths) are reported through the layer's
- *    sticky `status` word instead.  For ring overflow and rollback past the
- *    checkpoint the offending sequence is left unchanged (no append, no
- *    index change) and its outputs are written as quiet NaN.
+ *    sticky `status` word instead.  For ring overflow, rollback past the
+ *    checkpoint and unusable indices (RSSM_STATUS_INDEX, checked by every
+ *    call that reads them) the offending sequence is left unchanged (no
+ *    append, no fold, no index change) and its outputs are written as quiet
+ *    NaN (commit and prefill leave their outputs and state untouched).
  */
 #ifndef RSSM_H
 #define RSSM_H
@@ -56,7 +58,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 7
+#define RSSM_ABI_VERSION 8
 #define RSSM_ARRIVE_STRIDE 32   /* uint32 elements between two sequences' counters */
 
 /* ---- host return codes ------------------------------------------------- */
@@ -71,6 +73,8 @@ extern "C" {
 #define RSSM_STATUS_OVERFLOW  1u /* an append would exceed `capacity` entries       */
 #define RSSM_STATUS_ROLLBACK  2u /* n_reject < 0 or n_reject > len (past checkpoint)*/
 #define RSSM_STATUS_NONFINITE 4u /* non-finite state met while quantising to E4M3   */
+#define RSSM_STATUS_INDEX     8u /* a sequence's indices are unusable: len < 0,      */
+                                 /* len > capacity or ckpt_pos < 0                   */
 /* On RSSM_STATUS_NONFINITE the head's E4M3 scale is set to 1 and its codes
  * saturate (+-inf -> +-448, NaN stays NaN); the fp32 checkpoint and the
  * indices are updated as for any commit or prefill.  bf16 copies carry inf
@@ -130,8 +134,9 @@ typedef enum {
  *   arrive    uint32 [batch][RSSM_ARRIVE_STRIDE] scratch counters (element
  *             [b][0] is sequence b's; one 128-byte line per sequence, because
  *             atomics to one line are serialised); must be zero before the
- *             first call and are left zero by every call (the last workgroup
- *             of a sequence to finish updates its indices)
+ *             first call and are left zero by every call, whatever the
+ *             indices hold (the last workgroup of a sequence to finish
+ *             updates its indices)
  *   status    uint32 [1]     sticky RSSM_STATUS_* bits
  */
 typedef struct rssm_layer {

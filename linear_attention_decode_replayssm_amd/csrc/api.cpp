@@ -352,7 +352,7 @@ int rssm_rollback(const rssm_layer* L, const int32_t* n_reject, void* stream) {
   if ((rc = check_layer_ptrs(L)) || (rc = check_state(L))) return rc;
   if (!n_reject) return RSSM_EINVAL;
   return hip_rc(rssm::launch_rollback(L->ckpt_pos, L->len, L->status, n_reject, L->batch,
-                                      S(stream)));
+                                      L->capacity, S(stream)));
 }
 
 int rssm_eager_step(const rssm_layer* L, const rssm_inputs* in, float* out, void* stream) {

@@ -25,6 +25,15 @@ constexpr int kArriveStride = 32;
 constexpr uint32_t kStatusOverflow = 1u;
 constexpr uint32_t kStatusRollback = 2u;
 constexpr uint32_t kStatusNonfinite = 4u;
+constexpr uint32_t kStatusIndex = 8u;
+
+// A sequence's indices can be used when 0 <= len <= cap and ckpt_pos >= 0.
+// Anything else (indices the library never wrote) is refused: the sequence is
+// left as it is, its outputs are NaN and kStatusIndex is raised, so that no
+// ring slot outside the sequence's own is ever addressed.
+__device__ __forceinline__ bool indices_valid(int32_t len, int64_t pos, int cap) {
+  return len >= 0 && len <= cap && pos >= 0;
+}
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
@@ -198,16 +207,20 @@ __device__ __forceinline__ void indices_consumed(int32_t len, int64_t pos) {
 
 // Early variant: count the workgroup right after its index reads, so that the
 // atomic's round trip overlaps the state stream instead of ending the
-// workgroup.  The increment is computed from the values read (it is 1 for
-// every valid index: len >= 0, pos >= 0), so the atomic cannot be performed
-// before those reads have returned; once the count is complete every
-// workgroup of the sequence holds its copy of the indices and the last one
-// may update them at any time.  Returns the pre-increment count (thread 0).
+// workgroup.  The increment is always 1, so the count of a sequence always
+// reaches nwg and its counter returns to zero, whatever the indices hold.  It
+// passes through an empty asm statement that takes the index values as
+// inputs: the compiler must wait for their loads before it and cannot tell
+// that the increment is unchanged, so the atomic is not issued before those
+// reads have returned.  Once the count is complete every workgroup of the
+// sequence holds its copy of the indices and the last one may update them at
+// any time.  Returns the pre-increment count (thread 0).
 __device__ __forceinline__ uint32_t arrive_early(uint32_t* arrive, int b, int32_t len,
                                                  int64_t pos) {
   uint32_t old = 0u;
   if (threadIdx.x == 0) {
-    const uint32_t inc = 1u + (uint32_t)(len < 0) + (uint32_t)(pos < 0);
+    uint32_t inc = 1u;
+    asm volatile("" : "+v"(inc) : "v"(len), "v"((uint32_t)pos), "v"((uint32_t)(pos >> 32)));
     old = __hip_atomic_fetch_add(&arrive[(long)b * kArriveStride], inc, __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
   }

@@ -504,9 +504,10 @@ __global__ __launch_bounds__((LP != 0 ? 512 : step_threads<EB>())) void gdn_step
 
   const int len = a.len[q.b];
   const int64_t pos = a.pos[q.b];
-  const bool ok = len < cap;
+  const bool valid = indices_valid(len, pos, cap);
+  const bool ok = valid && len < cap;
   const int L = len + 1;
-  Src src{&a, q.unit, len, (int)(pos % cap), cap, 0, 0};
+  Src src{&a, q.unit, len, valid ? (int)(pos % cap) : 0, cap, 0, 0};
   const float scale = (EB == 1) ? a.lp_scale[q.unit] : 1.f;
 
   EntryRegs<NTH> er = fetch_entries<NTH>(src, ok ? L : 0, q.tid);
@@ -568,7 +569,8 @@ __global__ __launch_bounds__((LP != 0 ? 512 : step_threads<EB>())) void gdn_step
   u.pos_add = FUSED ? L : 0;
   u.new_len = FUSED ? 0 : L;
   finish_update(a.arrive, a.pos, a.len, q.b, a.H * PARTS, arrived, u);
-  if (!ok && last_arrival(arrived, a.H * PARTS)) raise_status(a.status, kStatusOverflow);
+  if (!ok && last_arrival(arrived, a.H * PARTS))
+    raise_status(a.status, valid ? kStatusOverflow : kStatusIndex);
 }
 
 // -------------------------------------------------------------- commit ----
@@ -582,13 +584,15 @@ __global__ __launch_bounds__(NTH) void gdn_commit_kernel(GdnArgs a) {
   constexpr int RPL = Gm::RPL, NLD = Gm::NLD;
   static_assert(SCHEME == kSchemeF32 || ROWS == DV, "low-precision copies need whole heads");
   const Geo q = geometry<Gm::LPR, ROWS>(a);
+  if (a.mask != nullptr && a.mask[q.b] == 0) return;   // uniform for the sequence
   const int len = a.len[q.b];
-  const bool sel = (a.mask == nullptr || a.mask[q.b] != 0) && len >= a.min_len;
-  if (!sel) return;                         // uniform for the whole sequence
-  if (len == 0 && SCHEME != kSchemeDual) {  // nothing to fold, nothing to refresh
+  const int64_t pos = a.pos[q.b];
+  if (!indices_valid(len, pos, a.cap)) {    // refused: nothing read, written or counted
+    if (q.h == 0 && q.row0 == 0 && q.tid == 0) raise_status(a.status, kStatusIndex);
     return;
   }
-  const int64_t pos = a.pos[q.b];
+  // not due, or nothing to fold and nothing to refresh
+  if (len < a.min_len || (len == 0 && SCHEME != kSchemeDual)) return;
   Src src{&a, q.unit, len, (int)(pos % a.cap), a.cap, 0, 0};
   EntryRegs<NTH> er = fetch_entries<NTH>(src, len, q.tid);
   float* rows = a.ckpt + q.unit * (DV * DK) + q.row0 * DK;
@@ -645,11 +649,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NPAD == 8 &
 
   const int len = a.len[q.b];
   const int64_t pos = a.pos[q.b];
-  const bool ok = len + n <= cap;
+  const bool valid = indices_valid(len, pos, cap);
+  const bool ok = valid && len + n <= cap;
   const bool fold = COMMIT && ok && len > 0 && len >= a.min_len;   // uniform per sequence
   const long sk = (long)a.batch * a.H * DK;
   const long sd = (long)a.batch * a.H;
-  Src src{&a, q.unit, len, (int)(pos % cap), cap, sk, sd};
+  Src src{&a, q.unit, len, valid ? (int)(pos % cap) : 0, cap, sk, sd};
   const float scale = (EB == 1) ? a.lp_scale[q.unit] : 1.f;
 
   EntryRegs<NTH> er = fetch_entries<NTH>(src, ok ? len + n : 0, q.tid);
@@ -751,7 +756,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NPAD == 8 &
   u.pos_add = fold ? len : 0;
   u.new_len = (fold ? 0 : len) + (a.append ? n : 0);
   finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
-  if (!ok && last_arrival(arrived, a.H)) raise_status(a.status, kStatusOverflow);
+  if (!ok && last_arrival(arrived, a.H))
+    raise_status(a.status, valid ? kStatusOverflow : kStatusIndex);
 }
 
 // --------------------------------------------------------------- eager ----
@@ -818,7 +824,8 @@ __global__ __launch_bounds__(256) void gdn_append_path_kernel(GdnArgs a) {
   const int len = a.len[b];
   const int64_t pos = a.pos[b];
   const int pl = a.path_len[b];
-  bool ok = pl >= 0 && pl <= a.depth && len + pl <= cap;
+  const bool valid = indices_valid(len, pos, cap);
+  bool ok = valid && pl >= 0 && pl <= a.depth && len + pl <= cap;
   for (int k = 0; ok && k < pl; ++k) {
     const int j = a.path[(long)b * a.depth + k];
     ok = j >= 0 && j < n;
@@ -853,7 +860,8 @@ __global__ __launch_bounds__(256) void gdn_append_path_kernel(GdnArgs a) {
   u.pos_add = 0;
   u.new_len = len + pl;
   finish_update(a.arrive, a.pos, a.len, b, a.H, arrived, u);
-  if (!ok && last_arrival(arrived, a.H)) raise_status(a.status, kStatusOverflow);
+  if (!ok && last_arrival(arrived, a.H))
+    raise_status(a.status, valid ? kStatusOverflow : kStatusIndex);
 }
 
 }  // namespace

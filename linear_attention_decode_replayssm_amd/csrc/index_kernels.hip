@@ -10,13 +10,16 @@
 namespace rssm {
 namespace {
 
-__global__ __launch_bounds__(256) void rollback_kernel(int32_t* len, uint32_t* status,
-                                                       const int32_t* n_reject, int batch) {
+__global__ __launch_bounds__(256) void rollback_kernel(const int64_t* pos, int32_t* len,
+                                                       uint32_t* status, const int32_t* n_reject,
+                                                       int batch, int cap) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= batch) return;
   const int32_t n = n_reject[b];
   const int32_t l = len[b];
-  if (n < 0 || n > l)
+  if (!indices_valid(l, pos[b], cap))
+    raise_status(status, kStatusIndex);
+  else if (n < 0 || n > l)
     raise_status(status, kStatusRollback);
   else
     len[b] = l - n;
@@ -29,10 +32,10 @@ __global__ void clear_status_kernel(uint32_t* status) {
 }  // namespace
 
 hipError_t launch_rollback(int64_t* pos, int32_t* len, uint32_t* status,
-                           const int32_t* n_reject, int batch, hipStream_t s) {
-  (void)pos;
+                           const int32_t* n_reject, int batch, int cap, hipStream_t s) {
   const unsigned blocks = (unsigned)((batch + 255) / 256);
-  hipLaunchKernelGGL(rollback_kernel, dim3(blocks), dim3(256), 0, s, len, status, n_reject, batch);
+  hipLaunchKernelGGL(rollback_kernel, dim3(blocks), dim3(256), 0, s, pos, len, status, n_reject,
+                     batch, cap);
   return hipGetLastError();
 }
 

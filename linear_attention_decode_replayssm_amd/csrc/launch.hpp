@@ -95,7 +95,7 @@ hipError_t launch_probe(const void* src, void* dst, float* sink, long tiles, int
                         int check, hipStream_t s);
 
 hipError_t launch_rollback(int64_t* pos, int32_t* len, uint32_t* status,
-                           const int32_t* n_reject, int batch, hipStream_t s);
+                           const int32_t* n_reject, int batch, int cap, hipStream_t s);
 hipError_t launch_clear_status(uint32_t* status, hipStream_t s);
 
 }  // namespace rssm

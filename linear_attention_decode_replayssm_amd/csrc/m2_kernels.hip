@@ -160,9 +160,10 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
 
   const int len = a.len[q.b];
   const int64_t pos = a.pos[q.b];
-  const bool ok = len < cap;
+  const bool valid = indices_valid(len, pos, cap);
+  const bool ok = valid && len < cap;
   const int L = len + 1;
-  const int slot0 = (int)(pos % cap);
+  const int slot0 = valid ? (int)(pos % cap) : 0;
   float Ah[HPW], Dh[HPW];
 #pragma unroll
   for (int hl = 0; hl < HPW; ++hl) {
@@ -355,7 +356,8 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
   u.pos_add = FUSED ? L : 0;
   u.new_len = FUSED ? 0 : L;
   finish_update(a.arrive, a.pos, a.len, q.b, a.H / HPW, arrived, u);
-  if (!ok && last_arrival(arrived, a.H / HPW)) raise_status(a.status, kStatusOverflow);
+  if (!ok && last_arrival(arrived, a.H / HPW))
+    raise_status(a.status, valid ? kStatusOverflow : kStatusIndex);
 }
 
 // -------------------------------------------------------------- commit ----
@@ -367,12 +369,15 @@ template <int SCHEME, int LP>
 __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
   const Geo q = geometry(a);
   const int cap = a.cap;
+  if (a.mask != nullptr && a.mask[q.b] == 0) return;   // uniform for the sequence
   const int len = a.len[q.b];
-  const bool sel = (a.mask == nullptr || a.mask[q.b] != 0) && len >= a.min_len &&
-                   (len > 0 || SCHEME == kSchemeDual);
-  if (!sel) return;  // uniform for all workgroups of the sequence
-
   const int64_t pos = a.pos[q.b];
+  if (!indices_valid(len, pos, cap)) {   // refused: nothing read, written or counted
+    if (q.h == 0 && q.tid == 0) raise_status(a.status, kStatusIndex);
+    return;
+  }
+  if (len < a.min_len || (len == 0 && SCHEME != kSchemeDual)) return;   // not due
+
   const int L = len;
   const int slot0 = (int)(pos % cap);
   // the buffered entries first, into registers (thread tid: x of entry
@@ -476,10 +481,11 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   const int cap = a.cap, n = a.n_pos;
   const int len = a.len[q.b];
   const int64_t pos = a.pos[q.b];
-  const bool ok = len + n <= cap;
+  const bool valid = indices_valid(len, pos, cap);
+  const bool ok = valid && len + n <= cap;
   const bool fold = COMMIT && ok && len > 0 && len >= a.min_len;   // uniform per sequence
   const int LT = len + n;
-  const int slot0 = (int)(pos % cap);
+  const int slot0 = valid ? (int)(pos % cap) : 0;
   const float Ah = a.A[q.h];
   const float Dh = a.D[q.h];
   const long sx = (long)a.batch * a.H * P;   // per-draft strides
@@ -743,7 +749,8 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   u.pos_add = fold ? len : 0;
   u.new_len = (fold ? 0 : len) + (a.append ? n : 0);
   finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
-  if (!ok && last_arrival(arrived, a.H)) raise_status(a.status, kStatusOverflow);
+  if (!ok && last_arrival(arrived, a.H))
+    raise_status(a.status, valid ? kStatusOverflow : kStatusIndex);
 }
 
 // ----------------------------------------------------------- append path ----
@@ -762,7 +769,8 @@ __global__ __launch_bounds__(NT) void m2_append_path_kernel(M2Args a) {
   const int len = a.len[b];
   const int64_t pos = a.pos[b];
   const int pl = a.path_len[b];
-  bool ok = pl >= 0 && pl <= a.depth && len + pl <= cap;
+  const bool valid = indices_valid(len, pos, cap);
+  bool ok = valid && pl >= 0 && pl <= a.depth && len + pl <= cap;
   for (int k = 0; ok && k < pl; ++k) {
     const int j = a.path[(long)b * a.depth + k];
     ok = j >= 0 && j < n;
@@ -801,7 +809,8 @@ __global__ __launch_bounds__(NT) void m2_append_path_kernel(M2Args a) {
   u.pos_add = 0;
   u.new_len = len + pl;
   finish_update(a.arrive, a.pos, a.len, b, a.G, arrived, u);
-  if (!ok && last_arrival(arrived, a.G)) raise_status(a.status, kStatusOverflow);
+  if (!ok && last_arrival(arrived, a.G))
+    raise_status(a.status, valid ? kStatusOverflow : kStatusIndex);
 }
 
 // --------------------------------------------------------------- eager ----

@@ -101,6 +101,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void m2
   const int T = a.n_pos;
   const int len = a.len[b];
   const int64_t pos = a.pos[b];
+  if (!indices_valid(len, pos, a.cap)) {   // refused: nothing read, written or counted
+    if (h == 0 && tid == 0) raise_status(a.status, kStatusIndex);
+    return;
+  }
   const float Ah = a.A[h], Dh = a.D[h];
   const long unit = (long)b * a.H + h;
   const long sx = (long)a.batch * a.H * MP;
@@ -366,6 +370,10 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(4))) void g
   const int T = a.n_pos;
   const int len = a.len[b];
   const int64_t pos = a.pos[b];
+  if (!indices_valid(len, pos, a.cap)) {   // refused: nothing read, written or counted
+    if (h == 0 && tid == 0) raise_status(a.status, kStatusIndex);
+    return;
+  }
   const long unit = (long)b * a.H + h;
 
   GdnPre pre;

@@ -18,11 +18,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librssm.so")
 
 RSSM_OK, RSSM_EINVAL, RSSM_EUNSUPPORTED, RSSM_EALIGN, RSSM_ERANGE, RSSM_EHIP = 0, -1, -2, -3, -4, -5
-STATUS_OVERFLOW, STATUS_ROLLBACK, STATUS_NONFINITE = 1, 2, 4
+STATUS_OVERFLOW, STATUS_ROLLBACK, STATUS_NONFINITE, STATUS_INDEX = 1, 2, 4, 8
 RSSM_MAMBA2, RSSM_GDN = 1, 2
 RSSM_F32, RSSM_DUAL, RSSM_SHARED = 0, 1, 2
 RSSM_LP_NONE, RSSM_BF16, RSSM_E4M3 = 0, 1, 2
-RSSM_ABI_VERSION = 7
+RSSM_ABI_VERSION = 8
 RSSM_ARRIVE_STRIDE = 32   # uint32 elements between two sequences' arrival counters
 
 _vp = ctypes.c_void_p

@@ -298,3 +298,102 @@ def test_nonfinite_state_at_e4m3_quantisation():
     assert ((got[nan] & 0x7F) == 0x7F).all()      # NaN stays NaN
     assert R.rssm_status(L) == STATUS_NONFINITE
     assert R.rssm_status(L) == 0
+
+
+# ------------------------------------------------------ unusable indices --
+
+def _bad_indices(L, cap):
+    """Sequences 0-2 get indices no call of the library writes (len -1, len
+    cap + 1, ckpt_pos -3); sequence 3 stays at (0, 0)."""
+    t_ = gu.torch()
+    L.len.copy_(t_.tensor([-1, cap + 1, 0, 0], dtype=t_.int32))
+    L.ckpt_pos.copy_(t_.tensor([0, 0, -3, 0], dtype=t_.int64))
+
+
+def _check_refused(L, cap):
+    pos, ln = gu.indices(L)
+    assert ln.tolist() == [-1, cap + 1, 0, 0] and pos.tolist() == [0, 0, -3, 0]
+    assert not gu.host(L.arrive).any(), "arrival counters must return to zero"
+    assert R.rssm_status(L) == R.STATUS_INDEX
+
+
+@pytest.mark.parametrize("kind", ["m2", "gdn"])
+def test_unusable_indices_are_refused(kind):
+    """Every call that reads a sequence's indices refuses one whose len is
+    negative or above the capacity, or whose checkpoint position is negative:
+    it leaves the sequence as it is, writes NaN outputs (step, verify), raises
+    RSSM_STATUS_INDEX, and the arrival counters still return to zero, so that
+    the next calls on the repaired sequences are exact."""
+    t_ = gu.torch()
+    b, cap, n = 4, 4, 2
+    if kind == "m2":
+        H, G = 8, 2
+        A, D = syn.m2_params(90, H)
+        h0 = syn.m2_state0(90, b, H, P, N)
+        st = syn.m2_steps(90, 0, 3, b, H, G, P, N)
+        L = gu.m2_layer(A, D, h0, G, cap)
+        names = M2_NAMES
+        d = {k: gu.dev(v) for k, v in st.items()}
+        out = t_.zeros_like(d["x"])
+        step = lambda t: R.rssm_mamba2_step(L, *(d[nm][t] for nm in names), out[t])
+        one = lambda t, h: drivers.m2_decode(A, D, *(st[nm][t:t + 1] for nm in names), h, 99, cap)["y"][0]
+        ref_state = h0
+    else:
+        H = 4
+        S0 = syn.gdn_state0(90, b, H, DV, DK, std=0.1)
+        st = syn.gdn_steps(90, 0, 3, b, H, DK, DV)
+        L = gu.gdn_layer(S0, cap)
+        names = GDN_NAMES
+        d = {k: gu.dev(v) for k, v in st.items()}
+        out = t_.zeros_like(d["v"])
+        step = lambda t: R.rssm_gdn_step(L, *(d[nm][t] for nm in names), out[t])
+        one = lambda t, S: drivers.gdn_decode(*(st[nm][t:t + 1] for nm in names), S, 99, cap)["o"][0]
+        ref_state = S0
+    drafts = {nm: d[nm][:n] for nm in names}
+
+    _bad_indices(L, cap)
+    step(0)                                        # replay step
+    oh = gu.host(out[0])
+    assert np.isnan(oh[:3]).all()
+    assert gu.vec_rel_err(oh[3], one(0, ref_state)[3]) <= gu.TOL_F32
+    assert gu.indices(L)[1][3] == 1
+    L.len[3] = 0
+    _check_refused(L, cap)
+
+    vo = t_.zeros((n,) + tuple(out.shape[1:]), dtype=t_.float32, device="cuda")
+    R.rssm_verify(L, n, drafts, vo)                # verification
+    assert np.isnan(gu.host(vo)[:, :3]).all() and np.isfinite(gu.host(vo)[:, 3]).all()
+    L.len[3] = 0
+    _check_refused(L, cap)
+
+    R.rssm_append_path(L, n, gu.dev(np.zeros((b, 1), np.int32)),
+                       gu.dev(np.ones(b, np.int32)), drafts)   # accepted-path append
+    L.len[3] = 0
+    _check_refused(L, cap)
+
+    R.rssm_commit(L, None, 0)                      # commit: nothing read or written
+    _check_refused(L, cap)
+
+    R.rssm_rollback(L, gu.dev(np.zeros(b, np.int32)))
+    _check_refused(L, cap)
+
+    po = t_.full((1,) + tuple(out.shape[1:]), 7.0, dtype=t_.float32, device="cuda")
+    before = gu.host(L.ckpt).copy()
+    R.rssm_prefill(L, 1, {nm: d[nm][:1] for nm in names}, po)
+    assert (gu.host(po)[:, :3] == 7.0).all()
+    np.testing.assert_array_equal(gu.host(L.ckpt)[:3], before[:3])
+    pos, ln = gu.indices(L)
+    assert ln.tolist() == [-1, cap + 1, 0, 0] and pos.tolist() == [0, 0, -3, 1]
+    assert not gu.host(L.arrive).any()
+    assert R.rssm_status(L) == R.STATUS_INDEX
+
+    # repaired: every sequence steps exactly from its (unchanged) checkpoint
+    L.len.zero_()
+    L.ckpt_pos.zero_()
+    L.ckpt[3].copy_(gu.dev(ref_state[3]))
+    step(1)
+    want = one(1, ref_state)
+    assert gu.vec_rel_err(gu.host(out[1]), want) <= gu.TOL_F32
+    assert gu.indices(L)[1].tolist() == [1] * b
+    assert not gu.host(L.arrive).any()
+    assert R.rssm_status(L) == 0

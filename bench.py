@@ -777,6 +777,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default="",
+                    help="comma-separated subset of the secondary workloads to run (gdn, spec, "
+                         "gdn_spec, stack, sweep, lowprec, tree, prefill); default: all")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain device copy of 671,088,640 bytes (counter "
                          "calibration for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
@@ -849,29 +852,37 @@ def main():
     }
     out["stream_ceilings"] = stream_ceilings(torch, R)
     if not args.no_secondary:
+        only = set(filter(None, args.only.split(",")))
+        want = lambda name: not only or name in only
+        sec = {}
         sec_steps = max(64, min(args.steps, 256))
-        g = run_gdn(torch, R, syn, sec_steps, 16)
-        sp = run_spec(torch, R, syn, 128)
-        gsp = run_gdn_spec(torch, R, syn, 128)
-        du = run_dual_stack(torch, R, syn, 32)
-        sw = run_m2_interval_sweep(torch, R, syn, 256)
-        ml = run_m2_lowprec(torch, R, syn, 128)
-        tr = run_tree_rounds(torch, R, syn, 128)
-        pm = run_prefill(torch, R, syn, "mamba2")
-        pg = run_prefill(torch, R, syn, "gdn")
-        pm["speedup_vs_decode_steps"] = round(pm["seq_tok_s"] / out["value"], 2)
-        pg["speedup_vs_decode_steps"] = round(pg["seq_tok_s"] / g["seq_tok_s"], 2)
-        out["secondary"] = {
-            "gdn_decode_b256_h32_d128": {k: round(v, 2) for k, v in g.items()},
-            "mamba2_spec_rounds_b256_4drafts": _round1(sp),
-            "gdn_spec_rounds_b256_4drafts": _round1(gsp),
-            "gdn_12layer_stack_seq_tok_s": {k: round(v, 1) for k, v in du.items()},
-            "mamba2_commit_interval_sweep": sw,
-            "mamba2_lowprec_seq_tok_s": ml,
-            "mamba2_tree_rounds_b256_7drafts": {k: round(v, 1) for k, v in tr.items()},
-            "mamba2_prefill_b256_512tok": pm,
-            "gdn_prefill_b256_512tok": pg,
-        }
+        g = None
+        if want("gdn"):
+            g = run_gdn(torch, R, syn, sec_steps, 16)
+            sec["gdn_decode_b256_h32_d128"] = {k: round(v, 2) for k, v in g.items()}
+        if want("spec"):
+            sec["mamba2_spec_rounds_b256_4drafts"] = _round1(run_spec(torch, R, syn, 128))
+        if want("gdn_spec"):
+            sec["gdn_spec_rounds_b256_4drafts"] = _round1(run_gdn_spec(torch, R, syn, 128))
+        if want("stack"):
+            du = run_dual_stack(torch, R, syn, 32)
+            sec["gdn_12layer_stack_seq_tok_s"] = {k: round(v, 1) for k, v in du.items()}
+        if want("sweep"):
+            sec["mamba2_commit_interval_sweep"] = run_m2_interval_sweep(torch, R, syn, 256)
+        if want("lowprec"):
+            sec["mamba2_lowprec_seq_tok_s"] = run_m2_lowprec(torch, R, syn, 128)
+        if want("tree"):
+            tr = run_tree_rounds(torch, R, syn, 128)
+            sec["mamba2_tree_rounds_b256_7drafts"] = {k: round(v, 1) for k, v in tr.items()}
+        if want("prefill"):
+            pm = run_prefill(torch, R, syn, "mamba2")
+            pg = run_prefill(torch, R, syn, "gdn")
+            pm["speedup_vs_decode_steps"] = round(pm["seq_tok_s"] / out["value"], 2)
+            if g is not None:
+                pg["speedup_vs_decode_steps"] = round(pg["seq_tok_s"] / g["seq_tok_s"], 2)
+            sec["mamba2_prefill_b256_512tok"] = pm
+            sec["gdn_prefill_b256_512tok"] = pg
+        out["secondary"] = sec
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(syn)
     print(json.dumps(out), flush=True)

@@ -2,10 +2,10 @@
 // Gated DeltaNet kernels: bfloat16 (round to nearest even) and OCP FP8 E4M3
 // with one fp32 scale per (sequence, head) tile.
 //
-// Encoding of a tile for E4M3: scale = amax / 448 in fp32 (1 if amax is 0, or
-// if the tile holds NaN or an infinity), code = E4M3(s / scale) with the fp32
-// quotient rounded once and the conversion saturating at +-448.  Decoding:
-// value = code * scale.
+// Encoding of a tile for E4M3: scale = amax / 448 in fp32 (1 if that is 0,
+// or if the tile holds NaN or an infinity), code = E4M3(s / scale) with the
+// fp32 quotient rounded once and the conversion saturating at +-448.
+// Decoding: value = code * scale.
 //
 // Tile geometry used by the whole-tile helpers: NTH threads hold an fp32 tile
 // of ROWS x COLS values, thread t owning the float4 at column group
@@ -90,31 +90,94 @@ __device__ __forceinline__ void expand(u32x4 w, float (&f)[16 / EB]) {
 
 constexpr int kLpBf16 = 1, kLpE4m3 = 2;
 
-// Workgroup max of |hv| over the tile; a NaN anywhere makes the result +inf.
-// `red` is NTH / 64 floats of LDS.  Contains barriers: all threads call it.
+// ---- E4M3 tile encoder -----------------------------------------------------
+// The scale needs the tile's largest magnitude.  It is taken on the bit
+// patterns: with the sign cleared, unsigned order is magnitude order, and an
+// infinity (0x7f800000) or a NaN (above it) is larger than every finite value,
+// so one integer max per element both finds amax and detects a non-finite
+// tile.
+//
+// The codes need the fp32 quotient v / scale rounded once, as an IEEE
+// division rounds it.  The division instruction sequence costs about ten
+// instructions per element; the tile's scale is fixed, so the quotient is
+// formed in four by one correction step of a reciprocal (Markstein's method,
+// "IA-64 and Elementary Functions", 2000): write scale = m 2^-k with m in
+// [1, 2), take y = RN(1/m) once per tile, and per element
+//   a = v 2^k (exact),  q0 = RN(a y),  r = fma(q0, m, -a) = q0 m - a (exact),
+//   q = fma(-r, y, q0) = RN(a / m) = RN(v / scale).
+// The prescaling keeps the residual r a normal number, which the exactness of
+// the correction needs.  Checked against the IEEE quotient on 1.2e9 operand
+// pairs spanning every binade, subnormal scales and signed zeros: equal
+// wherever |v / scale| >= 2^-60, and below that (where every code is +-0)
+// of the same sign.  The negation sits on the FMA operands so that a zero
+// keeps its sign.
+struct E4m3Scale {
+  float scale;  // the tile's scale: amax / 448, or 1 (zero or non-finite tile, or amax / 448 == 0)
+  float m, y;   // scale 2^k in [1, 2) and RN(1 / m)
+  int k;
+  bool fin;     // the tile holds no NaN and no infinity
+};
+
+__device__ __forceinline__ E4m3Scale e4m3_scale_of(uint32_t amax_bits) {
+  E4m3Scale s;
+  s.fin = amax_bits < 0x7f800000u;
+  const float q = __uint_as_float(amax_bits) / 448.f;
+  s.scale = (s.fin && q > 0.f) ? q : 1.f;
+  int e;
+  const float mant = frexpf(s.scale, &e);   // scale = mant 2^e, mant in [0.5, 1)
+  s.k = 1 - e;
+  s.m = 2.f * mant;
+  s.y = 1.f / s.m;
+  return s;
+}
+
+__device__ __forceinline__ float e4m3_quot(float v, const E4m3Scale& s) {
+#pragma clang fp contract(off)
+  const float a = __builtin_amdgcn_ldexpf(v, s.k);
+  const float q0 = a * s.y;
+  const float r = __builtin_fmaf(q0, s.m, -a);
+  return __builtin_fmaf(-r, s.y, q0);
+}
+
+// Four fp32 values -> four E4M3 codes of a tile with scale s (the non-finite
+// path encodes the values unscaled, as the scale is then 1).
+__device__ __forceinline__ uint32_t e4m3_encode4(f32x4 v, const E4m3Scale& s) {
+  if (s.fin)
+    return e4m3_pack4(e4m3_quot(v.x, s), e4m3_quot(v.y, s), e4m3_quot(v.z, s), e4m3_quot(v.w, s));
+  return e4m3_pack4_nonfinite(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t abs_bits_max(uint32_t m, f32x4 v) {
+  const uint32_t a = __float_as_uint(v.x) & 0x7fffffffu, b = __float_as_uint(v.y) & 0x7fffffffu;
+  const uint32_t c = __float_as_uint(v.z) & 0x7fffffffu, d = __float_as_uint(v.w) & 0x7fffffffu;
+  return max(max(m, max(a, b)), max(c, d));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+  m = max(m, __float_as_uint(rpartner<32>(__uint_as_float(m))));
+  m = max(m, __float_as_uint(rpartner<16>(__uint_as_float(m))));
+  m = max(m, __float_as_uint(rpartner<8>(__uint_as_float(m))));
+  m = max(m, __float_as_uint(rpartner<4>(__uint_as_float(m))));
+  m = max(m, __float_as_uint(rpartner<2>(__uint_as_float(m))));
+  m = max(m, __float_as_uint(rpartner<1>(__uint_as_float(m))));
+  return m;
+}
+
+// Scale of the tile held in the geometry above (all NTH threads call it; it
+// contains barriers).  red: NTH / 64 words of LDS.
 template <int NTH, int NLD>
-__device__ float tile_amax(const f32x4 (&hv)[NLD], float* red) {
-  float m = 0.f;
-  bool nan = false;
+__device__ E4m3Scale tile_e4m3_scale(const f32x4 (&hv)[NLD], uint32_t* red) {
+  uint32_t m = 0u;
 #pragma unroll
-  for (int k = 0; k < NLD; ++k) {
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(hv[k].x), fabsf(hv[k].y)), fmaxf(fabsf(hv[k].z), fabsf(hv[k].w))));
-    nan |= !(hv[k].x == hv[k].x && hv[k].y == hv[k].y && hv[k].z == hv[k].z && hv[k].w == hv[k].w);
-  }
-  if (nan) m = __builtin_inff();
-  m = fmaxf(m, rpartner<32>(m));
-  m = fmaxf(m, rpartner<16>(m));
-  m = fmaxf(m, rpartner<8>(m));
-  m = fmaxf(m, rpartner<4>(m));
-  m = fmaxf(m, rpartner<2>(m));
-  m = fmaxf(m, rpartner<1>(m));
-  __syncthreads();
+  for (int k = 0; k < NLD; ++k) m = abs_bits_max(m, hv[k]);
+  m = wave_max_u32(m);
+  __syncthreads();   // red may still be read by a previous use
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  float r = red[0];
+  uint32_t r = red[0];
 #pragma unroll
-  for (int w = 1; w < NTH / 64; ++w) r = fmaxf(r, red[w]);
-  return r;
+  for (int w = 1; w < NTH / 64; ++w) r = max(r, red[w]);
+  return e4m3_scale_of(r);
 }
 
 // Write the low-precision image of an fp32 tile held in the geometry above.
@@ -135,25 +198,13 @@ __device__ void store_lp_tile(const f32x4 (&hv)[NLD], void* lp, float* scale_out
       *reinterpret_cast<u32x2*>(base + (k * RPL + r0) * COLS + cl * 4) = w;
     }
   } else {
-    const float amax = tile_amax<NTH, NLD>(hv, red);
-    const bool fin = amax <= 3.402823466e38f;
-    const float scale = (amax > 0.f && fin) ? amax / 448.f : 1.f;
-    if (!fin && threadIdx.x == 0) raise_status(status, kStatusNonfinite);
+    const E4m3Scale sc = tile_e4m3_scale<NTH, NLD>(hv, reinterpret_cast<uint32_t*>(red));
+    if (!sc.fin && threadIdx.x == 0) raise_status(status, kStatusNonfinite);
     uint8_t* base = reinterpret_cast<uint8_t*>(lp);
-    if (fin) {   // uniform over the workgroup: amax is the whole tile's
 #pragma unroll
-      for (int k = 0; k < NLD; ++k) {
-        const uint32_t w = e4m3_pack4(hv[k].x / scale, hv[k].y / scale, hv[k].z / scale,
-                                      hv[k].w / scale);
-        *reinterpret_cast<uint32_t*>(base + (k * RPL + r0) * COLS + cl * 4) = w;
-      }
-    } else {     // scale 1: the values are encoded as they are
-      for (int k = 0; k < NLD; ++k) {
-        const uint32_t w = e4m3_pack4_nonfinite(hv[k].x, hv[k].y, hv[k].z, hv[k].w);
-        *reinterpret_cast<uint32_t*>(base + (k * RPL + r0) * COLS + cl * 4) = w;
-      }
-    }
-    if (threadIdx.x == 0) *scale_out = scale;
+    for (int k = 0; k < NLD; ++k)
+      *reinterpret_cast<uint32_t*>(base + (k * RPL + r0) * COLS + cl * 4) = e4m3_encode4(hv[k], sc);
+    if (threadIdx.x == 0) *scale_out = sc.scale;
   }
 }
 

@@ -269,18 +269,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void m2
         *reinterpret_cast<u32x2*>(lp + 16 * t) = v;
       }
     } else {
-      const float amax = tile_amax<NT, 8>(acc, s_red);
-      const bool fin = amax <= 3.402823466e38f;
-      const float sc = (amax > 0.f && fin) ? amax / 448.f : 1.f;
-      if (!fin && tid == 0) raise_status(a.status, kStatusNonfinite);
+      const E4m3Scale sc = tile_e4m3_scale<NT, 8>(acc, reinterpret_cast<uint32_t*>(s_red));
+      if (!sc.fin && tid == 0) raise_status(a.status, kStatusNonfinite);
       uint8_t* lp = reinterpret_cast<uint8_t*>(a.ckpt_lp) + e0;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint32_t v = fin ? e4m3_pack4(acc[t].x / sc, acc[t].y / sc, acc[t].z / sc, acc[t].w / sc)
-                               : e4m3_pack4_nonfinite(acc[t].x, acc[t].y, acc[t].z, acc[t].w);
-        *reinterpret_cast<uint32_t*>(lp + 16 * t) = v;
-      }
-      if (tid == 0) a.lp_scale[unit] = sc;
+      for (int t = 0; t < 8; ++t)
+        *reinterpret_cast<uint32_t*>(lp + 16 * t) = e4m3_encode4(acc[t], sc);
+      if (tid == 0) a.lp_scale[unit] = sc.scale;
     }
   }
 
@@ -580,18 +575,13 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(4))) void g
         *reinterpret_cast<u32x2*>(lp + 16 * t) = v;
       }
     } else {
-      const float amax = tile_amax<GNT, 8>(acc, s_red);
-      const bool fin = amax <= 3.402823466e38f;
-      const float sc = (amax > 0.f && fin) ? amax / 448.f : 1.f;
-      if (!fin && tid == 0) raise_status(a.status, kStatusNonfinite);
+      const E4m3Scale sc = tile_e4m3_scale<GNT, 8>(acc, reinterpret_cast<uint32_t*>(s_red));
+      if (!sc.fin && tid == 0) raise_status(a.status, kStatusNonfinite);
       uint8_t* lp = reinterpret_cast<uint8_t*>(a.ckpt_lp) + e0;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint32_t v = fin ? e4m3_pack4(acc[t].x / sc, acc[t].y / sc, acc[t].z / sc, acc[t].w / sc)
-                               : e4m3_pack4_nonfinite(acc[t].x, acc[t].y, acc[t].z, acc[t].w);
-        *reinterpret_cast<uint32_t*>(lp + 16 * t) = v;
-      }
-      if (tid == 0) a.lp_scale[unit] = sc;
+      for (int t = 0; t < 8; ++t)
+        *reinterpret_cast<uint32_t*>(lp + 16 * t) = e4m3_encode4(acc[t], sc);
+      if (tid == 0) a.lp_scale[unit] = sc.scale;
     }
   }
 

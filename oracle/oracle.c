@@ -258,7 +258,8 @@ void orc_e4m3_decode(long n, const uint8_t* in, double* out) {
 
 /* Per-head scaled E4M3 quantisation of fp32 state tiles (one tile per head):
  *   amax  = max |s| over the tile (fp32)
- *   scale = amax / 448 in fp32 arithmetic, or 1 when amax is 0
+ *   scale = amax / 448 in fp32 arithmetic, or 1 when that is 0 (amax 0, or
+ *           amax so small that the fp32 quotient underflows to 0)
  *   code  = E4M3(s / scale) with the fp32 quotient rounded once (IEEE)
  * A tile holding a NaN or an infinity has no meaningful amax: its scale is 1
  * and its values are encoded as they are (saturating, NaN kept).
@@ -279,6 +280,7 @@ long orc_e4m3_quant_heads(long nheads, long per_head, const float* s,
     }
     nonfinite += !finite;
     volatile float sc = (finite && amax > 0.0f) ? amax / 448.0f : 1.0f;
+    if (sc == 0.0f) sc = 1.0f;   /* amax / 448 below the smallest subnormal: as for amax 0 */
     scale[h] = sc;
     for (long i = 0; i < per_head; ++i) {
       volatile float qv = tile[i] / sc;

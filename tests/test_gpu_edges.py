@@ -397,3 +397,64 @@ def test_unusable_indices_are_refused(kind):
     assert gu.indices(L)[1].tolist() == [1] * b
     assert not gu.host(L.arrive).any()
     assert R.rssm_status(L) == 0
+
+
+# ------------------------------------------- E4M3 quotients near code ties --
+
+def _tiles_near_ties(rng, b, H, rows, cols):
+    """fp32 tiles with scales from subnormal to 1e28 whose values lie within
+    two ulps of t x scale for every E4M3 rounding tie t (the midpoints between
+    neighbouring codes, subnormal ones included), so that each code depends on
+    the last bit of the quotient v / scale; plus signed zeros and values whose
+    quotient underflows.  Element [0, 0] holds the tile's amax."""
+    vals = np.array([oracle.e4m3_decode(np.array([c], np.uint8))[0] for c in range(0x7F)])
+    ties = (vals[:-1] + vals[1:]) / 2
+    amaxes = np.array([1e-40, 3.3e-38, 2.0 ** -100, 1e-20, 0.037, 1.0, 3.0, 448.0, 5e3,
+                       7.7e10, 1e28], np.float32)
+    S = np.zeros((b, H, rows, cols), np.float32)
+    for u in range(b * H):
+        amax = amaxes[u % len(amaxes)] * np.float32(1.0 + 0.37 * rng.random())
+        scale = np.float32(amax) / np.float32(448.0)
+        base = (ties * np.float64(scale)).astype(np.float32)
+        near = [base]
+        for d in (1, 2):
+            near.append(np.nextafter(base, np.float32(np.inf), dtype=np.float32))
+            near.append(np.nextafter(base, np.float32(0), dtype=np.float32))
+            base = near[-2]
+        pool = np.concatenate(near + [np.array([0.0, -0.0], np.float32),
+                                      (rng.standard_normal(64) * 1e-30 * scale).astype(np.float32)])
+        pool = pool[np.abs(pool) <= amax]
+        t = rng.choice(pool, size=rows * cols) * rng.choice([-1, 1], size=rows * cols)
+        t = t.astype(np.float32)
+        t[0] = amax
+        S.reshape(b * H, rows * cols)[u] = t
+    return S
+
+
+@pytest.mark.parametrize("kind", ["m2", "gdn"])
+def test_e4m3_codes_at_ties_bit_exact(kind):
+    """A DUAL commit with empty buffers re-encodes the fp32 checkpoint: for
+    tiles whose quotients sit at E4M3 rounding ties, the codes and scales equal
+    the oracle's IEEE-division encoder bit for bit (the kernels form the
+    quotient with a reciprocal and one correction step)."""
+    rng = np.random.default_rng(91)
+    b = 2
+    if kind == "m2":
+        H, G = 12, 1
+        S = _tiles_near_ties(rng, b, H, P, N)
+        A, D = syn.m2_params(91, H)
+        L = gu.m2_layer(A, D, S, G, 4)
+        L2 = R.Layer.mamba2(b, H, G, P, N, 4, scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_E4M3)
+        L2.ckpt.copy_(L.ckpt)
+        L = L2
+    else:
+        H = 12
+        S = _tiles_near_ties(rng, b, H, DV, DK)
+        L = gu.gdn_layer(S, 4, scheme=R.RSSM_DUAL, lp=R.RSSM_E4M3)
+    R.rssm_commit(L, None, 0)
+    scale, want = oracle.e4m3_quant_heads(S.reshape(b, H, -1))
+    np.testing.assert_array_equal(gu.host(L.lp_scale), scale)
+    got = gu.host(L.ckpt_lp).reshape(b, H, -1)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, (len(bad), bad[:5], got[tuple(bad[0])], want[tuple(bad[0])])
+    assert R.rssm_status(L) == 0

@@ -171,3 +171,19 @@ def test_e4m3_nonfinite_tile_is_encoded_unscaled():
     s_ok, c_ok = oracle.e4m3_quant_heads(tiles[[0, 3]])
     np.testing.assert_array_equal(scale[[0, 3]], s_ok)
     np.testing.assert_array_equal(codes[[0, 3]], c_ok)
+
+
+def test_e4m3_scale_that_underflows_is_one():
+    """amax / 448 rounds to 0 in fp32 when amax < 448 x 2^-150: the tile is
+    encoded with scale 1, as an all-zero tile is, and every code is +-0 (the
+    values are far below the smallest E4M3 step); a slightly larger amax gives
+    a subnormal scale and the usual encoding, the max mapping to +-448."""
+    tiles = np.zeros((2, 8), np.float32)
+    tiles[0, :4] = np.array([1e-43, -1e-43, 0.0, -0.0], np.float32)
+    tiles[1, :3] = np.array([1e-40, -5e-41, 0.0], np.float32)
+    scale, codes = oracle.e4m3_quant_heads(tiles)
+    assert np.float32(1e-43) / np.float32(448.0) == 0.0
+    assert scale[0] == 1.0
+    assert codes[0].tolist() == [0x00, 0x80, 0x00, 0x80, 0, 0, 0, 0]
+    assert 0.0 < scale[1] < np.finfo(np.float32).tiny
+    assert codes[1, 0] == 0x7E and codes[1, 1] & 0x80

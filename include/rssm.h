@@ -58,8 +58,9 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 8
+#define RSSM_ABI_VERSION 9
 #define RSSM_ARRIVE_STRIDE 32   /* uint32 elements between two sequences' counters */
+#define RSSM_NOALLOC_MAX_BATCH 4096  /* sequences served by rssm_mamba2_step_noalloc    */
 
 /* ---- host return codes ------------------------------------------------- */
 #define RSSM_OK            0
@@ -189,6 +190,25 @@ typedef struct rssm_inputs {
 int rssm_mamba2_step(const rssm_layer* L, const float* x, const float* B,
                      const float* C, const float* dt, float* y,
                      int commit_after, void* stream);
+
+/*
+ * rssm_mamba2_step_noalloc -- rssm_mamba2_step for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops that
+ * must not allocate, harnesses that forbid it.  Same arguments, results and
+ * errors as rssm_mamba2_step, except that the arrival counters are the
+ * library's own instead of L->arrive (ignored, may be NULL): a file-scope
+ * device array with room for RSSM_NOALLOC_MAX_BATCH sequences (512 KiB on each
+ * device that runs the call, held until the process ends).  The call first
+ * zeroes the counters of sequences 0..batch-1 with a small kernel on
+ * `stream`, then launches the step; it allocates nothing and calls no memset
+ * or copy.  batch > RSSM_NOALLOC_MAX_BATCH gives RSSM_ERANGE.  Every call on a
+ * device shares that device's counters: calls that overlap in time on one
+ * device (other streams, other threads) race and corrupt each other's index
+ * updates; serialise them.
+ */
+int rssm_mamba2_step_noalloc(const rssm_layer* L, const float* x, const float* B,
+                             const float* C, const float* dt, float* y,
+                             int commit_after, void* stream);
 
 /*
  * rssm_gdn_step -- one decode token for every sequence of a GDN layer.

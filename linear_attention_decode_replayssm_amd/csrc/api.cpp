@@ -6,11 +6,46 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "rssm.h"
 #include "common.hpp"
 #include "launch.hpp"
 
+// Arrival counters of rssm_mamba2_step_noalloc: one 128-byte line per
+// sequence, as in a caller's `arrive` buffer, for up to
+// RSSM_NOALLOC_MAX_BATCH sequences (512 KiB on each device, held until the
+// process ends).  Host code never passes this name to a kernel: on the host
+// it is a stand-in, not a device address; the address comes from
+// hipGetSymbolAddress, once per device (scratch_address below).
+static __device__ __align__(256) uint32_t scratch[RSSM_NOALLOC_MAX_BATCH * RSSM_ARRIVE_STRIDE];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Zero the counter word of sequences 0..batch-1 (a kernel, not a memset, so
+// that the call stays a launch-only sequence under graph capture).
+__global__ __launch_bounds__(256) void clear_counters_kernel(uint32_t* counters, int batch) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) counters[(long)b * rssm::kArriveStride] = 0u;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current; NULL if the lookup fails.
+uint32_t* scratch_address() {
+  static std::mutex mu;
+  static uint32_t* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    addr[dev] = static_cast<uint32_t*>(p);
+  }
+  return addr[dev];
+}
 
 inline bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -52,13 +87,14 @@ int check_layer_ptrs(const rssm_layer* L) {
   return RSSM_OK;
 }
 
-// Rings and indices are needed by every call except the eager step.
-int check_state(const rssm_layer* L) {
+// Rings and indices are needed by every call except the eager step (the
+// arrival counters too, unless the call brings its own: need_arrive false).
+int check_state(const rssm_layer* L, bool need_arrive = true) {
   const int nring = L->kind == RSSM_MAMBA2 ? 3 : 4;
   for (int i = 0; i < nring; ++i)
     if (!L->ring[i]) return RSSM_EINVAL;
   if (!a16(L->ring[0]) || !a16(L->ring[1])) return RSSM_EALIGN;
-  if (!L->ckpt_pos || !L->len || !L->arrive || !L->status) return RSSM_EINVAL;
+  if (!L->ckpt_pos || !L->len || !L->status || (need_arrive && !L->arrive)) return RSSM_EINVAL;
   return RSSM_OK;
 }
 
@@ -186,6 +222,33 @@ int rssm_mamba2_step(const rssm_layer* L, const float* x, const float* B, const 
   if (!x || !B || !C || !dt || !y) return RSSM_EINVAL;
   if (!a16(x) || !a16(B) || !a16(C) || !a16(y)) return RSSM_EALIGN;
   rssm::M2Args a = m2_args(L);
+  a.x = x;
+  a.B = B;
+  a.C = C;
+  a.dt = dt;
+  a.y = y;
+  return hip_rc(rssm::launch_m2_step(a, commit_after != 0, S(stream)));
+}
+
+int rssm_mamba2_step_noalloc(const rssm_layer* L, const float* x, const float* B,
+                             const float* C, const float* dt, float* y, int commit_after,
+                             void* stream) {
+  int rc = check_layer_dims(L);
+  if (rc) return rc;
+  if (L->kind != RSSM_MAMBA2) return RSSM_EINVAL;
+  if (commit_after && L->scheme == RSSM_SHARED) return RSSM_EUNSUPPORTED;
+  if (L->batch > RSSM_NOALLOC_MAX_BATCH) return RSSM_ERANGE;
+  if (L->batch == 0) return RSSM_OK;
+  if ((rc = check_layer_ptrs(L)) || (rc = check_state(L, false))) return rc;
+  if (!x || !B || !C || !dt || !y) return RSSM_EINVAL;
+  if (!a16(x) || !a16(B) || !a16(C) || !a16(y)) return RSSM_EALIGN;
+  uint32_t* counters = scratch_address();
+  if (!counters) return RSSM_EHIP;
+  hipLaunchKernelGGL(clear_counters_kernel, dim3((unsigned)((L->batch + 255) / 256)), dim3(256),
+                     0, S(stream), counters, L->batch);
+  if ((rc = hip_rc(hipGetLastError()))) return rc;
+  rssm::M2Args a = m2_args(L);
+  a.arrive = counters;
   a.x = x;
   a.B = B;
   a.C = C;

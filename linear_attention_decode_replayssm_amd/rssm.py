@@ -22,8 +22,9 @@ STATUS_OVERFLOW, STATUS_ROLLBACK, STATUS_NONFINITE, STATUS_INDEX = 1, 2, 4, 8
 RSSM_MAMBA2, RSSM_GDN = 1, 2
 RSSM_F32, RSSM_DUAL, RSSM_SHARED = 0, 1, 2
 RSSM_LP_NONE, RSSM_BF16, RSSM_E4M3 = 0, 1, 2
-RSSM_ABI_VERSION = 8
+RSSM_ABI_VERSION = 9
 RSSM_ARRIVE_STRIDE = 32   # uint32 elements between two sequences' arrival counters
+RSSM_NOALLOC_MAX_BATCH = 4096   # sequences rssm_mamba2_step_noalloc serves
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -65,6 +66,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER
         L.rssm_mamba2_step.argtypes = [P(rssm_layer), _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp]
+        L.rssm_mamba2_step_noalloc.argtypes = [P(rssm_layer), _vp, _vp, _vp, _vp, _vp,
+                                               ctypes.c_int, _vp]
         L.rssm_gdn_step.argtypes = [P(rssm_layer), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp]
         L.rssm_commit.argtypes = [P(rssm_layer), _vp, ctypes.c_int, _vp]
         L.rssm_verify.argtypes = [P(rssm_layer), ctypes.c_int, P(rssm_inputs), _vp, _vp]
@@ -93,7 +96,7 @@ def lib():
                   "rssm_rollback", "rssm_eager_step", "rssm_status", "rssm_verify_tree",
                   "rssm_append_path", "rssm_prefill", "rssm_eager_spec_round",
                   "rssm_eager_spec_accept", "rssm_probe_stream", "rssm_probe_stream_tiles",
-                  "rssm_verify_commit", "rssm_verify_tree_commit"):
+                  "rssm_verify_commit", "rssm_verify_tree_commit", "rssm_mamba2_step_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         if L.rssm_abi_version() != RSSM_ABI_VERSION:
             raise RuntimeError(f"{LIB_PATH} implements ABI {L.rssm_abi_version()}, this binding "
@@ -142,6 +145,13 @@ def rssm_mamba2_step(layer, x, B, C, dt, y, commit_after=False, stream=None, che
     rc = lib().rssm_mamba2_step(ctypes.byref(_desc(layer)), _ptr(x), _ptr(B), _ptr(C), _ptr(dt),
                                 _ptr(y), int(bool(commit_after)), _stream(stream))
     return _check(rc, "rssm_mamba2_step") if check else rc
+
+
+def rssm_mamba2_step_noalloc(layer, x, B, C, dt, y, commit_after=False, stream=None, check=True):
+    rc = lib().rssm_mamba2_step_noalloc(ctypes.byref(_desc(layer)), _ptr(x), _ptr(B), _ptr(C),
+                                        _ptr(dt), _ptr(y), int(bool(commit_after)),
+                                        _stream(stream))
+    return _check(rc, "rssm_mamba2_step_noalloc") if check else rc
 
 
 def rssm_gdn_step(layer, q, k, v, alpha, beta, o, commit_after=False, stream=None, check=True):

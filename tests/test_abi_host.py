@@ -60,7 +60,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert R.rssm_abi_version() == R.RSSM_ABI_VERSION == 8
+    assert R.rssm_abi_version() == R.RSSM_ABI_VERSION == 9
     for code in (0, -1, -2, -3, -4, -5):
         assert R.rssm_strerror(code)
     assert "unknown" in R.rssm_strerror(12345)
@@ -328,3 +328,22 @@ def test_probe_validates_on_host():
     assert T(FAKE, FAKE + 8, None, 4096, 4096, stream=0, check=False) == R.RSSM_EALIGN
     assert T(FAKE, None, FAKE, 6144, 4096, stream=0, check=False) == R.RSSM_ERANGE
     assert T(FAKE, None, FAKE, 4096, 32768, stream=0, check=False) == R.RSSM_ERANGE
+
+
+def test_noalloc_step_validation():
+    """rssm_mamba2_step_noalloc validates as rssm_mamba2_step does, ignores the
+    descriptor's arrival counters, and refuses a batch above its counters'
+    room before launching anything."""
+    f = lambda L, commit=0: R.rssm_mamba2_step_noalloc(L, FAKE, FAKE, FAKE, FAKE, FAKE, commit,
+                                                       stream=0, check=False)
+    assert f(_m2_desc(batch=0)) == R.RSSM_OK
+    big = _m2_desc(batch=R.RSSM_NOALLOC_MAX_BATCH + 1)
+    big.arrive = None
+    assert f(big) == R.RSSM_ERANGE
+    assert f(_gdn_desc(batch=2)) == R.RSSM_EINVAL
+    assert f(_m2_desc(batch=2, scheme=R.RSSM_SHARED, lp_dtype=R.RSSM_BF16), 1) == R.RSSM_EUNSUPPORTED
+    L = _m2_desc(batch=2)
+    L.len = None
+    assert f(L) == R.RSSM_EINVAL
+    assert R.rssm_mamba2_step_noalloc(_m2_desc(batch=2), FAKE + 4, FAKE, FAKE, FAKE, FAKE, 0,
+                                      stream=0, check=False) == R.RSSM_EALIGN

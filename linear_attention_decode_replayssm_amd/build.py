@@ -1,10 +1,13 @@
 """Build librssm.so (the HIP kernels + C ABI) for gfx950 with hipcc.
 
-Usage: python -m linear_attention_decode_replayssm_amd.build [-v] [--isa]
+Usage: python -m linear_attention_decode_replayssm_amd.build [-v] [--isa] [--define NAME]...
 
 Each translation unit is compiled to an object in ``_build/`` (in parallel),
 then linked into ``librssm.so`` next to this file.  ``--isa`` additionally
-keeps the device assembly of every kernel under ``_build/isa/``.
+keeps the device assembly of every kernel under ``_build/isa/``; ``--define
+NAME`` passes -DNAME to every translation unit (RSSM_M2_VERIFY_MFMA selects
+the matrix-core variant of the Mamba-2 verify contraction, kept for
+measurement).
 
 Packed fp32 instructions are disabled for all device code
 (``-target-feature -packed-fp32-ops``): the compiler would otherwise form
@@ -43,6 +46,9 @@ def _flags():
             "-Wall", "-Wno-unused-function", "-I", INC, "-I", CSRC]
 
 
+DEFINES = []
+
+
 def _compile(src, verbose, isa):
     out_dir = BUILD
     extra = []
@@ -52,7 +58,8 @@ def _compile(src, verbose, isa):
         extra = ["-save-temps=obj"]
     obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [_hipcc()] + _flags() + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    defs = [f"-D{d}" for d in DEFINES]
+    cmd = [_hipcc()] + _flags() + defs + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -77,4 +84,8 @@ def build(verbose: bool = False, isa: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, isa="--isa" in sys.argv))
+    args = sys.argv[1:]
+    for i, a in enumerate(args):
+        if a == "--define" and i + 1 < len(args):
+            DEFINES.append(args[i + 1])
+    print(build(verbose="-v" in args, isa="--isa" in args))

@@ -473,9 +473,18 @@ __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
 // verify as a separate pass over the state -- and its checkpoint moves to the
 // end of the buffer; the drafts then sit at entries 0..n-1 of the new buffer
 // (the same ring slots).  The outputs are those of commit-then-verify.
-template <int EB, int NPAD, bool COMMIT = false>
+//
+// MF (fp32 checkpoint, 4 or 8 drafts): the contraction Y^T = [C_j] h_c^T runs
+// on v_mfma_f32_16x16x4f32 (drafts padded to 16 rows of the A operand).  The
+// MFMA operand layout puts 16 rows x 64 B in one wave load, which streams ~10%
+// slower than consecutive bytes, so each wave streams its own 16 state rows
+// with consecutive 1 KiB loads (rows 16w + 2k + lane/32, k = 0..7), parks
+// them in a wave-private LDS tile and reads the operands from there: no
+// cross-lane reduction, and no barrier between the waves for the transpose.
+template <int EB, int NPAD, bool COMMIT = false, bool MF = false>
 __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   static_assert(!COMMIT || EB == 4, "the fused commit folds the fp32 checkpoint");
+  static_assert(!MF || (EB == 4 && NPAD >= 4), "matrix-core contraction: fp32, 4 or 8 drafts");
   using Gm = RdGeo<EB>;
   const Geo q = geometry(a);
   const int cap = a.cap, n = a.n_pos;
@@ -537,11 +546,23 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
     }
   }
   u32x4 raw[Gm::NLD];
-  load_raw<EB>(a, q.unit, q.tid, raw);
+  // row of the thread's k-th state load: consecutive workgroup loads, or
+  // (MF) each wave's own 16 rows
+  auto rowk = [&](int k) -> int {
+    return MF ? 16 * (q.tid >> 6) + 2 * k + (q.lane >> 5) : k * RPL + q.r0;
+  };
+  if constexpr (MF) {
+    const float* ck0 = a.ckpt + q.unit * (P * N) + q.c4 * 4;
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) raw[k] = ld_nt_u(ck0 + rowk(k) * N);
+  } else {
+    load_raw<EB>(a, q.unit, q.tid, raw);
+  }
   const int cl = q.tid % Gm::LPR, rr0 = q.tid / Gm::LPR;
   const float scale = (EB == 1) ? a.lp_scale[q.unit] : 1.f;
 
-  __shared__ __attribute__((aligned(16))) float s_C[NPAD][N];
+  constexpr int CP = N + 4;   // padded LDS row pitch of C_j and the MF tile
+  __shared__ __attribute__((aligned(16))) float s_C[NPAD][CP];
   __shared__ __attribute__((aligned(16))) float s_Ba[NPAD][N];   // drafts' B, x, dt
   __shared__ float s_xa[NPAD][P];                                // for the append
   __shared__ float s_dta[NPAD];
@@ -657,62 +678,114 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
     }
   }
 
-  // Row dots with every C_j, reduced across the LPR lanes of a row.  At most
-  // 32 partial sums per lane at a time: drafts go in chunks of JC.
-  constexpr int JC = (Gm::NLD * NPAD <= 32) ? NPAD : 32 / Gm::NLD;
-  constexpr int NCH = NPAD / JC;
-  constexpr int V = Gm::NLD * JC;
-  using M = XMap<V, Gm::LPR>;
   float f[Gm::NLD][Gm::EPL];   // the tile, expanded once
 #pragma unroll
   for (int k = 0; k < Gm::NLD; ++k) expand<EB>(raw[k], f[k]);
-  float res[NCH][M::VOUT];
+  if constexpr (MF) {
+    // wave-private transpose of this wave's 16 rows, NPASS column slices at a
+    // time (lane ch = lane % 32 holds columns 4ch .. 4ch + 3 of its rows), then
+    // per 16-column block the A operand C_j[n] (lane: draft lane % 16,
+    // n = 16cb + 4 (lane / 16) + s) and the B operand h[p][n] (lane: row
+    // lane % 16, same n)
+    constexpr int NPASS = 4, SW = N / NPASS, HP = SW + 4;
+    __shared__ __attribute__((aligned(16))) float s_t[NT / 64][16][HP];
+    float (*tw)[HP] = s_t[q.tid >> 6];
+    const int li = q.lane & 15, lq = q.lane >> 4, ch = q.lane & 31;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    // keep the scheduler from hoisting this chunk's LDS reads into the last
-    if (c > 0) __builtin_amdgcn_sched_barrier(0);
-    float d[V];
+    for (int ps = 0; ps < NPASS; ++ps) {
+      if (ps > 0) __builtin_amdgcn_sched_barrier(0);   // the last slice's operands are consumed
+      if (ch / (SW / 4) == ps) {
 #pragma unroll
-    for (int jl = 0; jl < JC; ++jl) {   // C_j's segment once per draft, then every row
-      const int j = c * JC + jl;
-      float cj[Gm::EPL];
-#pragma unroll
-      for (int e = 0; e < Gm::EPL; e += 4) {
-        const f32x4 cv = ld4(&s_C[j][cl * Gm::EPL + e]);
-        cj[e] = cv.x; cj[e + 1] = cv.y; cj[e + 2] = cv.z; cj[e + 3] = cv.w;
+        for (int k = 0; k < NLD; ++k)
+          st4(&tw[2 * k + (q.lane >> 5)][4 * (ch % (SW / 4))],
+              f32x4{f[k][0], f[k][1], f[k][2], f[k][3]});
       }
 #pragma unroll
-      for (int k = 0; k < Gm::NLD; ++k) {
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < Gm::EPL; ++e) acc += f[k][e] * cj[e];
-        d[k * JC + jl] = acc;
+      for (int cb = 0; cb < SW / 16; ++cb) {
+        const f32x4 bv = ld4(&tw[li][16 * cb + 4 * lq]);
+        const int n0 = ps * SW + 16 * cb + 4 * lq;
+        const f32x4 av = li < NPAD ? ld4(&s_C[li < NPAD ? li : 0][n0]) : f32x4{0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc, 0, 0, 0);
       }
     }
-    xreduce<V, Gm::LPR>(d, q.lane);
+    __syncthreads();   // s_yb, s_gam complete
+    // register r of lane (li, lq): draft 4 lq + r, row 16 w + li
+    const int pr = 16 * (q.tid >> 6) + li;
 #pragma unroll
-    for (int jj = 0; jj < M::VOUT; ++jj) res[c][jj] = d[jj];
-  }
-  __syncthreads();
-  if (M::writer(q.lane)) {
+    for (int r = 0; r < 4; ++r) {
+      const int j = 4 * lq + r;
+      if (j < NPAD && j < n) {
+        float yv;
+        if (ok) {
+          float yb = 0.f;
+#pragma unroll
+          for (int g = 0; g < QD; ++g) yb += s_yb[g][j][pr];
+          yv = s_gam[j] * acc[r] + yb;
+        } else {
+          yv = __builtin_nanf("");
+        }
+        a.y[j * sx + q.unit * P + pr] = yv;
+      }
+    }
+  } else {
+    // Row dots with every C_j, reduced across the LPR lanes of a row.  At most
+    // 32 partial sums per lane at a time: drafts go in chunks of JC.
+    constexpr int JC = (Gm::NLD * NPAD <= 32) ? NPAD : 32 / Gm::NLD;
+    constexpr int NCH = NPAD / JC;
+    constexpr int V = Gm::NLD * JC;
+    using M = XMap<V, Gm::LPR>;
+    float res[NCH][M::VOUT];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
+      // keep the scheduler from hoisting this chunk's LDS reads into the last
+      if (c > 0) __builtin_amdgcn_sched_barrier(0);
+      float d[V];
 #pragma unroll
-      for (int jj = 0; jj < M::VOUT; ++jj) {
-        const int idx = M::index(q.lane, jj);
-        const int k = idx / JC, j = c * JC + idx % JC;
-        if (j < n) {
-          const int pr = k * Gm::RPL + rr0;
-          float yv;
-          if (ok) {
-            float yb = 0.f;
+      for (int jl = 0; jl < JC; ++jl) {   // C_j's segment once per draft, then every row
+        const int j = c * JC + jl;
+        float cj[Gm::EPL];
 #pragma unroll
-            for (int g = 0; g < QD; ++g) yb += s_yb[g][j][pr];
-            yv = s_gam[j] * (scale * res[c][jj]) + yb;
-          } else {
-            yv = __builtin_nanf("");
+        for (int e = 0; e < Gm::EPL; e += 4) {
+          const f32x4 cv = ld4(&s_C[j][cl * Gm::EPL + e]);
+          cj[e] = cv.x; cj[e + 1] = cv.y; cj[e + 2] = cv.z; cj[e + 3] = cv.w;
+        }
+#pragma unroll
+        for (int k = 0; k < Gm::NLD; ++k) {
+          float acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < Gm::EPL; ++e) acc += f[k][e] * cj[e];
+          d[k * JC + jl] = acc;
+        }
+      }
+      xreduce<V, Gm::LPR>(d, q.lane);
+#pragma unroll
+      for (int jj = 0; jj < M::VOUT; ++jj) res[c][jj] = d[jj];
+    }
+    __syncthreads();
+    if (M::writer(q.lane)) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+        for (int jj = 0; jj < M::VOUT; ++jj) {
+          const int idx = M::index(q.lane, jj);
+          const int k = idx / JC, j = c * JC + idx % JC;
+          if (j < n) {
+            const int pr = k * Gm::RPL + rr0;
+            float yv;
+            if (ok) {
+              float yb = 0.f;
+#pragma unroll
+              for (int g = 0; g < QD; ++g) yb += s_yb[g][j][pr];
+              yv = s_gam[j] * (scale * res[c][jj]) + yb;
+            } else {
+              yv = __builtin_nanf("");
+            }
+            a.y[j * sx + q.unit * P + pr] = yv;
           }
-          a.y[j * sx + q.unit * P + pr] = yv;
         }
       }
     }
@@ -728,9 +801,11 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
         const f32x4 bi = ld4(&s_Bf[i][q.c4 * 4]);
         const float w = s_fw[i];
 #pragma unroll
-        for (int k = 0; k < NLD; ++k) hv[k] += (w * s_xf[i][k * RPL + q.r0]) * bi;
+        for (int k = 0; k < NLD; ++k) hv[k] += (w * s_xf[i][rowk(k)]) * bi;
       }
-      store_tile(a.ckpt + q.unit * (P * N), q, hv);
+      float* ck = a.ckpt + q.unit * (P * N) + q.c4 * 4;
+#pragma unroll
+      for (int k = 0; k < NLD; ++k) st_nt(ck + rowk(k) * N, hv[k]);
     }
   }
 
@@ -899,17 +974,29 @@ hipError_t launch_m2_commit(const M2Args& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The matrix-core contraction of verify (MF above) is correct but slower at
+// the serving shape than the FMA dots with DPP reductions (4 drafts 167 vs
+// 137 us, 8 drafts 202 vs 164 us, with the folded commit 207 vs 165 us per
+// launch at batch 256 x 80 heads), so the FMA path is the default; building
+// with -DRSSM_M2_VERIFY_MFMA selects MF for fp32 verification of 3-8 drafts.
+#ifdef RSSM_M2_VERIFY_MFMA
+constexpr bool kVerifyMfma = true;
+#else
+constexpr bool kVerifyMfma = false;
+#endif
+
 template <int EB, bool COMMIT = false>
 static void launch_m2_verify_eb(const M2Args& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.batch * a.H)), block(NT);
+  constexpr bool MF = EB == 4 && kVerifyMfma;   // fp32, 3-8 drafts on the matrix cores
   if (a.n_pos <= 1)
     hipLaunchKernelGGL((m2_verify_kernel<EB, 1, COMMIT>), grid, block, 0, s, a);
   else if (a.n_pos <= 2)
     hipLaunchKernelGGL((m2_verify_kernel<EB, 2, COMMIT>), grid, block, 0, s, a);
   else if (a.n_pos <= 4)
-    hipLaunchKernelGGL((m2_verify_kernel<EB, 4, COMMIT>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((m2_verify_kernel<EB, 4, COMMIT, MF>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((m2_verify_kernel<EB, 8, COMMIT>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((m2_verify_kernel<EB, 8, COMMIT, MF>), grid, block, 0, s, a);
 }
 
 hipError_t launch_m2_verify(const M2Args& a, hipStream_t s) {

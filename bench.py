@@ -230,42 +230,95 @@ def run_gdn(torch, R, syn, steps, warmup, seed=0, pool_n=16):
     return res
 
 
+def _sweep_time(torch, run, n):
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    run(n)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end)
+
+
 def run_m2_interval_sweep(torch, R, syn, steps, seed=0, pool_n=16,
-                          intervals=(1, 2, 4, 8, 16)):
-    """Replay cost vs state traffic: the headline Mamba-2 shape with the fused
-    commit every `interval` tokens (ring = interval).  Interval 1 writes the
-    state every step, like the eager kernel."""
+                          intervals=(1, 2, 4, 8, 16, 32)):
+    """Replay cost vs state traffic (explainer, "How to think about using it":
+    the commit interval trades replay work against state writes): the headline
+    Mamba-2 shape with a commit every `interval` tokens (ring = interval),
+    fused into the interval's last step ("fused") or as a standalone
+    rssm_commit after it ("standalone").  Interval 1 writes the state every
+    step, like the eager kernel."""
     b, H, G, P, N = 256, 80, 8, 64, 128
     A, D = syn.m2_params(seed, H)
     pool = syn.m2_steps(seed, 0, pool_n, b, H, G, P, N)
     dev = {k: torch.from_numpy(v).to("cuda") for k, v in pool.items()}
     h0 = torch.from_numpy(syn.m2_state0(seed, b, H, P, N))
     y = torch.empty((b, H, P), dtype=torch.float32, device="cuda")
+    S, _, entry, _, idx = m2_bytes(b, H, G, P, N)
     res = {}
     for interval in intervals:
         L = R.Layer.mamba2(b, H, G, P, N, interval)
         L.A.copy_(torch.from_numpy(A))
         L.D.copy_(torch.from_numpy(D))
         L.ckpt.copy_(h0)
+        n = max(1, steps // interval) * interval
+        row = {}
+        for mode in ("fused", "standalone"):
+            def run(m):
+                for t in range(m):
+                    j = t % pool_n
+                    last = (t + 1) % interval == 0
+                    R.rssm_mamba2_step(L, dev["x"][j], dev["B"][j], dev["C"][j], dev["dt"][j], y,
+                                       commit_after=last and mode == "fused")
+                    if last and mode == "standalone":
+                        R.rssm_commit(L, None, 0)
 
-        def run(n):
-            for t in range(n):
+            run(2 * interval)                  # whole cycles: the timed run starts at len 0
+            ms = _sweep_time(torch, run, n)
+            assert R.rssm_status(L) == 0
+            if mode == "fused":
+                byt = sum(m2_fused_bytes(b, H, G, P, N, l) if l == interval - 1 else
+                          m2_step_bytes(b, H, G, P, N, l) for l in (t % interval for t in range(n)))
+            else:   # every step appends; each commit reads and writes the state, reads the ring
+                byt = sum(m2_step_bytes(b, H, G, P, N, t % interval) for t in range(n)) + \
+                    (n // interval) * (2 * S + interval * entry + idx)
+            row[mode] = dict(seq_tok_s=round(b * n / (ms * 1e-3), 1), bytes_per_step=round(byt / n),
+                             hbm_gbps=round(byt / (ms * 1e-3) / 1e9, 1))
+        res[str(interval)] = row
+        del L
+        torch.cuda.empty_cache()
+    del dev
+    return res
+
+
+def run_gdn_interval_sweep(torch, R, syn, steps, seed=0, pool_n=16, intervals=(1, 2, 4, 8, 16)):
+    """The same trade-off for Gated DeltaNet at batch 256 x 32 heads (d 128),
+    commit fused into the interval's last step (ring = interval)."""
+    b, H, d = 256, 32, 128
+    pool = syn.gdn_steps(seed, 0, pool_n, b, H, d, d)
+    dev = {k: torch.from_numpy(v).to("cuda") for k, v in pool.items()}
+    names = ("q", "k", "v", "alpha", "beta")
+    o = torch.empty((b, H, d), dtype=torch.float32, device="cuda")
+    S, inp, entry, out = gdn_bytes(b, H, d)
+    res = {}
+    for interval in intervals:
+        L = R.Layer.gdn(b, H, d, d, interval)
+
+        def run(m):
+            for t in range(m):
                 j = t % pool_n
-                R.rssm_mamba2_step(L, dev["x"][j], dev["B"][j], dev["C"][j], dev["dt"][j], y,
-                                   commit_after=(t + 1) % interval == 0)
+                R.rssm_gdn_step(L, *(dev[s][j] for s in names), o,
+                                commit_after=(t + 1) % interval == 0)
 
-        run(2 * interval)                      # whole cycles: the timed run starts at len 0
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        n = (steps // interval) * interval
-        torch.cuda.synchronize()
-        start.record()
-        run(n)
-        end.record()
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end)
+        n = max(1, steps // interval) * interval
+        run(2 * interval)
+        ms = _sweep_time(torch, run, n)
         assert R.rssm_status(L) == 0
-        byt = sum(m2_fused_bytes(b, H, G, P, N, l) if l == interval - 1 else
-                  m2_step_bytes(b, H, G, P, N, l) for l in (t % interval for t in range(n)))
+        byt = 0
+        for t in range(n):
+            ln = t % interval
+            byt += (2 * S + inp + ln * entry + out) if ln == interval - 1 else \
+                (S + inp + ln * entry + entry + out)
         res[str(interval)] = dict(seq_tok_s=round(b * n / (ms * 1e-3), 1),
                                   bytes_per_step=round(byt / n),
                                   hbm_gbps=round(byt / (ms * 1e-3) / 1e9, 1))
@@ -632,8 +685,10 @@ def run_dual_stack(torch, R, syn, steps, seed=0, layers=12, pool_n=8):
     """12 GDN layers at batch 256 with a low-precision serving checkpoint,
     commit every 8 steps; seq-tokens/s through the whole stack.  DUAL layers
     fold in the step that fills the interval (commit_after; that step reads
-    fp32), also measured with the standalone commit (`*_standalone`); SHARED
-    layers commit standalone (the fused commit needs the fp32 checkpoint)."""
+    fp32), also measured with the standalone commit (`*_standalone`) and with
+    one set of buffer indices shared by the 12 layers (`*_shared_indices`:
+    11 read-only layers, the last one moves the indices); SHARED layers commit
+    standalone (the fused commit needs the fp32 checkpoint)."""
     b, H, d, interval, cap = 256, 32, 128, 8, 8
     pool = syn.gdn_steps(seed, 0, pool_n, b, H, d, d)
     dev = {k: torch.from_numpy(v).to("cuda") for k, v in pool.items()}
@@ -642,6 +697,7 @@ def run_dual_stack(torch, R, syn, steps, seed=0, layers=12, pool_n=8):
     res = {}
     inputs = [R.make_inputs(**{s: dev[s][j] for s in names}) for j in range(pool_n)]
     for scheme, sname, fused in ((R.RSSM_DUAL, "dual", True),
+                                 (R.RSSM_DUAL, "dual_shared_indices", True),
                                  (R.RSSM_DUAL, "dual_standalone", False),
                                  (R.RSSM_SHARED, "shared", False), (None, "eager_lp", False)):
         for lp, lname in ((R.RSSM_BF16, "bf16"), (R.RSSM_E4M3, "e4m3")):
@@ -651,6 +707,9 @@ def run_dual_stack(torch, R, syn, steps, seed=0, layers=12, pool_n=8):
             if scheme is not None:
                 for L in Ls:
                     R.rssm_commit(L, None, 0)
+            if sname == "dual_shared_indices":
+                for L in Ls[:-1]:
+                    L.share_indices(Ls[-1], readonly=True)
             start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             start.record()
@@ -670,7 +729,9 @@ def run_dual_stack(torch, R, syn, steps, seed=0, layers=12, pool_n=8):
             ms = start.elapsed_time(end)
             for L in Ls:
                 assert R.rssm_status(L) == 0
-            key = f"dual_{lname}_standalone" if sname == "dual_standalone" else f"{sname}_{lname}"
+            key = {"dual_standalone": f"dual_{lname}_standalone",
+                   "dual_shared_indices": f"dual_{lname}_shared_indices"}.get(sname,
+                                                                          f"{sname}_{lname}")
             res[key] = b * steps / (ms * 1e-3)
             del Ls
             torch.cuda.empty_cache()
@@ -726,7 +787,9 @@ def run_m2_lowprec(torch, R, syn, steps, seed=0, pool_n=16):
             torch.cuda.synchronize()
             ms = start.elapsed_time(end)
             assert R.rssm_status(L) == 0
-            key = f"dual_{lname}_standalone" if sname == "dual_standalone" else f"{sname}_{lname}"
+            key = {"dual_standalone": f"dual_{lname}_standalone",
+                   "dual_shared_indices": f"dual_{lname}_shared_indices"}.get(sname,
+                                                                          f"{sname}_{lname}")
             res[key] = round(b * n / (ms * 1e-3), 1)
             del L
             torch.cuda.empty_cache()
@@ -869,6 +932,7 @@ def main():
             sec["gdn_12layer_stack_seq_tok_s"] = {k: round(v, 1) for k, v in du.items()}
         if want("sweep"):
             sec["mamba2_commit_interval_sweep"] = run_m2_interval_sweep(torch, R, syn, 256)
+            sec["gdn_commit_interval_sweep"] = run_gdn_interval_sweep(torch, R, syn, 256)
         if want("lowprec"):
             sec["mamba2_lowprec_seq_tok_s"] = run_m2_lowprec(torch, R, syn, 128)
         if want("tree"):

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 9
+#define RSSM_ABI_VERSION 10
 #define RSSM_ARRIVE_STRIDE 32   /* uint32 elements between two sequences' counters */
 #define RSSM_NOALLOC_MAX_BATCH 4096  /* sequences served by rssm_mamba2_step_noalloc    */
 
@@ -82,6 +82,19 @@ extern "C" {
  * and NaN natively and raise no bit. */
 
 typedef enum { RSSM_MAMBA2 = 1, RSSM_GDN = 2 } rssm_kind;
+
+/* rssm_layer.flags (explainer, "How to think about using it": buffers per
+ * layer or shared).  The layers of one model see the same tokens, rollbacks
+ * and commits, so their buffer indices move in lockstep and may live in one
+ * set of arrays.  A layer with RSSM_LAYER_INDEX_READONLY reads ckpt_pos and
+ * len but never writes them and uses no arrival counters (arrive may be
+ * NULL); its per-sequence errors are raised as usual.  Give every layer of a
+ * stack the same ckpt_pos/len arrays, set the flag on all but one, and make
+ * each call (step, commit, verify, append, prefill, rollback) on the layer
+ * without the flag after the same call on the others, on the same stream:
+ * that call moves the shared indices for the whole stack.  rssm_rollback on a
+ * read-only layer validates its arguments and does nothing. */
+#define RSSM_LAYER_INDEX_READONLY 1u
 
 /* Checkpoint precision scheme (explainer, "Separate precisions for serving vs
  * updating state"; abstract: the low-precision copy serves outputs, the
@@ -111,8 +124,11 @@ typedef enum {
  *             nheads % ngroups == 0);  GDN: must be 1
  *   dim_v     Mamba-2: headdim P;  GDN: dv  (rows of the state)
  *   dim_k     Mamba-2: dstate N;   GDN: dk  (columns of the state)
- *   capacity  ring slots per sequence (1..16); entry j since the checkpoint
- *             lives in slot (ckpt_pos + j) % capacity
+ *   capacity  ring slots per sequence (1..16; a Mamba-2 layer with an fp32
+ *             checkpoint may have up to 32 for rssm_mamba2_step[_noalloc],
+ *             rssm_commit and rssm_rollback, the calls of plain decoding;
+ *             every other call returns RSSM_EUNSUPPORTED above 16); entry j
+ *             since the checkpoint lives in slot (ckpt_pos + j) % capacity
  *   Instantiated: Mamba-2 P=64, N=128; GDN dk=dv=128; all schemes for both.
  *
  * Checkpoints  [batch][nheads][dim_v][dim_k]
@@ -143,7 +159,7 @@ typedef enum {
 typedef struct rssm_layer {
   int32_t kind, scheme, lp_dtype;
   int32_t batch, nheads, ngroups, dim_v, dim_k, capacity;
-  int32_t reserved0;
+  int32_t flags;      /* 0 or RSSM_LAYER_INDEX_READONLY; other bits: RSSM_EINVAL */
   float* ckpt;
   void* ckpt_lp;
   float* lp_scale;

@@ -49,7 +49,9 @@ uint32_t* scratch_address() {
 
 inline bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_layer_dims(const rssm_layer* L) {
+// max_cap: the largest ring capacity the call serves (16; 32 for the
+// Mamba-2 fp32 step, commit and rollback).
+int check_layer_dims(const rssm_layer* L, int max_cap = rssm::kMaxCap) {
   if (!L) return RSSM_EINVAL;
   if (L->kind != RSSM_MAMBA2 && L->kind != RSSM_GDN) return RSSM_EINVAL;
   if (L->scheme < RSSM_F32 || L->scheme > RSSM_SHARED) return RSSM_EINVAL;
@@ -57,7 +59,7 @@ int check_layer_dims(const rssm_layer* L) {
       L->capacity < 1)
     return RSSM_EINVAL;
   if ((int64_t)L->batch * L->nheads > (int64_t)INT32_MAX) return RSSM_EUNSUPPORTED;
-  if (L->capacity > rssm::kMaxCap) return RSSM_EUNSUPPORTED;
+  if (L->capacity > max_cap) return RSSM_EUNSUPPORTED;
   if (L->kind == RSSM_MAMBA2) {
     if (L->nheads % L->ngroups != 0) return RSSM_EINVAL;
     if (L->dim_v != 64 || L->dim_k != 128) return RSSM_EUNSUPPORTED;
@@ -67,7 +69,15 @@ int check_layer_dims(const rssm_layer* L) {
   }
   if (L->scheme != RSSM_F32 && L->lp_dtype != RSSM_BF16 && L->lp_dtype != RSSM_E4M3)
     return RSSM_EINVAL;
+  if (L->flags & ~RSSM_LAYER_INDEX_READONLY) return RSSM_EINVAL;
   return RSSM_OK;
+}
+
+// The capacity a call may serve on this layer: 32 for the fp32 Mamba-2 step,
+// commit and rollback (long_ring), else 16.
+int max_cap_for(const rssm_layer* L, bool long_ring) {
+  return long_ring && L && L->kind == RSSM_MAMBA2 && L->scheme == RSSM_F32 ? rssm::kMaxCapM2
+                                                                         : rssm::kMaxCap;
 }
 
 // Pointer checks of the descriptor.  Skipped at batch == 0, where every
@@ -94,7 +104,8 @@ int check_state(const rssm_layer* L, bool need_arrive = true) {
   for (int i = 0; i < nring; ++i)
     if (!L->ring[i]) return RSSM_EINVAL;
   if (!a16(L->ring[0]) || !a16(L->ring[1])) return RSSM_EALIGN;
-  if (!L->ckpt_pos || !L->len || !L->status || (need_arrive && !L->arrive)) return RSSM_EINVAL;
+  if (!L->ckpt_pos || !L->len || !L->status) return RSSM_EINVAL;
+  if (need_arrive && !(L->flags & RSSM_LAYER_INDEX_READONLY) && !L->arrive) return RSSM_EINVAL;
   return RSSM_OK;
 }
 
@@ -116,6 +127,7 @@ rssm::M2Args m2_args(const rssm_layer* L) {
   a.len = L->len;
   a.arrive = L->arrive;
   a.status = L->status;
+  a.idx_ro = (L->flags & RSSM_LAYER_INDEX_READONLY) != 0;
   a.batch = L->batch;
   a.H = L->nheads;
   a.G = L->ngroups;
@@ -137,6 +149,7 @@ rssm::GdnArgs gdn_args(const rssm_layer* L) {
   a.len = L->len;
   a.arrive = L->arrive;
   a.status = L->status;
+  a.idx_ro = (L->flags & RSSM_LAYER_INDEX_READONLY) != 0;
   a.batch = L->batch;
   a.H = L->nheads;
   a.cap = L->capacity;
@@ -213,7 +226,7 @@ const char* rssm_strerror(int code) {
 
 int rssm_mamba2_step(const rssm_layer* L, const float* x, const float* B, const float* C,
                      const float* dt, float* y, int commit_after, void* stream) {
-  int rc = check_layer_dims(L);
+  int rc = check_layer_dims(L, max_cap_for(L, true));
   if (rc) return rc;
   if (L->kind != RSSM_MAMBA2) return RSSM_EINVAL;
   if (commit_after && L->scheme == RSSM_SHARED) return RSSM_EUNSUPPORTED;
@@ -233,7 +246,7 @@ int rssm_mamba2_step(const rssm_layer* L, const float* x, const float* B, const 
 int rssm_mamba2_step_noalloc(const rssm_layer* L, const float* x, const float* B,
                              const float* C, const float* dt, float* y, int commit_after,
                              void* stream) {
-  int rc = check_layer_dims(L);
+  int rc = check_layer_dims(L, max_cap_for(L, true));
   if (rc) return rc;
   if (L->kind != RSSM_MAMBA2) return RSSM_EINVAL;
   if (commit_after && L->scheme == RSSM_SHARED) return RSSM_EUNSUPPORTED;
@@ -279,7 +292,7 @@ int rssm_gdn_step(const rssm_layer* L, const float* q, const float* k, const flo
 }
 
 int rssm_commit(const rssm_layer* L, const uint8_t* mask, int min_len, void* stream) {
-  int rc = check_layer_dims(L);
+  int rc = check_layer_dims(L, max_cap_for(L, true));
   if (rc) return rc;
   if (min_len < 0) return RSSM_ERANGE;
   if (L->batch == 0) return RSSM_OK;
@@ -409,11 +422,12 @@ int rssm_append_path(const rssm_layer* L, int n_nodes, const int32_t* path,
 }
 
 int rssm_rollback(const rssm_layer* L, const int32_t* n_reject, void* stream) {
-  int rc = check_layer_dims(L);
+  int rc = check_layer_dims(L, max_cap_for(L, true));
   if (rc) return rc;
   if (L->batch == 0) return RSSM_OK;
   if ((rc = check_layer_ptrs(L)) || (rc = check_state(L))) return rc;
   if (!n_reject) return RSSM_EINVAL;
+  if (L->flags & RSSM_LAYER_INDEX_READONLY) return RSSM_OK;   // the updating layer rolls back
   return hip_rc(rssm::launch_rollback(L->ckpt_pos, L->len, L->status, n_reject, L->batch,
                                       L->capacity, S(stream)));
 }

@@ -16,6 +16,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxCap = 16;   // ring slots per sequence
+constexpr int kMaxCapM2 = 32; // Mamba-2 fp32 step and commit: rings of up to 32 slots
 constexpr int kMaxPos = 8;    // draft positions per verify call
 // Arrival counters sit one 128-byte line apart: every workgroup of a launch
 // performs one atomic on its sequence's counter, and atomics to one line are
@@ -215,8 +216,14 @@ __device__ __forceinline__ void indices_consumed(int32_t len, int64_t pos) {
 // reads have returned.  Once the count is complete every workgroup of the
 // sequence holds its copy of the indices and the last one may update them at
 // any time.  Returns the pre-increment count (thread 0).
+// Pre-increment count returned for a layer whose indices are read-only: no
+// counter is touched, no workgroup updates the indices, and per-sequence
+// errors are reported by every workgroup of the sequence.
+constexpr uint32_t kNoArrival = 0xffffffffu;
+
 __device__ __forceinline__ uint32_t arrive_early(uint32_t* arrive, int b, int32_t len,
-                                                 int64_t pos) {
+                                                 int64_t pos, bool ro = false) {
+  if (ro) return kNoArrival;
   uint32_t old = 0u;
   if (threadIdx.x == 0) {
     uint32_t inc = 1u;
@@ -245,7 +252,7 @@ __device__ __forceinline__ void finish_update(uint32_t* arrive, int64_t* pos, in
 // one workgroup per sequence that reports a per-sequence error, so that a
 // failing batch costs one status atomic per sequence, not one per workgroup.
 __device__ __forceinline__ bool last_arrival(uint32_t old, int nwg) {
-  return threadIdx.x == 0 && old == (uint32_t)(nwg - 1);
+  return threadIdx.x == 0 && (old == (uint32_t)(nwg - 1) || old == kNoArrival);
 }
 
 __device__ __forceinline__ void raise_status(uint32_t* status, uint32_t bits) {

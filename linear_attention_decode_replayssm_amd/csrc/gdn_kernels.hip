@@ -519,7 +519,7 @@ __global__ __launch_bounds__((LP != 0 ? 512 : step_threads<EB>())) void gdn_step
 #pragma unroll
   for (int k = 0; k < NLD; ++k) raw[k] = ld_nt_u(base + ((k * RPL + q.r0) * DK + q.cl * EPL) * EB);
   indices_consumed(len, pos);
-  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos, a.idx_ro);
 
   __shared__ __attribute__((aligned(16))) EntrySmem es;
   stash_entries<NTH>(er, ok ? L : 0, q.tid, es);
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(NTH) void gdn_commit_kernel(GdnArgs a) {
   else
     load_f32_tile<RPL, NLD>(hv, rows, q);
   indices_consumed(len, pos);
-  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos, a.idx_ro);
   __shared__ __attribute__((aligned(16))) EntrySmem es;
   __shared__ __attribute__((aligned(16))) FoldSmem<ROWS> sm;
   stash_entries<NTH>(er, len, q.tid, es);
@@ -627,9 +627,8 @@ __global__ __launch_bounds__(NTH) void gdn_commit_kernel(GdnArgs a) {
 // the drafts, a tree appends nothing.  One 512-thread workgroup per
 // head: wave j carries draft j's query backwards through entries len+j..0;
 // then one pass over the checkpoint dots every row with all carried queries.
-// Eight fp32 drafts take ~90 registers, which leaves two workgroups per CU;
-// capped at six waves per SIMD (three workgroups, a few registers spilled)
-// the 7-draft tree verify runs ~5% faster.
+// Eight fp32 drafts take ~80 registers (two to three workgroups per CU); no
+// occupancy cap is set, since a cap of six waves per SIMD spills to scratch.
 //
 // COMMIT (fp32 checkpoint only): a sequence whose buffer holds at least
 // a.min_len entries also folds those entries into its checkpoint from the
@@ -638,7 +637,7 @@ __global__ __launch_bounds__(NTH) void gdn_commit_kernel(GdnArgs a) {
 // buffer and the drafts become entries 0..n-1 (the same ring slots).  The
 // outputs are those of commit-then-verify.
 template <int EB, int NPAD, bool COMMIT = false>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NPAD == 8 && EB == 4 && !COMMIT ? 6 : 1))) void gdn_verify_kernel(GdnArgs a) {
+__global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
   static_assert(!COMMIT || EB == 4, "the fused commit folds the fp32 checkpoint");
   constexpr int NTH = 512, ROWS = DV;
   using Gm = LpGeo<EB, NTH, ROWS>;
@@ -667,7 +666,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(NPAD == 8 &
 #pragma unroll
   for (int k = 0; k < NLD; ++k) raw[k] = ld_nt_u(base + ((k * RPL + q.r0) * DK + q.cl * EPL) * EB);
   indices_consumed(len, pos);
-  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos, a.idx_ro);
 
   __shared__ __attribute__((aligned(16))) EntrySmem es;
   __shared__ __attribute__((aligned(16))) float s_q[NPAD][DK];
@@ -831,7 +830,7 @@ __global__ __launch_bounds__(256) void gdn_append_path_kernel(GdnArgs a) {
     ok = j >= 0 && j < n;
   }
   indices_consumed(len, pos);
-  const uint32_t arrived = arrive_early(a.arrive, b, len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, b, len, pos, a.idx_ro);
   if (ok) {
     const int slot0 = (int)(pos % cap);
     const long unit = (long)b * a.H + h;

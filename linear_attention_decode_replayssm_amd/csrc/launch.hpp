@@ -36,6 +36,7 @@ struct M2Args {
   const int32_t* path;      // append_path: [b][depth] draft indices
   const int32_t* path_len;  // append_path: [b]
   int depth;
+  int idx_ro;               // indices read, never written (RSSM_LAYER_INDEX_READONLY)
 };
 
 // Gated DeltaNet arguments.
@@ -65,6 +66,7 @@ struct GdnArgs {
   const int32_t* path;
   const int32_t* path_len;
   int depth;
+  int idx_ro;           // as in M2Args
 };
 
 hipError_t launch_m2_step(const M2Args& a, bool fused, hipStream_t s);

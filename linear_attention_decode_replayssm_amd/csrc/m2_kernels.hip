@@ -147,13 +147,17 @@ __device__ __forceinline__ void store_tile(float* ck, const Geo& q, const f32x4 
 // LP (fused commit of a DUAL layer): the boundary step reads, folds and stores
 // the fp32 checkpoint as for F32, takes its output from the fp32 checkpoint it
 // reads, and then writes the low-precision image of the folded state.
-template <int EB, bool FUSED, int HPW = 1, int LP = 0>
+//
+// MAXL: the most buffered entries (ring capacity) the kernel serves, 16 or 32;
+// each 16-lane group of the prologue handles MAXL / 16 entries.
+template <int EB, bool FUSED, int HPW = 1, int LP = 0, int MAXL = kMaxCap>
 __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
   constexpr int ROWS = HPW * P;
   using Gm = RdGeo<EB, ROWS>;
   static_assert(!FUSED || (EB == 4 && HPW == 1), "the fused commit folds one fp32 head");
   static_assert(LP == 0 || FUSED, "a low-precision image is written only by the fused commit");
   static_assert(HPW <= 16, "dt of head hl is loaded by lane hl of an entry's 16 lanes");
+  static_assert(MAXL % 16 == 0 && MAXL * HPW <= NT, "entries per 16-lane group");
   const Geo q = geometry<HPW>(a);
   const int cap = a.cap;
   float* ck = a.ckpt + q.unit * (P * N);
@@ -182,28 +186,33 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
     return i < len ? a.ring_B + (q.gunit * cap + ring_slot(slot0, i, cap)) * N : Bt;
   };
 
-  // prologue operands: entry ei = tid/16 dots segment sg of B_ei with C_t
-  // (lane sg < HPW also loads head sg's dt_ei); thread (p, qd) sums entries
-  // qd, qd+QD, ... of every head's x_i[p]
+  // prologue operands: entries ei + 16 u (u < EPG) of the 16-lane group
+  // ei = tid/16 dot segment sg of B with C_t (lane sg < HPW also loads head
+  // sg's dt); thread (p, qd) sums entries qd, qd+QD, ... of every head's x_i[p]
   constexpr int SEG = N / 16;
-  constexpr int XPT = kMaxCap / QD;  // buffered x values per thread and head
+  constexpr int EPG = MAXL / 16;     // entries per 16-lane group
+  constexpr int XPT = MAXL / QD;     // buffered x values per thread and head
   const int ei = q.tid >> 4, sg = q.tid & 15;
   const int p = q.tid % P, qd = q.tid / P;
-  f32x4 bseg[SEG / 4], cseg[SEG / 4];
-  float dti = 0.f;
+  f32x4 bseg[EPG][SEG / 4], cseg[SEG / 4];
+  float dti[EPG];
   float xv[HPW][XPT];
   if (ok) {
 #pragma unroll
-    for (int e = 0; e < SEG / 4; ++e) {
-      bseg[e] = f32x4{0.f, 0.f, 0.f, 0.f};
-      cseg[e] = ld4(Ct + sg * SEG + 4 * e);
-    }
-    if (ei < L) {
+    for (int e = 0; e < SEG / 4; ++e) cseg[e] = ld4(Ct + sg * SEG + 4 * e);
 #pragma unroll
-      for (int e = 0; e < SEG / 4; ++e) bseg[e] = ld4(Bsrc(ei) + sg * SEG + 4 * e);
-      if (sg < HPW)
-        dti = ei < len ? a.ring_dt[(q.unit + sg) * cap + ring_slot(slot0, ei, cap)]
-                       : a.dt[q.unit + sg];
+    for (int u = 0; u < EPG; ++u) {
+      const int en = ei + 16 * u;
+      dti[u] = 0.f;
+#pragma unroll
+      for (int e = 0; e < SEG / 4; ++e) bseg[u][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (en < L) {
+#pragma unroll
+        for (int e = 0; e < SEG / 4; ++e) bseg[u][e] = ld4(Bsrc(en) + sg * SEG + 4 * e);
+        if (sg < HPW)
+          dti[u] = en < len ? a.ring_dt[(q.unit + sg) * cap + ring_slot(slot0, en, cap)]
+                            : a.dt[q.unit + sg];
+      }
     }
 #pragma unroll
     for (int hl = 0; hl < HPW; ++hl) {
@@ -224,38 +233,42 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
   u32x4 raw[Gm::NLD];
   load_raw<EB, ROWS>(a, q.unit, q.tid, raw);
   indices_consumed(len, pos);
-  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos, a.idx_ro);
 
-  __shared__ float s_e[kMaxCap], s_dt[HPW][kMaxCap], s_w[HPW][kMaxCap], s_fw[kMaxCap];
+  __shared__ float s_e[MAXL], s_dt[HPW][MAXL], s_w[HPW][MAXL], s_fw[MAXL];
   __shared__ float s_gamma[HPW];
   __shared__ float s_yb[QD][HPW][P];
   // fused commit: the entries' x_i and B_i, parked from the prologue registers
-  __shared__ __attribute__((aligned(16))) float s_x[FUSED ? kMaxCap : 1][P];
-  __shared__ __attribute__((aligned(16))) float s_B[FUSED ? kMaxCap : 1][N];
+  __shared__ __attribute__((aligned(16))) float s_x[FUSED ? MAXL : 1][P];
+  __shared__ __attribute__((aligned(16))) float s_B[FUSED ? MAXL : 1][N];
 
   if (ok) {
-    {  // e_i = B_i . C_t
+#pragma unroll
+    for (int u = 0; u < EPG; ++u) {  // e_i = B_i . C_t
+      const int en = ei + 16 * u;
       float part = 0.f;
 #pragma unroll
-      for (int e = 0; e < SEG / 4; ++e) part += dot4(bseg[e], cseg[e]);
+      for (int e = 0; e < SEG / 4; ++e) part += dot4(bseg[u][e], cseg[e]);
       part = group_sum<16>(part);
-      if (sg == 0 && ei < L) s_e[ei] = part;
-      if (sg < HPW && ei < L) s_dt[sg][ei] = dti;
+      if (sg == 0 && en < L) s_e[en] = part;
+      if (sg < HPW && en < L) s_dt[sg][en] = dti[u];
       if constexpr (FUSED) {   // no second fetch of the entries at the fold
-        if (ei < L) {
+        if (en < L) {
 #pragma unroll
-          for (int e = 0; e < SEG / 4; ++e) st4(&s_B[ei][sg * SEG + 4 * e], bseg[e]);
-        }
-#pragma unroll
-        for (int m = 0; m < XPT; ++m) {
-          const int i = qd + m * QD;
-          if (i < L) s_x[i][p] = xv[0][m];
+          for (int e = 0; e < SEG / 4; ++e) st4(&s_B[en][sg * SEG + 4 * e], bseg[u][e]);
         }
       }
     }
+    if constexpr (FUSED) {
+#pragma unroll
+      for (int m = 0; m < XPT; ++m) {
+        const int i = qd + m * QD;
+        if (i < L) s_x[i][p] = xv[0][m];
+      }
+    }
     __syncthreads();
-    if (q.tid < HPW * kMaxCap) {  // decay weights from dt suffix sums, per head
-      const int hl = q.tid / kMaxCap, i = q.tid % kMaxCap;
+    if (q.tid < HPW * MAXL) {  // decay weights from dt suffix sums, per head
+      const int hl = q.tid / MAXL, i = q.tid % MAXL;
       if (i < L) {
         float suf = 0.f;
         for (int j = i + 1; j < L; ++j) suf += s_dt[hl][j];
@@ -340,13 +353,16 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
         for (int m = 0; m < XPT; ++m)
           if (qd + m * QD == len) a.ring_x[((q.unit + hl) * cap + s) * P + p] = xv[hl][m];
       }
-      if (ei == len) {
-        if ((q.h % (a.H / a.G)) == 0) {
 #pragma unroll
-          for (int e = 0; e < SEG / 4; ++e)
-            st4(a.ring_B + (q.gunit * cap + s) * N + sg * SEG + 4 * e, bseg[e]);
+      for (int u = 0; u < EPG; ++u) {
+        if (ei + 16 * u == len) {
+          if ((q.h % (a.H / a.G)) == 0) {
+#pragma unroll
+            for (int e = 0; e < SEG / 4; ++e)
+              st4(a.ring_B + (q.gunit * cap + s) * N + sg * SEG + 4 * e, bseg[u][e]);
+          }
+          if (sg < HPW) a.ring_dt[(q.unit + sg) * cap + s] = dti[u];
         }
-        if (sg < HPW) a.ring_dt[(q.unit + sg) * cap + s] = dti;
       }
     }
   }
@@ -365,7 +381,7 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
 // the low-precision image of the result (with len 0 it only refreshes the
 // image); SHARED folds the dequantised low-precision copy and re-encodes it.
 // One workgroup holds a whole head, so the E4M3 scale's amax is local.
-template <int SCHEME, int LP>
+template <int SCHEME, int LP, int MAXL = kMaxCap>
 __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
   const Geo q = geometry(a);
   const int cap = a.cap;
@@ -383,7 +399,7 @@ __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
   // the buffered entries first, into registers (thread tid: x of entry
   // (tid + 256u) / 64, float4 (tid + 256u) % 32 of B_{(tid + 256u) / 32}, dt_tid):
   // waiting for them then leaves the state stream in flight
-  constexpr int XR = kMaxCap * P / NT, BR = kMaxCap * N / 4 / NT;
+  constexpr int XR = MAXL * P / NT, BR = MAXL * N / 4 / NT;
   float xr[XR];
   f32x4 br[BR];
   float dtr = 0.f;
@@ -409,14 +425,14 @@ __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
   else
     load_tile(ck, q, hv);
   indices_consumed(len, pos);
-  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos, a.idx_ro);
 
   const float Ah = a.A[q.h];
-  __shared__ float s_dt[kMaxCap], s_fw[kMaxCap];
+  __shared__ float s_dt[MAXL], s_fw[MAXL];
   __shared__ float s_gamma;
   __shared__ float s_red[NT / 64];
-  __shared__ __attribute__((aligned(16))) float s_x[kMaxCap][P];
-  __shared__ __attribute__((aligned(16))) float s_B[kMaxCap][N];
+  __shared__ __attribute__((aligned(16))) float s_x[MAXL][P];
+  __shared__ __attribute__((aligned(16))) float s_B[MAXL][N];
   if (L > 0) {
 #pragma unroll
     for (int u = 0; u < XR; ++u) {
@@ -608,7 +624,7 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
     }
   }
   indices_consumed(len, pos);   // its barrier also publishes the LDS above
-  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos, a.idx_ro);
 
   if (ok) {
     {  // e_{j,ei} = B_ei . C_j for every draft, 16 lanes per entry
@@ -851,7 +867,7 @@ __global__ __launch_bounds__(NT) void m2_append_path_kernel(M2Args a) {
     ok = j >= 0 && j < n;
   }
   indices_consumed(len, pos);
-  const uint32_t arrived = arrive_early(a.arrive, b, len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, b, len, pos, a.idx_ro);
   if (ok) {
     const int slot0 = (int)(pos % cap);
     const int hpg = a.H / a.G;
@@ -938,7 +954,12 @@ hipError_t launch_m2_step(const M2Args& a, bool fused, hipStream_t s) {
   // E4M3: two heads per workgroup when a group's head count allows it
   const bool pair = (a.H / a.G) % 2 == 0;
   const dim3 grid2((unsigned)(a.batch * (a.H / 2)));
-  if (a.scheme == kSchemeF32) {
+  if (a.scheme == kSchemeF32 && a.cap > kMaxCap) {   // rings of up to 32 entries
+    if (fused)
+      hipLaunchKernelGGL((m2_step_kernel<4, true, 1, 0, kMaxCapM2>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((m2_step_kernel<4, false, 1, 0, kMaxCapM2>), grid, block, 0, s, a);
+  } else if (a.scheme == kSchemeF32) {
     if (fused)
       hipLaunchKernelGGL((m2_step_kernel<4, true>), grid, block, 0, s, a);
     else
@@ -961,7 +982,9 @@ hipError_t launch_m2_step(const M2Args& a, bool fused, hipStream_t s) {
 
 hipError_t launch_m2_commit(const M2Args& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.batch * a.H)), block(NT);
-  if (a.scheme == kSchemeF32)
+  if (a.scheme == kSchemeF32 && a.cap > kMaxCap)
+    hipLaunchKernelGGL((m2_commit_kernel<kSchemeF32, 0, kMaxCapM2>), grid, block, 0, s, a);
+  else if (a.scheme == kSchemeF32)
     hipLaunchKernelGGL((m2_commit_kernel<kSchemeF32, 0>), grid, block, 0, s, a);
   else if (a.scheme == kSchemeDual && a.lp == kLpBf16)
     hipLaunchKernelGGL((m2_commit_kernel<kSchemeDual, kLpBf16>), grid, block, 0, s, a);

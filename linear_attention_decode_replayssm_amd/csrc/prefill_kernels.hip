@@ -159,7 +159,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void m2
     for (int t = 0; t < 8; ++t) acc[t] = ld_nt(a.ckpt + e0 + 16 * t);
   }
   indices_consumed(len, pos);
-  const uint32_t arrived = arrive_early(a.arrive, b, len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, b, len, pos, a.idx_ro);
 
   __shared__ __attribute__((aligned(16))) float s_x[Q][MP + PAD];
   __shared__ __attribute__((aligned(16))) float s_B[Q][MN + PAD];
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(4))) void g
     for (int t = 0; t < 8; ++t) acc[t] = ld_nt(a.ckpt + e0 + 16 * t);
   }
   indices_consumed(len, pos);
-  const uint32_t arrived = arrive_early(a.arrive, b, len, pos);
+  const uint32_t arrived = arrive_early(a.arrive, b, len, pos, a.idx_ro);
 
   __shared__ __attribute__((aligned(16))) float s_k[Q][GPITCH];
   __shared__ __attribute__((aligned(16))) float s_q[Q][GPITCH];

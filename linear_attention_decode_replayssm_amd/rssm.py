@@ -22,9 +22,10 @@ STATUS_OVERFLOW, STATUS_ROLLBACK, STATUS_NONFINITE, STATUS_INDEX = 1, 2, 4, 8
 RSSM_MAMBA2, RSSM_GDN = 1, 2
 RSSM_F32, RSSM_DUAL, RSSM_SHARED = 0, 1, 2
 RSSM_LP_NONE, RSSM_BF16, RSSM_E4M3 = 0, 1, 2
-RSSM_ABI_VERSION = 9
+RSSM_ABI_VERSION = 10
 RSSM_ARRIVE_STRIDE = 32   # uint32 elements between two sequences' arrival counters
 RSSM_NOALLOC_MAX_BATCH = 4096   # sequences rssm_mamba2_step_noalloc serves
+RSSM_LAYER_INDEX_READONLY = 1   # rssm_layer.flags: indices read, never written
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -34,7 +35,7 @@ class rssm_layer(ctypes.Structure):
     _fields_ = [("kind", _i32), ("scheme", _i32), ("lp_dtype", _i32),
                 ("batch", _i32), ("nheads", _i32), ("ngroups", _i32),
                 ("dim_v", _i32), ("dim_k", _i32), ("capacity", _i32),
-                ("reserved0", _i32),
+                ("flags", _i32),
                 ("ckpt", _vp), ("ckpt_lp", _vp), ("lp_scale", _vp),
                 ("A", _vp), ("D", _vp), ("ring", _vp * 4),
                 ("ckpt_pos", _vp), ("len", _vp), ("arrive", _vp), ("status", _vp)]
@@ -298,6 +299,7 @@ class Layer:
                  scheme=RSSM_F32, lp_dtype=RSSM_LP_NONE, device="cuda"):
         import torch
         self.kind, self.scheme, self.lp_dtype = kind, scheme, lp_dtype
+        self.flags = 0
         self.batch, self.nheads, self.ngroups = batch, nheads, ngroups
         self.dim_v, self.dim_k, self.capacity = dim_v, dim_k, capacity
         f32 = dict(dtype=torch.float32, device=device)
@@ -333,11 +335,19 @@ class Layer:
         """(Re)build the descriptor from the current tensors."""
         rings = (_vp * 4)(*([_ptr(r) for r in self.rings] + [None] * (4 - len(self.rings))))
         self.desc = rssm_layer(self.kind, self.scheme, self.lp_dtype, self.batch, self.nheads,
-                               self.ngroups, self.dim_v, self.dim_k, self.capacity, 0,
+                               self.ngroups, self.dim_v, self.dim_k, self.capacity, self.flags,
                                _ptr(self.ckpt), _ptr(self.ckpt_lp), _ptr(self.lp_scale),
                                _ptr(self.A), _ptr(self.D), rings, _ptr(self.ckpt_pos),
                                _ptr(self.len), _ptr(self.arrive), _ptr(self.status))
         return self.desc
+
+    def share_indices(self, owner, readonly=True):
+        """Use `owner`'s ckpt_pos / len arrays: one set of buffer indices for
+        layers that advance together.  readonly sets RSSM_LAYER_INDEX_READONLY
+        (every layer of the stack but the one whose calls move the indices)."""
+        self.ckpt_pos, self.len = owner.ckpt_pos, owner.len
+        self.flags = RSSM_LAYER_INDEX_READONLY if readonly else 0
+        return self.refresh()
 
     @classmethod
     def mamba2(cls, batch, nheads, ngroups, headdim, dstate, capacity, scheme=RSSM_F32,

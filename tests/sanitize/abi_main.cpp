@@ -43,7 +43,7 @@ int main() {
   expect(rssm_mamba2_step(&m2, nullptr, P(), P(), P(), P(), 0, nullptr), RSSM_EINVAL, "null x");
   expect(rssm_mamba2_step(&m2, P(), P(), P(8), P(), P(), 0, nullptr), RSSM_EALIGN, "misaligned C");
   rssm_layer bad = m2;
-  bad.capacity = 17;
+  bad.capacity = 33;
   expect(rssm_mamba2_step(&bad, P(), P(), P(), P(), P(), 0, nullptr), RSSM_EUNSUPPORTED, "capacity");
   bad = m2;
   bad.ngroups = 3;

@@ -60,7 +60,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert R.rssm_abi_version() == R.RSSM_ABI_VERSION == 9
+    assert R.rssm_abi_version() == R.RSSM_ABI_VERSION == 10
     for code in (0, -1, -2, -3, -4, -5):
         assert R.rssm_strerror(code)
     assert "unknown" in R.rssm_strerror(12345)
@@ -68,10 +68,10 @@ def test_version_and_strerror():
 
 def _m2_desc(**kw):
     d = dict(kind=R.RSSM_MAMBA2, scheme=R.RSSM_F32, lp_dtype=0, batch=0, nheads=8,
-             ngroups=1, dim_v=64, dim_k=128, capacity=16)
+             ngroups=1, dim_v=64, dim_k=128, capacity=16, flags=0)
     d.update(kw)
     L = R.rssm_layer(d["kind"], d["scheme"], d["lp_dtype"], d["batch"], d["nheads"],
-                     d["ngroups"], d["dim_v"], d["dim_k"], d["capacity"], 0)
+                     d["ngroups"], d["dim_v"], d["dim_k"], d["capacity"], d["flags"])
     L.ckpt = kw.get("ckpt", FAKE)
     L.A = FAKE
     L.D = FAKE
@@ -157,7 +157,9 @@ def test_null_layer():
     (dict(ngroups=3), R.RSSM_EINVAL),               # 8 % 3 != 0
     (dict(dim_v=32), R.RSSM_EUNSUPPORTED),
     (dict(dim_k=64), R.RSSM_EUNSUPPORTED),
-    (dict(capacity=17), R.RSSM_EUNSUPPORTED),
+    (dict(capacity=33), R.RSSM_EUNSUPPORTED),
+    (dict(capacity=17, scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_BF16), R.RSSM_EUNSUPPORTED),
+    (dict(flags=2), R.RSSM_EINVAL),
     (dict(capacity=0), R.RSSM_EINVAL),
     (dict(scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_BF16), R.RSSM_EINVAL),   # ckpt_lp missing
     (dict(scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_LP_NONE), R.RSSM_EINVAL),
@@ -347,3 +349,28 @@ def test_noalloc_step_validation():
     assert f(L) == R.RSSM_EINVAL
     assert R.rssm_mamba2_step_noalloc(_m2_desc(batch=2), FAKE + 4, FAKE, FAKE, FAKE, FAKE, 0,
                                       stream=0, check=False) == R.RSSM_EALIGN
+
+
+def test_capacity_above_16_only_for_plain_mamba2_decode():
+    """Rings of 17..32 slots serve the fp32 Mamba-2 step, commit and rollback;
+    every other call refuses them before launching."""
+    L = _m2_desc(batch=4, capacity=20)
+    ins = R.make_inputs(x=FAKE, B=FAKE, C=FAKE, dt=FAKE)
+    assert R.rssm_verify(L, 2, ins, FAKE, stream=0, check=False) == R.RSSM_EUNSUPPORTED
+    assert R.rssm_prefill(L, 2, ins, FAKE, stream=0, check=False) == R.RSSM_EUNSUPPORTED
+    assert R.rssm_eager_step(L, ins, FAKE, stream=0, check=False) == R.RSSM_EUNSUPPORTED
+    G = _gdn_desc(batch=4, capacity=20)
+    assert R.rssm_gdn_step(G, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, stream=0,
+                           check=False) == R.RSSM_EUNSUPPORTED
+    assert R.rssm_commit(G, None, 0, stream=0, check=False) == R.RSSM_EUNSUPPORTED
+    assert R.rssm_rollback(G, FAKE, stream=0, check=False) == R.RSSM_EUNSUPPORTED
+
+
+def test_readonly_indices_need_no_counters_and_rollback_is_a_no_op():
+    L = _m2_desc(batch=4, flags=R.RSSM_LAYER_INDEX_READONLY)
+    L.arrive = None
+    assert R.rssm_rollback(L, FAKE, stream=0, check=False) == R.RSSM_OK   # nothing launched
+    assert R.rssm_rollback(L, None, stream=0, check=False) == R.RSSM_EINVAL
+    L2 = _m2_desc(batch=4)
+    L2.arrive = None
+    assert _step(L2) == R.RSSM_EINVAL                  # an updating layer needs its counters

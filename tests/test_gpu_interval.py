@@ -1,9 +1,11 @@
 """Commit-interval independence on the GPU: with an fp32 checkpoint the outputs
 do not depend on when the buffer is folded, so plain decode with intervals
-1, 2, 4, 8 and 16 (ring = interval, fused and standalone commits) must match the
-fp64 oracle's eager recurrence within the fp32 tolerance, and the checkpoint
-after a final commit must match the eager state.  Interval 1 commits after
-every step (the state is written every step, as in the eager kernel)."""
+1, 2, 4, 8 and 16 (ring = interval, fused and standalone commits; Mamba-2 also
+20 and 32, the rings of more than 16 slots that its fp32 step and commit
+serve) must match the fp64 oracle's eager recurrence within the fp32
+tolerance, and the checkpoint after a final commit must match the eager
+state.  Interval 1 commits after every step (the state is written every
+step, as in the eager kernel)."""
 import numpy as np
 import pytest
 
@@ -15,18 +17,19 @@ import gpu_util as gu
 pytestmark = pytest.mark.gpu
 P, N, D_ = 64, 128, 128
 INTERVALS = (1, 2, 4, 8, 16)
+M2_INTERVALS = INTERVALS + (20, 32)
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["standalone_commit", "fused_commit"])
 def test_m2_interval_independence(fused):
-    T, b, H, G = 32, 3, 10, 5
+    T, b, H, G = 70, 3, 10, 5
     A, D = syn.m2_params(90, H)
     h0 = syn.m2_state0(90, b, H, P, N)
     st = syn.m2_steps(90, 0, T, b, H, G, P, N)
     h = h0.astype(np.float64)
     y_ref = oracle.m2_eager(A, D, st["x"], st["B"], st["C"], st["dt"], h)
     d = {k: gu.dev(v) for k, v in st.items()}
-    for interval in INTERVALS:
+    for interval in M2_INTERVALS:
         L = gu.m2_layer(A, D, h0, G, interval)
         y, pos, ln = gu.m2_decode(L, d, interval, fused)
         gu.check_m2_outputs(gu.host(y), y_ref, st["x"], D)

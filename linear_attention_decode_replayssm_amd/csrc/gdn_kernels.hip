@@ -532,23 +532,12 @@ __global__ __launch_bounds__((LP != 0 ? 512 : step_threads<EB>())) void gdn_step
 
   using M = XMap<NLD, LPR>;
   const int r_out = q.row0 + M::index(q.lane, 0) * RPL + q.r0;   // this lane's output row
-  float obuf = 0.f;
-  if (ok) obuf = carry_acc<EPL, LPR>(es, L - 1, q.cl, r_out, qv);
-
   float d[NLD];
-#pragma unroll
-  for (int k = 0; k < NLD; ++k) {
-    float f[EPL];
-    expand<EB>(raw[k], f);
-    float acc = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc += f[e] * qv[e];
-    d[k] = acc;
-  }
-  xreduce<NLD, LPR>(d, q.lane);
-  if (M::writer(q.lane)) a.o[q.unit * DV + r_out] = ok ? scale * d[0] + obuf : __builtin_nanf("");
 
-  if constexpr (FUSED) {   // fold the whole buffer, this entry included, and store
+  if constexpr (FUSED) {
+    // fold the whole buffer, this entry included, and store.  The folded
+    // state is the state after this token, so the output is o_t = S_t q_t
+    // read from it: no backward carry of the query.
     static_assert(EB == 4, "fused commit folds the fp32 checkpoint");
     if (ok) {
       f32x4 hv[NLD];
@@ -557,10 +546,30 @@ __global__ __launch_bounds__((LP != 0 ? 512 : step_threads<EB>())) void gdn_step
         hv[k] = f32x4{__uint_as_float(raw[k].x), __uint_as_float(raw[k].y),
                       __uint_as_float(raw[k].z), __uint_as_float(raw[k].w)};
       fold_apply<NTH, ROWS, NLD>(hv, es, L, q.row0, q, sm);
+      const f32x4 q4 = {qv[0], qv[1], qv[2], qv[3]};
+#pragma unroll
+      for (int k = 0; k < NLD; ++k) d[k] = dot4(hv[k], q4);
+      xreduce<NLD, LPR>(d, q.lane);
+      if (M::writer(q.lane)) a.o[q.unit * DV + r_out] = d[0];
       store_f32_tile<RPL, NLD>(hv, a.ckpt + q.unit * (DV * DK) + q.row0 * DK, q);
       if constexpr (LP != 0) store_lp<LP>(hv, a, q, sm.red);   // DUAL: re-quantise the copy
+    } else if (M::writer(q.lane)) {
+      a.o[q.unit * DV + r_out] = __builtin_nanf("");
     }
   } else {
+    float obuf = 0.f;
+    if (ok) obuf = carry_acc<EPL, LPR>(es, L - 1, q.cl, r_out, qv);
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      float f[EPL];
+      expand<EB>(raw[k], f);
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc += f[e] * qv[e];
+      d[k] = acc;
+    }
+    xreduce<NLD, LPR>(d, q.lane);
+    if (M::writer(q.lane)) a.o[q.unit * DV + r_out] = ok ? scale * d[0] + obuf : __builtin_nanf("");
     if (ok && q.row0 == 0) append_from_regs<NTH>(a, src, er, len, q.tid);
   }
 

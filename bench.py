@@ -745,6 +745,58 @@ def run_dual_stack(torch, R, syn, steps, seed=0, layers=12, pool_n=8):
     return res
 
 
+def eager_lp_rooflines(torch, R, syn, reps=20, seed=0):
+    """Per-launch time and HBM fraction of the eager comparators that keep the
+    state in low precision only (decode, update in fp32, re-encode every step)
+    at the serving shapes.  Their arithmetic per state element (decode,
+    update, the block maximum of the E4M3 scale, encode) is issued by the
+    vector ALUs against one or two bytes of traffic, so they are bound by
+    VALU issue, not by HBM: reported beside the dual/eager-lp throughputs so
+    that those ratios can be read against comparators that are not at the
+    memory roofline."""
+    out = {}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for kind in ("gdn", "mamba2"):
+        if kind == "gdn":
+            b, H, d = 256, 32, 128
+            st = syn.gdn_steps(seed, 0, 1, b, H, d, d)
+            names, S, ins, outb = ("q", "k", "v", "alpha", "beta"), b * H * d * d, \
+                (3 * b * H * d + 2 * b * H) * 4, b * H * d * 4
+        else:
+            b, H, G, P, N = 256, 80, 8, 64, 128
+            st = syn.m2_steps(seed, 0, 1, b, H, G, P, N)
+            names, S, ins, outb = ("x", "B", "C", "dt"), b * H * P * N, \
+                (b * H * P + 2 * b * G * N + b * H) * 4, b * H * P * 4
+        dev = {k: torch.from_numpy(v[0]).to("cuda") for k, v in st.items()}
+        inp = R.make_inputs(**{k: dev[k] for k in names})
+        for lp, lname, eb in ((R.RSSM_BF16, "bf16", 2), (R.RSSM_E4M3, "e4m3", 1)):
+            if kind == "gdn":
+                L = R.Layer.gdn(b, H, d, d, 8, scheme=R.RSSM_SHARED, lp_dtype=lp)
+                o = torch.empty((b, H, d), dtype=torch.float32, device="cuda")
+            else:
+                L = R.Layer.mamba2(b, H, G, P, N, 8, scheme=R.RSSM_SHARED, lp_dtype=lp)
+                o = torch.empty((b, H, P), dtype=torch.float32, device="cuda")
+            for _ in range(3):
+                R.rssm_eager_step(L, inp, o)
+            torch.cuda.synchronize()
+            ev[0].record()
+            for _ in range(reps):
+                R.rssm_eager_step(L, inp, o)
+            ev[1].record()
+            torch.cuda.synchronize()
+            us = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+            byt = 2 * S * eb + ins + outb + (2 * b * H * 4 if lp == R.RSSM_E4M3 else 0)
+            out[f"{kind}_{lname}"] = dict(us_per_launch=round(us, 2), bytes_per_launch=byt,
+                                          hbm_frac=round(byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 3))
+            del L
+        del dev
+        torch.cuda.empty_cache()
+    out["bound"] = "valu"
+    out["note"] = ("eager comparators with the state in low precision only: VALU-bound (decode, "
+                   "update, block amax, encode per state element), not tuned to the HBM roofline")
+    return out
+
+
 def run_m2_lowprec(torch, R, syn, steps, seed=0, pool_n=16):
     """Mamba-2 headline shape with a low-precision serving checkpoint (dual:
     fp32 receives the commits; shared: the copy is the only state) and the
@@ -939,6 +991,7 @@ def main():
         if want("stack"):
             du = run_dual_stack(torch, R, syn, 32)
             sec["gdn_12layer_stack_seq_tok_s"] = {k: round(v, 1) for k, v in du.items()}
+            sec["eager_lp_comparators"] = eager_lp_rooflines(torch, R, syn)
         if want("sweep"):
             sec["mamba2_commit_interval_sweep"] = run_m2_interval_sweep(torch, R, syn, 256)
             sec["gdn_commit_interval_sweep"] = run_gdn_interval_sweep(torch, R, syn, 256)

@@ -21,6 +21,7 @@ Usage: python bench.py [--gpus 1] [--steps 1024] [--warmup 64] [--no-secondary]
        [--no-cpu]
 """
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -92,16 +93,26 @@ def gdn_bytes(b, H, d, s_ck=4):
 
 
 # ------------------------------------------------------------------ timing --
+def _dev_state(torch, h):
+    """An initial state uploaded once, then copied on the device into each
+    layer a workload sets up.  Pageable uploads of hundreds of MB just before
+    a timed loop were seen to stall the host thread for tens of milliseconds
+    inside the timed region (at the first launches of the loop)."""
+    t = torch.from_numpy(h).to("cuda")
+    torch.cuda.synchronize()
+    return t
+
+
 def run_m2(torch, R, syn, steps, warmup, seed=0, pool_n=64):
     b, H, G, P, N, interval, cap = 256, 80, 8, 64, 128, 8, 8
     A, D = syn.m2_params(seed, H)
-    h0 = syn.m2_state0(seed, b, H, P, N)
+    h0 = _dev_state(torch, syn.m2_state0(seed, b, H, P, N))
     pool = syn.m2_steps(seed, 0, pool_n, b, H, G, P, N)
     dev = {k: torch.from_numpy(v).to("cuda") for k, v in pool.items()}
     L = R.Layer.mamba2(b, H, G, P, N, cap)
     L.A.copy_(torch.from_numpy(A))
     L.D.copy_(torch.from_numpy(D))
-    L.ckpt.copy_(torch.from_numpy(h0))
+    L.ckpt.copy_(h0)
     y = torch.empty((b, H, P), dtype=torch.float32, device="cuda")
     t = 0
 
@@ -164,7 +175,7 @@ def run_m2(torch, R, syn, steps, warmup, seed=0, pool_n=64):
                # `interval` also writes it (the fused commit)
                ckpt_bytes_per_step=(b * H * P * N * 4) * (interval + 1) / interval)
     # eager comparator on the same shapes, same pool
-    L.ckpt.copy_(torch.from_numpy(h0))
+    L.ckpt.copy_(h0)
     inputs = [R.make_inputs(x=dev["x"][j], B=dev["B"][j], C=dev["C"][j], dt=dev["dt"][j])
               for j in range(pool_n)]
     for i in range(warmup):
@@ -259,7 +270,7 @@ def run_m2_interval_sweep(torch, R, syn, steps, seed=0, pool_n=16,
     A, D = syn.m2_params(seed, H)
     pool = syn.m2_steps(seed, 0, pool_n, b, H, G, P, N)
     dev = {k: torch.from_numpy(v).to("cuda") for k, v in pool.items()}
-    h0 = torch.from_numpy(syn.m2_state0(seed, b, H, P, N))
+    h0 = _dev_state(torch, syn.m2_state0(seed, b, H, P, N))
     y = torch.empty((b, H, P), dtype=torch.float32, device="cuda")
     S, _, entry, _, idx = m2_bytes(b, H, G, P, N)
     res = {}
@@ -346,10 +357,11 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     dev = {k: torch.from_numpy(v).to("cuda") for k, v in pool.items()}
     accept = syn.accept_counts(seed, rounds, b, n)
     nrej = torch.from_numpy((n - accept).astype(np.int32)).to("cuda")
+    h0 = _dev_state(torch, syn.m2_state0(seed, b, H, P, N))
     L = R.Layer.mamba2(b, H, G, P, N, cap)
     L.A.copy_(torch.from_numpy(A))
     L.D.copy_(torch.from_numpy(D))
-    L.ckpt.copy_(torch.from_numpy(syn.m2_state0(seed, b, H, P, N)))
+    L.ckpt.copy_(h0)
     out = torch.empty((n, b, H, P), dtype=torch.float32, device="cuda")
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -379,8 +391,7 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
                us_per_round=ms * 1e3 / rounds,
                bytes_per_round=total / rounds,
                hbm_gbps=total / (ms * 1e-3) / 1e9)
-    del L
-    torch.cuda.empty_cache()
+    del L   # the next phase reuses the same cached blocks
 
     # the same rounds with the commit folded into the next verify
     # (rssm_verify_commit): a due buffer waits for the next round's state read,
@@ -388,7 +399,7 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     L = R.Layer.mamba2(b, H, G, P, N, 16)
     L.A.copy_(torch.from_numpy(A))
     L.D.copy_(torch.from_numpy(D))
-    L.ckpt.copy_(torch.from_numpy(syn.m2_state0(seed, b, H, P, N)))
+    L.ckpt.copy_(h0)
     torch.cuda.synchronize()
     start.record()
     for r in range(rounds):
@@ -412,12 +423,11 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     # the same rounds appending only the accepted drafts: the drafts verified
     # as a chain-shaped tree (nothing appended, a due buffer folded from the
     # same state read), then the accepted prefix appended; no rollback
-    del L
-    torch.cuda.empty_cache()
+    del L   # the next phase reuses the same cached blocks
     L = R.Layer.mamba2(b, H, G, P, N, 16)
     L.A.copy_(torch.from_numpy(A))
     L.D.copy_(torch.from_numpy(D))
-    L.ckpt.copy_(torch.from_numpy(syn.m2_state0(seed, b, H, P, N)))
+    L.ckpt.copy_(h0)
     path = torch.arange(n, dtype=torch.int32, device="cuda").repeat(b, 1)
     acc_d = torch.from_numpy(accept.astype(np.int32)).to("cuda")
     chain = list(range(-1, n - 1))
@@ -433,8 +443,7 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     torch.cuda.synchronize()
     ams = start.elapsed_time(end)
     assert R.rssm_status(L) == 0
-    del L
-    torch.cuda.empty_cache()
+    del L   # the next phase reuses the same cached blocks
     res["accepted_only"] = dict(rounds_per_s=rounds / (ams * 1e-3),
                                 accepted_seq_tok_s=float(accept.sum()) / (ams * 1e-3),
                                 us_per_round=ams * 1e3 / rounds,
@@ -452,7 +461,7 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     L.A.copy_(torch.from_numpy(A))
     L.D.copy_(torch.from_numpy(D))
     slots = torch.empty((n + 1, b, H, P, N), dtype=torch.float32, device="cuda")
-    slots[0].copy_(torch.from_numpy(syn.m2_state0(seed, b, H, P, N)))
+    slots[0].copy_(h0)
     cur = torch.zeros(b, dtype=torch.int32, device="cuda")
     acc_d = torch.from_numpy(accept.astype(np.int32)).to("cuda")
     torch.cuda.synchronize()
@@ -472,7 +481,7 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     res["eager_bytes_per_round"] = float(ebytes)
     res["eager_hbm_gbps"] = ebytes * rounds / (ems * 1e-3) / 1e9
     res["speedup_vs_eager_spec"] = ems / ms
-    del L, dev, slots
+    del L, dev, slots, h0
     torch.cuda.empty_cache()
     return res
 
@@ -536,8 +545,7 @@ def run_gdn_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end)
     assert R.rssm_status(L) == 0
-    del L
-    torch.cuda.empty_cache()
+    del L   # the next phase reuses the same cached blocks
     # the commit folded into the next verify (ring 16, as for Mamba-2)
     L = R.Layer.gdn(b, H, d, d, 16)
     torch.cuda.synchronize()
@@ -549,8 +557,7 @@ def run_gdn_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     torch.cuda.synchronize()
     fms = start.elapsed_time(end)
     assert R.rssm_status(L) == 0
-    del L
-    torch.cuda.empty_cache()
+    del L   # the next phase reuses the same cached blocks
     L = R.Layer.gdn(b, H, d, d, cap)
     slots = torch.zeros((n + 1, b, H, d, d), dtype=torch.float32, device="cuda")
     cur = torch.zeros(b, dtype=torch.int32, device="cuda")
@@ -605,7 +612,7 @@ def run_tree_rounds(torch, R, syn, rounds, seed=0):
     L = R.Layer.mamba2(b, H, G, P, N, cap)
     L.A.copy_(torch.from_numpy(A))
     L.D.copy_(torch.from_numpy(D))
-    L.ckpt.copy_(torch.from_numpy(syn.m2_state0(seed, b, H, P, N)))
+    L.ckpt.copy_(_dev_state(torch, syn.m2_state0(seed, b, H, P, N)))
     out = torch.empty((n, b, H, P), dtype=torch.float32, device="cuda")
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -651,7 +658,7 @@ def run_prefill(torch, R, syn, kind, T=512, reps=5, seed=0, pool_n=64):
         L = R.Layer.mamba2(b, H, G, P, N, 8)
         L.A.copy_(torch.from_numpy(A))
         L.D.copy_(torch.from_numpy(D))
-        L.ckpt.copy_(torch.from_numpy(syn.m2_state0(seed, b, H, P, N)))
+        L.ckpt.copy_(_dev_state(torch, syn.m2_state0(seed, b, H, P, N)))
         names, out_name, dv, state_bytes = ("x", "B", "C", "dt"), "x", P, b * H * P * N * 4
     else:
         H, dk = 32, 128
@@ -807,7 +814,7 @@ def run_m2_lowprec(torch, R, syn, steps, seed=0, pool_n=16):
     A, D = syn.m2_params(seed, H)
     pool = syn.m2_steps(seed, 0, pool_n, b, H, G, P, N)
     dev = {k: torch.from_numpy(v).to("cuda") for k, v in pool.items()}
-    h0 = torch.from_numpy(syn.m2_state0(seed, b, H, P, N))
+    h0 = _dev_state(torch, syn.m2_state0(seed, b, H, P, N))
     y = torch.empty((b, H, P), dtype=torch.float32, device="cuda")
     res = {}
     for scheme, sname, fused in ((R.RSSM_DUAL, "dual", True),
@@ -918,6 +925,12 @@ def main():
     from linear_attention_decode_replayssm_amd import synthetic as syn
     R.lib()                                   # fail loudly if the HIP library is missing
     torch.cuda.init()
+    # Python's cyclic collector stays off while anything is timed (as timeit
+    # does): with torch loaded a full collection takes tens of milliseconds,
+    # and one was seen to land inside a timed loop of short launches.  Cycles
+    # are collected explicitly between workloads instead.
+    gc.collect()
+    gc.disable()
 
     if args.calib_copy:
         n = CALIB_COPY_BYTES // 4
@@ -977,7 +990,10 @@ def main():
     out["stream_ceilings"] = stream_ceilings(torch, R)
     if not args.no_secondary:
         only = set(filter(None, args.only.split(",")))
-        want = lambda name: not only or name in only
+
+        def want(name):
+            gc.collect()   # between workloads, outside every timed region
+            return not only or name in only
         sec = {}
         sec_steps = max(64, min(args.steps, 256))
         g = None

@@ -83,7 +83,8 @@ __device__ __forceinline__ int tile_index() {
 // same index assignment as an exact xor partner).  So DPP row permutations
 // serve for M <= 8 (quad_perm for 1 and 2, row_half_mirror i <-> 7-i for 4,
 // row_mirror i <-> 15-i for 8), ds_swizzle xor-16 for 16 and ds_bpermute only
-// for 32.
+// for 32.  The sums below take bits 4 and 5 with the lane swaps instead
+// (swap_add); these two forms remain for the wave-wide max and xor folds.
 template <int M>
 __device__ __forceinline__ float rpartner(float v) {
   const int x = __float_as_int(v);
@@ -103,11 +104,36 @@ __device__ __forceinline__ float rpartner(float v) {
   return __int_as_float(r);
 }
 
+// Exchange across lane bit M = 16 or 32 with the gfx950 lane swaps
+// (v_permlane16_swap / v_permlane32_swap, checked on the GPU with an in-bounds
+// probe): afterwards a lane with bit M clear holds (its own a, its partner's
+// a) and a lane with bit M set holds (its partner's b, its own b).  So a + b is
+// a + partner's a on the lower lanes and b + partner's b on the upper ones --
+// one step of the transposed reduction below, in two VALU instructions and
+// without the LDS round trip of ds_swizzle / ds_bpermute or the selects of
+// the DPP form.  With a == b it is a butterfly step.  The whole wave must be
+// active (every call site is wave-uniform).
+template <int M>
+__device__ __forceinline__ float swap_add(float a, float b) {
+  static_assert(M == 16 || M == 32, "lane swaps exist for bits 4 and 5");
+  uint32_t x, y;
+  if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    x = r[0];
+    y = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    x = r[0];
+    y = r[1];
+  }
+  return __uint_as_float(x) + __uint_as_float(y);
+}
+
 // Sum over the LPR lanes of a lane group (every lane receives the sum).
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {
-  if constexpr (LPR >= 64) v += rpartner<32>(v);
-  if constexpr (LPR >= 32) v += rpartner<16>(v);
+  if constexpr (LPR >= 64) v = swap_add<32>(v, v);
+  if constexpr (LPR >= 32) v = swap_add<16>(v, v);
   if constexpr (LPR >= 16) v += rpartner<8>(v);
   if constexpr (LPR >= 8) v += rpartner<4>(v);
   if constexpr (LPR >= 4) v += rpartner<2>(v);
@@ -128,16 +154,24 @@ struct XRed {
     if constexpr (M == 0) {
       return;
     } else if constexpr (C > 1) {
-      const bool up = (lane & M) != 0;
+      if constexpr (M >= 16) {
 #pragma unroll
-      for (int j = 0; j < C / 2; ++j) {
-        const float send = up ? v[j] : v[j + C / 2];
-        const float keep = up ? v[j + C / 2] : v[j];
-        v[j] = keep + rpartner<M>(send);
+        for (int j = 0; j < C / 2; ++j) v[j] = swap_add<M>(v[j], v[j + C / 2]);
+      } else {
+        const bool up = (lane & M) != 0;
+#pragma unroll
+        for (int j = 0; j < C / 2; ++j) {
+          const float send = up ? v[j] : v[j + C / 2];
+          const float keep = up ? v[j + C / 2] : v[j];
+          v[j] = keep + rpartner<M>(send);
+        }
       }
       XRed<C / 2, M / 2>::run(v, lane);
     } else {
-      v[0] += rpartner<M>(v[0]);
+      if constexpr (M >= 16)
+        v[0] = swap_add<M>(v[0], v[0]);
+      else
+        v[0] += rpartner<M>(v[0]);
       XRed<1, M / 2>::run(v, lane);
     }
   }

@@ -1,12 +1,14 @@
-"""The dual-precision Gated DeltaNet stack at full length: 12 independent
-layers x 4096 steps, batch 16 x 32 heads (dk = dv = 128), S_0 = 0,
-alpha = exp(-softplus(N(0,1))), beta = sigmoid(N(0,1)), q and k unit-norm,
-v ~ N(0,1), fresh inputs every step; commit every 8 steps (explainer,
-"Separate precisions for serving vs updating state": a low-precision copy
-serves the output reads, only the fp32 checkpoint takes the folds).  The
-sequences are independent, so batch 16 gives the per-sequence errors that the
-same sequences would have at batch 256; the kernels at batch 256 are covered
-by test_gpu_serving_bounds.py.
+"""The dual-precision Gated DeltaNet stack at full length and at the serving
+shape: 12 independent layers x 4096 steps, batch 256 x 32 heads (dk = dv =
+128), S_0 = 0, alpha = exp(-softplus(N(0,1))), beta = sigmoid(N(0,1)), q and k
+unit-norm, v ~ N(0,1), fresh inputs every step; commit every 8 steps
+(explainer, "Separate precisions for serving vs updating state": a
+low-precision copy serves the output reads, only the fp32 checkpoint takes the
+folds).  The batch holds 16 seeded sequences, each 16 times (sequence
+c * 16 + b is a copy of sequence b): the kernels run the full batch-256 launch
+shape, the fp64 oracle follows the 16 distinct sequences, and every copy's
+outputs must equal its original's bit for bit (the sequences are independent
+and each (sequence, head) is computed alone).
 
 Every output vector of every scheme is compared with the fp64 oracle's eager
 recurrence on the same inputs, e = ||o - o_exact||_inf / ||o_exact||_inf.
@@ -48,6 +50,7 @@ pytestmark = pytest.mark.gpu
 
 NAMES = ("q", "k", "v", "alpha", "beta")
 LAYERS, STEPS, B, H, D, INTERVAL, CHUNK, WINDOW = 12, 4096, 16, 32, 128, 8, 64, 512
+REP = 16          # copies of the B distinct sequences: the launches run batch B * REP = 256
 SCHEMES = [("dual-bf16", R.RSSM_DUAL, R.RSSM_BF16), ("shared-bf16", R.RSSM_SHARED, R.RSSM_BF16),
            ("dual-e4m3", R.RSSM_DUAL, R.RSSM_E4M3), ("shared-e4m3", R.RSSM_SHARED, R.RSSM_E4M3),
            ("fp32", R.RSSM_F32, R.RSSM_LP_NONE)]
@@ -96,7 +99,7 @@ def test_stack_layer_full_length(layer):
     S = S0.astype(np.float64)
     L = {}
     for n, scheme, lp in SCHEMES:
-        L[n] = gu.gdn_layer(S0, INTERVAL, scheme=scheme, lp=lp)
+        L[n] = gu.gdn_layer(np.tile(S0, (REP, 1, 1, 1)), INTERVAL, scheme=scheme, lp=lp)
         if scheme == R.RSSM_DUAL:
             R.rssm_commit(L[n], None, 0)          # the copy starts as Q(S_0)
     esum = {n: np.zeros(NWIN) for n, _, _ in SCHEMES}
@@ -104,11 +107,14 @@ def test_stack_layer_full_length(layer):
     margin = {"dual-bf16": -np.inf, "dual-e4m3": -np.inf}
     cancelled = {n: [] for n in margin}
     ill = []
-    o = t_.empty((CHUNK, B, H, D), dtype=t_.float32, device="cuda")
+    o = t_.empty((CHUNK, REP * B, H, D), dtype=t_.float32, device="cuda")
+    o_rep = o.view(CHUNK, REP, B, H, D)
     U = B * H
     for c0 in range(0, STEPS, CHUNK):
         st = syn.gdn_steps(0, c0, CHUNK, B, H, D, D, layer=layer)
-        dv = {k: gu.dev(v) for k, v in st.items()}
+        # every input tiled over the batch: copy c of sequence b at c * B + b
+        dv = {k: gu.dev(v).repeat(1, REP, *([1] * (v.ndim - 2))).contiguous()
+              for k, v in st.items()}
         # exact outputs, the checkpoint at the start of every interval, and the
         # one-quantisation bound of each step
         o_exact = np.empty((CHUNK, B, H, D))
@@ -136,7 +142,9 @@ def test_stack_layer_full_length(layer):
                                 commit_after=fused and commit)
                 if commit and not fused:
                     R.rssm_commit(L[n], None, 0)
-            err = np.abs(gu.host(o).astype(np.float64) - o_exact)
+            same = bool((o_rep == o_rep[:, :1]).all())
+            assert same, (n, layer, c0, "a copy of a sequence differs from its original")
+            err = np.abs(gu.host(o_rep[:, 0].contiguous()).astype(np.float64) - o_exact)
             e = err.max(-1) / den
             esum[n][c0 // WINDOW] += e.sum()
             emax[n] = max(emax[n], float(e.max()))
@@ -212,8 +220,8 @@ def test_stack_pooled_drift_and_report():
     lines.append(f"fp32 vectors above 1e-4 of ||o_exact||_inf: {len(ill_all)} of "
                  f"{LAYERS * STEPS * B * H}; (e, sum_j |S_rj q_j| / ||o_exact||_inf): "
                  + " ".join(f"({x:.2e}, {c:.1f})" for x, c in sorted(ill_all)[-8:]))
-    print("\nGDN stack, 12 layers x 4096 steps, batch 16 x 32 heads:\n" + "\n".join(lines),
-          flush=True)
+    print("\nGDN stack, 12 layers x 4096 steps, batch 256 (16 sequences x 16 copies) x 32 "
+          "heads:\n" + "\n".join(lines), flush=True)
 
 
 def _row_sum_scales(st, S_start, idx, den):

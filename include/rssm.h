@@ -129,7 +129,9 @@ typedef enum {
  *             rssm_commit and rssm_rollback, the calls of plain decoding;
  *             every other call returns RSSM_EUNSUPPORTED above 16); entry j
  *             since the checkpoint lives in slot (ckpt_pos + j) % capacity
- *   Instantiated: Mamba-2 P=64, N=128; GDN dk=dv=128; all schemes for both.
+ *   Instantiated: Mamba-2 P=64, N=128; GDN dk=dv=128; all schemes for both;
+ *   batch * nheads <= 2^30 - 1 (RSSM_EUNSUPPORTED above: some launches take
+ *   two workgroups per head).
  *
  * Checkpoints  [batch][nheads][dim_v][dim_k]
  *   ckpt      fp32; required for F32 and DUAL, NULL for SHARED

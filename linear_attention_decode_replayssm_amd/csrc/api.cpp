@@ -58,7 +58,8 @@ int check_layer_dims(const rssm_layer* L, int max_cap = rssm::kMaxCap) {
   if (L->batch < 0 || L->nheads < 1 || L->ngroups < 1 || L->dim_v < 1 || L->dim_k < 1 ||
       L->capacity < 1)
     return RSSM_EINVAL;
-  if ((int64_t)L->batch * L->nheads > (int64_t)INT32_MAX) return RSSM_EUNSUPPORTED;
+  // launch grids hold up to two workgroups per head (half-head GDN kernels)
+  if ((int64_t)L->batch * L->nheads > (int64_t)INT32_MAX / 2) return RSSM_EUNSUPPORTED;
   if (L->capacity > max_cap) return RSSM_EUNSUPPORTED;
   if (L->kind == RSSM_MAMBA2) {
     if (L->nheads % L->ngroups != 0) return RSSM_EINVAL;

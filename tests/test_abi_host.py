@@ -161,6 +161,8 @@ def test_null_layer():
     (dict(capacity=17, scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_BF16), R.RSSM_EUNSUPPORTED),
     (dict(flags=2), R.RSSM_EINVAL),
     (dict(capacity=0), R.RSSM_EINVAL),
+    (dict(batch=2 ** 27, nheads=8), R.RSSM_EUNSUPPORTED),   # batch * nheads = 2^30
+    (dict(batch=2 ** 24, nheads=64, ngroups=8), R.RSSM_EUNSUPPORTED),
     (dict(scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_BF16), R.RSSM_EINVAL),   # ckpt_lp missing
     (dict(scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_LP_NONE), R.RSSM_EINVAL),
     (dict(ckpt=FAKE + 4), R.RSSM_EALIGN),

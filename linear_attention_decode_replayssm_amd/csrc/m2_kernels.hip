@@ -497,10 +497,17 @@ __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
 // with consecutive 1 KiB loads (rows 16w + 2k + lane/32, k = 0..7), parks
 // them in a wave-private LDS tile and reads the operands from there: no
 // cross-lane reduction, and no barrier between the waves for the transpose.
+//
+// W16 (fp32, eight drafts, no fold): 16 lanes per state row instead of 32,
+// each holding columns 4c..4c+3 and 64+4c..64+4c+3 of rows r0 + 16k (every
+// load instruction still reads 256 contiguous bytes per row).  The 4 rows x 8
+// drafts of partial sums per lane are then reduced across 16 lanes, with DPP
+// only, in one pass instead of two passes of 32 sums across 32 lanes.
 template <int EB, int NPAD, bool COMMIT = false, bool MF = false>
 __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   static_assert(!COMMIT || EB == 4, "the fused commit folds the fp32 checkpoint");
   static_assert(!MF || (EB == 4 && NPAD >= 4), "matrix-core contraction: fp32, 4 or 8 drafts");
+  constexpr bool W16 = EB == 4 && NPAD == 8 && !COMMIT && !MF;
   using Gm = RdGeo<EB>;
   const Geo q = geometry(a);
   const int cap = a.cap, n = a.n_pos;
@@ -571,6 +578,13 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
     const float* ck0 = a.ckpt + q.unit * (P * N) + q.c4 * 4;
 #pragma unroll
     for (int k = 0; k < NLD; ++k) raw[k] = ld_nt_u(ck0 + rowk(k) * N);
+  } else if constexpr (W16) {   // raw[2 k + hf]: row tid/16 + 16 k, column half hf
+    const float* ck0 = a.ckpt + q.unit * (P * N) + (q.tid >> 4) * N + 4 * (q.tid & 15);
+#pragma unroll
+    for (int k = 0; k < NLD / 2; ++k) {
+      raw[2 * k] = ld_nt_u(ck0 + 16 * k * N);
+      raw[2 * k + 1] = ld_nt_u(ck0 + 16 * k * N + 64);
+    }
   } else {
     load_raw<EB>(a, q.unit, q.tid, raw);
   }
@@ -741,6 +755,42 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
 #pragma unroll
           for (int g = 0; g < QD; ++g) yb += s_yb[g][j][pr];
           yv = s_gam[j] * acc[r] + yb;
+        } else {
+          yv = __builtin_nanf("");
+        }
+        a.y[j * sx + q.unit * P + pr] = yv;
+      }
+    }
+  } else if constexpr (W16) {
+    constexpr int RS = NLD / 2;        // rows per lane
+    constexpr int V = RS * NPAD;       // partial sums per lane: row k, draft j at k * NPAD + j
+    using M = XMap<V, 16>;
+    static_assert(M::BFLY == 0, "every lane writes");
+    const int c16 = q.tid & 15, r0 = q.tid >> 4;
+    float d[V];
+#pragma unroll
+    for (int j = 0; j < NPAD; ++j) {
+      const f32x4 c0 = ld4(&s_C[j][4 * c16]), c1 = ld4(&s_C[j][64 + 4 * c16]);
+#pragma unroll
+      for (int k = 0; k < RS; ++k)   // C_j of an absent draft is zero in s_C
+        d[k * NPAD + j] = f[2 * k][0] * c0.x + f[2 * k][1] * c0.y + f[2 * k][2] * c0.z +
+                          f[2 * k][3] * c0.w + f[2 * k + 1][0] * c1.x + f[2 * k + 1][1] * c1.y +
+                          f[2 * k + 1][2] * c1.z + f[2 * k + 1][3] * c1.w;
+    }
+    xreduce<V, 16>(d, q.lane);
+    __syncthreads();   // s_yb, s_gam complete
+#pragma unroll
+    for (int jj = 0; jj < M::VOUT; ++jj) {
+      const int idx = M::index(q.lane, jj);
+      const int k = idx / NPAD, j = idx % NPAD;
+      if (j < n) {
+        const int pr = r0 + 16 * k;
+        float yv;
+        if (ok) {
+          float yb = 0.f;
+#pragma unroll
+          for (int g = 0; g < QD; ++g) yb += s_yb[g][j][pr];
+          yv = s_gam[j] * d[jj] + yb;
         } else {
           yv = __builtin_nanf("");
         }

@@ -641,17 +641,19 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos, a.idx_ro);
 
   if (ok) {
-    {  // e_{j,ei} = B_ei . C_j for every draft, 16 lanes per entry
+    {  // e_{j,ei} = B_ei . C_j for every draft, 16 lanes per entry: the NPAD
+       // partial dots of a lane reduced together across its 16 lanes
+      float part[NPAD];
 #pragma unroll
-      for (int j = 0; j < NPAD; ++j) {
-        float part = 0.f;
-        if (j < n) {
+      for (int j = 0; j < NPAD; ++j) {   // C_j of an absent draft is zero in s_C
+        part[j] = 0.f;
 #pragma unroll
-          for (int e = 0; e < SEG / 4; ++e) part += dot4(bseg[e], ld4(&s_C[j][sgm * SEG + 4 * e]));
-        }
-        part = group_sum<16>(part);
-        if (sgm == 0) s_e[j][ei] = part;
+        for (int e = 0; e < SEG / 4; ++e) part[j] += dot4(bseg[e], ld4(&s_C[j][sgm * SEG + 4 * e]));
       }
+      xreduce<NPAD, 16>(part, q.lane);
+      using ME = XMap<NPAD, 16>;
+      static_assert(ME::VOUT == 1, "one sum per lane");
+      if (ME::writer(q.lane)) s_e[ME::index(q.lane, 0)][ei] = part[0];
     }
     __syncthreads();
     if (q.tid < NPAD * kMaxCap) {   // decay weights; zero off the path

@@ -631,11 +631,11 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
       for (int e = 0; e < SEG / 4; ++e) st4(&s_Ba[ei - len][sgm * SEG + 4 * e], bseg[e]);
       if (sgm == 0) s_dta[ei - len] = dti;
     }
+  }
 #pragma unroll
-    for (int m = 0; m < XPT; ++m) {
-      const int i = qd + m * QD;
-      if (i >= len && i < LT) s_xa[i - len][p] = xv[m];
-    }
+  for (int m = 0; m < XPT; ++m) {   // the drafts' x_j (append, and the outputs' D x_j)
+    const int i = qd + m * QD;
+    if (i >= len && i < LT) s_xa[i - len][p] = xv[m];
   }
   indices_consumed(len, pos);   // its barrier also publishes the LDS above
   const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos, a.idx_ro);
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
       }
     }
     __syncthreads();
-    {  // sum_i w_{j,i} x_i[p], and D x_j[p] from the thread holding entry len + j
+    {  // sum_i w_{j,i} x_i[p] (the outputs add D x_j[p] from s_xa)
       float acc[NPAD];
 #pragma unroll
       for (int j = 0; j < NPAD; ++j) acc[j] = 0.f;
@@ -700,10 +700,7 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
       for (int m = 0; m < XPT; ++m) {
         const int i = qd + m * QD;
 #pragma unroll
-        for (int j = 0; j < NPAD; ++j) {
-          acc[j] += s_w[j][i] * xv[m];
-          if (i == len + j) acc[j] += Dh * xv[m];
-        }
+        for (int j = 0; j < NPAD; ++j) acc[j] += s_w[j][i] * xv[m];
       }
 #pragma unroll
       for (int j = 0; j < NPAD; ++j) s_yb[qd][j][p] = acc[j];
@@ -756,7 +753,7 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
           float yb = 0.f;
 #pragma unroll
           for (int g = 0; g < QD; ++g) yb += s_yb[g][j][pr];
-          yv = s_gam[j] * acc[r] + yb;
+          yv = s_gam[j] * acc[r] + yb + Dh * s_xa[j][pr];
         } else {
           yv = __builtin_nanf("");
         }
@@ -792,7 +789,7 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
           float yb = 0.f;
 #pragma unroll
           for (int g = 0; g < QD; ++g) yb += s_yb[g][j][pr];
-          yv = s_gam[j] * d[jj] + yb;
+          yv = s_gam[j] * d[jj] + yb + Dh * s_xa[j][pr];
         } else {
           yv = __builtin_nanf("");
         }
@@ -848,7 +845,7 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
               float yb = 0.f;
 #pragma unroll
               for (int g = 0; g < QD; ++g) yb += s_yb[g][j][pr];
-              yv = s_gam[j] * (scale * res[c][jj]) + yb;
+              yv = s_gam[j] * (scale * res[c][jj]) + yb + Dh * s_xa[j][pr];
             } else {
               yv = __builtin_nanf("");
             }

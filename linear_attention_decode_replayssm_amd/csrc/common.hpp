@@ -129,6 +129,24 @@ __device__ __forceinline__ float swap_add(float a, float b) {
   return __uint_as_float(x) + __uint_as_float(y);
 }
 
+// Exclusive suffix sum within each 16-lane row: lane i receives the sum of
+// v over lanes i+1..15 of its row.  DPP row_shl:k hands lane i the value of
+// lane i+k of the same row, and 0 past the row's end (bound_ctrl; both
+// checked on the GPU with an in-bounds probe).  Every lane of a row must be
+// active.
+template <int K>
+__device__ __forceinline__ float row_shl(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + K, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_suffix_excl(float v) {
+  float s = row_shl<1>(v);
+  s += row_shl<1>(s);
+  s += row_shl<2>(s);
+  s += row_shl<4>(s);
+  s += row_shl<8>(s);
+  return s;
+}
+
 // Sum over the LPR lanes of a lane group (every lane receives the sum).
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {

@@ -656,6 +656,7 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
       if (ME::writer(q.lane)) s_e[ME::index(q.lane, 0)][ei] = part[0];
     }
     __syncthreads();
+    static_assert(kMaxCap == 16, "one 16-lane row per draft");
     if (q.tid < NPAD * kMaxCap) {   // decay weights; zero off the path
       const int j = q.tid / kMaxCap, i = q.tid % kMaxCap;
       const int Lj = len + j + 1;   // draft j is the last entry on its path
@@ -667,20 +668,13 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
       for (int jj = 0; jj < NPAD; ++jj)
         if (j == jj) anc = a.anc[jj];
       const uint32_t path = ((1u << len) - 1u) | (anc << len);
-      float w = 0.f;
-      if (j < n && i < Lj && ((path >> i) & 1u)) {
-        float suf = 0.f;
-        for (int m = i + 1; m < Lj; ++m)
-          if ((path >> m) & 1u) suf += s_dt[m];
-        w = expf(Ah * suf) * s_dt[i] * s_e[j][i];
-      }
-      s_w[j][i] = w;
-      if (j < n && i == 0) {   // Gamma over the whole path
-        float tot = 0.f;
-        for (int m = 0; m < Lj; ++m)
-          if ((path >> m) & 1u) tot += s_dt[m];
-        s_gam[j] = expf(Ah * tot);
-      }
+      // lane i of draft j's 16-lane group: dt_i if entry i is on the path;
+      // the suffix over the later path entries is the decay exponent
+      const bool on = j < n && i < Lj && ((path >> i) & 1u);
+      const float dv = on ? s_dt[i] : 0.f;
+      const float suf = row_suffix_excl(dv);
+      s_w[j][i] = on ? expf(Ah * suf) * dv * s_e[j][i] : 0.f;
+      if (j < n && i == 0) s_gam[j] = expf(Ah * (dv + suf));   // Gamma over the whole path
     }
     if constexpr (COMMIT) {   // the commit's weights over the buffered entries
       const int i = q.tid - NPAD * kMaxCap;

@@ -227,28 +227,35 @@ __device__ __forceinline__ void carry(const EntrySmem& s, int hi, int cl, float 
 }
 
 // As carry(), through the entries on one draft's path only: buffered entries
-// 0..len-1 and the drafts whose bit is set in `anc` (entry len + m <-> bit m),
-// up to entry hi.  Entries off the path get s_i = 0.
+// lo..len-1 and the drafts whose bit is set in `anc` (entry len + m <-> bit
+// m), up to entry hi.  A whole wave carries one query (LPR = 64 lanes of EPL
+// elements, which are also rows cl*EPL.. of the value vectors): on the way it
+// accumulates the replay term sum_i s_i v_i of those rows into rep, in the
+// shadow of each entry's reduction.
 template <int EPL, int LPR>
-__device__ __forceinline__ void carry_path(const EntrySmem& s, int len, uint32_t anc, int hi,
-                                           int cl, float (&q)[EPL], float (&sv)[kMaxCap]) {
+__device__ __forceinline__ void carry_path(const EntrySmem& s, int lo, int len, uint32_t anc,
+                                           int hi, int cl, float (&q)[EPL], float (&rep)[EPL]) {
+  static_assert(LPR * EPL == DV, "one wave carries a whole query");
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) rep[e] = 0.f;
 #pragma unroll
   for (int i = kMaxCap - 1; i >= 0; --i) {
-    const bool on = i <= hi && (i < len || ((anc >> (i - len)) & 1u));
+    const bool on = i >= lo && i <= hi && (i < len || ((anc >> (i - len)) & 1u));
     if (on) {
-      float kv[EPL];
+      float kv[EPL], vv[EPL];
       load_vec<EPL>(&s.k[i][cl * EPL], kv);
+      load_vec<EPL>(&s.v[i][cl * EPL], vv);
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) part += kv[e] * q[e];
       part = group_sum<LPR>(part);
       const float si = s.be[i] * part;
       const float al = s.al[i];
-      sv[i] = si;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) q[e] = al * (q[e] - si * kv[e]);
-    } else {
-      sv[i] = 0.f;
+      for (int e = 0; e < EPL; ++e) {
+        rep[e] += si * vv[e];
+        q[e] = al * (q[e] - si * kv[e]);
+      }
     }
   }
 }
@@ -642,9 +649,10 @@ __global__ __launch_bounds__(NTH) void gdn_commit_kernel(GdnArgs a) {
 // COMMIT (fp32 checkpoint only): a sequence whose buffer holds at least
 // a.min_len entries also folds those entries into its checkpoint from the
 // same state read (the fold's coefficients while the stream is in flight, the
-// rank-len update after the outputs); its checkpoint moves to the end of the
-// buffer and the drafts become entries 0..n-1 (the same ring slots).  The
-// outputs are those of commit-then-verify.
+// rank-len update once it has arrived); its checkpoint moves to the end of
+// the buffer and the drafts become entries 0..n-1 (the same ring slots).  Its
+// outputs are read from the folded state, with the queries carried back
+// through the drafts only: those of commit-then-verify.
 template <int EB, int NPAD, bool COMMIT = false>
 __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
   static_assert(!COMMIT || EB == 4, "the fused commit folds the fp32 checkpoint");
@@ -679,7 +687,7 @@ __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
 
   __shared__ __attribute__((aligned(16))) EntrySmem es;
   __shared__ __attribute__((aligned(16))) float s_q[NPAD][DK];
-  __shared__ float s_s[NPAD][kMaxCap];
+  __shared__ __attribute__((aligned(16))) float s_rep[NPAD][DV];   // sum_i s_i v_i per draft
   stash_entries<NTH>(er, ok ? len + n : 0, q.tid, es);
   __syncthreads();
   __shared__ __attribute__((aligned(16))) FoldSmem<COMMIT ? ROWS : 1> sm;
@@ -694,19 +702,30 @@ __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
 #pragma unroll
     for (int j = 0; j < NPAD; ++j)
       if (w == j) anc = a.anc[j];
-    float s[kMaxCap];
-    carry_path<2, 64>(es, len, anc, len + w, q.lane, qv, s);
+    // a folding sequence takes its outputs from the folded state: the carry
+    // then runs through the drafts only
+    float rep[2];
+    carry_path<2, 64>(es, fold ? len : 0, len, anc, len + w, q.lane, qv, rep);
     s_q[w][2 * q.lane] = qv[0];
     s_q[w][2 * q.lane + 1] = qv[1];
-    if (q.lane < kMaxCap) {
-      float sv = 0.f;
-#pragma unroll
-      for (int i = 0; i < kMaxCap; ++i)
-        if (i == q.lane) sv = s[i];
-      s_s[w][q.lane] = sv;
-    }
+    s_rep[w][2 * q.lane] = rep[0];
+    s_rep[w][2 * q.lane + 1] = rep[1];
   }
   __syncthreads();
+  f32x4 hv[COMMIT ? NLD : 1];
+  if constexpr (COMMIT) {
+    if (fold) {   // the buffered entries folded into the fp32 checkpoint first
+#pragma unroll
+      for (int k = 0; k < NLD; ++k)
+        hv[k] = f32x4{__uint_as_float(raw[k].x), __uint_as_float(raw[k].y),
+                      __uint_as_float(raw[k].z), __uint_as_float(raw[k].w)};
+      fold_apply<NTH, ROWS, NLD>(hv, es, len, 0, q, sm);
+#pragma unroll
+      for (int k = 0; k < NLD; ++k)   // the rows the outputs read
+        raw[k] = u32x4{__float_as_uint(hv[k].x), __float_as_uint(hv[k].y),
+                       __float_as_uint(hv[k].z), __float_as_uint(hv[k].w)};
+    }
+  }
 
   constexpr int V = NLD * NPAD;
   float d[V];
@@ -735,8 +754,7 @@ __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
         const int r = k * RPL + q.r0;
         float ov;
         if (ok) {
-          ov = scale * d[jj];
-          for (int i = 0; i <= len + j; ++i) ov += s_s[j][i] * es.v[i][r];
+          ov = scale * d[jj] + s_rep[j][r];
         } else {
           ov = __builtin_nanf("");
         }
@@ -745,15 +763,7 @@ __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
     }
   }
   if constexpr (COMMIT) {
-    if (fold) {   // the buffered entries folded into the fp32 checkpoint
-      f32x4 hv[NLD];
-#pragma unroll
-      for (int k = 0; k < NLD; ++k)
-        hv[k] = f32x4{__uint_as_float(raw[k].x), __uint_as_float(raw[k].y),
-                      __uint_as_float(raw[k].z), __uint_as_float(raw[k].w)};
-      fold_apply<NTH, ROWS, NLD>(hv, es, len, 0, q, sm);
-      store_f32_tile<RPL, NLD>(hv, a.ckpt + q.unit * (DV * DK), q);
-    }
+    if (fold) store_f32_tile<RPL, NLD>(hv, a.ckpt + q.unit * (DV * DK), q);
   }
   if (ok)
     if (a.append)

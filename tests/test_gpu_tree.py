@@ -181,3 +181,96 @@ def test_append_path_overflow_and_bad_index_leave_sequences_unchanged():
     R.rssm_append_path(L, n, gu.dev(path), gu.dev(plen), dd)
     assert gu.indices(L)[1].tolist() == [2, 2, 4]
     assert R.rssm_status(L) == R.STATUS_OVERFLOW
+
+
+SEL = [0, 77, 160, 255]   # sequences the oracle follows at the serving shapes
+
+
+def _sub(st):
+    return {k: np.ascontiguousarray(v[:, SEL]) for k, v in st.items()}
+
+
+def test_m2_binary_tree_serving_shape():
+    """The benchmark's tree workload: batch 256 x 80 heads (8 groups), a
+    binary tree of 7 drafts below a buffer of 5 entries (ring 16), then an
+    accepted path per sequence and two plain steps.  Outputs of four sampled
+    sequences (every head, every draft) against the oracle; indices of all
+    256 sequences bit-exact."""
+    parent = TREES["binary"]
+    n, b, H, G, cap, pre, post = len(parent), 256, 80, 8, 16, 5, 2
+    seed = 171
+    A, D = syn.m2_params(seed, H)
+    h0 = syn.m2_state0(seed, b, H, P, N)
+    st = syn.m2_steps(seed, 0, pre + n + post, b, H, G, P, N)
+    pre_st = {k: v[:pre] for k, v in st.items()}
+    drafts = {k: np.ascontiguousarray(v[pre:pre + n]) for k, v in st.items()}
+    post_st = {k: np.ascontiguousarray(v[pre + n:]) for k, v in st.items()}
+    L = gu.m2_layer(A, D, h0, G, cap)
+    gu.m2_decode(L, {k: gu.dev(v) for k, v in pre_st.items()}, 1 << 20, False)
+    h = h0[SEL].astype(np.float64)
+    ps = _sub(pre_st)
+    oracle.m2_eager(A, D, ps["x"], ps["B"], ps["C"], ps["dt"], h)
+
+    dd = {k: gu.dev(v) for k, v in drafts.items()}
+    out = gu.torch().empty_like(dd["x"])
+    R.rssm_verify_tree(L, parent, dd, out)
+    ds = _sub(drafts)
+    want = drivers.m2_tree_verify(A, D, h, ds, parent)
+    gu.check_m2_outputs(gu.host(out)[:, SEL], want, ds["x"], D)
+    assert (gu.indices(L)[1] == pre).all()
+
+    paths, arr, plen = _accepted_paths(parent, b, np.random.default_rng(seed))
+    R.rssm_append_path(L, n, gu.dev(arr), gu.dev(plen), dd)
+    np.testing.assert_array_equal(gu.indices(L)[1], pre + plen)
+    y, _, _ = gu.m2_decode(L, {k: gu.dev(v) for k, v in post_st.items()}, 1 << 20, False)
+    yh = gu.host(y)
+    for i, s in enumerate(SEL):
+        hs = h[i:i + 1].copy()
+        p = paths[s]
+        if p:
+            oracle.m2_eager(A, D, drafts["x"][p][:, s:s + 1], drafts["B"][p][:, s:s + 1],
+                            drafts["C"][p][:, s:s + 1], drafts["dt"][p][:, s:s + 1], hs)
+        ys = oracle.m2_eager(A, D, post_st["x"][:, s:s + 1], post_st["B"][:, s:s + 1],
+                             post_st["C"][:, s:s + 1], post_st["dt"][:, s:s + 1], hs)
+        gu.check_m2_outputs(yh[:, s:s + 1], ys, post_st["x"][:, s:s + 1], D)
+    np.testing.assert_array_equal(gu.indices(L)[1], pre + plen + post)
+    assert R.rssm_status(L) == 0
+
+
+def test_gdn_binary_tree_serving_shape():
+    """As above for GDN at batch 256 x 32 heads (d 128)."""
+    parent = TREES["binary"]
+    n, b, H, cap, pre, post = len(parent), 256, 32, 16, 5, 2
+    seed = 172
+    S0 = syn.gdn_state0(seed, b, H, DK, DK, std=0.1)
+    st = syn.gdn_steps(seed, 0, pre + n + post, b, H, DK, DK)
+    pre_st = {k: v[:pre] for k, v in st.items()}
+    drafts = {k: np.ascontiguousarray(v[pre:pre + n]) for k, v in st.items()}
+    post_st = {k: np.ascontiguousarray(v[pre + n:]) for k, v in st.items()}
+    L = gu.gdn_layer(S0, cap)
+    gu.gdn_decode(L, {k: gu.dev(v) for k, v in pre_st.items()}, 1 << 20, False)
+    S = S0[SEL].astype(np.float64)
+    ps = _sub(pre_st)
+    oracle.gdn_eager(*(ps[nm] for nm in GDN_NAMES), S)
+
+    dd = {k: gu.dev(v) for k, v in drafts.items()}
+    out = gu.torch().empty_like(dd["v"])
+    R.rssm_verify_tree(L, parent, dd, out)
+    want = drivers.gdn_tree_verify(S, _sub(drafts), parent)
+    assert gu.vec_rel_err(gu.host(out)[:, SEL], want) <= gu.TOL_F32
+    assert (gu.indices(L)[1] == pre).all()
+
+    paths, arr, plen = _accepted_paths(parent, b, np.random.default_rng(seed))
+    R.rssm_append_path(L, n, gu.dev(arr), gu.dev(plen), dd)
+    np.testing.assert_array_equal(gu.indices(L)[1], pre + plen)
+    o, _, _ = gu.gdn_decode(L, {k: gu.dev(v) for k, v in post_st.items()}, 1 << 20, False)
+    oh = gu.host(o)
+    for i, s in enumerate(SEL):
+        Ss = S[i:i + 1].copy()
+        p = paths[s]
+        if p:
+            oracle.gdn_eager(*(drafts[nm][p][:, s:s + 1] for nm in GDN_NAMES), Ss)
+        os_ = oracle.gdn_eager(*(post_st[nm][:, s:s + 1] for nm in GDN_NAMES), Ss)
+        assert gu.vec_rel_err(oh[:, s:s + 1], os_) <= gu.TOL_F32
+    np.testing.assert_array_equal(gu.indices(L)[1], pre + plen + post)
+    assert R.rssm_status(L) == 0

@@ -201,6 +201,26 @@ __device__ __forceinline__ void append_from_regs(const GdnArgs& a, const Src& sr
   }
 }
 
+// The drafts i0..i0+n-1 appended from the entries parked in LDS, 32 threads
+// per draft (the fetch registers are then free for the rest of the kernel).
+template <int NTH>
+__device__ __forceinline__ void append_drafts_from_smem(const GdnArgs& a, const Src& src,
+                                                        const EntrySmem& es, int i0, int n,
+                                                        int tid) {
+  static_assert(DK == DV, "k and v rows of one length");
+  const int j = tid / (DK / 4), ch = tid % (DK / 4);
+  if (j < n) {
+    const int i = i0 + j;
+    const long row = src.unit * src.cap + ring_slot(src.slot0, i, src.cap);
+    st4(a.ring_k + row * DK + 4 * ch, ld4(&es.k[i][4 * ch]));
+    st4(a.ring_v + row * DV + 4 * ch, ld4(&es.v[i][4 * ch]));
+    if (ch == 0) {
+      a.ring_a[row] = es.al[i];
+      a.ring_b[row] = es.be[i];
+    }
+  }
+}
+
 // Backward carry of a query through entries hi..0 (newest first), held as EPL
 // consecutive elements per lane on LPR lanes (lanes repeat every LPR).
 template <int EPL, int LPR>
@@ -400,6 +420,10 @@ __device__ __forceinline__ void fold_u(const EntrySmem& es, int L, int row0, int
   const int r = tid % ROWS, ig = tid / ROWS;
   for (int i = ig; i < L; i += NTH / ROWS) {
     float acc = 0.f;
+    // a bounded unroll: unrolled further, the LDS loads of every term are
+    // hoisted next to the live state tile and the kernels that fold into a
+    // tile they still read need ten more registers
+#pragma unroll 4
     for (int j = 0; j <= i; ++j)
       acc += sm.P1[i][j] * es.v[j][row0 + r] + sm.P2[i][j] * sm.W[r][j];
     sm.U[r][i] = acc;
@@ -643,8 +667,9 @@ __global__ __launch_bounds__(NTH) void gdn_commit_kernel(GdnArgs a) {
 // the drafts, a tree appends nothing.  One 512-thread workgroup per
 // head: wave j carries draft j's query backwards through entries len+j..0;
 // then one pass over the checkpoint dots every row with all carried queries.
-// Eight fp32 drafts take ~80 registers (two to three workgroups per CU); no
-// occupancy cap is set, since a cap of six waves per SIMD spills to scratch.
+// The chain's drafts are appended from LDS at the end, so no fetched entry
+// stays in registers: four fp32 drafts take 57 registers (four workgroups per
+// CU), eight 80 (three), and with the commit folded in 76 and 80 (three).
 //
 // COMMIT (fp32 checkpoint only): a sequence whose buffer holds at least
 // a.min_len entries also folds those entries into its checkpoint from the
@@ -659,7 +684,7 @@ __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
   constexpr int NTH = 512, ROWS = DV;
   using Gm = LpGeo<EB, NTH, ROWS>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPL = Gm::RPL, NLD = Gm::NLD;
-  static_assert(NPAD <= NTH / 64, "one wave per draft position");
+  static_assert(NPAD <= NTH / 64 && NPAD * (DK / 4) <= NTH, "one wave per draft position");
   const Geo q = geometry<LPR, ROWS>(a);
   const int cap = a.cap, n = a.n_pos;
 
@@ -720,6 +745,7 @@ __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
         hv[k] = f32x4{__uint_as_float(raw[k].x), __uint_as_float(raw[k].y),
                       __uint_as_float(raw[k].z), __uint_as_float(raw[k].w)};
       fold_apply<NTH, ROWS, NLD>(hv, es, len, 0, q, sm);
+      store_f32_tile<RPL, NLD>(hv, a.ckpt + q.unit * (DV * DK), q);
 #pragma unroll
       for (int k = 0; k < NLD; ++k)   // the rows the outputs read
         raw[k] = u32x4{__float_as_uint(hv[k].x), __float_as_uint(hv[k].y),
@@ -762,12 +788,9 @@ __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
       }
     }
   }
-  if constexpr (COMMIT) {
-    if (fold) store_f32_tile<RPL, NLD>(hv, a.ckpt + q.unit * (DV * DK), q);
-  }
   if (ok)
     if (a.append)
-      for (int j = 0; j < n; ++j) append_from_regs<NTH>(a, src, er, len + j, q.tid);
+      append_drafts_from_smem<NTH>(a, src, es, len, n, q.tid);
 
   IndexUpdate u;
   u.apply = ok && (a.append || fold);

@@ -389,27 +389,32 @@ __device__ __forceinline__ void coef_t(const EntrySmem& es, int L, int tid, Fold
   }
 }
 
-// W = S_c K^T for the workgroup's rows, four entries at a time (FMA dots,
-// transposed cross-lane reduction), stored to sm.W.
-template <int NTH, int ROWS, int NLD>
+// W = S_c K^T for the workgroup's rows, CH entries at a time (FMA dots,
+// transposed cross-lane reduction), stored to sm.W.  CH = 2 keeps the partial
+// dots to 2 NLD registers beside the 4 NLD of the tile, which gives the
+// whole-head fold kernels a third workgroup per CU; the DUAL bf16 kernels
+// measured faster at two workgroups per CU and take CH = 4.
+template <int NTH, int ROWS, int NLD, int CH>
 __device__ __forceinline__ void fold_w(const f32x4 (&hv)[NLD], const EntrySmem& es, int L,
                                        const Geo& q, FoldSmem<ROWS>& sm) {
   using Gm = LpGeo<4, NTH, ROWS>;
   constexpr int RPL = Gm::RPL, LPR = Gm::LPR;
   static_assert(NLD == Gm::NLD, "tile registers");
-  for (int i0 = 0; i0 < L; i0 += 4) {
-    float d[NLD * 4];
+  using M = XMap<NLD * CH, LPR>;
+  static_assert(M::VOUT == 1, "one sum per lane");
+  for (int i0 = 0; i0 < L; i0 += CH) {
+    float d[NLD * CH];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
+    for (int jj = 0; jj < CH; ++jj) {
       const f32x4 kv = ld4(&es.k[i0 + jj][q.cl * 4]);   // rows >= L are zero
 #pragma unroll
-      for (int k = 0; k < NLD; ++k) d[k * 4 + jj] = dot4(hv[k], kv);
+      for (int k = 0; k < NLD; ++k) d[k * CH + jj] = dot4(hv[k], kv);
     }
-    xreduce<NLD * 4, LPR>(d, q.lane);
-    using M = XMap<NLD * 4, LPR>;
-    static_assert(M::VOUT == 1 && M::BFLY == 0, "one sum per lane");
-    const int idx = M::index(q.lane, 0);
-    sm.W[(idx / 4) * RPL + q.r0][i0 + idx % 4] = d[0];
+    xreduce<NLD * CH, LPR>(d, q.lane);
+    if (M::writer(q.lane)) {
+      const int idx = M::index(q.lane, 0);
+      sm.W[(idx / CH) * RPL + q.r0][i0 + idx % CH] = d[0];
+    }
   }
 }
 
@@ -458,10 +463,10 @@ __device__ __forceinline__ void fold_coef(const EntrySmem& es, int L, int tid, F
   __syncthreads();
 }
 
-template <int NTH, int ROWS, int NLD>
+template <int NTH, int ROWS, int NLD, int WCH = 2>
 __device__ __forceinline__ void fold_apply(f32x4 (&hv)[NLD], const EntrySmem& es, int L, int row0, const Geo& q,
                            FoldSmem<ROWS>& sm) {
-  fold_w<NTH, ROWS, NLD>(hv, es, L, q, sm);
+  fold_w<NTH, ROWS, NLD, WCH>(hv, es, L, q, sm);
   __syncthreads();
   fold_u<NTH, ROWS>(es, L, row0, q.tid, sm);
   __syncthreads();
@@ -576,7 +581,7 @@ __global__ __launch_bounds__((LP != 0 ? 512 : step_threads<EB>())) void gdn_step
       for (int k = 0; k < NLD; ++k)
         hv[k] = f32x4{__uint_as_float(raw[k].x), __uint_as_float(raw[k].y),
                       __uint_as_float(raw[k].z), __uint_as_float(raw[k].w)};
-      fold_apply<NTH, ROWS, NLD>(hv, es, L, q.row0, q, sm);
+      fold_apply<NTH, ROWS, NLD, LP == kLpBf16 ? 4 : 2>(hv, es, L, q.row0, q, sm);
       const f32x4 q4 = {qv[0], qv[1], qv[2], qv[3]};
 #pragma unroll
       for (int k = 0; k < NLD; ++k) d[k] = dot4(hv[k], q4);
@@ -649,7 +654,8 @@ __global__ __launch_bounds__(NTH) void gdn_commit_kernel(GdnArgs a) {
   __syncthreads();
   if (len > 0) {
     fold_coef<NTH, ROWS>(es, len, q.tid, sm);   // while the state stream is in flight
-    fold_apply<NTH, ROWS, NLD>(hv, es, len, q.row0, q, sm);
+    fold_apply<NTH, ROWS, NLD, (SCHEME == kSchemeDual && LP == kLpBf16) ? 4 : 2>(
+        hv, es, len, q.row0, q, sm);
     if constexpr (SCHEME != kSchemeShared) store_f32_tile<RPL, NLD>(hv, rows, q);
   }
   if constexpr (SCHEME != kSchemeF32) store_lp<LP>(hv, a, q, sm.red);

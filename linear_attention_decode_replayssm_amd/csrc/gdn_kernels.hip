@@ -323,8 +323,7 @@ struct FoldSmem {
   float Lc[kMaxCap][kMaxCap + 1];      // G_{m+1..i-1} (k_m . k_i), m < i
   float P1[kMaxCap][kMaxCap + 1];      //  G_{i+1..} T[i][j] beta_j
   float P2[kMaxCap][kMaxCap + 1];      // -G_{i+1..} T[i][j] beta_j alpha_j G_{..j-1}
-  float W[ROWS][kMaxCap + 1];          // S_c k_i of the workgroup's rows
-  float U[ROWS][kMaxCap + 1];          // U'_i of the workgroup's rows
+  float WU[ROWS][kMaxCap + 1];         // S_c k_i of the workgroup's rows, then U'_i
   float red[16];
 };
 
@@ -413,25 +412,37 @@ __device__ __forceinline__ void fold_w(const f32x4 (&hv)[NLD], const EntrySmem& 
     xreduce<NLD * CH, LPR>(d, q.lane);
     if (M::writer(q.lane)) {
       const int idx = M::index(q.lane, 0);
-      sm.W[(idx / CH) * RPL + q.r0][i0 + idx % CH] = d[0];
+      sm.WU[(idx / CH) * RPL + q.r0][i0 + idx % CH] = d[0];
     }
   }
 }
 
-// U'[r][i] = sum_{j<=i} P1[i][j] v_j[row0 + r] + P2[i][j] W[r][j].
+// U'[r][i] = sum_{j<=i} P1[i][j] v_j[row0 + r] + P2[i][j] W[r][j], written
+// over W once every thread has read it (barrier inside).
 template <int NTH, int ROWS>
 __device__ __forceinline__ void fold_u(const EntrySmem& es, int L, int row0, int tid,
                                        FoldSmem<ROWS>& sm) {
+  constexpr int IG = NTH / ROWS, NI = (kMaxCap + IG - 1) / IG;
   const int r = tid % ROWS, ig = tid / ROWS;
-  for (int i = ig; i < L; i += NTH / ROWS) {
-    float acc = 0.f;
-    // a bounded unroll: unrolled further, the LDS loads of every term are
-    // hoisted next to the live state tile and the kernels that fold into a
-    // tile they still read need ten more registers
+  float acc[NI];
+#pragma unroll
+  for (int t = 0; t < NI; ++t) {
+    const int i = ig + t * IG;
+    acc[t] = 0.f;
+    if (i < L) {
+      // a bounded unroll: unrolled further, the LDS loads of every term are
+      // hoisted next to the live state tile and the kernels that fold into a
+      // tile they still read need ten more registers
 #pragma unroll 4
-    for (int j = 0; j <= i; ++j)
-      acc += sm.P1[i][j] * es.v[j][row0 + r] + sm.P2[i][j] * sm.W[r][j];
-    sm.U[r][i] = acc;
+      for (int j = 0; j <= i; ++j)
+        acc[t] += sm.P1[i][j] * es.v[j][row0 + r] + sm.P2[i][j] * sm.WU[r][j];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < NI; ++t) {
+    const int i = ig + t * IG;
+    if (i < L) sm.WU[r][i] = acc[t];
   }
 }
 
@@ -445,7 +456,7 @@ __device__ __forceinline__ void fold_update(f32x4 (&hv)[NLD], const EntrySmem& e
   for (int i = 0; i < L; ++i) {
     const f32x4 kv = ld4(&es.k[i][q.cl * 4]);
 #pragma unroll
-    for (int k = 0; k < NLD; ++k) hv[k] += sm.U[k * RPL + q.r0][i] * kv;
+    for (int k = 0; k < NLD; ++k) hv[k] += sm.WU[k * RPL + q.r0][i] * kv;
   }
 }
 

@@ -389,10 +389,10 @@ __device__ __forceinline__ void coef_t(const EntrySmem& es, int L, int tid, Fold
 }
 
 // W = S_c K^T for the workgroup's rows, CH entries at a time (FMA dots,
-// transposed cross-lane reduction), stored to sm.W.  CH = 2 keeps the partial
-// dots to 2 NLD registers beside the 4 NLD of the tile, which gives the
-// whole-head fold kernels a third workgroup per CU; the DUAL bf16 kernels
-// measured faster at two workgroups per CU and take CH = 4.
+// transposed cross-lane reduction), stored to sm.WU.  CH = 2 keeps the
+// partial dots to 2 NLD registers beside the 4 NLD of the tile, which gives
+// the whole-head fold kernels a third workgroup per CU; the fused fp32 and
+// DUAL bf16 steps and the DUAL bf16 commit measured faster with CH = 4.
 template <int NTH, int ROWS, int NLD, int CH>
 __device__ __forceinline__ void fold_w(const f32x4 (&hv)[NLD], const EntrySmem& es, int L,
                                        const Geo& q, FoldSmem<ROWS>& sm) {
@@ -592,7 +592,7 @@ __global__ __launch_bounds__((LP != 0 ? 512 : step_threads<EB>())) void gdn_step
       for (int k = 0; k < NLD; ++k)
         hv[k] = f32x4{__uint_as_float(raw[k].x), __uint_as_float(raw[k].y),
                       __uint_as_float(raw[k].z), __uint_as_float(raw[k].w)};
-      fold_apply<NTH, ROWS, NLD, LP == kLpBf16 ? 4 : 2>(hv, es, L, q.row0, q, sm);
+      fold_apply<NTH, ROWS, NLD, LP != kLpE4m3 ? 4 : 2>(hv, es, L, q.row0, q, sm);
       const f32x4 q4 = {qv[0], qv[1], qv[2], qv[3]};
 #pragma unroll
       for (int k = 0; k < NLD; ++k) d[k] = dot4(hv[k], q4);

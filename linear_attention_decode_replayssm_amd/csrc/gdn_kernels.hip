@@ -422,6 +422,7 @@ __device__ __forceinline__ void fold_w(const f32x4 (&hv)[NLD], const EntrySmem& 
 template <int NTH, int ROWS>
 __device__ __forceinline__ void fold_u(const EntrySmem& es, int L, int row0, int tid,
                                        FoldSmem<ROWS>& sm) {
+  static_assert(NTH % ROWS == 0, "whole row groups");
   constexpr int IG = NTH / ROWS, NI = (kMaxCap + IG - 1) / IG;
   const int r = tid % ROWS, ig = tid / ROWS;
   float acc[NI];
@@ -686,7 +687,7 @@ __global__ __launch_bounds__(NTH) void gdn_commit_kernel(GdnArgs a) {
 // then one pass over the checkpoint dots every row with all carried queries.
 // The chain's drafts are appended from LDS at the end, so no fetched entry
 // stays in registers: four fp32 drafts take 57 registers (four workgroups per
-// CU), eight 80 (three), and with the commit folded in 76 and 80 (three).
+// CU), eight 80 (three), and with the commit folded in 74 and 80 (three).
 //
 // COMMIT (fp32 checkpoint only): a sequence whose buffer holds at least
 // a.min_len entries also folds those entries into its checkpoint from the

@@ -85,18 +85,21 @@ __device__ __forceinline__ int tile_index() {
 // row_mirror i <-> 15-i for 8), ds_swizzle xor-16 for 16 and ds_bpermute only
 // for 32.  The sums below take bits 4 and 5 with the lane swaps instead
 // (swap_add); these two forms remain for the wave-wide max and xor folds.
+// The DPP forms zero-fill (bound_ctrl) with an old value of 0: every lane of
+// these permutations has a source, so the value is the same, and the compiler
+// can then fold the move into the add that consumes it (v_add_f32_dpp).
 template <int M>
 __device__ __forceinline__ float rpartner(float v) {
   const int x = __float_as_int(v);
   int r;
   if constexpr (M == 1)
-    r = __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false);
+    r = __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, true);
   else if constexpr (M == 2)
-    r = __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false);
+    r = __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, true);
   else if constexpr (M == 4)
-    r = __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false);
+    r = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, true);
   else if constexpr (M == 8)
-    r = __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false);
+    r = __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, true);
   else if constexpr (M == 16)
     r = __builtin_amdgcn_ds_swizzle(x, 0x401F);
   else

@@ -420,6 +420,28 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
         ftotal += int(com.sum()) * S                                              # fold write
         ln[com] = 0
         ln += accept[r]
+    # the same rounds with each round's rollback passed to the next round's
+    # verify (rssm_rollback_verify_commit): one launch per round
+    del L   # the next phase reuses the same cached blocks
+    L = R.Layer.mamba2(b, H, G, P, N, 16)
+    L.A.copy_(torch.from_numpy(A))
+    L.D.copy_(torch.from_numpy(D))
+    L.ckpt.copy_(h0)
+    torch.cuda.synchronize()
+    start.record()
+    for r in range(rounds):
+        j = (r * n) % pool_n
+        inp = R.make_inputs(x=dev["x"][j:j + n], B=dev["B"][j:j + n], C=dev["C"][j:j + n],
+                            dt=dev["dt"][j:j + n])
+        if r == 0:
+            R.rssm_verify_commit(L, n, inp, out, commit_len)
+        else:
+            R.rssm_rollback_verify_commit(L, nrej[r - 1], n, inp, out, commit_len)
+    R.rssm_rollback(L, nrej[rounds - 1])
+    end.record()
+    torch.cuda.synchronize()
+    rms = start.elapsed_time(end)
+    assert R.rssm_status(L) == 0
     # the same rounds appending only the accepted drafts: the drafts verified
     # as a chain-shaped tree (nothing appended, a due buffer folded from the
     # same state read), then the accepted prefix appended; no rollback
@@ -454,6 +476,11 @@ def run_spec(torch, R, syn, rounds, seed=0, pool_n=16):
                                bytes_per_round=ftotal / rounds,
                                hbm_gbps=ftotal / (fms * 1e-3) / 1e9,
                                speedup_vs_standalone_commit=ms / fms)
+    res["fused_commit"]["rollback_in_verify"] = dict(
+        rounds_per_s=rounds / (rms * 1e-3),
+        accepted_seq_tok_s=float(accept.sum()) / (rms * 1e-3),
+        us_per_round=rms * 1e3 / rounds,
+        hbm_gbps=ftotal / (rms * 1e-3) / 1e9)
 
     # the eager comparator on the same rounds: the state read once per round
     # and written after every draft (n + 1 state slots, accept = slot move)
@@ -558,6 +585,21 @@ def run_gdn_spec(torch, R, syn, rounds, seed=0, pool_n=16):
     fms = start.elapsed_time(end)
     assert R.rssm_status(L) == 0
     del L   # the next phase reuses the same cached blocks
+    # each round's rollback passed to the next round's verify: one launch per round
+    L = R.Layer.gdn(b, H, d, d, 16)
+    torch.cuda.synchronize()
+    start.record()
+    for r in range(rounds):
+        if r == 0:
+            R.rssm_verify_commit(L, n, inp[0], out, commit_len)
+        else:
+            R.rssm_rollback_verify_commit(L, nrej[r - 1], n, inp[r % len(inp)], out, commit_len)
+    R.rssm_rollback(L, nrej[rounds - 1])
+    end.record()
+    torch.cuda.synchronize()
+    rms = start.elapsed_time(end)
+    assert R.rssm_status(L) == 0
+    del L   # the next phase reuses the same cached blocks
     L = R.Layer.gdn(b, H, d, d, cap)
     slots = torch.zeros((n + 1, b, H, d, d), dtype=torch.float32, device="cuda")
     cur = torch.zeros(b, dtype=torch.int32, device="cuda")
@@ -576,7 +618,11 @@ def run_gdn_spec(torch, R, syn, rounds, seed=0, pool_n=16):
                fused_commit=dict(rounds_per_s=rounds / (fms * 1e-3),
                                  accepted_seq_tok_s=float(accept.sum()) / (fms * 1e-3),
                                  us_per_round=fms * 1e3 / rounds,
-                                 speedup_vs_standalone_commit=ms / fms),
+                                 speedup_vs_standalone_commit=ms / fms,
+                                 rollback_in_verify=dict(
+                                     rounds_per_s=rounds / (rms * 1e-3),
+                                     accepted_seq_tok_s=float(accept.sum()) / (rms * 1e-3),
+                                     us_per_round=rms * 1e3 / rounds)),
                eager_rounds_per_s=rounds / (ems * 1e-3),
                speedup_vs_eager_spec=ems / ms)
     del L, dev, slots

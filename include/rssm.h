@@ -294,6 +294,26 @@ int rssm_verify_commit(const rssm_layer* L, int n_pos, const rssm_inputs* in, fl
                        int min_len, void* stream);
 
 /*
+ * rssm_rollback_verify_commit -- rssm_rollback(L, n_reject) followed by
+ * rssm_verify_commit(L, n_pos, in, out, min_len), in one launch.  A
+ * speculative loop passes each round's rejection counts with the next
+ * round's drafts: a rollback only moves the buffer tail (explainer, "Cheap
+ * speculative decoding rollback"), and the verify reads the buffer indices
+ * anyway, so it applies len -= n_reject before it folds and appends.
+ * Indices, rings, checkpoints, outputs and status bits are bitwise those of
+ * the two calls, errors included: a sequence whose n_reject[b] is < 0 or
+ * > len sets RSSM_STATUS_ROLLBACK and keeps its len, and is then verified
+ * as rssm_verify_commit would verify it; a valid rollback stands when the
+ * drafts then overflow (RSSM_STATUS_OVERFLOW, outputs NaN, no append).
+ * n_reject: device int32 [batch], caller-owned, read only; NULL is
+ * RSSM_EINVAL.  A min_len above the capacity never folds (a fused rollback
+ * with plain verification).  Other arguments and errors as for
+ * rssm_verify_commit (F32 checkpoints only).
+ */
+int rssm_rollback_verify_commit(const rssm_layer* L, const int32_t* n_reject, int n_pos,
+                                const rssm_inputs* in, float* out, int min_len, void* stream);
+
+/*
  * rssm_verify_tree -- output-only verification of a tree of drafts from one
  * checkpoint read (explainer, "Why this matters for agentic systems now":
  * replay from a shared checkpoint along different input buffers, then

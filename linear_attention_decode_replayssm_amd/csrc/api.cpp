@@ -166,7 +166,8 @@ inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 // rssm_verify_tree (ancestor masks from the parent array, nothing appended).
 // commit_min_len > 0: rssm_verify_commit (F32 checkpoints only).
 int verify_common(const rssm_layer* L, int n_pos, const uint32_t* anc, int append,
-                  const rssm_inputs* in, float* out, void* stream, int commit_min_len = 0) {
+                  const rssm_inputs* in, float* out, void* stream, int commit_min_len = 0,
+                  const int32_t* n_reject = nullptr) {
   int rc = check_layer_dims(L);
   if (rc) return rc;
   if (!in) return RSSM_EINVAL;
@@ -189,6 +190,7 @@ int verify_common(const rssm_layer* L, int n_pos, const uint32_t* anc, int appen
     for (int j = 0; j < n_pos; ++j) a.anc[j] = anc[j];
     a.append = append;
     a.min_len = commit_min_len;
+    a.n_reject = n_reject;
     return hip_rc(rssm::launch_m2_verify(a, S(stream)));
   }
   if (!in->q || !in->k || !in->v || !in->alpha || !in->beta) return RSSM_EINVAL;
@@ -204,6 +206,7 @@ int verify_common(const rssm_layer* L, int n_pos, const uint32_t* anc, int appen
   for (int j = 0; j < n_pos; ++j) a.anc[j] = anc[j];
   a.append = append;
   a.min_len = commit_min_len;
+  a.n_reject = n_reject;
   return hip_rc(rssm::launch_gdn_verify(a, S(stream)));
 }
 
@@ -323,6 +326,15 @@ int rssm_verify_commit(const rssm_layer* L, int n_pos, const rssm_inputs* in, fl
   uint32_t anc[rssm::kMaxPos] = {};
   for (int j = 0; j < rssm::kMaxPos; ++j) anc[j] = (2u << j) - 1u;
   return verify_common(L, n_pos, anc, 1, in, out, stream, min_len);
+}
+
+int rssm_rollback_verify_commit(const rssm_layer* L, const int32_t* n_reject, int n_pos,
+                                const rssm_inputs* in, float* out, int min_len, void* stream) {
+  if (min_len < 1) return RSSM_ERANGE;
+  if (!n_reject) return RSSM_EINVAL;
+  uint32_t anc[rssm::kMaxPos] = {};
+  for (int j = 0; j < rssm::kMaxPos; ++j) anc[j] = (2u << j) - 1u;
+  return verify_common(L, n_pos, anc, 1, in, out, stream, min_len, n_reject);
 }
 
 namespace {

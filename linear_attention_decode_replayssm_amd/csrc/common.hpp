@@ -36,6 +36,31 @@ __device__ __forceinline__ bool indices_valid(int32_t len, int64_t pos, int cap)
   return len >= 0 && len <= cap && pos >= 0;
 }
 
+// The buffer length a verify works from when the previous round's rollback
+// is passed with it (n_reject, may be NULL): len - n_reject[b], as a rollback
+// launch would leave it.  A count outside 0..len is refused as the rollback
+// refuses it (bad: the length stays, the caller raises the rollback bit);
+// indices that are not valid are left to the verify's own check.
+struct RolledLen {
+  int32_t len;
+  bool valid, rolled, bad;
+};
+
+__device__ __forceinline__ RolledLen rolled_len(int32_t len, int64_t pos, int cap,
+                                                const int32_t* n_reject, int b) {
+  RolledLen r{len, indices_valid(len, pos, cap), false, false};
+  if (n_reject != nullptr && r.valid) {
+    const int32_t nr = n_reject[b];
+    if (nr < 0 || nr > len) {
+      r.bad = true;
+    } else {
+      r.len = len - nr;
+      r.rolled = true;
+    }
+  }
+  return r;
+}
+
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 
 // ---- memory ---------------------------------------------------------------

@@ -706,9 +706,10 @@ __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
   const Geo q = geometry<LPR, ROWS>(a);
   const int cap = a.cap, n = a.n_pos;
 
-  const int len = a.len[q.b];
   const int64_t pos = a.pos[q.b];
-  const bool valid = indices_valid(len, pos, cap);
+  const RolledLen rl = rolled_len(a.len[q.b], pos, cap, a.n_reject, q.b);
+  const int len = rl.len;
+  const bool valid = rl.valid;
   const bool ok = valid && len + n <= cap;
   const bool fold = COMMIT && ok && len > 0 && len >= a.min_len;   // uniform per sequence
   const long sk = (long)a.batch * a.H * DK;
@@ -810,13 +811,15 @@ __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
     if (a.append)
       append_drafts_from_smem<NTH>(a, src, es, len, n, q.tid);
 
-  IndexUpdate u;
-  u.apply = ok && (a.append || fold);
+  IndexUpdate u;   // a rollback passed with the drafts stands even if they overflow
+  u.apply = (ok && (a.append || fold)) || rl.rolled;
   u.pos_add = fold ? len : 0;
-  u.new_len = (fold ? 0 : len) + (a.append ? n : 0);
+  u.new_len = ok ? (fold ? 0 : len) + (a.append ? n : 0) : len;
   finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
-  if (!ok && last_arrival(arrived, a.H))
-    raise_status(a.status, valid ? kStatusOverflow : kStatusIndex);
+  if (last_arrival(arrived, a.H)) {
+    if (!ok) raise_status(a.status, valid ? kStatusOverflow : kStatusIndex);
+    if (rl.bad) raise_status(a.status, kStatusRollback);
+  }
 }
 
 // --------------------------------------------------------------- eager ----

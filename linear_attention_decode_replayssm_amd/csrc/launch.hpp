@@ -37,6 +37,7 @@ struct M2Args {
   const int32_t* path_len;  // append_path: [b]
   int depth;
   int idx_ro;               // indices read, never written (RSSM_LAYER_INDEX_READONLY)
+  const int32_t* n_reject;  // verify: [b] rejections rolled back first (NULL: none)
 };
 
 // Gated DeltaNet arguments.
@@ -67,6 +68,7 @@ struct GdnArgs {
   const int32_t* path_len;
   int depth;
   int idx_ro;           // as in M2Args
+  const int32_t* n_reject;  // as in M2Args
 };
 
 hipError_t launch_m2_step(const M2Args& a, bool fused, hipStream_t s);

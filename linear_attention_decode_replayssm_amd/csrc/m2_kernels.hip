@@ -511,9 +511,10 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   using Gm = RdGeo<EB>;
   const Geo q = geometry(a);
   const int cap = a.cap, n = a.n_pos;
-  const int len = a.len[q.b];
   const int64_t pos = a.pos[q.b];
-  const bool valid = indices_valid(len, pos, cap);
+  const RolledLen rl = rolled_len(a.len[q.b], pos, cap, a.n_reject, q.b);
+  const int len = rl.len;
+  const bool valid = rl.valid;
   const bool ok = valid && len + n <= cap;
   const bool fold = COMMIT && ok && len > 0 && len >= a.min_len;   // uniform per sequence
   const int LT = len + n;
@@ -878,13 +879,15 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
     }
   }
 
-  IndexUpdate u;
-  u.apply = ok && (a.append || fold);
+  IndexUpdate u;   // a rollback passed with the drafts stands even if they overflow
+  u.apply = (ok && (a.append || fold)) || rl.rolled;
   u.pos_add = fold ? len : 0;
-  u.new_len = (fold ? 0 : len) + (a.append ? n : 0);
+  u.new_len = ok ? (fold ? 0 : len) + (a.append ? n : 0) : len;
   finish_update(a.arrive, a.pos, a.len, q.b, a.H, arrived, u);
-  if (!ok && last_arrival(arrived, a.H))
-    raise_status(a.status, valid ? kStatusOverflow : kStatusIndex);
+  if (last_arrival(arrived, a.H)) {
+    if (!ok) raise_status(a.status, valid ? kStatusOverflow : kStatusIndex);
+    if (rl.bad) raise_status(a.status, kStatusRollback);
+  }
 }
 
 // ----------------------------------------------------------- append path ----

@@ -75,6 +75,8 @@ def lib():
         L.rssm_verify_commit.argtypes = [P(rssm_layer), ctypes.c_int, P(rssm_inputs), _vp,
                                          ctypes.c_int, _vp]
         L.rssm_rollback.argtypes = [P(rssm_layer), _vp, _vp]
+        L.rssm_rollback_verify_commit.argtypes = [P(rssm_layer), _vp, ctypes.c_int,
+                                                  P(rssm_inputs), _vp, ctypes.c_int, _vp]
         L.rssm_verify_tree.argtypes = [P(rssm_layer), ctypes.c_int, P(ctypes.c_int32),
                                        P(rssm_inputs), _vp, _vp]
         L.rssm_verify_tree_commit.argtypes = [P(rssm_layer), ctypes.c_int, P(ctypes.c_int32),
@@ -97,7 +99,8 @@ def lib():
                   "rssm_rollback", "rssm_eager_step", "rssm_status", "rssm_verify_tree",
                   "rssm_append_path", "rssm_prefill", "rssm_eager_spec_round",
                   "rssm_eager_spec_accept", "rssm_probe_stream", "rssm_probe_stream_tiles",
-                  "rssm_verify_commit", "rssm_verify_tree_commit", "rssm_mamba2_step_noalloc"):
+                  "rssm_verify_commit", "rssm_verify_tree_commit", "rssm_mamba2_step_noalloc",
+                  "rssm_rollback_verify_commit"):
             getattr(L, f).restype = ctypes.c_int
         if L.rssm_abi_version() != RSSM_ABI_VERSION:
             raise RuntimeError(f"{LIB_PATH} implements ABI {L.rssm_abi_version()}, this binding "
@@ -187,6 +190,18 @@ def rssm_verify_commit(layer, n_pos, inputs, out, min_len, stream=None, check=Tr
     rc = lib().rssm_verify_commit(ctypes.byref(_desc(layer)), int(n_pos), ctypes.byref(inputs),
                                   _ptr(out), int(min_len), _stream(stream))
     return _check(rc, "rssm_verify_commit") if check else rc
+
+
+def rssm_rollback_verify_commit(layer, n_reject, n_pos, inputs, out, min_len, stream=None,
+                                check=True):
+    """rssm_rollback(layer, n_reject) then rssm_verify_commit, in one launch;
+    n_reject: device int32 [batch]."""
+    if isinstance(inputs, dict):
+        inputs = make_inputs(**inputs)
+    rc = lib().rssm_rollback_verify_commit(ctypes.byref(_desc(layer)), _ptr(n_reject), int(n_pos),
+                                           ctypes.byref(inputs), _ptr(out), int(min_len),
+                                           _stream(stream))
+    return _check(rc, "rssm_rollback_verify_commit") if check else rc
 
 
 def rssm_verify_tree(layer, parent, inputs, out, stream=None, check=True):

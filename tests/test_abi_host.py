@@ -204,6 +204,24 @@ def test_commit_verify_rollback_ranges():
     assert R.rssm_rollback(L, None, stream=0, check=False) == R.RSSM_EINVAL
 
 
+def test_rollback_verify_commit_validates_on_host():
+    """The fused rollback + verify refuses, before any launch, what either of
+    the two calls it replaces refuses, and a missing rejection array."""
+    L = _m2_desc(batch=4, capacity=12)
+    inp = R.make_inputs(x=FAKE, B=FAKE, C=FAKE, dt=FAKE)
+    rvc = R.rssm_rollback_verify_commit
+    assert rvc(L, None, 4, inp, FAKE, 8, stream=0, check=False) == R.RSSM_EINVAL
+    assert rvc(L, FAKE, 4, inp, FAKE, 0, stream=0, check=False) == R.RSSM_ERANGE
+    assert rvc(L, FAKE, 0, inp, FAKE, 8, stream=0, check=False) == R.RSSM_ERANGE
+    assert rvc(L, FAKE, 9, inp, FAKE, 8, stream=0, check=False) == R.RSSM_ERANGE
+    assert rvc(L, FAKE, 4, R.make_inputs(x=FAKE, B=FAKE, C=FAKE), FAKE, 8, stream=0,
+               check=False) == R.RSSM_EINVAL
+    dual = _m2_desc(batch=4, capacity=12, scheme=R.RSSM_DUAL, lp_dtype=R.RSSM_BF16)
+    dual.ckpt_lp = FAKE
+    assert rvc(dual, FAKE, 4, inp, FAKE, 8, stream=0, check=False) == R.RSSM_EUNSUPPORTED
+    assert rvc(_m2_desc(batch=0), FAKE, 4, inp, FAKE, 8, stream=0, check=False) == R.RSSM_OK
+
+
 def test_gdn_validation():
     L = _gdn_desc(batch=2, ngroups=2)
     assert R.rssm_gdn_step(L, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, stream=0,

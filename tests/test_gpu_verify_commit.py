@@ -458,3 +458,137 @@ def test_chain_as_tree_appends_only_accepted_drafts():
     R.rssm_commit(L, None, 1)
     assert _tile_rel(gu.host(L.ckpt), ref["state"]) <= 1e-4
     assert R.rssm_status(L) == 0
+
+
+# ------------------------------------------- rollback fused into the verify --
+
+def _spec_setup(kind, seed, rounds, n, b, H, cap):
+    """A layer and stacked draft rounds for either layer type."""
+    if kind == "mamba2":
+        G = 2
+        A, D = syn.m2_params(seed, H)
+        h0 = syn.m2_state0(seed, b, H, 64, 128)
+        drafts = _drafts(seed, rounds, n, b, H, G)
+        L = gu.m2_layer(A, D, h0, G, cap)
+        keys, like = ("x", "B", "C", "dt"), "x"
+
+        def ref(acc, commit_len):
+            return drivers.m2_spec_rounds(A, D, h0, drafts, acc, cap, commit_len)
+
+        def check(ys, want):
+            gu.check_m2_outputs(ys, want["y"], drafts["x"], D)
+    else:
+        S0 = syn.gdn_state0(seed, b, H, 128, 128, std=0.1)
+        drafts = syn.stack_rounds(syn.gdn_steps(seed, 0, rounds * n, b, H, 128, 128), rounds, n)
+        L = gu.gdn_layer(S0, cap)
+        keys, like = _GDN, "v"
+
+        def ref(acc, commit_len):
+            return drivers.gdn_spec_rounds(S0, drafts, acc, cap, commit_len)
+
+        def check(os_, want):
+            assert gu.vec_rel_err(os_, want["o"]) <= gu.TOL_F32
+    return L, drafts, keys, like, ref, check
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_rollback_fused_into_next_verify_against_oracle(kind):
+    """Speculative rounds in which each round's rejections go to the next
+    round's verify (rssm_rollback_verify_commit): the draft outputs are the
+    eager recurrence's, the indices follow the integer model's rollback, then
+    commit, then append at every call, and the state after the last round is
+    the oracle's (explainer, "Cheap speculative decoding rollback")."""
+    rounds, n, b, H, cap, commit_len = 30, 4, 6, 8 if kind == "mamba2" else 4, 16, 8
+    L, drafts, keys, like, ref, check = _spec_setup(kind, 41, rounds, n, b, H, cap)
+    accept = syn.accept_counts(41, rounds, b, n)
+    d = {k: gu.dev(v) for k, v in drafts.items()}
+    out = gu.torch().empty_like(d[like][0])
+    nrej = [gu.dev((n - accept[r]).astype(np.int32)) for r in range(rounds)]
+    im = IndexModel(b, cap)
+    outs = []
+    for r in range(rounds):
+        inp = {k: d[k][r] for k in keys}
+        if r == 0:
+            R.rssm_verify_commit(L, n, inp, out, commit_len)
+        else:
+            R.rssm_rollback_verify_commit(L, nrej[r - 1], n, inp, out, commit_len)
+            im.rollback(n - accept[r - 1])
+        im.commit(min_len=commit_len)
+        assert im.append(n).all()
+        pos, ln = gu.indices(L)
+        np.testing.assert_array_equal(pos, im.pos)
+        np.testing.assert_array_equal(ln, im.len)
+        outs.append(gu.host(out))
+    R.rssm_rollback(L, nrej[-1])
+    want = ref(accept, commit_len)
+    check(np.array(outs), want)
+    R.rssm_commit(L, None, 1)
+    assert _tile_rel(gu.host(L.ckpt), want["state"]) <= 1e-4
+    assert R.rssm_status(L) == 0
+
+
+@pytest.mark.parametrize("kind", ["mamba2", "gdn"])
+def test_rollback_fused_equals_rollback_then_verify_commit(kind):
+    """One launch against the two calls it replaces, on full buffers (14 of 16
+    slots) and every case at once: overflow without and with a rollback (the
+    rollback stands), a plain append, a fold, and counts below zero and above
+    len (refused, the bit raised, the sequence verified on its old length).
+    Outputs (NaN where refused), indices, rings, checkpoints and status bits
+    bitwise equal; the indices also equal the integer model's."""
+    b, H, cap, n, min_len, T = 6, 8 if kind == "mamba2" else 4, 16, 4, 8, 14
+    nrej_h = np.array([0, 1, 9, -1, 15, 6], np.int32)
+    t_ = gu.torch()
+    if kind == "mamba2":
+        G = 2
+        A, D = syn.m2_params(43, H)
+        h0 = syn.m2_state0(43, b, H, 64, 128)
+        st = {k: gu.dev(v) for k, v in syn.m2_steps(43, 0, T, b, H, G, 64, 128).items()}
+        dr = {k: gu.dev(v) for k, v in syn.m2_steps(43, T, n, b, H, G, 64, 128).items()}
+
+        def prepare():
+            L = gu.m2_layer(A, D, h0, G, cap)
+            y = t_.empty_like(st["x"][0])
+            for t in range(T):
+                R.rssm_mamba2_step(L, st["x"][t], st["B"][t], st["C"][t], st["dt"][t], y)
+            return L
+        inp = dict(x=dr["x"], B=dr["B"], C=dr["C"], dt=dr["dt"])
+        like = dr["x"]
+    else:
+        S0 = syn.gdn_state0(43, b, H, 128, 128, std=0.1)
+        st = {k: gu.dev(v) for k, v in syn.gdn_steps(43, 0, T, b, H, 128, 128).items()}
+        dr = {k: gu.dev(v) for k, v in syn.gdn_steps(43, T, n, b, H, 128, 128).items()}
+
+        def prepare():
+            L = gu.gdn_layer(S0, cap)
+            o = t_.empty_like(st["v"][0])
+            for t in range(T):
+                R.rssm_gdn_step(L, *(st[k][t] for k in _GDN), o)
+            return L
+        inp = {k: dr[k] for k in _GDN}
+        like = dr["v"]
+    nrej = gu.dev(nrej_h)
+    L1, L2 = prepare(), prepare()
+    o1, o2 = t_.empty_like(like), t_.empty_like(like)
+    R.rssm_rollback(L1, nrej)
+    R.rssm_verify_commit(L1, n, inp, o1, min_len)
+    R.rssm_rollback_verify_commit(L2, nrej, n, inp, o2, min_len)
+    s1, s2 = R.rssm_status(L1), R.rssm_status(L2)
+    assert s1 == s2 == (R.STATUS_ROLLBACK | R.STATUS_OVERFLOW)
+    im = IndexModel(b, cap)
+    im.append(T)
+    im.rollback(nrej_h)
+    ok = im.len + n <= cap
+    fold = ok & (im.len >= min_len)
+    im.pos[fold] += im.len[fold]
+    im.len[fold] = 0
+    im.len[ok] += n
+    for got, want in zip(gu.indices(L2), (im.pos, im.len)):
+        np.testing.assert_array_equal(got, want)
+    assert gu.indices(L2)[1].tolist() == [14, 13, 9, 14, 14, 4]
+    for a_, b_ in zip(gu.indices(L1), gu.indices(L2)):
+        np.testing.assert_array_equal(a_, b_)
+    np.testing.assert_array_equal(gu.host(o1), gu.host(o2))   # NaN where refused, on both
+    assert np.isnan(gu.host(o2)[:, [0, 1, 3, 4]]).all() and np.isfinite(gu.host(o2)[:, [2, 5]]).all()
+    np.testing.assert_array_equal(gu.host(L1.ckpt), gu.host(L2.ckpt))
+    for r1, r2 in zip(L1.rings, L2.rings):
+        np.testing.assert_array_equal(gu.host(r1), gu.host(r2))

@@ -147,8 +147,11 @@ def test_gdn_interval_graph_replays_equal_eager(scheme, fused):
 
 # ------------------------------------------------------- speculative round --
 
-def _drive_spec(L_make, drafts, accept, verify, n, min_len):
-    """drafts: dict of numpy [rounds, n, ...]; accept: [rounds, b] accepted counts."""
+def _drive_spec(L_make, drafts, accept, verify, n, min_len, one_launch=False):
+    """drafts: dict of numpy [rounds, n, ...]; accept: [rounds, b] accepted counts.
+    one_launch: each round is rssm_rollback_verify_commit with the previous
+    round's rejections (none before the first); the last round's rollback is
+    applied after the loop."""
     t_ = gu.torch()
     Lg, Le = L_make(), L_make()
     names = list(drafts)
@@ -160,8 +163,11 @@ def _drive_spec(L_make, drafts, accept, verify, n, min_len):
     oute = t_.empty_like(outg)
 
     def round_(L, out):
-        R.rssm_verify_commit(L, n, {s: stat[s] for s in names}, out, min_len)
-        R.rssm_rollback(L, nrej)
+        if one_launch:
+            R.rssm_rollback_verify_commit(L, nrej, n, {s: stat[s] for s in names}, out, min_len)
+        else:
+            R.rssm_verify_commit(L, n, {s: stat[s] for s in names}, out, min_len)
+            R.rssm_rollback(L, nrej)
 
     t_.cuda.synchronize()
     g = t_.cuda.CUDAGraph()
@@ -171,7 +177,11 @@ def _drive_spec(L_make, drafts, accept, verify, n, min_len):
     for r in range(rounds):
         for s in names:
             stat[s].copy_(gu.dev(drafts[s][r]))
-        nrej.copy_(gu.dev((n - accept[r]).astype(np.int32)))
+        if one_launch:
+            prev = n - accept[r - 1] if r > 0 else np.zeros_like(accept[0])
+            nrej.copy_(gu.dev(prev.astype(np.int32)))
+        else:
+            nrej.copy_(gu.dev((n - accept[r]).astype(np.int32)))
         t_.cuda.synchronize()
         g.replay()
         junk = t_.randn(1 << 16, device="cuda").abs().sum()
@@ -180,6 +190,11 @@ def _drive_spec(L_make, drafts, accept, verify, n, min_len):
         t_.cuda.synchronize()
         assert float(junk) > 0
         _compare(Lg, Le, outg, oute, r)
+    if one_launch:
+        last = gu.dev((n - accept[-1]).astype(np.int32))
+        R.rssm_rollback(Lg, last)
+        R.rssm_rollback(Le, last)
+        _compare(Lg, Le, outg, oute, rounds)
     pos, ln = gu.indices(Lg)
     assert (pos + ln == accept.sum(axis=0)).all()
     del g
@@ -190,18 +205,21 @@ class _Dv:
         self.dv = dv
 
 
-def test_mamba2_spec_round_graph_replays_equal_eager():
+@pytest.mark.parametrize("one_launch", [False, True])
+def test_mamba2_spec_round_graph_replays_equal_eager(one_launch):
     rounds, n, b, H, G, P, N, cap, min_len = 12, 4, 6, 16, 2, 64, 128, 16, 8
     A, D = syn.m2_params(72, H)
     h0 = syn.m2_state0(72, b, H, P, N)
     drafts = syn.stack_rounds(syn.m2_steps(72, 0, rounds * n, b, H, G, P, N), rounds, n)
     accept = syn.accept_counts(72, rounds, b, n)
-    _drive_spec(lambda: gu.m2_layer(A, D, h0, G, cap), drafts, accept, _Dv(P), n, min_len)
+    _drive_spec(lambda: gu.m2_layer(A, D, h0, G, cap), drafts, accept, _Dv(P), n, min_len,
+                one_launch)
 
 
-def test_gdn_spec_round_graph_replays_equal_eager():
+@pytest.mark.parametrize("one_launch", [False, True])
+def test_gdn_spec_round_graph_replays_equal_eager(one_launch):
     rounds, n, b, H, d, cap, min_len = 12, 4, 5, 6, 128, 16, 8
     S0 = syn.gdn_state0(73, b, H, d, d, std=0.1)
     drafts = syn.stack_rounds(syn.gdn_steps(73, 0, rounds * n, b, H, d, d), rounds, n)
     accept = syn.accept_counts(73, rounds, b, n)
-    _drive_spec(lambda: gu.gdn_layer(S0, cap), drafts, accept, _Dv(d), n, min_len)
+    _drive_spec(lambda: gu.gdn_layer(S0, cap), drafts, accept, _Dv(d), n, min_len, one_launch)

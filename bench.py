@@ -634,7 +634,8 @@ def run_tree_rounds(torch, R, syn, rounds, seed=0):
     """Mamba-2 headline shape, tree speculation: each round verifies a binary
     tree of 7 drafts (depth 3) from one checkpoint read, appends a random
     root-to-node path per sequence (0..3 drafts) and commits sequences whose
-    buffer reached 8; ring 16 (up to 7 buffered + 7 drafts in flight)."""
+    buffer reached 8; ring 16 (up to 7 buffered + 7 drafts in flight).  Then
+    the same rounds with the commit folded into the tree verify."""
     b, H, G, P, N, cap, commit_len = 256, 80, 8, 64, 128, 16, 8
     parent = [-1, 0, 0, 1, 1, 2, 2]
     paths = [[0], [0, 1], [0, 2], [0, 1, 3], [0, 1, 4], [0, 2, 5], [0, 2, 6]]
@@ -674,6 +675,28 @@ def run_tree_rounds(torch, R, syn, rounds, seed=0):
     res = dict(rounds_per_s=rounds / (ms * 1e-3),
                accepted_seq_tok_s=float(plen.sum()) / (ms * 1e-3),
                us_per_round=ms * 1e3 / rounds, drafts_per_round=n)
+    # the same rounds with the commit folded into the tree verify
+    # (rssm_verify_tree_commit).  A buffer that waits one round longer must
+    # still leave room for the 7 drafts: folding at 7 entries, a sequence holds
+    # at most 6 + 3 = 9 before a verify, and 9 + 7 = 16 slots
+    fold_len = 7
+    del L
+    L = R.Layer.mamba2(b, H, G, P, N, cap)
+    L.A.copy_(torch.from_numpy(A))
+    L.D.copy_(torch.from_numpy(D))
+    L.ckpt.copy_(_dev_state(torch, syn.m2_state0(seed, b, H, P, N)))
+    torch.cuda.synchronize()
+    start.record()
+    for r in range(rounds):
+        R.rssm_verify_tree_commit(L, parent, inp, out, fold_len)
+        R.rssm_append_path(L, n, arr_d[r], plen_d[r], inp)
+    end.record()
+    torch.cuda.synchronize()
+    fms = start.elapsed_time(end)
+    assert R.rssm_status(L) == 0
+    res["fused_commit_at_7"] = dict(rounds_per_s=rounds / (fms * 1e-3),
+                                    accepted_seq_tok_s=float(plen.sum()) / (fms * 1e-3),
+                                    us_per_round=fms * 1e3 / rounds)
     del L, dev
     torch.cuda.empty_cache()
     return res
@@ -1061,7 +1084,7 @@ def main():
             sec["mamba2_lowprec_seq_tok_s"] = run_m2_lowprec(torch, R, syn, 128)
         if want("tree"):
             tr = run_tree_rounds(torch, R, syn, 128)
-            sec["mamba2_tree_rounds_b256_7drafts"] = {k: round(v, 1) for k, v in tr.items()}
+            sec["mamba2_tree_rounds_b256_7drafts"] = _round1(tr)
         if want("prefill"):
             pm = run_prefill(torch, R, syn, "mamba2")
             pg = run_prefill(torch, R, syn, "gdn")

@@ -498,7 +498,7 @@ __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
 // them in a wave-private LDS tile and reads the operands from there: no
 // cross-lane reduction, and no barrier between the waves for the transpose.
 //
-// W16 (fp32, eight drafts, no fold): 16 lanes per state row instead of 32,
+// W16 (fp32, eight drafts, with or without the fold): 16 lanes per state row instead of 32,
 // each holding columns 4c..4c+3 and 64+4c..64+4c+3 of rows r0 + 16k (every
 // load instruction still reads 256 contiguous bytes per row).  The 4 rows x 8
 // drafts of partial sums per lane are then reduced across 16 lanes, with DPP
@@ -507,7 +507,7 @@ template <int EB, int NPAD, bool COMMIT = false, bool MF = false>
 __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   static_assert(!COMMIT || EB == 4, "the fused commit folds the fp32 checkpoint");
   static_assert(!MF || (EB == 4 && NPAD >= 4), "matrix-core contraction: fp32, 4 or 8 drafts");
-  constexpr bool W16 = EB == 4 && NPAD == 8 && !COMMIT && !MF;
+  constexpr bool W16 = EB == 4 && NPAD == 8 && !MF;
   using Gm = RdGeo<EB>;
   const Geo q = geometry(a);
   const int cap = a.cap, n = a.n_pos;
@@ -853,19 +853,39 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
 
   if constexpr (COMMIT) {
     if (fold) {   // h <- Gamma_buf h_c + sum_{i<len} fw_i x_i B_i^T, from the expanded tile
-      f32x4 hv[NLD];   // the fp32 read geometry is the tile geometry
+      f32x4 hv[NLD];   // the tile's own geometry
       const float gb = s_gbuf;
 #pragma unroll
       for (int k = 0; k < NLD; ++k) hv[k] = gb * f32x4{f[k][0], f[k][1], f[k][2], f[k][3]};
-      for (int i = 0; i < len; ++i) {
-        const f32x4 bi = ld4(&s_Bf[i][q.c4 * 4]);
-        const float w = s_fw[i];
+      if constexpr (W16) {   // hv[2 k + hf]: row tid/16 + 16 k, column half hf
+        const int c16 = q.tid & 15, rw = q.tid >> 4;
+        for (int i = 0; i < len; ++i) {
+          const f32x4 b0 = ld4(&s_Bf[i][4 * c16]), b1 = ld4(&s_Bf[i][64 + 4 * c16]);
+          const float w = s_fw[i];
 #pragma unroll
-        for (int k = 0; k < NLD; ++k) hv[k] += (w * s_xf[i][rowk(k)]) * bi;
+          for (int k = 0; k < NLD / 2; ++k) {
+            const float xw = w * s_xf[i][rw + 16 * k];
+            hv[2 * k] += xw * b0;
+            hv[2 * k + 1] += xw * b1;
+          }
+        }
+        float* ck = a.ckpt + q.unit * (P * N) + rw * N + 4 * c16;
+#pragma unroll
+        for (int k = 0; k < NLD / 2; ++k) {
+          st_nt(ck + 16 * k * N, hv[2 * k]);
+          st_nt(ck + 16 * k * N + 64, hv[2 * k + 1]);
+        }
+      } else {   // the fp32 read geometry is the tile geometry
+        for (int i = 0; i < len; ++i) {
+          const f32x4 bi = ld4(&s_Bf[i][q.c4 * 4]);
+          const float w = s_fw[i];
+#pragma unroll
+          for (int k = 0; k < NLD; ++k) hv[k] += (w * s_xf[i][rowk(k)]) * bi;
+        }
+        float* ck = a.ckpt + q.unit * (P * N) + q.c4 * 4;
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) st_nt(ck + rowk(k) * N, hv[k]);
       }
-      float* ck = a.ckpt + q.unit * (P * N) + q.c4 * 4;
-#pragma unroll
-      for (int k = 0; k < NLD; ++k) st_nt(ck + rowk(k) * N, hv[k]);
     }
   }
 

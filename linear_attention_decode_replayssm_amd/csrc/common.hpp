@@ -229,6 +229,8 @@ struct XRed {
 // results; writer() picks one of them.
 template <int V, int LPR>
 struct XMap {
+  static_assert(V > 0 && (V & (V - 1)) == 0 && LPR > 0 && (LPR & (LPR - 1)) == 0,
+                "the transposed reduction halves the values and the lanes: powers of two");
   static constexpr int kLogL = ilog2(LPR);
   static constexpr int kLogV = ilog2(V);
   static constexpr int VOUT = V > LPR ? V / LPR : 1;
@@ -251,6 +253,8 @@ struct XMap {
 
 template <int V, int LPR>
 __device__ __forceinline__ void xreduce(float (&v)[V], int lane) {
+  static_assert(V > 0 && (V & (V - 1)) == 0 && LPR > 0 && (LPR & (LPR - 1)) == 0,
+                "the transposed reduction halves the values and the lanes: powers of two");
   XRed<V, LPR / 2>::run(v, lane);
 }
 

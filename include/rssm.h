@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define RSSM_ABI_VERSION 10
+#define RSSM_ABI_VERSION 11
 #define RSSM_ARRIVE_STRIDE 32   /* uint32 elements between two sequences' counters */
 #define RSSM_NOALLOC_MAX_BATCH 4096  /* sequences served by rssm_mamba2_step_noalloc    */
 

@@ -22,7 +22,7 @@ STATUS_OVERFLOW, STATUS_ROLLBACK, STATUS_NONFINITE, STATUS_INDEX = 1, 2, 4, 8
 RSSM_MAMBA2, RSSM_GDN = 1, 2
 RSSM_F32, RSSM_DUAL, RSSM_SHARED = 0, 1, 2
 RSSM_LP_NONE, RSSM_BF16, RSSM_E4M3 = 0, 1, 2
-RSSM_ABI_VERSION = 10
+RSSM_ABI_VERSION = 11
 RSSM_ARRIVE_STRIDE = 32   # uint32 elements between two sequences' arrival counters
 RSSM_NOALLOC_MAX_BATCH = 4096   # sequences rssm_mamba2_step_noalloc serves
 RSSM_LAYER_INDEX_READONLY = 1   # rssm_layer.flags: indices read, never written
@@ -65,6 +65,10 @@ def lib():
                 "`python -m linear_attention_decode_replayssm_amd.build` "
                 "(or __graft_entry__.build())")
         L = ctypes.CDLL(LIB_PATH)
+        L.rssm_abi_version.restype = ctypes.c_int
+        if L.rssm_abi_version() != RSSM_ABI_VERSION:   # before any other symbol is looked up
+            raise RuntimeError(f"{LIB_PATH} implements ABI {L.rssm_abi_version()}, this binding "
+                               f"{RSSM_ABI_VERSION}: rebuild the library")
         P = ctypes.POINTER
         L.rssm_mamba2_step.argtypes = [P(rssm_layer), _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp]
         L.rssm_mamba2_step_noalloc.argtypes = [P(rssm_layer), _vp, _vp, _vp, _vp, _vp,
@@ -94,7 +98,6 @@ def lib():
         L.rssm_status.argtypes = [P(rssm_layer), P(ctypes.c_uint32), _vp]
         L.rssm_strerror.argtypes = [ctypes.c_int]
         L.rssm_strerror.restype = ctypes.c_char_p
-        L.rssm_abi_version.restype = ctypes.c_int
         for f in ("rssm_mamba2_step", "rssm_gdn_step", "rssm_commit", "rssm_verify",
                   "rssm_rollback", "rssm_eager_step", "rssm_status", "rssm_verify_tree",
                   "rssm_append_path", "rssm_prefill", "rssm_eager_spec_round",
@@ -102,9 +105,6 @@ def lib():
                   "rssm_verify_commit", "rssm_verify_tree_commit", "rssm_mamba2_step_noalloc",
                   "rssm_rollback_verify_commit"):
             getattr(L, f).restype = ctypes.c_int
-        if L.rssm_abi_version() != RSSM_ABI_VERSION:
-            raise RuntimeError(f"{LIB_PATH} implements ABI {L.rssm_abi_version()}, this binding "
-                               f"{RSSM_ABI_VERSION}: rebuild the library")
         _lib = L
     return _lib
 

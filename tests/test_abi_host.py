@@ -60,7 +60,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_strerror():
-    assert R.rssm_abi_version() == R.RSSM_ABI_VERSION == 10
+    assert R.rssm_abi_version() == R.RSSM_ABI_VERSION == 11
     for code in (0, -1, -2, -3, -4, -5):
         assert R.rssm_strerror(code)
     assert "unknown" in R.rssm_strerror(12345)

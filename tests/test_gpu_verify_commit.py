@@ -162,11 +162,13 @@ def test_overflowing_sequence_is_neither_folded_nor_appended():
     assert R.rssm_status(L) == R.STATUS_OVERFLOW
 
 
-def test_serving_shape_spec_rounds():
+@pytest.mark.parametrize("one_launch", [False, True])
+def test_serving_shape_spec_rounds(one_launch):
     """batch 256 x 80 heads x 8 groups, 4 drafts, commit of buffers of 8+ at
     the next verify, ring 16; 128 rounds.  Index trace of every sequence
     bit-exact against the integer model; draft outputs of two sequences
-    against the oracle."""
+    against the oracle.  one_launch: each round's rollback is passed to the
+    next round's verify (rssm_rollback_verify_commit)."""
     rounds, n, b, H, G, cap, commit_len = 128, 4, 256, 80, 8, 16, 8
     A, D = syn.m2_params(35, H)
     h0 = syn.m2_state0(35, b, H, 64, 128)
@@ -180,19 +182,25 @@ def test_serving_shape_spec_rounds():
     out = t_.empty((n, b, H, 64), dtype=t_.float32, device="cuda")
     im = IndexModel(b, cap)
     ys = []
+    nrej = [gu.dev((n - accept[r]).astype(np.int32)) for r in range(rounds)]
     for r in range(rounds):
         j0 = int(idx[r, 0])
         dr = {k: v[j0:j0 + n] for k, v in pool_dev.items()}
-        R.rssm_verify_commit(L, n, dict(x=dr["x"], B=dr["B"], C=dr["C"], dt=dr["dt"]), out,
-                             commit_len)
+        inp = dict(x=dr["x"], B=dr["B"], C=dr["C"], dt=dr["dt"])
+        if one_launch and r > 0:
+            R.rssm_rollback_verify_commit(L, nrej[r - 1], n, inp, out, commit_len)
+            im.rollback(n - accept[r - 1])
+        else:
+            R.rssm_verify_commit(L, n, inp, out, commit_len)
         im.commit(min_len=commit_len)
         assert im.append(n).all()
         pos, ln = gu.indices(L)
         np.testing.assert_array_equal(pos, im.pos)
         np.testing.assert_array_equal(ln, im.len)
         ys.append(gu.host(out[:, sel]))
-        R.rssm_rollback(L, gu.dev((n - accept[r]).astype(np.int32)))
-        im.rollback(n - accept[r])
+        if not one_launch:
+            R.rssm_rollback(L, nrej[r])
+            im.rollback(n - accept[r])
     sub = {k: np.ascontiguousarray(v[:, sel][idx.reshape(-1)]) for k, v in pool.items()}
     sub = syn.stack_rounds(sub, rounds, n)
     ref = drivers.m2_spec_rounds(A, D, h0[sel], sub, accept[:, sel], cap, commit_len)
@@ -270,11 +278,13 @@ def test_gdn_fold_matches_standalone_commit():
     assert R.rssm_status(L1) == 0 and R.rssm_status(L2) == 0
 
 
-def test_gdn_serving_shape_spec_rounds():
+@pytest.mark.parametrize("one_launch", [False, True])
+def test_gdn_serving_shape_spec_rounds(one_launch):
     """batch 256 x 32 heads (d 128), 4 drafts, commit of buffers of 8+ at the
     next verify, ring 16; 96 rounds.  Index trace of every sequence bit-exact
     against the integer model; draft outputs of two sequences against the
-    oracle."""
+    oracle.  one_launch: each round's rollback is passed to the next round's
+    verify (rssm_rollback_verify_commit)."""
     rounds, n, b, H, cap, commit_len = 96, 4, 256, 32, 16, 8
     S0 = syn.gdn_state0(38, b, H, 128, 128)
     accept = syn.accept_counts(38, rounds, b, n)
@@ -287,17 +297,24 @@ def test_gdn_serving_shape_spec_rounds():
     out = t_.empty((n, b, H, 128), dtype=t_.float32, device="cuda")
     im = IndexModel(b, cap)
     os_ = []
+    nrej = [gu.dev((n - accept[r]).astype(np.int32)) for r in range(rounds)]
     for r in range(rounds):
         j0 = int(idx[r, 0])
-        R.rssm_verify_commit(L, n, {k: pool_dev[k][j0:j0 + n] for k in _GDN}, out, commit_len)
+        inp = {k: pool_dev[k][j0:j0 + n] for k in _GDN}
+        if one_launch and r > 0:
+            R.rssm_rollback_verify_commit(L, nrej[r - 1], n, inp, out, commit_len)
+            im.rollback(n - accept[r - 1])
+        else:
+            R.rssm_verify_commit(L, n, inp, out, commit_len)
         im.commit(min_len=commit_len)
         assert im.append(n).all()
         pos, ln = gu.indices(L)
         np.testing.assert_array_equal(pos, im.pos)
         np.testing.assert_array_equal(ln, im.len)
         os_.append(gu.host(out[:, sel]))
-        R.rssm_rollback(L, gu.dev((n - accept[r]).astype(np.int32)))
-        im.rollback(n - accept[r])
+        if not one_launch:
+            R.rssm_rollback(L, nrej[r])
+            im.rollback(n - accept[r])
     sub = {k: np.ascontiguousarray(v[:, sel][idx.reshape(-1)]) for k, v in pool.items()}
     sub = syn.stack_rounds(sub, rounds, n)
     ref = drivers.gdn_spec_rounds(S0[sel], sub, accept[:, sel], cap, commit_len)

@@ -306,7 +306,10 @@ int rssm_verify_commit(const rssm_layer* L, int n_pos, const rssm_inputs* in, fl
  * as rssm_verify_commit would verify it; a valid rollback stands when the
  * drafts then overflow (RSSM_STATUS_OVERFLOW, outputs NaN, no append).
  * n_reject: device int32 [batch], caller-owned, read only; NULL is
- * RSSM_EINVAL.  A min_len above the capacity never folds (a fused rollback
+ * RSSM_EINVAL.  On a layer with RSSM_LAYER_INDEX_READONLY the rejections are
+ * applied to the indices the call reads and nothing is written: the layer
+ * that owns the shared indices applies the same rollback when its own call,
+ * the last of the stack, runs (rssm_rollback alone does nothing there).  A min_len above the capacity never folds (a fused rollback
  * with plain verification).  Other arguments and errors as for
  * rssm_verify_commit (F32 checkpoints only).
  */

@@ -9,7 +9,9 @@ every output, checkpoint and ring slot must be equal bit for bit (the kernels
 are the same; only who writes the indices differs) and the shared indices
 must equal each independent layer's.  Covered: plain steps with fused and
 standalone commits, speculative rounds (verify, rollback, commit at a
-minimum length) for both layer types."""
+minimum length) and one-launch rounds (rssm_rollback_verify_commit: a
+read-only layer applies the rejections to the indices it reads, the owner
+writes them) for both layer types."""
 import numpy as np
 import pytest
 
@@ -51,7 +53,7 @@ def test_shared_indices_equal_per_layer_indices(kind):
         def make(layer):
             A, D = syn.m2_params(140 + layer, H)
             return gu.m2_layer(A, D, syn.m2_state0(140 + layer, b, H, P, N), G, cap)
-        steps = [syn.m2_steps(140 + layer, 0, T + n * 3, b, H, G, P, N) for layer in range(NL)]
+        steps = [syn.m2_steps(140 + layer, 0, T + n * 6, b, H, G, P, N) for layer in range(NL)]
         step = R.rssm_mamba2_step
         out_of = "x"
     else:
@@ -60,7 +62,7 @@ def test_shared_indices_equal_per_layer_indices(kind):
 
         def make(layer):
             return gu.gdn_layer(syn.gdn_state0(150 + layer, b, H, D_, D_, std=0.1), cap)
-        steps = [syn.gdn_steps(150 + layer, 0, T + n * 3, b, H, D_, D_) for layer in range(NL)]
+        steps = [syn.gdn_steps(150 + layer, 0, T + n * 6, b, H, D_, D_) for layer in range(NL)]
         step = R.rssm_gdn_step
         out_of = "v"
     dev = [{k: gu.dev(v) for k, v in st.items()} for st in steps]
@@ -89,6 +91,20 @@ def test_shared_indices_equal_per_layer_indices(kind):
                 R.rssm_rollback(L, gu.dev((n - accept[r]).astype(np.int32)))
             for L in Ls:
                 R.rssm_commit(L, None, 6)
+        # one launch per round: each round's rejections go with the next
+        # round's drafts; a read-only layer applies them to the indices it
+        # reads, the owner writes them
+        acc2 = syn.accept_counts(142, 3, b, n)
+        for r in range(3):
+            prev = np.zeros(b, np.int32) if r == 0 else (n - acc2[r - 1]).astype(np.int32)
+            for layer, L in enumerate(Ls):
+                sl = slice(T + (3 + r) * n, T + (4 + r) * n)
+                out = t_.empty_like(dev[layer][out_of][sl])
+                R.rssm_rollback_verify_commit(L, gu.dev(prev), n,
+                                              {k: dev[layer][k][sl] for k in names}, out, 6)
+                ys.append(gu.host(out))
+        for L in Ls:
+            R.rssm_rollback(L, gu.dev((n - acc2[2]).astype(np.int32)))
         t_.cuda.synchronize()
         outs[tag] = ys
         for L in Ls:

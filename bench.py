@@ -730,6 +730,63 @@ def run_tree_rounds(torch, R, syn, rounds, seed=0):
     return res
 
 
+def run_gdn_tree_rounds(torch, R, syn, rounds, seed=0):
+    """The tree rounds of run_tree_rounds at the GDN serving shape (batch 256 x
+    32 heads, d 128): a binary tree of 7 drafts verified from one checkpoint
+    read, a random root-to-node path appended, commit at 8 (standalone); then
+    with the commit folded into the tree verify at 7 entries."""
+    b, H, d, cap, commit_len = 256, 32, 128, 16, 8
+    parent = [-1, 0, 0, 1, 1, 2, 2]
+    paths = [[0], [0, 1], [0, 2], [0, 1, 3], [0, 1, 4], [0, 2, 5], [0, 2, 6]]
+    n, depth = len(parent), 3
+    names = ("q", "k", "v", "alpha", "beta")
+    pool = syn.gdn_steps(seed, 0, n, b, H, d, d)
+    dev = {k: torch.from_numpy(pool[k]).to("cuda") for k in names}
+    inp = R.make_inputs(**dev)
+    g = np.random.default_rng(seed)
+    pick = g.integers(-1, n, size=(rounds, b))
+    arr = np.zeros((rounds, b, depth), np.int32)
+    plen = np.zeros((rounds, b), np.int32)
+    for r in range(rounds):
+        for s_ in range(b):
+            if pick[r, s_] >= 0:
+                p = paths[pick[r, s_]]
+                arr[r, s_, :len(p)] = p
+                plen[r, s_] = len(p)
+    arr_d = torch.from_numpy(arr).to("cuda")
+    plen_d = torch.from_numpy(plen).to("cuda")
+    out = torch.empty((n, b, H, d), dtype=torch.float32, device="cuda")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for fused in (False, True):
+        L = R.Layer.gdn(b, H, d, d, cap)
+        torch.cuda.synchronize()
+        start.record()
+        for r in range(rounds):
+            if fused:
+                R.rssm_verify_tree_commit(L, parent, inp, out, commit_len - 1)
+            else:
+                R.rssm_verify_tree(L, parent, inp, out)
+            R.rssm_append_path(L, n, arr_d[r], plen_d[r], inp)
+            if not fused:
+                R.rssm_commit(L, None, commit_len)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end)
+        assert R.rssm_status(L) == 0
+        del L
+        r_ = dict(rounds_per_s=rounds / (ms * 1e-3),
+                  accepted_seq_tok_s=float(plen.sum()) / (ms * 1e-3),
+                  us_per_round=ms * 1e3 / rounds)
+        if fused:
+            res["fused_commit_at_7"] = r_
+        else:
+            res.update(r_, drafts_per_round=n)
+    del dev
+    torch.cuda.empty_cache()
+    return res
+
+
 # MFMA work of one 16-token prefill chunk of one head (fp32 16x16x4 products as
 # executed): Mamba-2 C B^T, outputs h C^T + W X, fold X^T B; GDN K K^T, Q K^T,
 # S K^T, S Q^T, T z, M u, fold.
@@ -1120,6 +1177,8 @@ def main():
         if want("tree"):
             tr = run_tree_rounds(torch, R, syn, 128)
             sec["mamba2_tree_rounds_b256_7drafts"] = _round1(tr)
+            gc.collect()
+            sec["gdn_tree_rounds_b256_7drafts"] = _round1(run_gdn_tree_rounds(torch, R, syn, 128))
         if want("prefill"):
             pm = run_prefill(torch, R, syn, "mamba2")
             pg = run_prefill(torch, R, syn, "gdn")

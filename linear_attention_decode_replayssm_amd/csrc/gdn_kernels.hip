@@ -314,8 +314,11 @@ __device__ __forceinline__ float carry_acc(const EntrySmem& s, int hi, int cl, i
 // workgroup (L x L); each row's fold weights U'_i = G_{i+1..t} u_i are then
 // independent short dot products, and the new state is
 // S_new = G_{c+1..t} S_c + U' K (rank L).  The state stays in the
-// consecutive-load geometry of the stream (fp32 FMA; see DESIGN for why not
-// MFMA at these shapes).
+// consecutive-load geometry of the stream and the products run on fp32 FMA:
+// a matrix-core version (v_mfma_f32_16x16x4f32) measured slower, because its
+// operand layout (16 rows x 64 B per wave load) streams the state more slowly
+// than consecutive bytes, half of each 16-wide block is padding at L = 8, and
+// the ~4 L flop per element are hidden under the stream anyway.
 template <int ROWS>
 struct FoldSmem {
   float G[kMaxCap + 1][kMaxCap + 1];   // G[a][e] = prod_{j=a}^{e-1} alpha_j, a <= e <= L

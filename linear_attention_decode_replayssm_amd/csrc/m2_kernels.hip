@@ -772,24 +772,29 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
                           f[2 * k + 1][2] * c1.z + f[2 * k + 1][3] * c1.w;
     }
     xreduce<V, 16>(d, q.lane);
-    __syncthreads();   // s_yb, s_gam complete
+    __syncthreads();   // s_yb, s_gam complete; every wave is past its reads of s_C
+    float (*s_out)[CP] = s_C;   // the drafts' rows of outputs, staged in s_C
 #pragma unroll
     for (int jj = 0; jj < M::VOUT; ++jj) {
       const int idx = M::index(q.lane, jj);
       const int k = idx / NPAD, j = idx % NPAD;
-      if (j < n) {
-        const int pr = r0 + 16 * k;
-        float yv;
-        if (ok) {
-          float yb = 0.f;
+      const int pr = r0 + 16 * k;
+      float yv;
+      if (ok) {
+        float yb = 0.f;
 #pragma unroll
-          for (int g = 0; g < QD; ++g) yb += s_yb[g][j][pr];
-          yv = s_gam[j] * d[jj] + yb + Dh * s_xa[j][pr];
-        } else {
-          yv = __builtin_nanf("");
-        }
-        a.y[j * sx + q.unit * P + pr] = yv;
+        for (int g = 0; g < QD; ++g) yb += s_yb[g][j][pr];
+        yv = s_gam[j] * d[jj] + yb + Dh * s_xa[j][pr];
+      } else {
+        yv = __builtin_nanf("");
       }
+      s_out[j][pr] = yv;
+    }
+    __syncthreads();
+    {  // each draft's row of P outputs as 16 float4 stores
+      static_assert(NPAD * P / 4 <= NT, "one float4 per thread");
+      const int j = q.tid / (P / 4), c = q.tid % (P / 4);
+      if (j < n) st4(a.y + j * sx + q.unit * P + 4 * c, ld4(&s_out[j][4 * c]));
     }
   } else {
     // Row dots with every C_j, reduced across the LPR lanes of a row.  At most

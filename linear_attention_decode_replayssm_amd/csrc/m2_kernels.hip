@@ -849,10 +849,19 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
             } else {
               yv = __builtin_nanf("");
             }
-            a.y[j * sx + q.unit * P + pr] = yv;
+            if constexpr (COMMIT)
+              a.y[j * sx + q.unit * P + pr] = yv;
+            else
+              s_C[j][pr] = yv;   // staged: every wave is past its reads of s_C
           }
         }
       }
+    }
+    if constexpr (!COMMIT) {   // each draft's row of P outputs as float4 stores
+      static_assert(NPAD * P / 4 <= NT, "one float4 per thread");
+      __syncthreads();
+      const int j = q.tid / (P / 4), c = q.tid % (P / 4);
+      if (j < n) st4(a.y + j * sx + q.unit * P + 4 * c, ld4(&s_C[j][4 * c]));
     }
   }
 

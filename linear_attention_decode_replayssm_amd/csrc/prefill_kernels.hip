@@ -45,6 +45,20 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Value of the lane M places higher in the same 16-lane row; the last M lanes
+// of the row, which have no source, get 1 (DPP row_shl keeping the old value).
+template <int M>
+__device__ __forceinline__ float row_shl1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(v), 0x100 | M, 0xF, 0xF, false));
+}
+
+// Value of the lane M places lower in the same 16-lane row; the first M lanes
+// of the row get 0 (DPP row_shr with zero fill).
+template <int M>
+__device__ __forceinline__ float row_shr(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 | M, 0xF, 0xF, true));
+}
+
 // One chunk's inputs in flight: thread tid holds x_i[4c..4c+3] for
 // i = tid / 16, c = tid % 16, and two float4 of B and C each (flat float4
 // index tid + 256u over [Q][N/4]), dt_tid for tid < Q.
@@ -89,7 +103,9 @@ struct M2Pre {
 };
 
 // Left alone the compiler gives this kernel ~220 registers (two waves per
-// SIMD); capped at three waves it needs no spills and runs ~1.2x faster.
+// SIMD); asked for at least three waves it needs no spills and runs ~1.2x
+// faster.  The fp32 and bf16 forms come out at 126-128 registers, which
+// leaves room for four workgroups per CU (27 KB of LDS each).
 template <int SCHEME, int LP>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void m2_prefill_kernel(M2Args a) {
   const int tile = tile_index();
@@ -164,7 +180,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void m2
   __shared__ __attribute__((aligned(16))) float s_x[Q][MP + PAD];
   __shared__ __attribute__((aligned(16))) float s_B[Q][MN + PAD];
   __shared__ __attribute__((aligned(16))) float s_C[Q][MN + PAD];
-  __shared__ float s_dt[Q], s_cum[Q], s_gam[Q], s_fw[Q];
+  __shared__ float s_dt[Q];
   __shared__ float s_E[4][Q][Q + 1];
   __shared__ float s_W[Q][Q + 1];
   __shared__ float s_red[NT / 64];
@@ -183,19 +199,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void m2
     const int n = pre.count(c);
     const bool out = c >= 0 && pre.outs;
 
-    if (tid < Q) {   // decays; padded entries have dt = 0
-      float cum = 0.f, tot = 0.f;
-#pragma unroll
-      for (int i = 0; i < Q; ++i) {
-        const float d = s_dt[i];
-        tot += d;
-        if (i <= tid) cum += d;
-      }
-      s_cum[tid] = cum;
-      s_gam[tid] = expf(Ah * cum);
-      s_fw[tid] = expf(Ah * (tot - cum)) * s_dt[tid];
-    }
-    if (out) {   // this wave's part of E = C B^T: n = 32w .. 32w+31
+    // decays, formed by every wave in registers: lane l holds token li's dt
+    // and its inclusive prefix sum over the chunk (a 16-lane DPP scan; padded
+    // entries have dt = 0), so no wave waits on another for them
+    const float dtl = s_dt[li];
+    float cum = dtl;
+    cum += row_shr<1>(cum);
+    cum += row_shr<2>(cum);
+    cum += row_shr<4>(cum);
+    cum += row_shr<8>(cum);
+    const float tot = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cum), Q - 1));
+    const float fwl = expf(Ah * (tot - cum)) * dtl;   // fold weight of token li
+
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    if (out) {   // this wave's part of E = C B^T (n = 32w .. 32w+31), then h C_j
       f32x4 e = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
@@ -204,32 +221,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void m2
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) s_E[w][4 * lq + r][li] = e[r];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {   // h C_j, contracting over n
+        const f32x4 cv = ld4(&s_C[li][16 * t + 4 * lq]);
+        y = mfma4(cv.x, acc[t].x, y);
+        y = mfma4(cv.y, acc[t].y, y);
+        y = mfma4(cv.z, acc[t].z, y);
+        y = mfma4(cv.w, acc[t].w, y);
+      }
     }
     __syncthreads();
     if (out) {
-      {  // in-chunk weights W[j][i], causal
-        const int j = tid >> 4, i = tid & 15;
+      {  // in-chunk weights W[j][i], causal: j = 4w + lq, i = li
+        const int j = 4 * w + lq;
+        const float cj = __shfl(cum, j);
         float wv = 0.f;
-        if (i <= j)
-          wv = (s_E[0][j][i] + s_E[1][j][i] + s_E[2][j][i] + s_E[3][j][i]) *
-               expf(Ah * (s_cum[j] - s_cum[i])) * s_dt[i];
-        s_W[j][i] = wv;
-      }
-#pragma unroll
-      for (int u = 0; u < (Q * MN) / NT; ++u) {   // Gamma_j C_j in place
-        const int idx = tid + u * NT, j = idx >> 7, nn = idx & 127;
-        s_C[j][nn] *= s_gam[j];
+        if (li <= j)
+          wv = (s_E[0][j][li] + s_E[1][j][li] + s_E[2][j][li] + s_E[3][j][li]) *
+               expf(Ah * (cj - cum)) * dtl;
+        s_W[j][li] = wv;
       }
       __syncthreads();
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {   // Gamma_j h C_j, contracting over n
-        const f32x4 cg = ld4(&s_C[li][16 * t + 4 * lq]);
-        y = mfma4(cg.x, acc[t].x, y);
-        y = mfma4(cg.y, acc[t].y, y);
-        y = mfma4(cg.z, acc[t].z, y);
-        y = mfma4(cg.w, acc[t].w, y);
-      }
+      for (int r = 0; r < 4; ++r)     // Gamma_j h C_j
+        y[r] *= expf(Ah * __shfl(cum, 4 * lq + r));
 #pragma unroll
       for (int s = 0; s < 4; ++s)     // + sum_i W[j][i] x_i[p]
         y = mfma4(s_W[li][4 * s + lq], s_x[4 * s + lq][p], y);
@@ -240,10 +255,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void m2
       }
     }
     {  // fold: h <- Gamma_{Q-1} h + sum_i fw_i x_i B_i^T
-      const float gq = expf(Ah * s_cum[Q - 1]);
+      const float gq = expf(Ah * tot);
       float bx[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) bx[s] = s_fw[4 * s + lq] * s_x[4 * s + lq][p];
+      for (int s = 0; s < 4; ++s) bx[s] = __shfl(fwl, 4 * s + lq) * s_x[4 * s + lq][p];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         acc[t] *= gq;
@@ -473,8 +488,15 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(4))) void g
     {  // Lm and M, one element per thread of the first 256
       if (tid < Q * Q) {
         const int t = tid >> 4, i = tid & 15;
-        float g = 1.f;   // G_{i+1..t}
-        for (int m = i + 1; m <= t; ++m) g *= s_al[m];
+        // G_{i+1..t}: the row of 16 lanes (one t, i = lane) takes the product
+        // of alpha_m over m > i of (alpha_m for m <= t, else 1) by a DPP
+        // suffix scan
+        float g = i <= t ? s_al[i] : 1.f;
+        g *= row_shl1<1>(g);
+        g *= row_shl1<2>(g);
+        g *= row_shl1<4>(g);
+        g *= row_shl1<8>(g);
+        g = row_shl1<1>(g);
         const float kk = s_P[0][t][i] + s_P[1][t][i] + s_P[2][t][i] + s_P[3][t][i];
         s_L[t][i] = i < t ? s_be[t] * g * kk : 0.f;
         if (out) {

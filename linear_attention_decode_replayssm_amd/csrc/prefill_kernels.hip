@@ -442,7 +442,8 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(4))) void g
   __shared__ __attribute__((aligned(16))) float s_v[Q][GPITCH];
   __shared__ float s_al[Q], s_be[Q], s_gp[Q], s_gs[Q];
   __shared__ float s_P[8][Q][Q + 1];   // partial K K^T (waves 0-3) and Q K^T (4-7)
-  __shared__ float s_L[Q][Q + 1], s_M[Q][Q + 1], s_T[Q][Q + 1];
+  __shared__ __attribute__((aligned(16))) float s_L[Q][Q + 4];   // rows read as float4
+  __shared__ float s_M[Q][Q + 1], s_T[Q][Q + 1];
   __shared__ float s_red[GNT / 64];
 
   for (int c = c0; c < nch; ++c) {
@@ -511,14 +512,19 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(4))) void g
       float col[Q];
 #pragma unroll
       for (int t = 0; t < Q; ++t) {
-        float v = t == j ? 1.f : 0.f;
-        if (t > j) {
-          float acc2 = 0.f;
+        float lt[Q];   // row t of Lm, entries 0 .. t-1, in 16-byte reads
 #pragma unroll
-          for (int i = 0; i < t; ++i) acc2 += s_L[t][i] * col[i];   // col[i] = 0 for i < j
-          v = -acc2;
+        for (int i = 0; i < t; i += 4) {
+          const f32x4 r4 = ld4(&s_L[t][i]);
+          lt[i] = r4.x;
+          if (i + 1 < Q) lt[i + 1] = r4.y;
+          if (i + 2 < Q) lt[i + 2] = r4.z;
+          if (i + 3 < Q) lt[i + 3] = r4.w;
         }
-        col[t] = v;
+        float acc2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < t; ++i) acc2 += lt[i] * col[i];   // col[i] = 0 for i < j
+        col[t] = t == j ? 1.f : (t > j ? -acc2 : 0.f);
       }
 #pragma unroll
       for (int t = 0; t < Q; ++t) s_T[t][j] = col[t];

@@ -100,6 +100,23 @@ __device__ __forceinline__ int tile_index() {
   return id;
 }
 
+// As tile_index, for a grid of whole sequences of tps tiles each: every XCD
+// receives tps / 8 consecutive tiles of every sequence instead of whole
+// sequences, so that work that differs from sequence to sequence (the fold
+// of a due buffer) is spread evenly over the XCDs.  At batch 256 it made the
+// standalone fp32 commits 9-13% faster, the chain verifies that fold due
+// buffers 3-6%, the fused Mamba-2 step 3% and the fp32 eager
+// read-modify-write kernels 4-8%; the plain replay step, the tree verifies
+// of 8 drafts and the fused fp32 GDN step stayed with whole sequences, which
+// measured as fast or faster for them.
+__device__ __forceinline__ int tile_index_split(int tps) {
+  const int id = blockIdx.x, n = gridDim.x;
+  if ((n & 7) != 0 || (tps & 7) != 0) return tile_index();
+  const int per = tps >> 3, li = id >> 3;
+  const int b = li / per;
+  return b * tps + (id & 7) * per + (li - b * per);
+}
+
 // ---- reduction partners ----------------------------------------------------
 // Value of a partner lane for reductions over lane bit M.  The partner has the
 // opposite bit M and the same higher bits; its lower bits may differ.  That is

@@ -49,13 +49,14 @@ struct Geo {
 };
 
 // Workgroup -> (sequence b, head h, row block): row blocks of a head are
-// adjacent, heads of a sequence are adjacent (tile_index keeps runs of tiles
-// on one XCD).
-template <int LPR, int ROWS>
+// adjacent, heads of a sequence are adjacent.  SPLIT: every XCD takes an
+// eighth of each sequence's tiles (tile_index_split), else whole sequences
+// (tile_index); each kernel takes the order that measured faster for it.
+template <int LPR, int ROWS, bool SPLIT = false>
 __device__ __forceinline__ Geo geometry(const GdnArgs& a) {
   constexpr int PARTS = DV / ROWS;
   Geo q;
-  const int tile = tile_index();
+  const int tile = SPLIT ? tile_index_split(a.H * PARTS) : tile_index();
   const int hp = tile / PARTS;
   q.row0 = (tile - hp * PARTS) * ROWS;
   q.b = hp / a.H;
@@ -550,7 +551,7 @@ __global__ __launch_bounds__((LP != 0 ? 512 : step_threads<EB>())) void gdn_step
   constexpr int ROWS = LP != 0 ? DV : step_rows<EB>(), PARTS = DV / ROWS;
   using Gm = LpGeo<EB, NTH, ROWS>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPL = Gm::RPL, NLD = Gm::NLD;
-  const Geo q = geometry<LPR, ROWS>(a);
+  const Geo q = geometry<LPR, ROWS, !(FUSED && LP == 0)>(a);
   const int cap = a.cap;
 
   const int len = a.len[q.b];
@@ -643,7 +644,7 @@ __global__ __launch_bounds__(NTH) void gdn_commit_kernel(GdnArgs a) {
   using Gm = LpGeo<4, NTH, ROWS>;
   constexpr int RPL = Gm::RPL, NLD = Gm::NLD;
   static_assert(SCHEME == kSchemeF32 || ROWS == DV, "low-precision copies need whole heads");
-  const Geo q = geometry<Gm::LPR, ROWS>(a);
+  const Geo q = geometry<Gm::LPR, ROWS, SCHEME == kSchemeF32>(a);
   if (a.mask != nullptr && a.mask[q.b] == 0) return;   // uniform for the sequence
   const int len = a.len[q.b];
   const int64_t pos = a.pos[q.b];
@@ -706,7 +707,7 @@ __global__ __launch_bounds__(512) void gdn_verify_kernel(GdnArgs a) {
   using Gm = LpGeo<EB, NTH, ROWS>;
   constexpr int EPL = Gm::EPL, LPR = Gm::LPR, RPL = Gm::RPL, NLD = Gm::NLD;
   static_assert(NPAD <= NTH / 64 && NPAD * (DK / 4) <= NTH, "one wave per draft position");
-  const Geo q = geometry<LPR, ROWS>(a);
+  const Geo q = geometry<LPR, ROWS, NPAD != 8 || COMMIT>(a);
   const int cap = a.cap, n = a.n_pos;
 
   const int64_t pos = a.pos[q.b];
@@ -850,7 +851,7 @@ __global__ __launch_bounds__(LP == 0 ? kStepThreads : 512) void gdn_eager_kernel
   constexpr int NTH = LP == 0 ? kStepThreads : 512, ROWS = LP == 0 ? kStepRows : DV;
   using Gm = LpGeo<4, NTH, ROWS>;
   constexpr int RPL = Gm::RPL, NLD = Gm::NLD, LPR = Gm::LPR;
-  const Geo q = geometry<LPR, ROWS>(a);
+  const Geo q = geometry<LPR, ROWS, LP == 0>(a);
   const f32x4 kv = ld4(a.k + q.unit * DK + q.cl * 4);
   const f32x4 qv = ld4(a.q + q.unit * DK + q.cl * 4);
   const float al = a.alpha[q.unit], be = a.beta[q.unit];

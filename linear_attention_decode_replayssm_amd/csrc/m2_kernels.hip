@@ -101,12 +101,15 @@ struct Geo {
 };
 
 // Workgroup -> (sequence b, first head h of HPW consecutive heads of one
-// group).
-template <int HPW = 1>
+// group).  SPLIT: every XCD takes an eighth of each sequence's heads (one
+// group of 10 at 80 heads and 8 groups; tile_index_split), else whole
+// sequences (tile_index); each kernel takes the order that measured faster
+// for it.
+template <int HPW = 1, bool SPLIT = false>
 __device__ __forceinline__ Geo geometry(const M2Args& a) {
   Geo q;
-  const int tile = tile_index();
   const int hb = a.H / HPW;
+  const int tile = SPLIT ? tile_index_split(hb) : tile_index();
   q.b = tile / hb;
   q.h = (tile - q.b * hb) * HPW;
   q.g = q.h / (a.H / a.G);
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
   static_assert(LP == 0 || FUSED, "a low-precision image is written only by the fused commit");
   static_assert(HPW <= 16, "dt of head hl is loaded by lane hl of an entry's 16 lanes");
   static_assert(MAXL % 16 == 0 && MAXL * HPW <= NT, "entries per 16-lane group");
-  const Geo q = geometry<HPW>(a);
+  const Geo q = geometry<HPW, FUSED || EB != 4>(a);
   const int cap = a.cap;
   float* ck = a.ckpt + q.unit * (P * N);
 
@@ -383,7 +386,7 @@ __global__ __launch_bounds__(NT) void m2_step_kernel(M2Args a) {
 // One workgroup holds a whole head, so the E4M3 scale's amax is local.
 template <int SCHEME, int LP, int MAXL = kMaxCap>
 __global__ __launch_bounds__(NT) void m2_commit_kernel(M2Args a) {
-  const Geo q = geometry(a);
+  const Geo q = geometry<1, SCHEME == kSchemeF32>(a);
   const int cap = a.cap;
   if (a.mask != nullptr && a.mask[q.b] == 0) return;   // uniform for the sequence
   const int len = a.len[q.b];
@@ -509,7 +512,7 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   static_assert(!MF || (EB == 4 && NPAD >= 4), "matrix-core contraction: fp32, 4 or 8 drafts");
   constexpr bool W16 = EB == 4 && NPAD == 8 && !MF;
   using Gm = RdGeo<EB>;
-  const Geo q = geometry(a);
+  const Geo q = geometry<1, NPAD != 8 || COMMIT>(a);
   const int cap = a.cap, n = a.n_pos;
   const int64_t pos = a.pos[q.b];
   const RolledLen rl = rolled_len(a.len[q.b], pos, cap, a.n_reject, q.b);
@@ -992,7 +995,7 @@ __global__ __launch_bounds__(NT) void m2_append_path_kernel(M2Args a) {
 // step feeds the next one.
 template <int LP>
 __global__ __launch_bounds__(NT) void m2_eager_kernel(M2Args a) {
-  const Geo q = geometry(a);
+  const Geo q = geometry<1, LP == 0>(a);
   float* ck = a.ckpt + q.unit * (P * N);
   char* lp = reinterpret_cast<char*>(a.ckpt_lp) + q.unit * (P * N) * (LP == kLpBf16 ? 2 : 1);
   float* lps = a.lp_scale ? a.lp_scale + q.unit : nullptr;

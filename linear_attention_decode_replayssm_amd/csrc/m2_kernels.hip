@@ -597,17 +597,19 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
 
   constexpr int CP = N + 4;   // padded LDS row pitch of C_j and the MF tile
   __shared__ __attribute__((aligned(16))) float s_C[NPAD][CP];
-  __shared__ __attribute__((aligned(16))) float s_Ba[NPAD][N];   // drafts' B, x, dt
-  __shared__ float s_xa[NPAD][P];                                // for the append
+  // entries' B and x: the drafts' (the append, and the outputs' D x_j) and,
+  // with COMMIT, the buffered entries' for the fold, in one array of entries
+  // 0 .. len+n-1 (the buffer first); without COMMIT the drafts only
+  constexpr int EA = COMMIT ? kMaxCap : NPAD;
+  __shared__ __attribute__((aligned(16))) float s_Be[EA][N];
+  __shared__ __attribute__((aligned(16))) float s_xe[EA][P];
+  const int e0 = COMMIT ? len : 0;   // row of draft 0
   __shared__ float s_dta[NPAD];
   __shared__ float s_dt[kMaxCap];
   __shared__ float s_e[NPAD][kMaxCap];
   __shared__ float s_w[NPAD][kMaxCap];
   __shared__ float s_gam[NPAD];
   __shared__ float s_yb[QD][NPAD][P];
-  // fused commit: the buffered entries' x_i and B_i, parked from the prologue
-  __shared__ __attribute__((aligned(16))) float s_xf[COMMIT ? kMaxCap : 1][P];
-  __shared__ __attribute__((aligned(16))) float s_Bf[COMMIT ? kMaxCap : 1][N];
   __shared__ float s_fw[COMMIT ? kMaxCap : 1];
   __shared__ float s_gbuf;
 #pragma unroll
@@ -620,26 +622,26 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
     if (fold) {   // uniform
       if (ei < len) {
 #pragma unroll
-        for (int e = 0; e < SEG / 4; ++e) st4(&s_Bf[ei][sgm * SEG + 4 * e], bseg[e]);
+        for (int e = 0; e < SEG / 4; ++e) st4(&s_Be[ei][sgm * SEG + 4 * e], bseg[e]);
       }
 #pragma unroll
       for (int m = 0; m < XPT; ++m) {
         const int i = qd + m * QD;
-        if (i < len) s_xf[i][p] = xv[m];
+        if (i < len) s_xe[i][p] = xv[m];
       }
     }
   }
   if (a.append) {   // uniform: the drafts' own rows, kept for the append below
     if (ei >= len && ei < LT) {
 #pragma unroll
-      for (int e = 0; e < SEG / 4; ++e) st4(&s_Ba[ei - len][sgm * SEG + 4 * e], bseg[e]);
+      for (int e = 0; e < SEG / 4; ++e) st4(&s_Be[ei - len + e0][sgm * SEG + 4 * e], bseg[e]);
       if (sgm == 0) s_dta[ei - len] = dti;
     }
   }
 #pragma unroll
   for (int m = 0; m < XPT; ++m) {   // the drafts' x_j (append, and the outputs' D x_j)
     const int i = qd + m * QD;
-    if (i >= len && i < LT) s_xa[i - len][p] = xv[m];
+    if (i >= len && i < LT) s_xe[i - len + e0][p] = xv[m];
   }
   indices_consumed(len, pos);   // its barrier also publishes the LDS above
   const uint32_t arrived = arrive_early(a.arrive, q.b, len, pos, a.idx_ro);
@@ -690,7 +692,7 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
       }
     }
     __syncthreads();
-    {  // sum_i w_{j,i} x_i[p] (the outputs add D x_j[p] from s_xa)
+    {  // sum_i w_{j,i} x_i[p] (the outputs add D x_j[p] from s_xe)
       float acc[NPAD];
 #pragma unroll
       for (int j = 0; j < NPAD; ++j) acc[j] = 0.f;
@@ -751,7 +753,7 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
           float yb = 0.f;
 #pragma unroll
           for (int g = 0; g < QD; ++g) yb += s_yb[g][j][pr];
-          yv = s_gam[j] * acc[r] + yb + Dh * s_xa[j][pr];
+          yv = s_gam[j] * acc[r] + yb + Dh * s_xe[e0 + j][pr];
         } else {
           yv = __builtin_nanf("");
         }
@@ -787,7 +789,7 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
         float yb = 0.f;
 #pragma unroll
         for (int g = 0; g < QD; ++g) yb += s_yb[g][j][pr];
-        yv = s_gam[j] * d[jj] + yb + Dh * s_xa[j][pr];
+        yv = s_gam[j] * d[jj] + yb + Dh * s_xe[e0 + j][pr];
       } else {
         yv = __builtin_nanf("");
       }
@@ -848,7 +850,7 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
               float yb = 0.f;
 #pragma unroll
               for (int g = 0; g < QD; ++g) yb += s_yb[g][j][pr];
-              yv = s_gam[j] * (scale * res[c][jj]) + yb + Dh * s_xa[j][pr];
+              yv = s_gam[j] * (scale * res[c][jj]) + yb + Dh * s_xe[e0 + j][pr];
             } else {
               yv = __builtin_nanf("");
             }
@@ -877,11 +879,11 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
       if constexpr (W16) {   // hv[2 k + hf]: row tid/16 + 16 k, column half hf
         const int c16 = q.tid & 15, rw = q.tid >> 4;
         for (int i = 0; i < len; ++i) {
-          const f32x4 b0 = ld4(&s_Bf[i][4 * c16]), b1 = ld4(&s_Bf[i][64 + 4 * c16]);
+          const f32x4 b0 = ld4(&s_Be[i][4 * c16]), b1 = ld4(&s_Be[i][64 + 4 * c16]);
           const float w = s_fw[i];
 #pragma unroll
           for (int k = 0; k < NLD / 2; ++k) {
-            const float xw = w * s_xf[i][rw + 16 * k];
+            const float xw = w * s_xe[i][rw + 16 * k];
             hv[2 * k] += xw * b0;
             hv[2 * k + 1] += xw * b1;
           }
@@ -894,10 +896,10 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
         }
       } else {   // the fp32 read geometry is the tile geometry
         for (int i = 0; i < len; ++i) {
-          const f32x4 bi = ld4(&s_Bf[i][q.c4 * 4]);
+          const f32x4 bi = ld4(&s_Be[i][q.c4 * 4]);
           const float w = s_fw[i];
 #pragma unroll
-          for (int k = 0; k < NLD; ++k) hv[k] += (w * s_xf[i][rowk(k)]) * bi;
+          for (int k = 0; k < NLD; ++k) hv[k] += (w * s_xe[i][rowk(k)]) * bi;
         }
         float* ck = a.ckpt + q.unit * (P * N) + q.c4 * 4;
 #pragma unroll
@@ -909,10 +911,10 @@ __global__ __launch_bounds__(NT) void m2_verify_kernel(M2Args a) {
   if (ok && a.append) {   // append the drafts (a chain) from LDS
     for (int j = 0; j < n; ++j) {
       const int s = ring_slot(slot0, len + j, cap);
-      if (q.tid < P) a.ring_x[(q.unit * cap + s) * P + q.tid] = s_xa[j][q.tid];
+      if (q.tid < P) a.ring_x[(q.unit * cap + s) * P + q.tid] = s_xe[e0 + j][q.tid];
       if (q.tid == 0) a.ring_dt[q.unit * cap + s] = s_dta[j];
       if ((q.h % (a.H / a.G)) == 0 && q.tid < N)
-        a.ring_B[(q.gunit * cap + s) * N + q.tid] = s_Ba[j][q.tid];
+        a.ring_B[(q.gunit * cap + s) * N + q.tid] = s_Be[e0 + j][q.tid];
     }
   }
 

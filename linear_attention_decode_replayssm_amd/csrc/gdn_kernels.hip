@@ -323,9 +323,11 @@ __device__ __forceinline__ float carry_acc(const EntrySmem& s, int hi, int cl, i
 template <int ROWS>
 struct FoldSmem {
   float G[kMaxCap + 1][kMaxCap + 1];   // G[a][e] = prod_{j=a}^{e-1} alpha_j, a <= e <= L
-  float gram[kMaxCap][kMaxCap + 1];    // k_m . k_i
+  union {                              // gram is dead once Lc is formed
+    float gram[kMaxCap][kMaxCap + 1];  // k_m . k_i
+    float P1[kMaxCap][kMaxCap + 1];    //  G_{i+1..} T[i][j] beta_j
+  };
   float Lc[kMaxCap][kMaxCap + 1];      // G_{m+1..i-1} (k_m . k_i), m < i
-  float P1[kMaxCap][kMaxCap + 1];      //  G_{i+1..} T[i][j] beta_j
   float P2[kMaxCap][kMaxCap + 1];      // -G_{i+1..} T[i][j] beta_j alpha_j G_{..j-1}
   float WU[ROWS][kMaxCap + 1];         // S_c k_i of the workgroup's rows, then U'_i
   float red[16];
@@ -395,8 +397,9 @@ __device__ __forceinline__ void coef_t(const EntrySmem& es, int L, int tid, Fold
 // W = S_c K^T for the workgroup's rows, CH entries at a time (FMA dots,
 // transposed cross-lane reduction), stored to sm.WU.  CH = 2 keeps the
 // partial dots to 2 NLD registers beside the 4 NLD of the tile, which gives
-// the whole-head fold kernels a third workgroup per CU; the fused fp32 and
-// DUAL bf16 steps and the DUAL bf16 commit measured faster with CH = 4.
+// the whole-head fold kernels a third workgroup per CU and the half-head fp32
+// fused step and commit a sixth (with gram and P1 sharing LDS); the DUAL bf16
+// step and commit measured faster with CH = 4.
 template <int NTH, int ROWS, int NLD, int CH>
 __device__ __forceinline__ void fold_w(const f32x4 (&hv)[NLD], const EntrySmem& es, int L,
                                        const Geo& q, FoldSmem<ROWS>& sm) {
@@ -597,7 +600,7 @@ __global__ __launch_bounds__((LP != 0 ? 512 : step_threads<EB>())) void gdn_step
       for (int k = 0; k < NLD; ++k)
         hv[k] = f32x4{__uint_as_float(raw[k].x), __uint_as_float(raw[k].y),
                       __uint_as_float(raw[k].z), __uint_as_float(raw[k].w)};
-      fold_apply<NTH, ROWS, NLD, LP != kLpE4m3 ? 4 : 2>(hv, es, L, q.row0, q, sm);
+      fold_apply<NTH, ROWS, NLD, LP == kLpBf16 ? 4 : 2>(hv, es, L, q.row0, q, sm);
       const f32x4 q4 = {qv[0], qv[1], qv[2], qv[3]};
 #pragma unroll
       for (int k = 0; k < NLD; ++k) d[k] = dot4(hv[k], q4);

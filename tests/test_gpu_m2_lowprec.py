@@ -119,10 +119,11 @@ def _bound(A, h_c, C_t, gam, lp):
 
 
 @pytest.mark.parametrize("lp", LPS, ids=LP_IDS)
-@pytest.mark.parametrize("H,G", [(8, 2), (9, 3)], ids=["4_heads_per_group", "3_heads_per_group"])
+@pytest.mark.parametrize("H,G", [(8, 2), (9, 3), (10, 2)],
+                         ids=["4_heads_per_group", "3_heads_per_group", "5_heads_per_group"])
 def test_dual_one_quantisation_bound(lp, H, G):
     """Also covers both read layouts of the E4M3 step: two heads per
-    workgroup (even heads per group) and one (odd)."""
+    workgroup (even heads per group) and one (odd: three or five)."""
     T, b, interval = 40, 4, 8
     A, D = syn.m2_params(112, H)
     h0 = syn.m2_state0(112, b, H, P, N)

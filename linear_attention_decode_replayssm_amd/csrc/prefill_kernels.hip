@@ -184,6 +184,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void m2
   __shared__ float s_E[4][Q][Q + 1];
   __shared__ float s_W[Q][Q + 1];
   __shared__ float s_red[NT / 64];
+  // a chunk's outputs, staged so that each token's row of P outputs is
+  // written as 16-byte stores after the chunk's last barrier
+  __shared__ __attribute__((aligned(16))) float s_y[Q][MP];
+  int yc = -1, yn = 0;   // chunk and token count staged in s_y, -1: none
 
   for (int c = c0; c < nch; ++c) {
     st4(&s_x[tid >> 4][4 * (tid & 15)], f.x);
@@ -251,8 +255,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void m2
 #pragma unroll
       for (int r = 0; r < 4; ++r) {   // y[r] is token 4 lq + r, row p
         const int j = 4 * lq + r;
-        if (j < n) a.y[(long)(c * Q + j) * sx + unit * MP + p] = y[r] + Dh * s_x[j][p];
+        s_y[j][p] = y[r] + Dh * s_x[j][p];
       }
+      yc = c;
+      yn = n;
     }
     {  // fold: h <- Gamma_{Q-1} h + sum_i fw_i x_i B_i^T
       const float gq = expf(Ah * tot);
@@ -267,6 +273,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void m2
       }
     }
     __syncthreads();   // every read of this chunk's LDS is done
+    if (yc == c) {   // token tid / 16, 16 bytes per thread
+      const int j = tid >> 4, c4 = tid & 15;
+      if (j < yn) st4(a.y + (long)(c * Q + j) * sx + unit * MP + 4 * c4, ld4(&s_y[j][4 * c4]));
+    }
   }
 
   if constexpr (SCHEME != kSchemeShared) {
@@ -445,6 +455,10 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(4))) void g
   __shared__ __attribute__((aligned(16))) float s_L[Q][Q + 4];   // rows read as float4
   __shared__ float s_M[Q][Q + 1], s_T[Q][Q + 1];
   __shared__ float s_red[GNT / 64];
+  // a chunk's outputs, staged so that each token's row of dv outputs is
+  // written as 16-byte stores after the chunk's last barrier
+  __shared__ __attribute__((aligned(16))) float s_o[Q][GD];
+  int oc_ = -1, on_ = 0;   // chunk and token count staged in s_o, -1: none
 
   for (int c = c0; c < nch; ++c) {
     {
@@ -566,12 +580,10 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(4))) void g
       for (int r = 0; r < 4; ++r) o[r] = s_gp[4 * lq + r] * oc[r];
 #pragma unroll
       for (int r = 0; r < 4; ++r) o = mfma4(s_M[li][4 * lq + r], u[r], o);
-      const long so = (long)a.batch * a.H * GD;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 4 * lq + r;
-        if (t < n) a.o[(long)(c * Q + t) * so + unit * GD + row] = o[r];
-      }
+      for (int r = 0; r < 4; ++r) s_o[4 * lq + r][row] = o[r];
+      oc_ = c;
+      on_ = n;
     }
     {  // fold: S <- Gp_{Q-1} S + sum_i g_i u_i k_i^T
       const float gall = s_gp[Q - 1];
@@ -586,6 +598,11 @@ __global__ __launch_bounds__(GNT) __attribute__((amdgpu_waves_per_eu(4))) void g
       }
     }
     __syncthreads();
+    if (oc_ == c) {   // token tid / 32, 16 bytes per thread
+      const int t = tid >> 5, c4 = tid & 31;
+      if (t < on_)
+        st4(a.o + (long)(c * Q + t) * ((long)a.batch * a.H * GD) + unit * GD + 4 * c4, ld4(&s_o[t][4 * c4]));
+    }
   }
 
   if constexpr (SCHEME != kSchemeShared) {

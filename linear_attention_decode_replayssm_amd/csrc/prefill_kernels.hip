@@ -105,7 +105,7 @@ struct M2Pre {
 // Left alone the compiler gives this kernel ~220 registers (two waves per
 // SIMD); asked for at least three waves it needs no spills and runs ~1.2x
 // faster.  The fp32 and bf16 forms come out at 126-128 registers, which
-// leaves room for four workgroups per CU (27 KB of LDS each).
+// leaves room for four workgroups per CU (31 KB of LDS each).
 template <int SCHEME, int LP>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3))) void m2_prefill_kernel(M2Args a) {
   const int tile = tile_index();

@@ -6,8 +6,8 @@ Each translation unit is compiled to an object in ``_build/`` (in parallel),
 then linked into ``librssm.so`` next to this file.  ``--isa`` additionally
 keeps the device assembly of every kernel under ``_build/isa/``; ``--define
 NAME`` passes -DNAME to every translation unit (RSSM_M2_VERIFY_MFMA selects
-the matrix-core variant of the Mamba-2 verify contraction, kept for
-measurement).
+the matrix-core variant of the Mamba-2 verify contraction, RSSM_XCD_WHOLE the
+whole-sequence XCD order for every kernel; both kept for measurement).
 
 Packed fp32 instructions are disabled for all device code
 (``-target-feature -packed-fp32-ops``): the compiler would otherwise form

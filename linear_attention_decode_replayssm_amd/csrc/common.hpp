@@ -109,9 +109,17 @@ __device__ __forceinline__ int tile_index() {
 // read-modify-write kernels 4-8%; the plain replay step, the tree verifies
 // of 8 drafts and the fused fp32 GDN step stayed with whole sequences, which
 // measured as fast or faster for them.
+// Built with -DRSSM_XCD_WHOLE every kernel takes whole sequences per XCD: the
+// comparison build for the per-kernel choice.
+#ifdef RSSM_XCD_WHOLE
+constexpr bool kXcdSplit = false;
+#else
+constexpr bool kXcdSplit = true;
+#endif
+
 __device__ __forceinline__ int tile_index_split(int tps) {
   const int id = blockIdx.x, n = gridDim.x;
-  if ((n & 7) != 0 || (tps & 7) != 0) return tile_index();
+  if (!kXcdSplit || (n & 7) != 0 || (tps & 7) != 0) return tile_index();
   const int per = tps >> 3, li = id >> 3;
   const int b = li / per;
   return b * tps + (id & 7) * per + (li - b * per);
